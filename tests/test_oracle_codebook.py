@@ -1,0 +1,180 @@
+"""Pins for the oracle's Lloyd-Max codebook (tqref_codebook).
+
+What fixes it, independently of the oracle's own code:
+* the printed distortion per coordinate (golden fixture, Lloyd-Max Codebook
+  section of the GB10 benchmark page);
+* the closed form at one bit: c = +-sqrt(2/pi)/sqrt(d), D*d = 1 - 2/pi;
+* Max's published optimum quantizer for the unit Gaussian (Max 1960, Table 1):
+  2-bit outputs 0.4528, 1.510; 3-bit 0.2451, 0.7560, 1.344, 2.152;
+* optimality checked with scipy quadrature (not the oracle's closed forms):
+  every centroid is its cell's conditional mean and perturbations never lower D;
+* brute force: dynamic programming over all contiguous partitions of a fine
+  quantile grid of the law finds the global optimum, which must sit on the
+  solver's codebook.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy import integrate, stats
+
+import oracle
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "printed_values.json")))
+
+
+@pytest.mark.parametrize("case", GOLDEN["distortion_per_coord"]["cases"])
+def test_printed_distortion(case):
+    cb = oracle.codebook(case["d"], case["bits"])
+    assert f"{cb.dist_exact:.6f}" == case["printed"]
+    # the stored (fp16-rounded) codebook prints the same value
+    assert f"{cb.dist_stored:.6f}" == case["printed"]
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_one_bit_closed_form(d):
+    cb = oracle.codebook(d, 1)
+    c = np.sqrt(2 / np.pi) / np.sqrt(d)
+    np.testing.assert_allclose(cb.c_exact, [-c, c], rtol=1e-13)
+    np.testing.assert_allclose(cb.dist_exact * d, 1 - 2 / np.pi, rtol=1e-12)
+
+
+MAX_TABLE = {2: [0.4528, 1.510], 3: [0.2451, 0.7560, 1.344, 2.152]}
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_max_table(bits):
+    cb = oracle.codebook(128, bits)
+    half = cb.c_exact[len(cb.c_exact) // 2:] * np.sqrt(128)
+    np.testing.assert_allclose(half, MAX_TABLE[bits], atol=6e-4)
+
+
+@pytest.mark.parametrize("d,bits", [(64, 2), (128, 3), (256, 4), (128, 4), (32, 2)])
+def test_stored_codebook_rules(d, bits):
+    cb = oracle.codebook(d, bits)
+    L = 1 << bits
+    c = cb.centroids.astype(np.float64)
+    # fp16-representable and the fp16 rounding of the exact solution
+    assert np.array_equal(cb.centroids.astype(np.float16).astype(np.float32), cb.centroids)
+    assert np.array_equal(cb.c_exact.astype(np.float32).astype(np.float16).astype(np.float32),
+                          cb.centroids)
+    # symmetric, strictly increasing
+    assert np.array_equal(c, -c[::-1])
+    assert np.all(np.diff(c) > 0)
+    # boundaries: fp32 of the exact midpoints of the stored centroids
+    mid = 0.5 * (c[:-1] + c[1:])
+    assert np.array_equal(cb.boundaries, mid.astype(np.float32))
+    assert cb.boundaries[L // 2 - 1] == 0.0
+
+
+def _quad_moments(sigma, a, b):
+    f = stats.norm(0, sigma).pdf
+    m0 = integrate.quad(f, a, b, epsabs=0, epsrel=1e-12, limit=200)[0]
+    m1 = integrate.quad(lambda y: y * f(y), a, b, epsabs=0, epsrel=1e-12, limit=200)[0]
+    return m0, m1
+
+
+def _quad_distortion(sigma, c, t):
+    f = stats.norm(0, sigma).pdf
+    edges = np.concatenate([[-np.inf], t, [np.inf]])
+    D = 0.0
+    for l in range(len(c)):
+        D += integrate.quad(lambda y: (y - c[l]) ** 2 * f(y), edges[l], edges[l + 1],
+                            epsabs=0, epsrel=1e-11, limit=200)[0]
+    return D
+
+
+@pytest.mark.parametrize("d,bits", [(128, 2), (128, 3), (128, 4)])
+def test_centroid_condition_by_quadrature(d, bits):
+    cb = oracle.codebook(d, bits)
+    sigma = 1 / np.sqrt(d)
+    c = cb.c_exact
+    t = 0.5 * (c[:-1] + c[1:])
+    edges = np.concatenate([[-np.inf], t, [np.inf]])
+    for l in range(len(c)):
+        m0, m1 = _quad_moments(sigma, edges[l], edges[l + 1])
+        assert abs(m1 / m0 - c[l]) < 1e-9 * sigma
+    # analytic distortion agrees with independent quadrature
+    assert abs(_quad_distortion(sigma, c, t) - cb.dist_exact) < 1e-10 * cb.dist_exact * 10
+
+
+@pytest.mark.parametrize("d,bits", [(128, 2), (128, 3)])
+def test_perturbations_never_lower_distortion(d, bits):
+    cb = oracle.codebook(d, bits)
+    sigma = 1 / np.sqrt(d)
+    c0 = cb.c_exact.copy()
+    D0 = _quad_distortion(sigma, c0, 0.5 * (c0[:-1] + c0[1:]))
+    rng = np.random.default_rng(7)
+    for _ in range(12):
+        c = np.sort(c0 + rng.normal(0, 0.02 * sigma, size=c0.shape))
+        D = _quad_distortion(sigma, c, 0.5 * (c[:-1] + c[1:]))
+        assert D > D0
+    # moving one boundary alone also raises D
+    for l in range(len(c0) - 1):
+        for eps in (-0.01 * sigma, 0.01 * sigma):
+            t = 0.5 * (c0[:-1] + c0[1:])
+            t[l] += eps
+            assert _quad_distortion(sigma, c0, t) > D0
+
+
+def _dp_partition(x, L):
+    """Global optimum of squared error over contiguous partitions of sorted,
+    equally weighted points x into L cells (dynamic programming, numpy)."""
+    n = len(x)
+    S1 = np.concatenate([[0.0], np.cumsum(x)])
+    S2 = np.concatenate([[0.0], np.cumsum(x * x)])
+    i = np.arange(n + 1)
+
+    def cost_to(j):  # cost of cells (i, j] for all i < j
+        cnt = (j - i[:j]).astype(np.float64)
+        m1 = S1[j] - S1[:j]
+        return (S2[j] - S2[:j]) - m1 * m1 / cnt
+
+    best = np.full(n + 1, np.inf)
+    best[0] = 0.0
+    arg = np.zeros((L + 1, n + 1), dtype=np.int64)
+    for k in range(1, L + 1):
+        nb = np.full(n + 1, np.inf)
+        for j in range(1, n + 1):
+            v = best[:j] + cost_to(j)
+            a = int(np.argmin(v))
+            nb[j] = v[a]
+            arg[k, j] = a
+        best = nb
+    cuts = [n]
+    for k in range(L, 0, -1):
+        cuts.append(arg[k, cuts[-1]])
+    cuts = cuts[::-1]
+    cents = np.array([x[cuts[k]:cuts[k + 1]].mean() for k in range(L)])
+    return best[n] / n, cents
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_global_optimum_by_brute_force_on_grid(bits):
+    """Brute force: the best partition of a fine quantile grid of N(0, 1/d)
+    lands on the solver's codebook (no distant better configuration)."""
+    d = 128
+    sigma = 1 / np.sqrt(d)
+    n = 1200
+    x = stats.norm(0, sigma).ppf((np.arange(n) + 0.5) / n)
+    D_grid, c_grid = _dp_partition(x, 1 << bits)
+    cb = oracle.codebook(d, bits)
+    assert np.max(np.abs(c_grid - cb.c_exact)) < 0.01 * sigma
+    # the solver's codebook used on the same grid is within 0.1% of the grid optimum
+    t = 0.5 * (cb.c_exact[:-1] + cb.c_exact[1:])
+    k = np.searchsorted(t, x, side="left")
+    D_sol = np.mean((x - cb.c_exact[k]) ** 2)
+    assert D_grid <= D_sol * (1 + 1e-12)
+    assert D_sol < D_grid * (1 + 1e-3)
+
+
+def test_codebook_converges_for_all_widths():
+    for d in (64, 128, 256):
+        for bits in (1, 2, 3, 4, 5, 6):
+            cb = oracle.codebook(d, bits)
+            assert cb.iters > 0
+            # high-rate check: D*d approaches the Panter-Dite constant sqrt(3) pi / 2 * 4^-b
+            if bits >= 5:
+                pd = np.sqrt(3) * np.pi / 2 * 4.0 ** (-bits)
+                assert 0.8 < cb.dist_exact * d / pd < 1.05

@@ -1,0 +1,155 @@
+"""Pins for the oracle's quantizer (rotation, codes, packing, QJL signs, scalars).
+
+Independent references used here:
+* ``scipy.linalg.hadamard`` (Sylvester construction, natural order) for H;
+* one-hot inputs, whose rotated image is a known Hadamard column, so codes,
+  packed words and residual signs are predictable by hand;
+* brute force over all code vectors for tiny d;
+* a projection matrix that is a cyclic shift, which fixes the orientation of S;
+* numpy's float16 conversion for the stored scalars.
+"""
+import itertools
+
+import numpy as np
+import pytest
+from scipy.linalg import hadamard
+
+import oracle
+import synth
+
+
+def make_q(d, bits, m, seed=3, S=None):
+    diag = synth.diag_signs(seed, synth.ROLE_DIAG_K, d)
+    if m and S is None:
+        S = synth.proj_matrix_f16(seed, synth.ROLE_PROJ_K, m, d)
+    return oracle.Quantizer(d, bits, m, diag, S)
+
+
+def dvec(Q):
+    i = np.arange(Q.d)
+    return np.where((Q.diag[i // 32] >> (i % 32).astype(np.uint32)) & 1, -1.0, 1.0)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_one_hot_gives_hadamard_column(d):
+    Q = make_q(d, 2, 0)
+    H = hadamard(d).astype(np.float64)
+    D = dvec(Q)
+    for i in [0, 1, 5, d // 2 + 3, d - 1]:
+        x = np.zeros((1, d))
+        x[0, i] = 3.0
+        _, y = oracle.quantize(Q, x, want_y=True)
+        np.testing.assert_allclose(y[0], D[i] * H[:, i] / np.sqrt(d), atol=1e-15)
+
+
+def test_rotation_is_orthogonal():
+    d = 128
+    Q = make_q(d, 3, 0)
+    x = synth.normals(5, synth.ROLE_DATA_K, np.arange(64 * d)).reshape(64, d)
+    _, y = oracle.quantize(Q, x, want_y=True)
+    n = np.linalg.norm(x, axis=1)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), 1.0, atol=1e-13)
+    G = (x / n[:, None]) @ (x / n[:, None]).T
+    np.testing.assert_allclose(y @ y.T, G, atol=1e-13)
+    # and equals R x / ||x|| with R = H D / sqrt(d) built from scipy's H
+    R = hadamard(d) * dvec(Q)[None, :] / np.sqrt(d)
+    np.testing.assert_allclose(y, (x / n[:, None]) @ R.T, atol=1e-13)
+
+
+def test_one_hot_codes_and_packed_words():
+    d = 128
+    # 2-bit: |y| = 1/sqrt(d) lies above the outer boundary 0.981/sqrt(d) -> outer levels
+    Q = make_q(d, 2, 0)
+    D = dvec(Q)
+    for i, pattern in [(0, None), (1, 0x55555555)]:
+        x = np.zeros((1, d))
+        x[0, i] = 1.0
+        P = oracle.quantize(Q, x)
+        idx = oracle.unpack_codes(Q, P.codes)[0]
+        H = hadamard(d)[:, i] * D[i]
+        assert np.array_equal(idx, np.where(H > 0, 3, 0))
+        if pattern is not None:
+            w = pattern if D[i] > 0 else (~pattern) & 0xFFFFFFFF
+            # code 3 = both plane bits set at the positive coordinates
+            assert np.all(P.codes[0, 0] == w) and np.all(P.codes[0, 1] == w)
+    # 3-bit: |y| sqrt(d) = 1 lies between boundaries 0.5006 and 1.0500 -> levels 2 / 5
+    Q3 = make_q(d, 3, 0)
+    x = np.zeros((1, d))
+    x[0, 7] = 1.0
+    idx = oracle.unpack_codes(Q3, oracle.quantize(Q3, x).codes)[0]
+    H = hadamard(d)[:, 7] * dvec(Q3)[7]
+    assert np.array_equal(idx, np.where(H > 0, 5, 2))
+    assert np.allclose(Q3.cent[[2, 5]] * np.sqrt(d), [-0.7560, 0.7560], atol=1e-3)
+
+
+def test_packing_bit_layout_against_manual_unpack():
+    d, bits = 128, 3
+    Q = make_q(d, bits, 0)
+    x = synth.normals(9, synth.ROLE_DATA_K, np.arange(16 * d)).reshape(16, d)
+    P, y = oracle.quantize(Q, x, want_y=True)
+    # expected code index by counting boundaries below y (ties low)
+    idx = (y[:, :, None] > Q.cb.boundaries.astype(np.float64)[None, None, :]).sum(-1)
+    for v in range(16):
+        for p in range(bits):
+            for w in range(d // 32):
+                word = 0
+                for k in range(32):
+                    word |= int((idx[v, 32 * w + k] >> p) & 1) << k
+                assert int(P.codes[v, p, w]) == word
+
+
+@pytest.mark.parametrize("d,bits", [(4, 2), (8, 2), (4, 3)])
+def test_codes_are_the_brute_force_argmin(d, bits):
+    Q = make_q(d, bits, 0)
+    x = synth.normals(11, synth.ROLE_DATA_K, np.arange(40 * d)).reshape(40, d)
+    P, y = oracle.quantize(Q, x, want_y=True)
+    idx = oracle.unpack_codes(Q, P.codes)
+    c = Q.cent.astype(np.float64)
+    allc = np.array(list(itertools.product(range(1 << bits), repeat=d)))
+    for v in range(40):
+        err = ((y[v][None, :] - c[allc]) ** 2).sum(1)
+        assert np.array_equal(allc[np.argmin(err)], idx[v])
+
+
+def test_projection_orientation_with_shift_matrix():
+    """S with S[j, (j+1) % d] = 1 gives u_j = r_{j+1}; a transposed S would
+    give r_{j-1}. One-hot input e_3 makes r periodic with period 4."""
+    d = 128
+    S = np.zeros((d, d), np.float16)
+    S[np.arange(d), (np.arange(d) + 1) % d] = 1.0
+    Q = make_q(d, 3, d, S=S)  # 2-bit MSE + 1-bit QJL ("b=3 total")
+    Q = oracle.Quantizer(d, 2, d, Q.diag, S)
+    x = np.zeros((1, d))
+    x[0, 3] = 1.0
+    P, y, u = oracle.quantize(Q, x, want_y=True, want_u=True)
+    sgn = oracle.unpack_signs(Q, P.signs)[0]
+    # y = D3 H[:,3]/sqrt(d): outer level, residual sign opposite to y (|y| < c_outer)
+    h = hadamard(d)[:, 3] * dvec(Q)[3]
+    r_sign = -h
+    expect = (np.roll(r_sign, -1) >= 0).astype(int)   # r_{j+1}
+    wrong = (np.roll(r_sign, 1) >= 0).astype(int)     # r_{j-1}
+    assert np.array_equal(sgn, expect)
+    assert not np.array_equal(sgn, wrong)
+
+
+def test_stored_scalars_are_fp16_rne():
+    d = 64
+    Q = make_q(d, 2, d)
+    x = synth.normals(13, synth.ROLE_DATA_K, np.arange(200 * d)).reshape(200, d) * 7.3
+    P, y = oracle.quantize(Q, x, want_y=True)
+    n = np.linalg.norm(x, axis=1)
+    assert np.array_equal(P.norm, n.astype(np.float16).view(np.uint16))
+    c = Q.cent.astype(np.float64)[oracle.unpack_codes(Q, P.codes)]
+    g = np.linalg.norm(y - c, axis=1)
+    assert np.array_equal(P.rnorm, g.astype(np.float16).view(np.uint16))
+
+
+def test_zero_vector():
+    d = 128
+    for bits in (2, 3, 4):
+        Q = make_q(d, bits, d)
+        P, y = oracle.quantize(Q, np.zeros((1, d)), want_y=True)
+        assert np.all(y == 0)
+        L = 1 << bits
+        assert np.all(oracle.unpack_codes(Q, P.codes) == L // 2 - 1)
+        assert P.norm[0] == 0
