@@ -1,0 +1,250 @@
+"""Benchmark of the TurboQuant KV hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+quantize every layer's K (2-bit codes + 1-bit QJL sketch + fp16 norms) and V
+(codes + fp16 norm), then one decode-attention step over every layer's
+compressed cache (query preparation, the fused score/softmax/value scan and
+the combine). Inputs are resident in HBM before timing starts; caches are
+decoded only after all layers were quantized, so the decode reads them from
+HBM rather than from the last-level cache.
+
+Default workload: Llama-3.3-70B-shaped 128K decode, one layer's share
+(8 KV heads x 131072 tokens x head_dim 128, 64 query heads, G = 8) repeated
+over 80 layer instances with their own seeds. ``--workload 8k`` runs the
+Qwen2.5-3B-shaped 8K cache (36 layers x 2 KV heads x 8192 tokens) as one call
+per op over the whole model, with replicas to exceed the last-level cache.
+
+Prints ONE JSON line. ``value`` is whole-step packed-KV throughput:
+algorithmic bytes of all ops of a step / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "packed-KV GB/s & % HBM peak (quantize, score, decode-attn); keys/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", choices=["128k", "8k"], default="128k")
+    ap.add_argument("--replicas", type=int, default=5, help="8k workload: cache replicas")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=0, help="override layer count (debug)")
+    return ap.parse_args()
+
+
+def packed_bytes_per_vector(d, mse_bits, qjl):
+    b = mse_bits * d // 8 + 2
+    if qjl:
+        b += d // 8 + 2
+    return b
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "quantize": ["kv_cache_vector_03_amd/csrc/tq_quantize.hip", "kv_cache_vector_03_amd/csrc/tq_device.h"],
+    "decode_attn": ["kv_cache_vector_03_amd/csrc/tq_attn.hip", "kv_cache_vector_03_amd/csrc/tq_quantize.hip",
+                    "kv_cache_vector_03_amd/csrc/tq_device.h"],
+}
+
+
+def traffic_for(op, launch_alg_bytes, workload):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{op}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha") != source_sha(KERNEL_SOURCES[op]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; the method's data-parallel path "
+                                   "is measured per GPU (see DESIGN.md for how it would shard)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kv_cache_vector_03_amd as tq
+    import synth
+    from synth import gpu as sgpu
+    from synth import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = W.CONFIG5 if args.workload == "128k" else W.CONFIG3
+    d, T, G, H = cfg.d, cfg.tokens, cfg.G, cfg.kv_heads
+    layers = args.layers or cfg.layers
+    diag_k, S, diag_v = W.quantizer_inputs(d)
+    qk = tq.Quantizer(d, cfg.k_mse_bits, d, diag_k, S, dev)
+    qv = tq.Quantizer(d, cfg.v_bits, 0, diag_v, None, dev)
+
+    # ---- batches: one per layer (128k) or one per replica of the whole model (8k)
+    units = []
+    if args.workload == "128k":
+        for l in range(layers):
+            units.append(dict(layers=[l], ns=H))
+    else:
+        for r in range(args.replicas):
+            units.append(dict(layers=list(range(layers)), ns=layers * H))
+    t_gen = time.time()
+    for u in units:
+        nvec = u["ns"] * T
+        u["K"] = torch.empty((nvec, d), dtype=torch.float16, device=dev)
+        u["V"] = torch.empty((nvec, d), dtype=torch.float16, device=dev)
+        per = H * T
+        for li, l in enumerate(u["layers"]):
+            for role, buf in ((synth.ROLE_DATA_K, u["K"]), (synth.ROLE_DATA_V, u["V"])):
+                sc = sgpu.scales_to_device(W.kv_seed_scales(cfg, l, role), dev)
+                W.kv_layer_device(cfg, l, role, buf[li * per:(li + 1) * per], sc)
+        q = np.stack([W.kv_queries_host(cfg, l) for l in u["layers"]]).reshape(u["ns"], G, d)
+        u["Q"] = torch.from_numpy(np.ascontiguousarray(q)).to(dev)
+        u["PK"] = tq.Packed.empty(qk, nvec, dev)
+        u["PV"] = tq.Packed.empty(qv, nvec, dev)
+        u["out"] = torch.empty((u["ns"], G, d), dtype=torch.float32, device=dev)
+    max_ns = max(u["ns"] for u in units)
+    ws = tq.workspace(tq.tq_workspace_size(tq.TQ_OP_DECODE_ATTN, qk, max_ns, T, G), dev)
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+
+    stream = torch.cuda.current_stream()
+    ops = ("quantize_k", "quantize_v", "decode_attn")
+    events = {o: [] for o in ops}
+
+    def step(record):
+        def timed(op, fn):
+            if record:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                events[op].append((a, b))
+            else:
+                fn()
+        for u in units:
+            timed("quantize_k", lambda: tq.tq_quantize(qk, u["K"], u["PK"]))
+            timed("quantize_v", lambda: tq.tq_quantize(qv, u["V"], u["PV"]))
+        for u in units:
+            timed("decode_attn", lambda: tq.tq_decode_attn(qk, qv, u["PK"], u["PV"], u["ns"], T, G, u["Q"],
+                                                          u["out"], ws=ws))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # ---- algorithmic bytes per launch
+    kb = packed_bytes_per_vector(d, cfg.k_mse_bits, True)
+    vb = packed_bytes_per_vector(d, cfg.v_bits, False)
+    per_launch = {}
+    for u in units[:1]:
+        nvec = u["ns"] * T
+        per_launch["quantize_k"] = nvec * (2 * d + kb)
+        per_launch["quantize_v"] = nvec * (2 * d + vb)
+        per_launch["decode_attn"] = nvec * (kb + vb) + u["ns"] * G * d * (2 + 4)
+    units_per_launch = {"quantize_k": units[0]["ns"] * T, "quantize_v": units[0]["ns"] * T,
+                        "decode_attn": units[0]["ns"] * T}
+    launches = {o: len(events[o]) for o in ops}
+    kern = {}
+    for o in ops:
+        ms = [a.elapsed_time(b) for a, b in events[o]]
+        avg_s = float(np.mean(ms)) * 1e-3
+        gbs = per_launch[o] / avg_s / 1e9
+        kern[o] = {"us_per_launch": round(avg_s * 1e6, 2), "alg_bytes_per_launch": per_launch[o],
+                   "GB_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                   "keys_per_s": round(units_per_launch[o] / avg_s, 1),
+                   "launches_per_step": launches[o] // args.steps,
+                   "time_share": None}
+    tot = sum(kern[o]["us_per_launch"] * kern[o]["launches_per_step"] for o in ops)
+    for o in ops:
+        kern[o]["time_share"] = round(kern[o]["us_per_launch"] * kern[o]["launches_per_step"] / tot, 3)
+    step_bytes = sum(per_launch[o] * launches[o] // args.steps for o in ops)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dom = max(ops, key=lambda o: kern[o]["time_share"])
+    dom_key = "quantize" if dom.startswith("quantize") else "decode_attn"
+    roof = {"kernel": dom, "bound": "hbm", "achieved": kern[dom]["GB_per_s"], "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"],
+            "traffic": traffic_for(dom_key, per_launch[dom], args.workload)}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name if args.workload == "8k" else
+                   "llama-3.3-70b-shaped 128K decode, one layer's share, x80 layer instances",
+                   "layers": layers, "kv_heads": H, "tokens": T, "head_dim": d, "G": G,
+                   "k_bits": f"{cfg.k_mse_bits}+1qjl", "v_bits": cfg.v_bits, "input": "fp16",
+                   "batches_per_step": len(units)},
+        "keys_per_s": round(units_per_launch["decode_attn"] * launches["decode_attn"] / args.steps
+                            / (ms_per_step * 1e-3), 1),
+        "roofline": roof,
+        "kernels": kern,
+        "setup_s": round(t_gen, 2),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, diag_k, S, diag_v, kb, vb)
+    print(json.dumps(result))
+
+
+def cpu_baseline(cfg, diag_k, S, diag_v, kb, vb):
+    """The oracle on a bounded sample of the same workload: one stream's first
+    ``n`` tokens quantized (K and V) and decoded with its G query heads."""
+    import numpy as np
+
+    import oracle
+    import synth
+    from synth import workloads as W
+    d, G = cfg.d, cfg.G
+    n = min(cfg.tokens, 32768)
+    toks = np.arange(n)
+    K = W.kv_vectors_host(cfg, 0, synth.ROLE_DATA_K, 0, toks).astype(np.float64)
+    V = W.kv_vectors_host(cfg, 0, synth.ROLE_DATA_V, 0, toks).astype(np.float64)
+    Q = W.kv_queries_host(cfg, 0)[0:1].astype(np.float64)
+    qko = oracle.Quantizer(d, cfg.k_mse_bits, d, diag_k, S)
+    qvo = oracle.Quantizer(d, cfg.v_bits, 0, diag_v, None)
+    oracle.quantize(qko, K[:256])
+    t0 = time.perf_counter()
+    pk = oracle.quantize(qko, K)
+    pv = oracle.quantize(qvo, V)
+    oracle.decode_attn(qko, qvo, pk, pv, 1, n, G, Q)
+    dt = time.perf_counter() - t0
+    alg = n * (2 * d + kb) + n * (2 * d + vb) + n * (kb + vb) + G * d * 6
+    return {"value": round(alg / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"one stream (layer 0, KV head 0), first {n} tokens: quantize K and V, "
+                      f"decode with its {G} query heads; {dt:.2f} s"}
+
+
+if __name__ == "__main__":
+    main()

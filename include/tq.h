@@ -1,0 +1,176 @@
+/*
+ * tq.h -- C ABI of the TurboQuant KV-cache hot path for AMD MI355X (gfx950).
+ *
+ * What the library computes (sources are the benchmark pages; see each entry):
+ *  - a data-oblivious codebook per (d, bits): Lloyd-Max scalar quantizer for
+ *    the law of one coordinate after a random rotation ("[Benchmark]
+ *    TurboQuant 實測：KV Cache 3-bit 壓縮，真的零損失？", section
+ *    "TurboQuant 是什麼：30 秒懶人包", step one; section "Lloyd-Max Codebook");
+ *  - a quantizer: random +-1 diagonal and normalised Walsh-Hadamard rotation,
+ *    stored norm, per-coordinate codes, and for keys a 1-bit QJL sketch of
+ *    the residual with the residual norm (same section, step two);
+ *  - scores q.k estimated directly from packed keys, unbiased with QJL
+ *    (same section; "MSE-Only vs QJL：bias 差異確認");
+ *  - reconstruction of vectors (the "dequantize back to BF16" path of the
+ *    vLLM summary page, section "延遲：dequantization 是隱藏成本");
+ *  - a fused decode-attention step over compressed K and V.
+ *
+ * Conventions shared by every entry point:
+ *  - Ownership: the caller owns every buffer. The library never allocates
+ *    device memory and keeps no state between calls except the thread-local
+ *    error message.
+ *  - Device pointers are plain HIP device addresses on the current device;
+ *    "stream" is a hipStream_t (NULL = the default stream). GPU work is
+ *    enqueued asynchronously on that stream; nothing synchronises.
+ *  - Argument errors are detected on the host before any launch and return a
+ *    non-zero status; tq_last_error() then describes the problem. Launch
+ *    failures return TQ_ERR_DEVICE. n == 0 is a no-op returning TQ_OK.
+ *  - Alignment: every device buffer must be 16-byte aligned, except norm and
+ *    rnorm arrays (2-byte aligned).
+ *  - Supported shapes: d in {64, 128, 256}; mse_bits in 1..4;
+ *    qjl_m in {0, d}.
+ *  - Inputs with ||x|| >= 65504 overflow the fp16 norm and are out of
+ *    contract (stored norm becomes inf); non-finite inputs likewise.
+ *
+ * Packed layout of one vector (the contract tests are bit-exact on):
+ *  - codes: uint32 [mse_bits][d/32]. Bit k of word w of plane p is bit p of
+ *    the code index of rotated coordinate 32 w + k. The code index of a
+ *    coordinate y is the number of boundaries strictly below y.
+ *  - signs: uint32 [qjl_m/32]. Bit k of word w is 1 iff row 32 w + k of S
+ *    applied to the residual is >= 0.
+ *  - norm: fp16 (RNE) of ||x||; rnorm: fp16 (RNE) of the residual norm of the
+ *    rotated unit vector.
+ *  Vector v of an array of n vectors starts at codes + v*mse_bits*d/32,
+ *  signs + v*qjl_m/32, norm + v, rnorm + v.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define TQ_OK 0
+#define TQ_ERR_INVALID 1      /* null / misaligned pointer, negative size, bad dtype */
+#define TQ_ERR_UNSUPPORTED 2  /* d, bits, m or law outside the supported set */
+#define TQ_ERR_WORKSPACE 3    /* workspace missing or too small */
+#define TQ_ERR_DEVICE 4       /* HIP launch or runtime error */
+#define TQ_ERR_NOCONV 5       /* codebook iteration did not converge */
+
+/* element types of dense inputs / outputs */
+#define TQ_F32 0
+#define TQ_F16 1
+
+/* workspace query operations */
+#define TQ_OP_SCORES 1
+#define TQ_OP_DECODE_ATTN 2
+
+/* codebook laws */
+#define TQ_LAW_GAUSSIAN 0     /* N(0, 1/d) */
+
+/* Quantizer state. All pointers are device pointers owned by the caller. */
+typedef struct tq_quantizer {
+    int d;                       /* vector length: 64, 128 or 256 */
+    int mse_bits;                /* bits of the scalar codes: 1..4 */
+    int qjl_m;                   /* 0: codes only (values); d: codes + QJL signs (keys) */
+    const float* centroids;      /* [2^mse_bits], ascending, from tq_codebook */
+    const float* boundaries;     /* [2^mse_bits - 1], from tq_codebook */
+    const uint32_t* diag_signs;  /* [d/32]; bit i set: coordinate i is negated before H */
+    const uint16_t* S;           /* fp16 [qjl_m][d] row-major JL matrix; NULL if qjl_m == 0 */
+} tq_quantizer;
+
+/* Packed vectors (device pointers owned by the caller; layout above). */
+typedef struct tq_packed {
+    uint32_t* codes;             /* [n][mse_bits][d/32] */
+    uint32_t* signs;             /* [n][qjl_m/32]; NULL if qjl_m == 0 */
+    uint16_t* norm;              /* [n] fp16 */
+    uint16_t* rnorm;             /* [n] fp16; NULL if qjl_m == 0 */
+} tq_packed;
+
+/*
+ * tq_codebook -- host only, synchronous.
+ * Lloyd-Max quantizer with 2^bits levels for the coordinate law N(0, 1/d)
+ * (the law that reproduces the distortions printed in the "Lloyd-Max
+ * Codebook" section: 0.000270 at d=128, bits=3; 0.000135 at d=256).
+ * Writes centroids (host float[2^bits]; each value is fp16-representable,
+ * the fp16 RNE rounding of the exact solution, and the set is symmetric) and
+ * boundaries (host float[2^bits - 1]; fp32 RNE of the exact midpoints of the
+ * stored centroids). distortion (nullable) receives the analytic mean squared
+ * error per coordinate of the stored codebook under the law.
+ * Supports d in 1..65536, bits in 1..8, law TQ_LAW_GAUSSIAN.
+ * Returns TQ_OK, TQ_ERR_INVALID (null output), TQ_ERR_UNSUPPORTED, or
+ * TQ_ERR_NOCONV.
+ */
+int tq_codebook(int d, int bits, int law, float* centroids, float* boundaries,
+                double* distortion);
+
+/*
+ * tq_quantize -- quantize n vectors x[n][d] (row-major, TQ_F32 or TQ_F16)
+ * into out (layout above). For each vector: norm n = ||x||; rotated unit
+ * vector y = H (D .* x) / (sqrt(d) n) (y = 0 when n = 0); codes; and with
+ * qjl_m = d: residual r = y - c[code], rnorm = ||r||, signs of S r.
+ * Asynchronous on stream.
+ */
+int tq_quantize(const tq_quantizer* q, const void* x, int x_dtype, int64_t n,
+                const tq_packed* out, void* stream);
+
+/*
+ * tq_scores -- scores[n_q][n_keys] (fp32) of estimated <query, key> for
+ * queries[n_q][d] (TQ_F32 or TQ_F16) against n_keys packed keys:
+ *   s = n * ( <q', c[codes]> + rnorm * sqrt(pi/2) / m * sum_j (S q')_j (2 sign_j - 1) )
+ * with q' = H (D .* q) / sqrt(d). With qjl_m = 0 only the first term is used.
+ * ws: device workspace of at least tq_workspace_size(TQ_OP_SCORES, q, n_q, n_keys, 0)
+ * bytes (query preparation). Asynchronous on stream.
+ */
+int tq_scores(const tq_quantizer* q, const tq_packed* keys, int64_t n_keys,
+              const void* queries, int q_dtype, int64_t n_q, float* scores,
+              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tq_dequantize -- reconstruct out[n][d] (TQ_F32 or TQ_F16):
+ *   x_hat = n * D H ( c[codes] + [include_qjl] rnorm sqrt(pi/2)/m S^T (2 sign - 1) ) / sqrt(d).
+ * include_qjl is ignored when qjl_m = 0. The score of a query against x_hat
+ * equals tq_scores' estimate. Asynchronous on stream.
+ */
+int tq_dequantize(const tq_quantizer* q, const tq_packed* in, int64_t n, int include_qjl,
+                  void* out, int out_dtype, void* stream);
+
+/*
+ * tq_decode_attn -- one decode step of attention over compressed K/V.
+ * n_streams streams (one stream = one (layer, KV head) token sequence) of T
+ * tokens each; stream s, token t is packed vector s*T + t of k and of v.
+ * q: [n_streams][G][d] (TQ_F32 or TQ_F16), G query heads per KV head.
+ * For each stream s and head h:
+ *   z_t = score(q_{s,h}, K_{s,t}) * scale   (scale = 1/sqrt(d) when scale == 0)
+ *   out_{s,h} = sum_t softmax(z)_t * v_hat_{s,t}   (v_hat as tq_dequantize)
+ * out: fp32 [n_streams][G][d]. qk (keys) and qv (values) must have the same d.
+ * T >= 1; G in 1..16. ws: at least
+ * tq_workspace_size(TQ_OP_DECODE_ATTN, qk, n_streams, T, G) bytes.
+ * Asynchronous on stream.
+ */
+int tq_decode_attn(const tq_quantizer* qk, const tq_quantizer* qv,
+                   const tq_packed* k, const tq_packed* v,
+                   int64_t n_streams, int64_t T, int G,
+                   const void* q, int q_dtype, float scale, float* out,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tq_workspace_size -- device workspace bytes for op:
+ *   TQ_OP_SCORES:      n_a = n_q, n_b = n_keys, G ignored;
+ *   TQ_OP_DECODE_ATTN: n_a = n_streams, n_b = T, G = heads per stream.
+ * Returns 0 for unknown ops or unsupported quantizers.
+ */
+size_t tq_workspace_size(int op, const tq_quantizer* qk, int64_t n_a, int64_t n_b, int G);
+
+/* Thread-local description of the last error ("" if none). */
+const char* tq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

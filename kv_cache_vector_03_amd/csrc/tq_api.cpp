@@ -1,0 +1,107 @@
+// The extern "C" entry points: validate on the host, then enqueue kernels.
+#include <cmath>
+
+#include "tq.h"
+#include "tq_internal.h"
+
+using namespace tq;
+
+namespace {
+
+size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+int tq_quantize(const tq_quantizer* q, const void* x, int x_dtype, int64_t n,
+                const tq_packed* out, void* stream)
+{
+    clear_error();
+    int rc;
+    if ((rc = check_quantizer(q, "tq_quantize", "")) != TQ_OK) return rc;
+    if (n < 0) return fail(TQ_ERR_INVALID, "tq_quantize: n=%lld < 0", (long long)n);
+    if (n == 0) return TQ_OK;
+    if ((rc = check_dense(x, x_dtype, "tq_quantize", "x")) != TQ_OK) return rc;
+    if ((rc = check_packed(q, out, "tq_quantize", "out")) != TQ_OK) return rc;
+    return launch_quantize(q, x, x_dtype, n, out, (hipStream_t)stream);
+}
+
+int tq_scores(const tq_quantizer* q, const tq_packed* keys, int64_t n_keys,
+              const void* queries, int q_dtype, int64_t n_q, float* scores,
+              void* ws, size_t ws_bytes, void* stream)
+{
+    clear_error();
+    int rc;
+    if ((rc = check_quantizer(q, "tq_scores", "")) != TQ_OK) return rc;
+    if (n_keys < 0 || n_q < 0) return fail(TQ_ERR_INVALID, "tq_scores: negative size");
+    if (n_keys == 0 || n_q == 0) return TQ_OK;
+    if ((rc = check_packed(q, keys, "tq_scores", "keys")) != TQ_OK) return rc;
+    if ((rc = check_dense(queries, q_dtype, "tq_scores", "queries")) != TQ_OK) return rc;
+    if ((rc = check_dense(scores, TQ_F32, "tq_scores", "scores")) != TQ_OK) return rc;
+    size_t need = scores_ws(q, n_q);
+    if (!ws || ws_bytes < need)
+        return fail(TQ_ERR_WORKSPACE, "tq_scores: workspace %zu bytes < %zu", ws_bytes, need);
+    if ((uintptr_t)ws % 256) return fail(TQ_ERR_INVALID, "tq_scores: workspace must be 256-byte aligned");
+    float* qr = (float*)ws;
+    float* p = (float*)((char*)ws + up256((size_t)n_q * q->d * 4));
+    if ((rc = launch_qprep(q, queries, q_dtype, n_q, qr, p, (hipStream_t)stream)) != TQ_OK) return rc;
+    return launch_scores(q, keys, n_keys, qr, p, n_q, scores, (hipStream_t)stream);
+}
+
+int tq_dequantize(const tq_quantizer* q, const tq_packed* in, int64_t n, int include_qjl,
+                  void* out, int out_dtype, void* stream)
+{
+    clear_error();
+    int rc;
+    if ((rc = check_quantizer(q, "tq_dequantize", "")) != TQ_OK) return rc;
+    if (n < 0) return fail(TQ_ERR_INVALID, "tq_dequantize: n=%lld < 0", (long long)n);
+    if (n == 0) return TQ_OK;
+    if (q->qjl_m == 0) include_qjl = 0;
+    if (include_qjl) {
+        if ((rc = check_packed(q, in, "tq_dequantize", "in")) != TQ_OK) return rc;
+    } else {
+        tq_quantizer q0 = *q;
+        q0.qjl_m = 0;
+        if ((rc = check_packed(&q0, in, "tq_dequantize", "in")) != TQ_OK) return rc;
+    }
+    if ((rc = check_dense(out, out_dtype, "tq_dequantize", "out")) != TQ_OK) return rc;
+    return launch_dequantize(q, in, n, include_qjl ? 1 : 0, out, out_dtype, (hipStream_t)stream);
+}
+
+int tq_decode_attn(const tq_quantizer* qk, const tq_quantizer* qv,
+                   const tq_packed* k, const tq_packed* v,
+                   int64_t n_streams, int64_t T, int G,
+                   const void* q, int q_dtype, float scale, float* out,
+                   void* ws, size_t ws_bytes, void* stream)
+{
+    clear_error();
+    int rc;
+    if ((rc = check_quantizer(qk, "tq_decode_attn", "key")) != TQ_OK) return rc;
+    if ((rc = check_quantizer(qv, "tq_decode_attn", "value")) != TQ_OK) return rc;
+    if (qv->d != qk->d) return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attn: key d=%d != value d=%d", qk->d, qv->d);
+    if (qv->qjl_m != 0)
+        return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attn: value quantizer must be codes-only (qjl_m=0)");
+    if (n_streams < 0) return fail(TQ_ERR_INVALID, "tq_decode_attn: n_streams < 0");
+    if (G < 1 || G > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attn: G=%d not in 1..16", G);
+    if (n_streams == 0) return TQ_OK;
+    if (T < 1) return fail(TQ_ERR_INVALID, "tq_decode_attn: T=%lld < 1", (long long)T);
+    if (!std::isfinite(scale) || scale < 0) return fail(TQ_ERR_INVALID, "tq_decode_attn: bad scale");
+    if ((rc = check_packed(qk, k, "tq_decode_attn", "k")) != TQ_OK) return rc;
+    if ((rc = check_packed(qv, v, "tq_decode_attn", "v")) != TQ_OK) return rc;
+    if ((rc = check_dense(q, q_dtype, "tq_decode_attn", "q")) != TQ_OK) return rc;
+    if ((rc = check_dense(out, TQ_F32, "tq_decode_attn", "out")) != TQ_OK) return rc;
+    size_t need = decode_ws(qk, n_streams, T, G);
+    if (!ws || ws_bytes < need)
+        return fail(TQ_ERR_WORKSPACE, "tq_decode_attn: workspace %zu bytes < %zu", ws_bytes, need);
+    if ((uintptr_t)ws % 256) return fail(TQ_ERR_INVALID, "tq_decode_attn: workspace must be 256-byte aligned");
+    if (scale == 0.0f) scale = 1.0f / std::sqrt((float)qk->d);
+    int64_t nq = n_streams * G;
+    float* qr = (float*)ws;
+    float* p = (float*)((char*)ws + up256((size_t)nq * qk->d * 4));
+    float* parts = (float*)((char*)ws + scores_ws(qk, nq));
+    if ((rc = launch_qprep(qk, q, q_dtype, nq, qr, p, (hipStream_t)stream)) != TQ_OK) return rc;
+    return launch_decode(qk, qv, k, v, n_streams, T, G, qr, p, scale, out, parts, (hipStream_t)stream);
+}
+
+}  // extern "C"

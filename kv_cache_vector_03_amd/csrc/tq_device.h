@@ -1,0 +1,95 @@
+// Device helpers shared by the kernels: fp16 access, wave reductions and the
+// wave-layout Walsh-Hadamard transform.
+#ifndef TQ_DEVICE_H
+#define TQ_DEVICE_H
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq.h"
+
+namespace tq {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
+__device__ __forceinline__ uint16_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
+
+template <bool F16>
+__device__ __forceinline__ float load_elem(const void* p, int64_t i)
+{
+    if constexpr (F16) return h2f(static_cast<const uint16_t*>(p)[i]);
+    else return static_cast<const float*>(p)[i];
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+    return v;
+}
+
+// Natural-order (Sylvester) Walsh-Hadamard transform, unnormalised, of a
+// d = 64 R vector held across one wave: lane l, slot r holds coordinate
+// 64 r + l. Butterflies on the slot bits run in registers; the six lane bits
+// use cross-lane exchanges. Every butterfly maps (a, b) -> (a + b, a - b)
+// with a the element whose index bit is 0, so the result is H x exactly as
+// H_ij = (-1)^popcount(i & j) defines it. T is float or double.
+template <int R, typename T>
+__device__ __forceinline__ void fwht_wave(T (&v)[R], int lane)
+{
+#pragma unroll
+    for (int h = 1; h < R; h <<= 1)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (!(r & h)) {
+                T a = v[r], b = v[r + h];
+                v[r] = a + b;
+                v[r + h] = a - b;
+            }
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1)
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            T p = __shfl_xor(v[r], m);
+            v[r] = (lane & m) ? (p - v[r]) : (v[r] + p);
+        }
+}
+
+// sign flips of the random diagonal for the coordinates a lane holds
+template <int R>
+__device__ __forceinline__ void load_diag(const uint32_t* diag, int lane, uint32_t (&mask)[R])
+{
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        int c = 64 * r + lane;
+        mask[r] = ((diag[c >> 5] >> (c & 31)) & 1u) << 31;
+    }
+}
+
+__device__ __forceinline__ float flip(float x, uint32_t m) { return __uint_as_float(__float_as_uint(x) ^ m); }
+
+// c[k] for a small register table without dynamic register indexing
+template <int L>
+__device__ __forceinline__ float pick(const float (&c)[L], int k)
+{
+    float v = c[0];
+#pragma unroll
+    for (int l = 1; l < L; ++l) v = (k == l) ? c[l] : v;
+    return v;
+}
+
+// sqrt(pi/2)
+constexpr float kSqrtHalfPi = 1.2533141373155003f;
+
+}  // namespace tq
+
+#endif

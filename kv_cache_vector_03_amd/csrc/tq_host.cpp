@@ -1,0 +1,227 @@
+// Host side of the library: the codebook solver, argument validation and the
+// thread-local error message. Pure C++ (no device code), so every check here
+// can be exercised without a GPU.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "tq.h"
+#include "tq_internal.h"
+
+namespace tq {
+
+static thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_err[0] = 0; }
+
+// ---------------------------------------------------------------- codebook
+//
+// Lloyd-Max for N(0, sigma^2), sigma = 1/sqrt(d): alternate "boundaries at
+// midpoints of neighbouring centroids" and "centroid = conditional mean of its
+// cell" until the centroids move by less than tol * sigma. Initial centroids
+// are the Gaussian quantiles at (l + 1/2) / L, found by bisection.
+
+static double std_cdf_upper(double z) { return 0.5 * std::erfc(z / std::sqrt(2.0)); }
+
+// P(a < Z <= b) for standard normal Z, computed from the nearer tail
+static double std_mass(double a, double b)
+{
+    if (a >= 0) return std_cdf_upper(a) - std_cdf_upper(b);
+    if (b <= 0) return std_cdf_upper(-b) - std_cdf_upper(-a);
+    return 1.0 - std_cdf_upper(-a) - std_cdf_upper(b);
+}
+
+static double std_pdf(double z) { return std::isinf(z) ? 0.0 : std::exp(-0.5 * z * z) / std::sqrt(2.0 * M_PI); }
+
+static double std_quantile(double p)
+{
+    double lo = -40, hi = 40;
+    for (int i = 0; i < 200; ++i) {
+        double mid = 0.5 * (lo + hi);
+        if (1.0 - std_cdf_upper(mid) < p) lo = mid; else hi = mid;
+    }
+    return 0.5 * (lo + hi);
+}
+
+// round a double to the nearest binary16 value (ties to even); returns it as double
+static double round_to_half(double x)
+{
+    if (x == 0.0 || !std::isfinite(x)) return x;
+    double ax = std::fabs(x);
+    if (ax >= 65520.0) return std::copysign(INFINITY, x);
+    int e = std::ilogb(ax);                 // ax in [2^e, 2^(e+1))
+    int q = (e < -14 ? -14 : e) - 10;       // spacing 2^q (subnormals: 2^-24)
+    double scaled = std::ldexp(ax, -q);     // exact
+    double r = std::nearbyint(scaled);      // ties-to-even in the default mode
+    return std::copysign(std::ldexp(r, q), x);
+}
+
+// analytic E[(Y - c(Y))^2] under N(0, sigma^2) for cells split at t
+static double gauss_distortion(double sigma, int L, const double* c, const double* t)
+{
+    double D = 0;
+    for (int l = 0; l < L; ++l) {
+        double a = (l == 0) ? -INFINITY : t[l - 1] / sigma;
+        double b = (l == L - 1) ? INFINITY : t[l] / sigma;
+        double m0 = std_mass(a, b);
+        double m1 = sigma * (std_pdf(a) - std_pdf(b));
+        double ta = std::isinf(a) ? 0.0 : a * std_pdf(a);
+        double tb = std::isinf(b) ? 0.0 : b * std_pdf(b);
+        double m2 = sigma * sigma * (m0 + ta - tb);
+        D += m2 - 2 * c[l] * m1 + c[l] * c[l] * m0;
+    }
+    return D;
+}
+
+int codebook(int d, int bits, int law, float* cent, float* bnd, double* dist)
+{
+    if (!cent || !bnd) return fail(TQ_ERR_INVALID, "tq_codebook: null output");
+    if (law != TQ_LAW_GAUSSIAN) return fail(TQ_ERR_UNSUPPORTED, "tq_codebook: law %d unsupported", law);
+    if (d < 1 || d > 65536) return fail(TQ_ERR_UNSUPPORTED, "tq_codebook: d=%d outside 1..65536", d);
+    if (bits < 1 || bits > 8) return fail(TQ_ERR_UNSUPPORTED, "tq_codebook: bits=%d outside 1..8", bits);
+    const int L = 1 << bits;
+    const double sigma = 1.0 / std::sqrt((double)d);
+    double c[256], t[256], cn[256];
+    for (int l = 0; l < L; ++l) c[l] = sigma * std_quantile((l + 0.5) / L);
+    const double tol = (bits <= 4 ? 1e-15 : 1e-12) * sigma;
+    bool done = false;
+    for (int it = 0; it < 4000000 && !done; ++it) {
+        for (int l = 0; l + 1 < L; ++l) t[l] = 0.5 * (c[l] + c[l + 1]);
+        for (int l = 0; l < L; ++l) {
+            double a = (l == 0) ? -INFINITY : t[l - 1] / sigma;
+            double b = (l == L - 1) ? INFINITY : t[l] / sigma;
+            double m0 = std_mass(a, b);
+            cn[l] = m0 > 0 ? sigma * (std_pdf(a) - std_pdf(b)) / m0 : c[l];
+        }
+        // the law is symmetric: keep the solution exactly antisymmetric
+        for (int l = 0; l < L / 2; ++l) {
+            double v = 0.5 * (cn[L - 1 - l] - cn[l]);
+            cn[l] = -v;
+            cn[L - 1 - l] = v;
+        }
+        double move = 0;
+        for (int l = 0; l < L; ++l) {
+            move = std::fmax(move, std::fabs(cn[l] - c[l]));
+            c[l] = cn[l];
+        }
+        done = move < tol;
+    }
+    if (!done) return fail(TQ_ERR_NOCONV, "tq_codebook: no convergence for d=%d bits=%d", d, bits);
+    double cs[256], ts[256];
+    for (int l = 0; l < L; ++l) {
+        cs[l] = round_to_half(c[l]);
+        cent[l] = (float)cs[l];
+    }
+    for (int l = 0; l + 1 < L; ++l) {
+        bnd[l] = (float)(0.5 * (cs[l] + cs[l + 1]));   // exact midpoint, then RNE to fp32
+        ts[l] = (double)bnd[l];
+    }
+    if (dist) *dist = gauss_distortion(sigma, L, cs, ts);
+    return TQ_OK;
+}
+
+// ---------------------------------------------------------------- validation
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_quantizer(const tq_quantizer* q, const char* who, const char* role)
+{
+    if (!q) return fail(TQ_ERR_INVALID, "%s: %s quantizer is NULL", who, role);
+    if (q->d != 64 && q->d != 128 && q->d != 256)
+        return fail(TQ_ERR_UNSUPPORTED, "%s: %s d=%d not in {64,128,256}", who, role, q->d);
+    if (q->mse_bits < 1 || q->mse_bits > 4)
+        return fail(TQ_ERR_UNSUPPORTED, "%s: %s mse_bits=%d not in 1..4", who, role, q->mse_bits);
+    if (q->qjl_m != 0 && q->qjl_m != q->d)
+        return fail(TQ_ERR_UNSUPPORTED, "%s: %s qjl_m=%d must be 0 or d", who, role, q->qjl_m);
+    if (!q->centroids || !q->boundaries || !q->diag_signs)
+        return fail(TQ_ERR_INVALID, "%s: %s quantizer has a NULL table", who, role);
+    if (!aligned(q->centroids, 16) || !aligned(q->boundaries, 16) || !aligned(q->diag_signs, 16))
+        return fail(TQ_ERR_INVALID, "%s: %s quantizer tables must be 16-byte aligned", who, role);
+    if (q->qjl_m) {
+        if (!q->S) return fail(TQ_ERR_INVALID, "%s: %s S is NULL with qjl_m=%d", who, role, q->qjl_m);
+        if (!aligned(q->S, 16)) return fail(TQ_ERR_INVALID, "%s: %s S must be 16-byte aligned", who, role);
+    }
+    return TQ_OK;
+}
+
+int check_packed(const tq_quantizer* q, const tq_packed* p, const char* who, const char* role)
+{
+    if (!p) return fail(TQ_ERR_INVALID, "%s: %s packed descriptor is NULL", who, role);
+    if (!p->codes || !p->norm) return fail(TQ_ERR_INVALID, "%s: %s codes/norm NULL", who, role);
+    if (!aligned(p->codes, 16)) return fail(TQ_ERR_INVALID, "%s: %s codes must be 16-byte aligned", who, role);
+    if (!aligned(p->norm, 2)) return fail(TQ_ERR_INVALID, "%s: %s norm must be 2-byte aligned", who, role);
+    if (q->qjl_m) {
+        if (!p->signs || !p->rnorm) return fail(TQ_ERR_INVALID, "%s: %s signs/rnorm NULL with qjl_m>0", who, role);
+        if (!aligned(p->signs, 16)) return fail(TQ_ERR_INVALID, "%s: %s signs must be 16-byte aligned", who, role);
+        if (!aligned(p->rnorm, 2)) return fail(TQ_ERR_INVALID, "%s: %s rnorm must be 2-byte aligned", who, role);
+    }
+    return TQ_OK;
+}
+
+int check_dense(const void* p, int dtype, const char* who, const char* what)
+{
+    if (!p) return fail(TQ_ERR_INVALID, "%s: %s is NULL", who, what);
+    if (dtype != TQ_F32 && dtype != TQ_F16) return fail(TQ_ERR_INVALID, "%s: %s dtype %d unknown", who, what, dtype);
+    if (!aligned(p, 16)) return fail(TQ_ERR_INVALID, "%s: %s must be 16-byte aligned", who, what);
+    return TQ_OK;
+}
+
+// workspace layout helpers (sizes in bytes, each region 256-byte aligned)
+static size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+size_t scores_ws(const tq_quantizer* q, int64_t n_q)
+{
+    // prepared queries: fp32 q' [n_q][d] and p = S q' [n_q][m]
+    return up256((size_t)n_q * q->d * 4) + up256((size_t)n_q * (q->qjl_m ? q->qjl_m : 1) * 4);
+}
+
+int decode_chunks(int64_t T)
+{
+    int64_t tc = decode_chunk_tokens(T);
+    return (int)((T + tc - 1) / tc);
+}
+
+size_t decode_ws(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G)
+{
+    size_t nq = (size_t)n_streams * G;
+    size_t prep = scores_ws(qk, (int64_t)nq);
+    size_t parts = (size_t)n_streams * decode_chunks(T) * G * (qk->d + 2) * 4;
+    return prep + up256(parts);
+}
+
+}  // namespace tq
+
+extern "C" {
+
+int tq_codebook(int d, int bits, int law, float* centroids, float* boundaries, double* distortion)
+{
+    tq::clear_error();
+    return tq::codebook(d, bits, law, centroids, boundaries, distortion);
+}
+
+size_t tq_workspace_size(int op, const tq_quantizer* qk, int64_t n_a, int64_t n_b, int G)
+{
+    if (!qk || n_a < 0 || n_b < 0) return 0;
+    if (qk->d != 64 && qk->d != 128 && qk->d != 256) return 0;
+    if (qk->qjl_m != 0 && qk->qjl_m != qk->d) return 0;
+    if (op == TQ_OP_SCORES) return tq::scores_ws(qk, n_a);
+    if (op == TQ_OP_DECODE_ATTN) {
+        if (G < 1 || G > 16 || n_b < 1) return 0;
+        return tq::decode_ws(qk, n_a, n_b, G);
+    }
+    return 0;
+}
+
+const char* tq_last_error(void) { return tq::g_err; }
+
+}  // extern "C"

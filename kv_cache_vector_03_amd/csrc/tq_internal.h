@@ -1,0 +1,47 @@
+// Internal declarations shared by the host validation code and the kernels.
+#ifndef TQ_INTERNAL_H
+#define TQ_INTERNAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tq.h"
+
+typedef struct ihipStream_t* hipStream_t;
+
+namespace tq {
+
+int fail(int code, const char* fmt, ...);
+void clear_error();
+
+int check_quantizer(const tq_quantizer* q, const char* who, const char* role);
+int check_packed(const tq_quantizer* q, const tq_packed* p, const char* who, const char* role);
+int check_dense(const void* p, int dtype, const char* who, const char* what);
+
+size_t scores_ws(const tq_quantizer* q, int64_t n_q);
+size_t decode_ws(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G);
+int decode_chunks(int64_t T);
+
+// tokens per split-K chunk of the decode-attention kernel
+inline int64_t decode_chunk_tokens(int64_t T)
+{
+    (void)T;
+    return 256;
+}
+
+// kernel launchers (tq_*.hip); each returns TQ_OK or TQ_ERR_DEVICE
+int launch_quantize(const tq_quantizer* q, const void* x, int dtype, int64_t n,
+                    const tq_packed* out, hipStream_t s);
+int launch_qprep(const tq_quantizer* q, const void* queries, int dtype, int64_t nq,
+                 float* qr, float* p, hipStream_t s);
+int launch_scores(const tq_quantizer* q, const tq_packed* k, int64_t n_keys, const float* qr,
+                  const float* p, int64_t n_q, float* scores, hipStream_t s);
+int launch_dequantize(const tq_quantizer* q, const tq_packed* in, int64_t n, int include_qjl,
+                      void* out, int dtype, hipStream_t s);
+int launch_decode(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
+                  const tq_packed* v, int64_t n_streams, int64_t T, int G, const float* qr,
+                  const float* p, float scale, float* out, float* parts, hipStream_t s);
+
+}  // namespace tq
+
+#endif

@@ -1,0 +1,147 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/tq.h declares, its host codebook equals the oracle's bit for bit, and
+every argument error is caught on the host before any launch (fake, never
+dereferenced device addresses are used for the pointers)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_vector_03_amd as tq
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(tq.EXPORTS)
+    L = tq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_host_codebook_equals_oracle(d, bits):
+    cent, bnd, dist = tq.tq_codebook(d, bits)
+    ref = oracle.codebook(d, bits)
+    assert np.array_equal(cent, ref.centroids)
+    assert np.array_equal(bnd, ref.boundaries)
+    assert abs(dist - ref.dist_stored) <= 1e-12 * ref.dist_stored
+
+
+def test_codebook_wide_and_errors():
+    cent, bnd, _ = tq.tq_codebook(128, 6)
+    assert np.array_equal(cent, oracle.codebook(128, 6).centroids)
+    L = tq.lib()
+    buf = np.zeros(256, np.float32)
+    assert L.tq_codebook(128, 3, 1, buf.ctypes.data, buf.ctypes.data, None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_codebook(128, 0, 0, buf.ctypes.data, buf.ctypes.data, None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_codebook(128, 9, 0, buf.ctypes.data, buf.ctypes.data, None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_codebook(0, 3, 0, buf.ctypes.data, buf.ctypes.data, None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_codebook(128, 3, 0, None, buf.ctypes.data, None) == tq.TQ_ERR_INVALID
+    assert "null" in tq.tq_last_error()
+
+
+A = 0x10000  # fake 256-byte aligned device addresses; never dereferenced
+
+
+def qstruct(d=128, bits=2, m=128, S=True):
+    return tq.tq_quantizer(d, bits, m, A, A + 0x100, A + 0x200, (A + 0x300) if S else None)
+
+
+def pstruct(signs=True):
+    return tq.tq_packed(A + 0x1000, (A + 0x2000) if signs else None, A + 0x3000,
+                        (A + 0x4000) if signs else None)
+
+
+def quantize_rc(q, x=A + 0x8000, dtype=tq.TQ_F16, n=10, p=None):
+    L = tq.lib()
+    p = pstruct() if p is None else p
+    return L.tq_quantize(C.byref(q) if q is not None else None, x, dtype, n,
+                         C.byref(p) if p is not None else None, None)
+
+
+def test_quantize_argument_errors():
+    assert quantize_rc(None) == tq.TQ_ERR_INVALID
+    assert quantize_rc(qstruct(d=96)) == tq.TQ_ERR_UNSUPPORTED
+    assert quantize_rc(qstruct(d=32)) == tq.TQ_ERR_UNSUPPORTED
+    assert quantize_rc(qstruct(bits=0)) == tq.TQ_ERR_UNSUPPORTED
+    assert quantize_rc(qstruct(bits=5)) == tq.TQ_ERR_UNSUPPORTED
+    assert quantize_rc(qstruct(m=64)) == tq.TQ_ERR_UNSUPPORTED
+    assert quantize_rc(qstruct(S=False)) == tq.TQ_ERR_INVALID
+    assert quantize_rc(qstruct(), n=-1) == tq.TQ_ERR_INVALID
+    assert quantize_rc(qstruct(), x=None) == tq.TQ_ERR_INVALID
+    assert quantize_rc(qstruct(), x=A + 8) == tq.TQ_ERR_INVALID          # misaligned
+    assert quantize_rc(qstruct(), dtype=7) == tq.TQ_ERR_INVALID
+    assert quantize_rc(qstruct(), p=pstruct(signs=False)) == tq.TQ_ERR_INVALID
+    bad = pstruct()
+    bad.codes = A + 4
+    assert quantize_rc(qstruct(), p=bad) == tq.TQ_ERR_INVALID
+    bad = pstruct()
+    bad.norm = A + 1
+    assert quantize_rc(qstruct(), p=bad) == tq.TQ_ERR_INVALID
+    assert "aligned" in tq.tq_last_error() or "norm" in tq.tq_last_error()
+    # n == 0 is a no-op that succeeds without touching anything
+    assert quantize_rc(qstruct(), n=0, x=None, p=None) == tq.TQ_OK
+    # codes-only quantizer needs no signs
+    assert quantize_rc(qstruct(m=0, S=False), n=0) == tq.TQ_OK
+
+
+def test_scores_and_decode_argument_errors():
+    L = tq.lib()
+    q = qstruct()
+    p = pstruct()
+    need = L.tq_workspace_size(tq.TQ_OP_SCORES, C.byref(q), 64, 8192, 0)
+    assert need > 0
+    rc = L.tq_scores(C.byref(q), C.byref(p), 8192, A + 0x8000, tq.TQ_F16, 64, A + 0x9000,
+                     A + 0xA000, need - 1, None)
+    assert rc == tq.TQ_ERR_WORKSPACE
+    rc = L.tq_scores(C.byref(q), C.byref(p), 8192, A + 0x8000, tq.TQ_F16, 64, A + 0x9000,
+                     None, need, None)
+    assert rc == tq.TQ_ERR_WORKSPACE
+    rc = L.tq_scores(C.byref(q), C.byref(p), -1, A + 0x8000, tq.TQ_F16, 64, A + 0x9000,
+                     A + 0xA000, need, None)
+    assert rc == tq.TQ_ERR_INVALID
+    assert L.tq_scores(C.byref(q), C.byref(p), 0, None, 0, 64, None, None, 0, None) == tq.TQ_OK
+    qv = qstruct(bits=3, m=0, S=False)
+    pv = pstruct(signs=False)
+    wsd = L.tq_workspace_size(tq.TQ_OP_DECODE_ATTN, C.byref(q), 72, 8192, 8)
+    assert wsd > 0
+
+    def dec(qk=q, qvv=qv, ns=72, T=8192, G=8, scale=0.0, ws=A + 0x100000, wsb=wsd):
+        return L.tq_decode_attn(C.byref(qk), C.byref(qvv), C.byref(p), C.byref(pv), ns, T, G,
+                                A + 0x8000, tq.TQ_F16, C.c_float(scale), A + 0x9000, ws, wsb, None)
+
+    assert dec(wsb=wsd - 1) == tq.TQ_ERR_WORKSPACE
+    assert dec(G=0) == tq.TQ_ERR_UNSUPPORTED
+    assert dec(G=17) == tq.TQ_ERR_UNSUPPORTED
+    assert dec(T=0) == tq.TQ_ERR_INVALID
+    assert dec(scale=-1.0) == tq.TQ_ERR_INVALID
+    assert dec(scale=float("nan")) == tq.TQ_ERR_INVALID
+    assert dec(qvv=qstruct(bits=3, m=128)) == tq.TQ_ERR_UNSUPPORTED      # values carry no QJL
+    assert dec(qvv=qstruct(d=64, bits=3, m=0, S=False)) == tq.TQ_ERR_UNSUPPORTED
+    assert dec(ws=A + 0x100010) == tq.TQ_ERR_INVALID                     # workspace alignment
+    assert dec(ns=0) == tq.TQ_OK
+    assert L.tq_workspace_size(99, C.byref(q), 1, 1, 1) == 0
+    assert L.tq_workspace_size(tq.TQ_OP_DECODE_ATTN, C.byref(q), 1, 1, 0) == 0
+    assert L.tq_workspace_size(tq.TQ_OP_DECODE_ATTN, C.byref(qstruct(d=100)), 1, 1, 8) == 0
+
+
+def test_dequantize_argument_errors():
+    L = tq.lib()
+    q = qstruct()
+    # include_qjl with missing signs is an error; without QJL the signs are not needed
+    assert L.tq_dequantize(C.byref(q), C.byref(pstruct(signs=False)), 5, 1, A, tq.TQ_F32, None) == tq.TQ_ERR_INVALID
+    assert L.tq_dequantize(C.byref(q), C.byref(pstruct()), 5, 1, None, tq.TQ_F32, None) == tq.TQ_ERR_INVALID
+    assert L.tq_dequantize(C.byref(q), C.byref(pstruct()), -5, 1, A, tq.TQ_F32, None) == tq.TQ_ERR_INVALID
+    assert L.tq_dequantize(C.byref(q), C.byref(pstruct()), 0, 1, A, tq.TQ_F32, None) == tq.TQ_OK

@@ -1,0 +1,195 @@
+"""GPU parity of quantize, scores and dequantize against the oracle (through the C ABI).
+
+Sizes span several waves and blocks with ragged tails; configs 1 and 2 run in
+full. Scores are compared on identical packed inputs both ways: oracle-packed
+keys into both paths, and GPU-packed keys into both paths.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import workloads as W
+
+from parity import TOL, check_close, check_quantize
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def tqmod():
+    import kv_cache_vector_03_amd as tq
+    return tq
+
+
+def quantizers(d, bits, m, seed=7):
+    tq = tqmod()
+    diag = synth.diag_signs(seed, synth.ROLE_DIAG_K, d)
+    S = synth.proj_matrix_f16(seed, synth.ROLE_PROJ_K, d, d) if m else None
+    return tq.Quantizer(d, bits, m, diag, S, DEV), oracle.Quantizer(d, bits, m, diag, S)
+
+
+def gpu_quantize(qg, x_host):
+    tq = tqmod()
+    x = torch.from_numpy(np.ascontiguousarray(x_host)).to(DEV)
+    p = tq.Packed.empty(qg, x.shape[0], DEV)
+    tq.tq_quantize(qg, x, p)
+    torch.cuda.synchronize()
+    return p
+
+
+def to_oracle_packed(qo, host):
+    c, s, n, r = host
+    if qo.m == 0:
+        s = np.zeros((c.shape[0], 0), np.uint32)
+        r = np.zeros(c.shape[0], np.uint16)
+    return oracle.Packed(c, s, n, r)
+
+
+CASES = [(64, 2, 64), (64, 3, 0), (128, 1, 128), (128, 2, 128), (128, 3, 0), (128, 4, 0),
+         (128, 3, 128), (256, 2, 256), (256, 4, 0)]
+
+
+@pytest.mark.parametrize("d,bits,m", CASES)
+@pytest.mark.parametrize("dtype", [np.float32, np.float16])
+def test_quantize_parity(d, bits, m, dtype):
+    qg, qo = quantizers(d, bits, m)
+    n = 1000 + 13   # several blocks plus a ragged tail
+    x = synth.normals(17, synth.ROLE_DATA_K, np.arange(n * d)).reshape(n, d) * 3.0
+    x = x.astype(np.float32).astype(dtype)
+    p = gpu_quantize(qg, x)
+    check_quantize(qo, x.astype(np.float64), p.to_host())
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 65, 257])
+def test_quantize_ragged_counts(n):
+    qg, qo = quantizers(128, 2, 128)
+    x = synth.to_f16(synth.normals(19, synth.ROLE_DATA_K, np.arange(n * 128)).reshape(n, 128))
+    check_quantize(qo, x.astype(np.float64), gpu_quantize(qg, x).to_host())
+
+
+def test_quantize_zero_and_one_hot_vectors():
+    d = 128
+    qg, qo = quantizers(d, 2, d)
+    x = np.zeros((6, d), np.float32)
+    x[1, 0] = 1.0
+    x[2, 1] = -2.0
+    x[3, 77] = 0.5
+    x[4] = 1e-3
+    host = gpu_quantize(qg, x).to_host()
+    check_quantize(qo, x.astype(np.float64), host)
+    assert host[2][0] == 0   # zero vector: norm 0
+
+
+def test_quantize_output_untouched_beyond_n():
+    tq = tqmod()
+    qg, _ = quantizers(128, 2, 128)
+    x = torch.zeros((40, 128), dtype=torch.float16, device=DEV)
+    p = tq.Packed.empty(qg, 64, DEV)
+    for t in (p.codes, p.signs, p.norm, p.rnorm):
+        t.fill_(-1)
+    tq.tq_quantize(qg, x, p, n=40)
+    torch.cuda.synchronize()
+    assert torch.all(p.codes[40:] == -1) and torch.all(p.signs[40:] == -1)
+    assert torch.all(p.norm[40:] == -1) and torch.all(p.rnorm[40:] == -1)
+
+
+def test_config1_full():
+    keys, q = W.config1_host()
+    d = 128
+    diag_k, S, _ = W.quantizer_inputs(d)
+    tq = tqmod()
+    qg, qo = tq.Quantizer(d, 2, d, diag_k, S, DEV), oracle.Quantizer(d, 2, d, diag_k, S)
+    p = gpu_quantize(qg, keys)
+    host = p.to_host()
+    _, _, ref = check_quantize(qo, keys.astype(np.float64), host)
+    qd = torch.from_numpy(q).to(DEV)
+    sc = torch.empty((8, 1024), dtype=torch.float32, device=DEV)
+    tq.tq_scores(qg, p, 1024, qd, sc)
+    torch.cuda.synchronize()
+    check_close(sc.cpu().numpy(), oracle.scores(qo, to_oracle_packed(qo, host), q.astype(np.float64)),
+                what="scores on GPU-packed keys")
+    # oracle-packed keys into the GPU score kernel
+    po = tq.Packed.from_host(ref.codes, ref.signs, ref.norm, ref.rnorm, DEV)
+    tq.tq_scores(qg, po, 1024, qd, sc)
+    torch.cuda.synchronize()
+    check_close(sc.cpu().numpy(), oracle.scores(qo, ref, q.astype(np.float64)),
+                what="scores on oracle-packed keys")
+
+
+def test_config2_full_and_determinism():
+    keys, q = W.config2_host()
+    d = 128
+    diag_k, S, _ = W.quantizer_inputs(d)
+    tq = tqmod()
+    qg, qo = tq.Quantizer(d, 2, d, diag_k, S, DEV), oracle.Quantizer(d, 2, d, diag_k, S)
+    p = gpu_quantize(qg, keys)
+    host = p.to_host()
+    check_quantize(qo, keys.astype(np.float64), host)
+    p2 = gpu_quantize(qg, keys)
+    for a, b in zip(host, p2.to_host()):
+        assert np.array_equal(a, b)
+    qd = torch.from_numpy(q).to(DEV)
+    sc = torch.empty((64, 8192), dtype=torch.float32, device=DEV)
+    tq.tq_scores(qg, p, 8192, qd, sc)
+    torch.cuda.synchronize()
+    ref = oracle.scores(qo, to_oracle_packed(qo, host), q.astype(np.float64))
+    check_close(sc.cpu().numpy(), ref, what="config 2 scores")
+    sc2 = torch.empty_like(sc)
+    tq.tq_scores(qg, p, 8192, qd, sc2)
+    torch.cuda.synchronize()
+    assert torch.equal(sc, sc2)
+
+
+@pytest.mark.parametrize("d,bits,m", [(64, 3, 64), (128, 1, 0), (128, 4, 128), (256, 2, 256),
+                                      (256, 3, 0)])
+@pytest.mark.parametrize("n_q,n_keys", [(1, 1), (17, 257), (5, 1000)])
+def test_scores_shapes(d, bits, m, n_q, n_keys):
+    tq = tqmod()
+    qg, qo = quantizers(d, bits, m)
+    x = synth.normals(23, synth.ROLE_DATA_K, np.arange(n_keys * d)).reshape(n_keys, d).astype(np.float32)
+    q = synth.normals(23, synth.ROLE_QUERY, np.arange(n_q * d)).reshape(n_q, d).astype(np.float32)
+    p = gpu_quantize(qg, x)
+    sc = torch.empty((n_q, n_keys), dtype=torch.float32, device=DEV)
+    tq.tq_scores(qg, p, n_keys, torch.from_numpy(q).to(DEV), sc)
+    torch.cuda.synchronize()
+    check_close(sc.cpu().numpy(), oracle.scores(qo, to_oracle_packed(qo, p.to_host()), q.astype(np.float64)))
+
+
+@pytest.mark.parametrize("d,bits,m", [(64, 2, 64), (128, 2, 128), (128, 4, 0), (256, 3, 256)])
+@pytest.mark.parametrize("include_qjl", [True, False])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.float16])
+def test_dequantize_parity(d, bits, m, include_qjl, out_dtype):
+    tq = tqmod()
+    qg, qo = quantizers(d, bits, m)
+    n = 333
+    x = synth.normals(29, synth.ROLE_DATA_K, np.arange(n * d)).reshape(n, d).astype(np.float32) * 2
+    p = gpu_quantize(qg, x)
+    out = torch.empty((n, d), dtype=out_dtype, device=DEV)
+    tq.tq_dequantize(qg, p, n, include_qjl, out)
+    torch.cuda.synchronize()
+    ref = oracle.dequantize(qo, to_oracle_packed(qo, p.to_host()), include_qjl=include_qjl)
+    tol = TOL if out_dtype == torch.float32 else 2.0 ** -11 * np.abs(ref).max() + TOL
+    check_close(out.float().cpu().numpy(), ref, tol=tol, what="dequantize")
+
+
+def test_synth_gpu_twin_matches_host():
+    from synth import gpu
+    out = torch.empty(100003, dtype=torch.float32, device=DEV)
+    gpu.fill_f32(out, 77, synth.ROLE_DATA_K, first=12345)
+    ref = synth.to_f32(synth.normals(77, synth.ROLE_DATA_K, np.arange(12345, 12345 + 100003)))
+    assert np.array_equal(out.cpu().numpy(), ref)
+    cfg = W.CONFIG3
+    layer = 17
+    sc = gpu.scales_to_device(W.kv_seed_scales(cfg, layer, synth.ROLE_DATA_V), DEV)
+    kv = torch.empty((cfg.kv_heads * cfg.tokens, cfg.d), dtype=torch.float16, device=DEV)
+    W.kv_layer_device(cfg, layer, synth.ROLE_DATA_V, kv, sc)
+    toks = np.array([0, 1, 4095, 8191])
+    for h in range(cfg.kv_heads):
+        ref = W.kv_vectors_host(cfg, layer, synth.ROLE_DATA_V, h, toks)
+        assert np.array_equal(kv[h * cfg.tokens + toks].cpu().numpy(), ref)
+    u = torch.empty((50, 64), dtype=torch.float32, device=DEV)
+    gpu.unit_f32(u, 5, synth.ROLE_DATA_K, first_vec=1000)
+    assert np.array_equal(u.cpu().numpy(), synth.unit_vectors_f32(5, synth.ROLE_DATA_K, 50, 64, first=1000))
