@@ -32,12 +32,17 @@
  *  - Inputs with ||x|| >= 65504 overflow the fp16 norm and are out of
  *    contract (stored norm becomes inf); non-finite inputs likewise.
  *
- * Packed layout of one vector (the contract tests are bit-exact on):
- *  - codes: uint32 [mse_bits][d/32]. Bit k of word w of plane p is bit p of
- *    the code index of rotated coordinate 32 w + k. The code index of a
+ * Packed layout of one vector (the contract tests are bit-exact on). The
+ * layout is group-major: the d rotated coordinates form d/8 groups, group c
+ * holding coordinates c + (d/8) t for t = 0..7.
+ *  - codes: a little-endian bit stream of mse_bits * d bits stored as uint32
+ *    words (stream bit k = bit k%32 of word k/32). Group c occupies stream
+ *    bits [8 b c, 8 b c + 8 b) (b = mse_bits); inside it, code t occupies
+ *    bits [b t, b t + b), least significant bit first. The code of a
  *    coordinate y is the number of boundaries strictly below y.
- *  - signs: uint32 [qjl_m/32]. Bit k of word w is 1 iff row 32 w + k of S
- *    applied to the residual is >= 0.
+ *  - signs: a stream of qjl_m bits grouped the same way over the projection
+ *    rows: bit t of byte j0 is 1 iff row j0 + (qjl_m/8) t of S applied to the
+ *    residual is >= 0.
  *  - norm: fp16 (RNE) of ||x||; rnorm: fp16 (RNE) of the residual norm of the
  *    rotated unit vector.
  *  Vector v of an array of n vectors starts at codes + v*mse_bits*d/32,
@@ -85,7 +90,7 @@ typedef struct tq_quantizer {
 
 /* Packed vectors (device pointers owned by the caller; layout above). */
 typedef struct tq_packed {
-    uint32_t* codes;             /* [n][mse_bits][d/32] */
+    uint32_t* codes;             /* [n][mse_bits * d / 32] */
     uint32_t* signs;             /* [n][qjl_m/32]; NULL if qjl_m == 0 */
     uint16_t* norm;              /* [n] fp16 */
     uint16_t* rnorm;             /* [n] fp16; NULL if qjl_m == 0 */

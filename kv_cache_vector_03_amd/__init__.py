@@ -151,7 +151,7 @@ class Packed:
 
     @classmethod
     def empty(cls, q: Quantizer, n: int, device="cuda") -> "Packed":
-        codes = torch.empty((n, q.mse_bits, q.words), dtype=torch.int32, device=device)
+        codes = torch.empty((n, q.mse_bits * q.words), dtype=torch.int32, device=device)
         signs = torch.empty((n, q.qjl_m // 32), dtype=torch.int32, device=device) if q.qjl_m else None
         norm = torch.empty(n, dtype=torch.int16, device=device)
         rnorm = torch.empty(n, dtype=torch.int16, device=device) if q.qjl_m else None

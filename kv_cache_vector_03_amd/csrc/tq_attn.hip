@@ -39,14 +39,12 @@ __global__ __launch_bounds__(256) void k_scores(const uint32_t* __restrict__ cod
     if (threadIdx.x < L) sc[threadIdx.x] = cent[threadIdx.x];
     const int64_t key = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const bool act = key < n_keys;
-    uint32_t pw[B][W], sw[W];
+    uint32_t cw[B * W], sw[W];
     double nk = 0.0, gk = 0.0;
 #pragma unroll
-    for (int w = 0; w < W; ++w) {
+    for (int w = 0; w < B * W; ++w) cw[w] = act ? codes[key * (B * W) + w] : 0u;
 #pragma unroll
-        for (int b = 0; b < B; ++b) pw[b][w] = act ? codes[key * (B * W) + b * W + w] : 0u;
-        sw[w] = (QJL && act) ? signs[key * W + w] : 0u;
-    }
+    for (int w = 0; w < W; ++w) sw[w] = (QJL && act) ? signs[key * W + w] : 0u;
     if (act) {
         nk = (double)h2f(norm[key]);
         if (QJL) gk = (double)h2f(rnorm[key]) * (1.2533141373155003 / D);
@@ -66,14 +64,16 @@ __global__ __launch_bounds__(256) void k_scores(const uint32_t* __restrict__ cod
 #pragma unroll
         for (int qi = 0; qi < kQT; ++qi) am[qi] = aj[qi] = 0.0;
 #pragma unroll
-        for (int w = 0; w < W; ++w)
-            for (int k = 0; k < 32; ++k) {
-                const int i = 32 * w + k;
+        for (int i = 0; i < D; ++i) {
                 int idx = 0;
 #pragma unroll
-                for (int b = 0; b < B; ++b) idx |= (int)((pw[b][w] >> k) & 1u) << b;
+                for (int b = 0; b < B; ++b) {
+                    const int P = code_bit<D, B>(i, b);
+                    idx |= (int)((cw[P >> 5] >> (P & 31)) & 1u) << b;
+                }
                 const double c = (double)sc[idx];
-                const bool pos = (sw[w] >> k) & 1u;
+                const int SP = sign_bit<D>(i);
+                const bool pos = (sw[SP >> 5] >> (SP & 31)) & 1u;
 #pragma unroll
                 for (int qi = 0; qi < kQT; ++qi) {
                     am[qi] += (double)sq[qi][i] * c;
@@ -142,26 +142,28 @@ __global__ __launch_bounds__(256) void k_decode(const uint32_t* __restrict__ kco
         for (int h = 0; h < kMaxG; ++h) am[h] = aj[h] = 0.f;
         if (t < T) {
             const int64_t v = s * T + t;
+            uint32_t cw[BK * W], sw[W];
 #pragma unroll
-            for (int w = 0; w < W; ++w) {
-                uint32_t pw[BK];
+            for (int w = 0; w < BK * W; ++w) cw[w] = kcodes[v * (BK * W) + w];
 #pragma unroll
-                for (int b = 0; b < BK; ++b) pw[b] = kcodes[v * (BK * W) + b * W + w];
-                const uint32_t sw = QJL ? ksigns[v * W + w] : 0u;
-                for (int k = 0; k < 32; ++k) {
-                    const int i = 32 * w + k;
-                    int idx = 0;
+            for (int w = 0; w < W; ++w) sw[w] = QJL ? ksigns[v * W + w] : 0u;
+#pragma unroll 8
+            for (int i = 0; i < D; ++i) {
+                int idx = 0;
 #pragma unroll
-                    for (int b = 0; b < BK; ++b) idx |= (int)((pw[b] >> k) & 1u) << b;
-                    const float c = kc[idx];
-                    const float sg = ((sw >> k) & 1u) ? 1.f : -1.f;
-#pragma unroll
-                    for (int h = 0; h < kMaxG; ++h)
-                        if (h < G) {
-                            am[h] += sq[h][i] * c;
-                            if (QJL) aj[h] += sp[h][i] * sg;
-                        }
+                for (int b = 0; b < BK; ++b) {
+                    const int P = code_bit<D, BK>(i, b);
+                    idx |= (int)((cw[P >> 5] >> (P & 31)) & 1u) << b;
                 }
+                const float c = kc[idx];
+                const int SP = sign_bit<D>(i);
+                const float sg = ((sw[SP >> 5] >> (SP & 31)) & 1u) ? 1.f : -1.f;
+#pragma unroll
+                for (int h = 0; h < kMaxG; ++h)
+                    if (h < G) {
+                        am[h] += sq[h][i] * c;
+                        if (QJL) aj[h] += sp[h][i] * sg;
+                    }
             }
             const float nk = h2f(knorm[v]);
             const float gk = QJL ? h2f(krnorm[v]) * (kSqrtHalfPi / (float)D) : 0.f;
@@ -204,7 +206,10 @@ __global__ __launch_bounds__(256) void k_decode(const uint32_t* __restrict__ kco
         for (int tt = 0; tt < kTC; ++tt) {
             int idx = 0;
 #pragma unroll
-            for (int b = 0; b < BV; ++b) idx |= (int)((vw[tt][b * W + (i >> 5)] >> (i & 31)) & 1u) << b;
+            for (int b = 0; b < BV; ++b) {
+                const int P = code_bit<D, BV>(i, b);
+                idx |= (int)((vw[tt][P >> 5] >> (P & 31)) & 1u) << b;
+            }
             acc += z[h][tt] * vn[tt] * vc[idx];
         }
         parts[(((int64_t)s * n_chunks + chunk) * G + h) * (D + 2) + 2 + i] = acc;

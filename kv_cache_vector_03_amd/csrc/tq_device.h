@@ -87,6 +87,49 @@ __device__ __forceinline__ float pick(const float (&c)[L], int k)
     return v;
 }
 
+// Group-major packed layout: the D coordinates form D/8 groups, group c
+// holding coordinates c + (D/8) t for t = 0..7. Code bit p of coordinate i
+// sits at bit code_bit(i, p) of the vector's little-endian code stream; the
+// sign of projection row j at bit sign_bit(j) of the sign stream.
+template <int D, int B>
+__host__ __device__ constexpr int code_bit(int i, int p)
+{
+    return 8 * B * (i % (D / 8)) + B * (i / (D / 8)) + p;
+}
+
+template <int M>
+__host__ __device__ constexpr int sign_bit(int j)
+{
+    return 8 * (j % (M / 8)) + j / (M / 8);
+}
+
+// Replace lane LN of a VGPR with a wave-uniform value (v_writelane_b32 with an
+// immediate lane select; it ignores EXEC and leaves the other lanes untouched).
+template <int LN>
+__device__ __forceinline__ uint32_t write_lane(uint32_t dst, uint32_t val)
+{
+    asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(dst) : "s"(val), "n"(LN));
+    return dst;
+}
+
+template <int V>
+struct ic {
+    static constexpr int value = V;
+};
+
+// compile-time loop: f(ic<I>{}) for I in [B, E)
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    if constexpr (B < E) {
+        f(ic<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
 // sqrt(pi/2)
 constexpr float kSqrtHalfPi = 1.2533141373155003f;
 

@@ -1,14 +1,29 @@
 // Quantize, query preparation and dequantize kernels.
 //
-// Quantize (one wave per vector; lane l, slot r holds coordinate 64 r + l):
-//   norm by a wave reduction -> sign flips of the random diagonal -> wave
-//   FWHT -> scale by 1/(sqrt(d) n) -> code index by counting boundaries below
-//   each coordinate -> one ballot per bit plane and slot gives two packed
-//   words directly (bit k of the ballot is coordinate 64 r + k) -> with QJL:
-//   residual r = y - c[idx], its norm, projections S r (one row per lane),
-//   and a ballot of the signs.
-// The method is the two-stage quantizer of "[Benchmark] TurboQuant 實測：KV
-// Cache 3-bit 壓縮，真的零損失？", section "TurboQuant 是什麼：30 秒懶人包".
+// The quantizer is the two-stage method of "[Benchmark] TurboQuant 實測：KV
+// Cache 3-bit 壓縮，真的零損失？", section "TurboQuant 是什麼：30 秒懶人包":
+// random rotation, stored norm, per-coordinate Lloyd-Max codes, and for keys
+// a 1-bit Johnson-Lindenstrauss sketch of the residual plus its norm.
+//
+// d = 64, 128: "quad" kernel. Four lanes own one vector (lanes v, v+16, v+32,
+// v+48 of a wave; 16 vectors per wave pass), which is exactly the row layout
+// of the 16x16x32 MFMA A operand. Each lane loads a contiguous quarter of its
+// vector (staged through LDS so the global loads are fully coalesced), runs
+// the Walsh-Hadamard butterflies of the quarter's index bits in registers,
+// and finishes the two remaining butterflies with permlane16/32 swaps that
+// also transpose which coordinates a lane owns: afterwards a lane holds whole
+// code groups (coordinates c + (d/8) t, t = 0..7), so it can pack its part of
+// the group-major code stream alone. Codes come from sign bits: with the
+// symmetric codebook, the top code bit is [y > 0] and the lower bits are the
+// magnitude count #{M_j < |y|} (XOR-folded from the signs of M_j - |y|),
+// complemented for y <= 0; thresholds are scaled by sqrt(d) ||x|| instead of
+// normalising every coordinate. For keys the residual is split into fp16
+// hi + lo parts (both exact operands) and projected on MFMA against the fp16
+// matrix S; row order of S is permuted so that each ballot of the MFMA output
+// is two ready bytes of the group-major sign stream.
+//
+// d = 256: wave kernel (one wave per vector, coordinate 64 r + lane), packing
+// through LDS.
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -17,19 +32,326 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
+// ---------------------------------------------------------------- quad kernel
+
+template <int D>
+struct QuadShape {
+    static constexpr int Q4 = D / 4;                 // values per lane
+    static constexpr int LOG = D == 64 ? 6 : 7;
+    static constexpr int Y1 = LOG - 5, Y2 = LOG - 4; // coordinate bits that become lane bits
+    static constexpr int MY1 = 1 << Y1, MY2 = 1 << Y2;
+    static constexpr int G = D / 8, GL = D / 32;     // groups, groups per lane
+    static constexpr int KS = D / 32;                // MFMA k-steps
+    static constexpr int NT = D / 16;                // MFMA n-tiles (m = d rows of S)
+
+    // coordinate held in register r by lane quarter q after the transform
+    __host__ __device__ static constexpr int coord(int q, int r)
+    {
+        return (r & ~(MY1 | MY2)) | ((q & 1) << Y1) | ((q >> 1) << Y2) | (((r >> Y1) & 1) << (LOG - 2)) |
+               (((r >> Y2) & 1) << (LOG - 1));
+    }
+    // register holding code t of local group g (the same in every lane)
+    __host__ __device__ static constexpr int reg(int g, int t)
+    {
+        return g | (((t >> 1) & 1) << Y1) | (((t >> 2) & 1) << Y2) | ((t & 1) << (LOG - 3));
+    }
+    // S row feeding column n of n-tile nu (sign stream bits 16 nu .. 16 nu + 15)
+    __host__ __device__ static constexpr int proj_row(int nu, int n)
+    {
+        return 2 * nu + n / 8 + (D / 8) * (n % 8);
+    }
+};
+
 template <int D, int B, bool QJL, bool F16>
-__global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, int64_t n,
-                                                  const float* __restrict__ cent,
-                                                  const float* __restrict__ bnd,
-                                                  const uint32_t* __restrict__ diag,
-                                                  const uint16_t* __restrict__ S,
-                                                  uint32_t* __restrict__ codes,
-                                                  uint32_t* __restrict__ signs,
-                                                  uint16_t* __restrict__ norm,
-                                                  uint16_t* __restrict__ rnorm)
+__global__ __launch_bounds__(256) void k_quantize_quad(const void* __restrict__ x, int64_t n,
+                                                       const float* __restrict__ cent,
+                                                       const float* __restrict__ bnd,
+                                                       const uint32_t* __restrict__ diag,
+                                                       const uint16_t* __restrict__ S,
+                                                       uint32_t* __restrict__ codes,
+                                                       uint32_t* __restrict__ signs,
+                                                       uint16_t* __restrict__ norm,
+                                                       uint16_t* __restrict__ rnorm)
 {
-    constexpr int R = D / 64, L = 1 << B, W = D / 32;
+    using Sh = QuadShape<D>;
+    constexpr int Q4 = Sh::Q4, GL = Sh::GL, KS = Sh::KS, NT = Sh::NT;
+    constexpr int L = 1 << B, K = L / 2 - 1;
+    constexpr int ES = F16 ? 2 : 4;
+    constexpr int NV = 16;                           // vectors per wave pass
+    constexpr int ROW = D * ES + 16;                 // padded LDS row (conflict-free reads)
+    constexpr int CH = NV * D * ES / (16 * 64);      // 16-byte chunks per lane per pass
+    constexpr int LBITS = 8 * B * GL;                // code-stream bits owned by a lane
+    constexpr int LW = (LBITS + 31) / 32;
+    constexpr int CW = B * D / 32;                   // code words per vector
+    constexpr int SWN = D / 32;                      // sign words per vector
+
+    __shared__ __align__(16) unsigned char stage[kWavesPerBlock][NV * ROW];
+    __shared__ __align__(16) half8_t bfrag[QJL ? KS * NT * 64 : 1];
+
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int v = lane & 15, q = lane >> 4;
+
+    float Mth[K > 0 ? K : 1], Cm[K + 1];
+#pragma unroll
+    for (int j = 1; j <= K; ++j) Mth[j - 1] = bnd[L / 2 - 1 + j];
+#pragma unroll
+    for (int m = 0; m <= K; ++m) Cm[m] = cent[L / 2 + m];
+
+    // sign flips of this lane's initial coordinates q*Q4 + k
+    uint32_t fl[F16 ? Q4 / 2 : Q4];
+    {
+        uint32_t dbits[(Q4 + 31) / 32];
+#pragma unroll
+        for (int w = 0; w < (Q4 + 31) / 32; ++w) {
+            const int c0 = q * Q4 + 32 * w;
+            const uint32_t word = diag[c0 >> 5];
+            dbits[w] = Q4 >= 32 ? word : (word >> (c0 & 31));
+        }
+#pragma unroll
+        for (int k = 0; k < Q4; ++k) {
+            const uint32_t b = (dbits[k >> 5] >> (k & 31)) & 1u;
+            if constexpr (F16) {
+                if (k & 1) fl[k >> 1] |= b << 31;
+                else fl[k >> 1] = b << 15;
+            } else {
+                fl[k] = b << 31;
+            }
+        }
+    }
+
+    if constexpr (QJL) {
+        // B fragments: lane (qq, nn) of fragment (t, nu) holds S[proj_row(nu, nn)][coord(qq, 8t + e)]
+        for (int e = threadIdx.x; e < KS * NT * 64; e += 256) {
+            const int t = e / (NT * 64), nu = (e / 64) % NT, ln = e & 63;
+            const int qq = ln >> 4, nn = ln & 15;
+            const uint16_t* row = S + (int64_t)Sh::proj_row(nu, nn) * D;
+            half8_t f;
+#pragma unroll
+            for (int ee = 0; ee < 8; ++ee) {
+                const uint16_t h = row[Sh::coord(qq, 8 * t + ee)];
+                f[ee] = __builtin_bit_cast(_Float16, h);
+            }
+            bfrag[(t * NT + nu) * 64 + ln] = f;
+        }
+    }
+
+    const unsigned char* xb = static_cast<const unsigned char*>(x);
+    unsigned char* st = stage[wid];
+
+    for (int64_t base = (int64_t)blockIdx.x * (kWavesPerBlock * NV); base < n;
+         base += (int64_t)gridDim.x * (kWavesPerBlock * NV)) {
+        const int64_t vb = base + (int64_t)wid * NV;
+        // coalesced load of NV vectors into this wave's staging rows
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int off = (c * 64 + lane) * 16;
+            const int vec = off / (D * ES), in = off % (D * ES);
+            uint4 val = make_uint4(0, 0, 0, 0);
+            if (vb + vec < n) val = *reinterpret_cast<const uint4*>(xb + (vb * D) * ES + off);
+            *reinterpret_cast<uint4*>(st + vec * ROW + in) = val;
+        }
+        __syncthreads();
+
+        // this lane's quarter, with the diagonal flips and the first butterfly
+        float y[Q4];
+        float ss = 0.f;
+        if constexpr (F16) {
+#pragma unroll
+            for (int c = 0; c < Q4 / 8; ++c) {
+                const uint4 u = *reinterpret_cast<const uint4*>(st + v * ROW + q * Q4 * 2 + 16 * c);
+                const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t pr = w4[i] ^ fl[4 * c + i];
+                    const float a = h2f((uint16_t)(pr & 0xFFFF)), b = h2f((uint16_t)(pr >> 16));
+                    ss += a * a + b * b;
+                    y[8 * c + 2 * i] = a + b;
+                    y[8 * c + 2 * i + 1] = a - b;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < Q4 / 4; ++c) {
+                const uint4 u = *reinterpret_cast<const uint4*>(st + v * ROW + q * Q4 * 4 + 16 * c);
+                const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int i = 0; i < 4; i += 2) {
+                    const float a = __uint_as_float(w4[i] ^ fl[4 * c + i]);
+                    const float b = __uint_as_float(w4[i + 1] ^ fl[4 * c + i + 1]);
+                    ss += a * a + b * b;
+                    y[4 * c + i] = a + b;
+                    y[4 * c + i + 1] = a - b;
+                }
+            }
+        }
+        // remaining in-register butterflies (register bits 1 .. log2(Q4)-1)
+#pragma unroll
+        for (int h = 2; h < Q4; h <<= 1)
+#pragma unroll
+            for (int r = 0; r < Q4; ++r)
+                if (!(r & h)) {
+                    const float a = y[r], b = y[r + h];
+                    y[r] = a + b;
+                    y[r + h] = a - b;
+                }
+        // butterfly on index bit log2(d)-2 across lanes q^1; the swap leaves each
+        // lane holding one value of coordinate bit Y1 (register bit Y1 now means bit log2(d)-2)
+#pragma unroll
+        for (int r = 0; r < Q4; ++r)
+            if (!(r & Sh::MY1)) {
+                const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(y[r]),
+                                                                __float_as_uint(y[r | Sh::MY1]), false, false);
+                const float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
+                y[r] = a + b;
+                y[r | Sh::MY1] = a - b;
+            }
+        // butterfly on index bit log2(d)-1 across lanes q^2 (lane bit becomes Y2)
+#pragma unroll
+        for (int r = 0; r < Q4; ++r)
+            if (!(r & Sh::MY2)) {
+                const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(y[r]),
+                                                                __float_as_uint(y[r | Sh::MY2]), false, false);
+                const float a = __uint_as_float(p[0]), b = __uint_as_float(p[1]);
+                y[r] = a + b;
+                y[r | Sh::MY2] = a - b;
+            }
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        const float nrm = sqrtf(ss);
+        const float s = nrm > 0.f ? sqrtf((float)D) * nrm : 1.0f;
+        float Ms[K > 0 ? K : 1], Cs[K + 1];
+#pragma unroll
+        for (int j = 0; j < K; ++j) Ms[j] = Mth[j] * s;
+#pragma unroll
+        for (int m = 0; m <= K; ++m) Cs[m] = Cm[m] * s;
+
+        // codes: stream bits in descending order, shifted into LW words
+        uint32_t W[LW];
+#pragma unroll
+        for (int w = 0; w < LW; ++w) W[w] = 0;
+        float g2 = 0.f;
+#pragma unroll
+        for (int gp = GL - 1; gp >= 0; --gp)
+#pragma unroll
+            for (int t = 7; t >= 0; --t) {
+                const int r = Sh::reg(gp, t);
+                const float Y = y[r];
+                const uint32_t d2 = __float_as_uint(0.0f - Y);     // sign bit = [Y > 0]
+                uint32_t e[K > 0 ? K : 1];
+#pragma unroll
+                for (int j = 0; j < K; ++j) e[j] = __float_as_uint(Ms[j] - fabsf(Y));  // [|Y| > M_j s]
+#pragma unroll
+                for (int p = B - 1; p >= 0; --p) {
+                    uint32_t val;
+                    if (p == B - 1) {
+                        val = d2;
+                    } else {
+                        uint32_t xq = 0;
+#pragma unroll
+                        for (int j = 1; j <= K; ++j)
+                            if (j % (1 << p) == 0) xq ^= e[j - 1];
+                        val = ~(xq ^ d2);
+                    }
+                    const int P = 8 * B * gp + B * t + p;
+                    W[P >> 5] = __builtin_amdgcn_alignbit(W[P >> 5], val, 31);
+                }
+                if constexpr (QJL) {
+                    float mag = Cs[0];
+#pragma unroll
+                    for (int j = 0; j < K; ++j) mag = fabsf(Y) > Ms[j] ? Cs[j + 1] : mag;
+                    // c = +mag for Y > 0, -mag otherwise (y = 0 maps to the level just below 0)
+                    const float c = __uint_as_float((__float_as_uint(mag) & 0x7FFFFFFFu) | (~d2 & 0x80000000u));
+                    const float rr = Y - c;
+                    g2 += rr * rr;
+                    y[r] = rr;
+                }
+            }
+
+        const int64_t vec = vb + v;
+        const bool live = vec < n;
+        if (live) {
+            if constexpr (LBITS % 32 == 0) {
+                uint32_t* dst = codes + vec * CW + q * LW;
+#pragma unroll
+                for (int w = 0; w < LW; ++w) dst[w] = W[w];
+            } else {
+                uint16_t* dst = reinterpret_cast<uint16_t*>(codes + vec * CW) + q * (LBITS / 16);
+#pragma unroll
+                for (int h = 0; h < LBITS / 16; ++h) dst[h] = (uint16_t)(W[h >> 1] >> (16 * (h & 1)));
+            }
+        }
+
+        if constexpr (QJL) {
+            g2 += __shfl_xor(g2, 16);
+            g2 += __shfl_xor(g2, 32);
+            // residual in units of 1/(1024 s) (fp16 range), split into exact fp16 hi + lo
+            const float sc = 1024.0f / s;
+            half8_t ahi[KS], alo[KS];
+#pragma unroll
+            for (int t = 0; t < KS; ++t)
+#pragma unroll
+                for (int e2 = 0; e2 < 8; ++e2) {
+                    const float rs = y[8 * t + e2] * sc;
+                    const _Float16 hi = (_Float16)rs;
+                    ahi[t][e2] = hi;
+                    alo[t][e2] = (_Float16)(rs - (float)hi);
+                }
+            uint32_t SW[SWN];
+#pragma unroll
+            for (int w = 0; w < SWN; ++w) SW[w] = 0;
+#pragma unroll
+            for (int nu = 0; nu < NT; nu += 2) {
+                uint64_t mk[2][4];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int t = 0; t < KS; ++t) {
+                        const half8_t bf = bfrag[(t * NT + nu + hh) * 64 + lane];
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[t], bf, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[t], bf, acc, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) mk[hh][r4] = __ballot(acc[r4] >= 0.f);
+                }
+                // output row 4 g + r4 is vector 4 g + r4 of the pass; its 16 bits in each
+                // ballot are bits 16 g .. 16 g + 15
+                uint32_t sw = SW[nu >> 1];
+                static_for<0, 16>([&](auto k) {
+                    constexpr int g = decltype(k)::value / 4, r4 = decltype(k)::value % 4;
+                    const uint32_t lo = (uint32_t)(mk[0][r4] >> (16 * g)) & 0xFFFFu;
+                    const uint32_t hi = (uint32_t)(mk[1][r4] >> (16 * g)) & 0xFFFFu;
+                    sw = write_lane<4 * g + r4>(sw, lo | (hi << 16));
+                });
+                SW[nu >> 1] = sw;
+            }
+            if (live && q == 0) {
+#pragma unroll
+                for (int w = 0; w < SWN; ++w) signs[vec * SWN + w] = SW[w];
+                rnorm[vec] = f2h(sqrtf(g2) / s);
+            }
+        }
+        if (live && q == 0) norm[vec] = f2h(nrm);
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- wave kernel (d = 256)
+
+template <int D, int B, bool QJL, bool F16>
+__global__ __launch_bounds__(256) void k_quantize_wave(const void* __restrict__ x, int64_t n,
+                                                       const float* __restrict__ cent,
+                                                       const float* __restrict__ bnd,
+                                                       const uint32_t* __restrict__ diag,
+                                                       const uint16_t* __restrict__ S,
+                                                       uint32_t* __restrict__ codes,
+                                                       uint32_t* __restrict__ signs,
+                                                       uint16_t* __restrict__ norm,
+                                                       uint16_t* __restrict__ rnorm)
+{
+    constexpr int R = D / 64, L = 1 << B, G = D / 8;
     __shared__ float res[kWavesPerBlock][D];
+    __shared__ unsigned char cidx[kWavesPerBlock][D];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     float t[L - 1], c[L];
 #pragma unroll
@@ -44,7 +366,6 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
         const int64_t v = base + wid;
         const bool active = v < n;
         float y[R];
-        int idx[R];
         float ss = 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -56,52 +377,55 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
         for (int r = 0; r < R; ++r) y[r] = flip(y[r], dm[r]);
         fwht_wave<R>(y, lane);
         const float sc = nrm > 0.f ? 1.0f / (sqrtf((float)D) * nrm) : 0.f;
-        uint32_t myword = 0;
+        float g2 = 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             y[r] *= sc;
             int k = 0;
 #pragma unroll
             for (int l = 0; l < L - 1; ++l) k += (t[l] < y[r]) ? 1 : 0;
-            idx[r] = k;
-#pragma unroll
-            for (int p = 0; p < B; ++p) {
-                const uint64_t m = __ballot((k >> p) & 1);
-                if (lane == p * W + 2 * r) myword = (uint32_t)m;
-                if (lane == p * W + 2 * r + 1) myword = (uint32_t)(m >> 32);
-            }
-        }
-        if (active) {
-            if (lane < B * W) codes[v * (B * W) + lane] = myword;
-            if (lane == 0) norm[v] = f2h(nrm);
-        }
-        if constexpr (QJL) {
-            float g2 = 0.f;
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                float rr = y[r] - pick<L>(c, idx[r]);
+            cidx[wid][64 * r + lane] = (unsigned char)k;
+            if (QJL) {
+                const float rr = y[r] - pick<L>(c, k);
                 g2 += rr * rr;
                 res[wid][64 * r + lane] = rr;
             }
+        }
+        __syncthreads();
+        // one lane per group packs its 8 codes (8 B bits) into the byte stream
+        if (active && lane < G) {
+            uint32_t f = 0;
+#pragma unroll
+            for (int tt = 0; tt < 8; ++tt) f |= (uint32_t)cidx[wid][lane + G * tt] << (B * tt);
+            unsigned char* dst = reinterpret_cast<unsigned char*>(codes + v * (B * D / 32)) + B * lane;
+#pragma unroll
+            for (int b = 0; b < B; ++b) dst[b] = (unsigned char)(f >> (8 * b));
+        }
+        if (active && lane == 0) norm[v] = f2h(nrm);
+        if constexpr (QJL) {
             g2 = wave_sum(g2);
-            __syncthreads();
-            uint32_t sword = 0;
+            uint32_t sb[R];
 #pragma unroll
             for (int k = 0; k < R; ++k) {
                 const int j = 64 * k + lane;
                 const uint16_t* Sj = S + (int64_t)j * D;
                 float u = 0.f;
                 for (int i = 0; i < D; ++i) u += h2f(Sj[i]) * res[wid][i];
-                const uint64_t m = __ballot(u >= 0.f);
-                if (lane == 2 * k) sword = (uint32_t)m;
-                if (lane == 2 * k + 1) sword = (uint32_t)(m >> 32);
-            }
-            if (active) {
-                if (lane < W) signs[v * W + lane] = sword;
-                if (lane == 0) rnorm[v] = f2h(sqrtf(g2));
+                sb[k] = u >= 0.f ? 1u : 0u;
             }
             __syncthreads();
+#pragma unroll
+            for (int k = 0; k < R; ++k) cidx[wid][64 * k + lane] = (unsigned char)sb[k];
+            __syncthreads();
+            if (active && lane < G) {
+                uint32_t f = 0;
+#pragma unroll
+                for (int tt = 0; tt < 8; ++tt) f |= (uint32_t)cidx[wid][lane + G * tt] << tt;
+                reinterpret_cast<unsigned char*>(signs + v * (D / 32))[lane] = (unsigned char)f;
+            }
+            if (active && lane == 0) rnorm[v] = f2h(sqrtf(g2));
         }
+        __syncthreads();
     }
 }
 
@@ -126,8 +450,8 @@ __global__ __launch_bounds__(256) void k_qprep(const void* __restrict__ q, int64
         double y[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const float x = active ? load_elem<F16>(q, a * D + 64 * r + lane) : 0.f;
-            y[r] = (double)flip(x, dm[r]);
+            const float xv = active ? load_elem<F16>(q, a * D + 64 * r + lane) : 0.f;
+            y[r] = (double)flip(xv, dm[r]);
         }
         fwht_wave<R>(y, lane);
         const double sc = 1.0 / sqrt((double)D);
@@ -163,7 +487,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint32_t* __restrict__
                                                     const uint16_t* __restrict__ S,
                                                     void* __restrict__ out)
 {
-    constexpr int R = D / 64, W = D / 32, L = 1 << B;
+    constexpr int R = D / 64, L = 1 << B, CW = B * D / 32;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     float c[L];
 #pragma unroll
@@ -174,26 +498,30 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint32_t* __restrict__
          base += (int64_t)gridDim.x * kWavesPerBlock) {
         const int64_t v = base + wid;
         if (v >= n) continue;  // no block-level synchronisation below
-        const uint32_t* cv = codes + v * (B * W);
+        const uint32_t* cv = codes + v * CW;
         float a[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int i = 64 * r + lane;
             int k = 0;
 #pragma unroll
-            for (int p = 0; p < B; ++p) k |= (int)((cv[p * W + (i >> 5)] >> (i & 31)) & 1u) << p;
+            for (int p = 0; p < B; ++p) {
+                const int P = code_bit<D, B>(i, p);
+                k |= (int)((cv[P >> 5] >> (P & 31)) & 1u) << p;
+            }
             a[r] = pick<L>(c, k);
         }
         if constexpr (QJL) {
             const float g = h2f(rnorm[v]) * (kSqrtHalfPi / (float)D);
-            const uint32_t* sv = signs + v * W;
+            const uint32_t* sv = signs + v * (D / 32);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int i = 64 * r + lane;
                 float acc = 0.f;
                 for (int j = 0; j < D; ++j) {
-                    const float s = ((sv[j >> 5] >> (j & 31)) & 1u) ? 1.f : -1.f;
-                    acc += h2f(S[(int64_t)j * D + i]) * s;
+                    const int P = sign_bit<D>(j);
+                    const float sg = ((sv[P >> 5] >> (P & 31)) & 1u) ? 1.f : -1.f;
+                    acc += h2f(S[(int64_t)j * D + i]) * sg;
                 }
                 a[r] += g * acc;
             }
@@ -210,10 +538,10 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint32_t* __restrict__
     }
 }
 
-int grid_for(int64_t units, int per_block)
+int grid_for(int64_t units, int per_block, int cap = 65536)
 {
     int64_t b = (units + per_block - 1) / per_block;
-    return (int)(b < 65536 ? b : 65536);
+    return (int)(b < cap ? b : cap);
 }
 
 int device_status(const char* who)
@@ -229,13 +557,24 @@ template <int D, int B, bool QJL>
 void quantize_d_b(const tq_quantizer* q, const void* x, int dtype, int64_t n, const tq_packed* o,
                   hipStream_t s)
 {
-    dim3 grid(grid_for(n, kWavesPerBlock)), block(256);
-    if (dtype == TQ_F16)
-        hipLaunchKernelGGL((k_quantize<D, B, QJL, true>), grid, block, 0, s, x, n, q->centroids,
-                           q->boundaries, q->diag_signs, q->S, o->codes, o->signs, o->norm, o->rnorm);
-    else
-        hipLaunchKernelGGL((k_quantize<D, B, QJL, false>), grid, block, 0, s, x, n, q->centroids,
-                           q->boundaries, q->diag_signs, q->S, o->codes, o->signs, o->norm, o->rnorm);
+    dim3 block(256);
+    if constexpr (D <= 128) {
+        dim3 grid(grid_for(n, kWavesPerBlock * 16, 1024));
+        if (dtype == TQ_F16)
+            hipLaunchKernelGGL((k_quantize_quad<D, B, QJL, true>), grid, block, 0, s, x, n, q->centroids,
+                               q->boundaries, q->diag_signs, q->S, o->codes, o->signs, o->norm, o->rnorm);
+        else
+            hipLaunchKernelGGL((k_quantize_quad<D, B, QJL, false>), grid, block, 0, s, x, n, q->centroids,
+                               q->boundaries, q->diag_signs, q->S, o->codes, o->signs, o->norm, o->rnorm);
+    } else {
+        dim3 grid(grid_for(n, kWavesPerBlock));
+        if (dtype == TQ_F16)
+            hipLaunchKernelGGL((k_quantize_wave<D, B, QJL, true>), grid, block, 0, s, x, n, q->centroids,
+                               q->boundaries, q->diag_signs, q->S, o->codes, o->signs, o->norm, o->rnorm);
+        else
+            hipLaunchKernelGGL((k_quantize_wave<D, B, QJL, false>), grid, block, 0, s, x, n, q->centroids,
+                               q->boundaries, q->diag_signs, q->S, o->codes, o->signs, o->norm, o->rnorm);
+    }
 }
 
 template <int D>

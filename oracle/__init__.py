@@ -172,7 +172,7 @@ class Quantizer:
 
 @dataclass
 class Packed:
-    codes: np.ndarray    # uint32 [n, bits, words]
+    codes: np.ndarray    # uint32 [n, bits * words] (group-major bit stream)
     signs: np.ndarray    # uint32 [n, sign_words] (empty when m = 0)
     norm: np.ndarray     # uint16 [n] fp16 bits
     rnorm: np.ndarray    # uint16 [n] fp16 bits (zeros when m = 0)
@@ -187,7 +187,7 @@ class Packed:
 
 
 def empty_packed(Q: Quantizer, n: int) -> Packed:
-    return Packed(np.zeros((n, Q.bits, Q.words), np.uint32),
+    return Packed(np.zeros((n, Q.bits * Q.words), np.uint32),
                   np.zeros((n, max(Q.sign_words, 0)), np.uint32),
                   np.zeros(n, np.uint16), np.zeros(n, np.uint16))
 
@@ -257,18 +257,27 @@ def decode_attn(QK: Quantizer, QV: Quantizer, PK: Packed, PV: Packed, n_streams:
     return out.reshape(n_streams, G, QV.d)
 
 
+def _group_bit(n: int, bits: int, i: np.ndarray, p: int) -> np.ndarray:
+    """Stream bit of code bit p of coordinate i in the group-major layout."""
+    G = n // 8 if n >= 8 else 1
+    return 8 * bits * (i % G) + bits * (i // G) + p
+
+
 def unpack_codes(Q: Quantizer, codes: np.ndarray) -> np.ndarray:
-    """Code indices [n, d] from the bit-plane layout (test helper)."""
-    codes = np.asarray(codes, np.uint32).reshape(-1, Q.bits, Q.words)
+    """Code indices [n, d] from the group-major packed layout (test helper)."""
+    codes = np.asarray(codes, np.uint32).reshape(-1, Q.bits * Q.words)
     i = np.arange(Q.d)
     out = np.zeros((codes.shape[0], Q.d), np.int64)
     for p in range(Q.bits):
-        bits = (codes[:, p, i // 32] >> (i % 32).astype(np.uint32)) & 1
+        b = _group_bit(Q.d, Q.bits, i, p)
+        bits = (codes[:, b // 32] >> (b % 32).astype(np.uint32)) & 1
         out |= bits.astype(np.int64) << p
     return out
 
 
 def unpack_signs(Q: Quantizer, signs: np.ndarray) -> np.ndarray:
+    """Sign bits [n, m] (1 = projection >= 0) from the group-major layout."""
     signs = np.asarray(signs, np.uint32).reshape(-1, Q.sign_words)
     j = np.arange(Q.m)
-    return ((signs[:, j // 32] >> (j % 32).astype(np.uint32)) & 1).astype(np.int64)
+    b = _group_bit(Q.m, 1, j, 0)
+    return ((signs[:, b // 32] >> (b % 32).astype(np.uint32)) & 1).astype(np.int64)

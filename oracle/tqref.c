@@ -31,9 +31,13 @@
  *  - norm and gamma stored as fp16 (RNE); later steps use the stored values;
  *  - zero vector: y := 0.
  *
- * Packed layout: codes[v][p][w] (uint32), bit k of word w of plane p is bit p
- * of the code index of coordinate 32 w + k; signs[v][w] bit k is the sign bit
- * of projection row 32 w + k.
+ * Packed layout (group-major): the d coordinates form d/8 groups; group c
+ * holds coordinates c + (d/8) t for t = 0..7. A vector's codes are a bit
+ * stream of b*d bits (little-endian: stream bit k is bit k%32 of uint32 word
+ * k/32): group c occupies bits [8 b c, 8 b c + 8 b), and inside it code t
+ * occupies bits [b t, b t + b) with code bit p at b t + p. Signs use the same
+ * grouping of the m projection rows with one bit per code: bit t of byte j0
+ * is the sign bit of row j0 + (m/8) t.
  */
 #include <math.h>
 #include <stdint.h>
@@ -269,6 +273,20 @@ static int diag_sign(const uint32_t* D, int j) { return ((D[j >> 5] >> (j & 31))
 
 static int words_of(int d) { return (d + 31) / 32; }
 
+/* stream bit of code bit p of coordinate i (group-major layout) */
+static int64_t code_bit(int d, int bits, int i, int p)
+{
+    int G = d >= 8 ? d / 8 : 1, c = i % G, t = i / G;
+    return (int64_t)8 * bits * c + (int64_t)bits * t + p;
+}
+
+/* stream bit of the sign of projection row j */
+static int64_t sign_bit(int m, int j)
+{
+    int G = m >= 8 ? m / 8 : 1;
+    return (int64_t)8 * (j % G) + j / G;
+}
+
 /* the d x d matrix H D (entries +-1), built once per call */
 static double* build_HD(const tqref_quantizer* Q)
 {
@@ -323,13 +341,17 @@ void tqref_quantize(const tqref_quantizer* Q, const double* x, int64_t n,
             }
             uint32_t* cv = codes + v * (int64_t)Q->bits * W;
             memset(cv, 0, sizeof(uint32_t) * Q->bits * W);
+            (void)W;
             double g2 = 0;
             for (int i = 0; i < d; ++i) {
                 int k = 0;
                 for (int l = 0; l + 1 < nl; ++l) if ((double)Q->bnd[l] < y[i]) k++;
                 idx[i] = k;
                 for (int p = 0; p < Q->bits; ++p)
-                    if ((k >> p) & 1) cv[p * W + (i >> 5)] |= 1u << (i & 31);
+                    if ((k >> p) & 1) {
+                        int64_t b = code_bit(d, Q->bits, i, p);
+                        cv[b >> 5] |= 1u << (b & 31);
+                    }
                 r[i] = y[i] - (double)Q->cent[k];
                 g2 += r[i] * r[i];
             }
@@ -342,7 +364,10 @@ void tqref_quantize(const tqref_quantizer* Q, const double* x, int64_t n,
                     double u = 0;
                     for (int i = 0; i < d; ++i) u += Sd[(int64_t)j * d + i] * r[i];
                     if (u_out) u_out[v * m + j] = u;
-                    if (u >= 0) sv[j >> 5] |= 1u << (j & 31);
+                    if (u >= 0) {
+                        int64_t b = sign_bit(m, j);
+                        sv[b >> 5] |= 1u << (b & 31);
+                    }
                 }
                 rnorm16[v] = tqref_double_to_half(sqrt(g2));
             }
@@ -353,14 +378,22 @@ void tqref_quantize(const tqref_quantizer* Q, const double* x, int64_t n,
 }
 
 /* code index of coordinate i of packed vector cv */
-static int code_at(const uint32_t* cv, int bits, int W, int i)
+static int code_at(const uint32_t* cv, int d, int bits, int i)
 {
     int k = 0;
-    for (int p = 0; p < bits; ++p) k |= (int)((cv[p * W + (i >> 5)] >> (i & 31)) & 1) << p;
+    for (int p = 0; p < bits; ++p) {
+        int64_t b = code_bit(d, bits, i, p);
+        k |= (int)((cv[b >> 5] >> (b & 31)) & 1) << p;
+    }
     return k;
 }
 
-static int sign_at(const uint32_t* sv, int j) { return ((sv[j >> 5] >> (j & 31)) & 1) ? 1 : -1; }
+/* +1 / -1 from the stored sign of projection row j (m rows) */
+static int sign_at(const uint32_t* sv, int m, int j)
+{
+    int64_t b = sign_bit(m, j);
+    return ((sv[b >> 5] >> (b & 31)) & 1) ? 1 : -1;
+}
 
 /* query prep: qr = H D q / sqrt(d); p = S qr (p only when m > 0) */
 static void prep_query(const tqref_quantizer* Q, const double* Sd, const double* HD,
@@ -378,13 +411,13 @@ static void prep_query(const tqref_quantizer* Q, const double* Sd, const double*
 static double score_one(const tqref_quantizer* Q, const double* qr, const double* p,
                         const uint32_t* cv, const uint32_t* sv, uint16_t n16, uint16_t g16)
 {
-    int d = Q->d, W = words_of(d);
+    int d = Q->d;
     double mse = 0;
-    for (int i = 0; i < d; ++i) mse += qr[i] * (double)Q->cent[code_at(cv, Q->bits, W, i)];
+    for (int i = 0; i < d; ++i) mse += qr[i] * (double)Q->cent[code_at(cv, d, Q->bits, i)];
     double s = mse;
     if (Q->m > 0) {
         double qj = 0;
-        for (int j = 0; j < Q->m; ++j) qj += p[j] * sign_at(sv, j);
+        for (int j = 0; j < Q->m; ++j) qj += p[j] * sign_at(sv, Q->m, j);
         s += tqref_half_to_double(g16) * sqrt(M_PI / 2.0) / Q->m * qj;
     }
     return tqref_half_to_double(n16) * s;
@@ -425,13 +458,13 @@ void tqref_dequantize(const tqref_quantizer* Q, const uint32_t* codes, const uin
 #pragma omp for schedule(static)
         for (int64_t v = 0; v < n; ++v) {
             const uint32_t* cv = codes + v * (int64_t)Q->bits * W;
-            for (int i = 0; i < d; ++i) a[i] = Q->cent[code_at(cv, Q->bits, W, i)];
+            for (int i = 0; i < d; ++i) a[i] = Q->cent[code_at(cv, d, Q->bits, i)];
             if (m > 0 && include_qjl) {
                 double g = tqref_half_to_double(rnorm16[v]) * sqrt(M_PI / 2.0) / m;
                 for (int i = 0; i < d; ++i) {
                     double s = 0;
                     for (int j = 0; j < m; ++j)
-                        s += Sd[(int64_t)j * d + i] * sign_at(signs + v * WS, j);
+                        s += Sd[(int64_t)j * d + i] * sign_at(signs + v * WS, m, j);
                     a[i] += g * s;
                 }
             }
@@ -489,7 +522,7 @@ void tqref_decode_attn(const tqref_quantizer* QK, const tqref_quantizer* QV,
                 l += w;
                 double wn = w * tqref_half_to_double(vnorm[v]);
                 const uint32_t* cv = vcodes + v * (int64_t)QV->bits * WV;
-                for (int i = 0; i < QV->d; ++i) acc[i] += wn * (double)QV->cent[code_at(cv, QV->bits, WV, i)];
+                for (int i = 0; i < QV->d; ++i) acc[i] += wn * (double)QV->cent[code_at(cv, QV->d, QV->bits, i)];
             }
             for (int j = 0; j < QV->d; ++j) {
                 double sacc = 0;

@@ -61,17 +61,20 @@ def test_one_hot_codes_and_packed_words():
     # 2-bit: |y| = 1/sqrt(d) lies above the outer boundary 0.981/sqrt(d) -> outer levels
     Q = make_q(d, 2, 0)
     D = dvec(Q)
-    for i, pattern in [(0, None), (1, 0x55555555)]:
+    for i in (0, 1):
         x = np.zeros((1, d))
         x[0, i] = 1.0
         P = oracle.quantize(Q, x)
         idx = oracle.unpack_codes(Q, P.codes)[0]
         H = hadamard(d)[:, i] * D[i]
         assert np.array_equal(idx, np.where(H > 0, 3, 0))
-        if pattern is not None:
-            w = pattern if D[i] > 0 else (~pattern) & 0xFFFFFFFF
-            # code 3 = both plane bits set at the positive coordinates
-            assert np.all(P.codes[0, 0] == w) and np.all(P.codes[0, 1] == w)
+        # group c holds coordinates c + 16 t, all of the parity of c; each group is a
+        # 16-bit field of eight 2-bit codes, two groups per word (even group low)
+        if i == 0:
+            w = 0xFFFFFFFF if D[0] > 0 else 0
+        else:
+            w = 0x0000FFFF if D[1] > 0 else 0xFFFF0000
+        assert np.all(P.codes[0] == w), [hex(v) for v in P.codes[0]]
     # 3-bit: |y| sqrt(d) = 1 lies between boundaries 0.5006 and 1.0500 -> levels 2 / 5
     Q3 = make_q(d, 3, 0)
     x = np.zeros((1, d))
@@ -82,20 +85,35 @@ def test_one_hot_codes_and_packed_words():
     assert np.allclose(Q3.cent[[2, 5]] * np.sqrt(d), [-0.7560, 0.7560], atol=1e-3)
 
 
-def test_packing_bit_layout_against_manual_unpack():
-    d, bits = 128, 3
+@pytest.mark.parametrize("d,bits", [(128, 3), (64, 2), (256, 4), (128, 1)])
+def test_packing_bit_layout_against_manual_pack(d, bits):
+    """Group-major stream: group c = coordinates c + (d/8) t; code t of group c
+    at stream bits 8*bits*c + bits*t .. +bits-1; words little-endian."""
     Q = make_q(d, bits, 0)
     x = synth.normals(9, synth.ROLE_DATA_K, np.arange(16 * d)).reshape(16, d)
     P, y = oracle.quantize(Q, x, want_y=True)
-    # expected code index by counting boundaries below y (ties low)
     idx = (y[:, :, None] > Q.cb.boundaries.astype(np.float64)[None, None, :]).sum(-1)
+    G = d // 8
     for v in range(16):
-        for p in range(bits):
-            for w in range(d // 32):
-                word = 0
-                for k in range(32):
-                    word |= int((idx[v, 32 * w + k] >> p) & 1) << k
-                assert int(P.codes[v, p, w]) == word
+        stream = 0
+        for c in range(G):
+            for t in range(8):
+                stream |= int(idx[v, c + G * t]) << (8 * bits * c + bits * t)
+        words = [(stream >> (32 * w)) & 0xFFFFFFFF for w in range(bits * d // 32)]
+        assert [int(a) for a in P.codes[v]] == words
+
+
+def test_sign_layout_against_manual_pack():
+    d = 128
+    Q = make_q(d, 2, d)
+    x = synth.normals(10, synth.ROLE_DATA_K, np.arange(8 * d)).reshape(8, d)
+    P, u = oracle.quantize(Q, x, want_u=True)
+    for v in range(8):
+        stream = 0
+        for j in range(d):
+            if u[v, j] >= 0:
+                stream |= 1 << (8 * (j % 16) + j // 16)
+        assert [int(a) for a in P.signs[v]] == [(stream >> (32 * w)) & 0xFFFFFFFF for w in range(4)]
 
 
 @pytest.mark.parametrize("d,bits", [(4, 2), (8, 2), (4, 3)])
