@@ -91,17 +91,16 @@ int tq_decode_attn(const tq_quantizer* qk, const tq_quantizer* qv,
     if ((rc = check_packed(qv, v, "tq_decode_attn", "v")) != TQ_OK) return rc;
     if ((rc = check_dense(q, q_dtype, "tq_decode_attn", "q")) != TQ_OK) return rc;
     if ((rc = check_dense(out, TQ_F32, "tq_decode_attn", "out")) != TQ_OK) return rc;
-    size_t need = decode_ws(qk, n_streams, T, G);
-    if (!ws || ws_bytes < need)
-        return fail(TQ_ERR_WORKSPACE, "tq_decode_attn: workspace %zu bytes < %zu", ws_bytes, need);
+    const DecodePlan plan = decode_plan(qk, n_streams, T, G);
+    if (!ws || ws_bytes < plan.total)
+        return fail(TQ_ERR_WORKSPACE, "tq_decode_attn: workspace %zu bytes < %zu", ws_bytes, plan.total);
     if ((uintptr_t)ws % 256) return fail(TQ_ERR_INVALID, "tq_decode_attn: workspace must be 256-byte aligned");
     if (scale == 0.0f) scale = 1.0f / std::sqrt((float)qk->d);
-    int64_t nq = n_streams * G;
-    float* qr = (float*)ws;
-    float* p = (float*)((char*)ws + up256((size_t)nq * qk->d * 4));
-    float* parts = (float*)((char*)ws + scores_ws(qk, nq));
+    const int64_t nq = n_streams * G;
+    float* qr = (float*)((char*)ws + plan.off_qr);
+    float* p = (float*)((char*)ws + plan.off_p);
     if ((rc = launch_qprep(qk, q, q_dtype, nq, qr, p, (hipStream_t)stream)) != TQ_OK) return rc;
-    return launch_decode(qk, qv, k, v, n_streams, T, G, qr, p, scale, out, parts, (hipStream_t)stream);
+    return launch_decode(qk, qv, k, v, n_streams, T, G, plan, ws, scale, out, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void k_decode(const uint32_t* __restrict__ kco
         m = wave_max(m);
         float l = 0.f;
         for (int tt = lane; tt < kTC; tt += 64) {
-            const float w = (z[h][tt] == -INFINITY) ? 0.f : __expf(z[h][tt] - m);
+            const float w = (z[h][tt] == -INFINITY) ? 0.f : exp2f(z[h][tt] - m);
             z[h][tt] = w;
             l += w;
         }
@@ -216,34 +216,60 @@ __global__ __launch_bounds__(256) void k_decode(const uint32_t* __restrict__ kco
     }
 }
 
-// merge chunk partials of one (stream, head) and rotate back to the value domain
+// Merge the chunk partials of one (stream, head) and rotate back to the value
+// domain. Partials hold (max, sum, accumulator) with max in log2 units. Four
+// waves each merge a strided subset of the chunks; wave 0 finishes.
 template <int D>
-__global__ __launch_bounds__(64) void k_combine(const float* __restrict__ parts, int n_chunks, int G,
-                                                const uint32_t* __restrict__ vdiag,
-                                                float* __restrict__ out)
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ parts, int n_chunks, int G,
+                                                 const uint32_t* __restrict__ vdiag,
+                                                 float* __restrict__ out)
 {
     constexpr int R = D / 64;
-    const int lane = threadIdx.x;
+    __shared__ float wm[4], wl[4];
+    __shared__ float wo[4][D];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int64_t sh = blockIdx.x;  // s * G + h
     const int64_t s = sh / G, h = sh % G;
     float M = -INFINITY;
-    for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, parts[((s * n_chunks + c) * G + h) * (D + 2)]);
+    for (int c = wid; c < n_chunks; c += 4) M = fmaxf(M, parts[((s * n_chunks + c) * G + h) * (D + 2)]);
     float acc[R], l = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.f;
-    for (int c = 0; c < n_chunks; ++c) {
+    for (int c = wid; c < n_chunks; c += 4) {
         const float* part = parts + ((s * n_chunks + c) * G + h) * (D + 2);
         const float m = part[0];
         if (m == -INFINITY) continue;
-        const float f = __expf(m - M);
+        const float f = exp2f(m - M);
         l += f * part[1];
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] += f * part[2 + 64 * r + lane];
     }
+    if (lane == 0) {
+        wm[wid] = M;
+        wl[wid] = l;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) wo[wid][64 * r + lane] = acc[r];
+    __syncthreads();
+    if (wid != 0) return;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) Mx = fmaxf(Mx, wm[w]);
+    float L = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        if (wm[w] == -INFINITY) continue;
+        const float f = exp2f(wm[w] - Mx);
+        L += f * wl[w];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] += f * wo[w][64 * r + lane];
+    }
     fwht_wave<R>(acc, lane);
     uint32_t dm[R];
     load_diag<R>(vdiag, lane, dm);
-    const float sc = 1.0f / (sqrtf((float)D) * l);
+    const float sc = 1.0f / (sqrtf((float)D) * L);
 #pragma unroll
     for (int r = 0; r < R; ++r) out[sh * D + 64 * r + lane] = flip(acc[r], dm[r]) * sc;
 }
@@ -313,8 +339,7 @@ void decode_d(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k
         case 3: qjl ? decode_bv<D, 3, true>(qk, qv, k, v, n_streams, T, G, qr, p, scale, parts, n_chunks, s) : decode_bv<D, 3, false>(qk, qv, k, v, n_streams, T, G, qr, p, scale, parts, n_chunks, s); break;
         default: qjl ? decode_bv<D, 4, true>(qk, qv, k, v, n_streams, T, G, qr, p, scale, parts, n_chunks, s) : decode_bv<D, 4, false>(qk, qv, k, v, n_streams, T, G, qr, p, scale, parts, n_chunks, s); break;
     }
-    hipLaunchKernelGGL((k_combine<D>), dim3((unsigned)(n_streams * G)), dim3(64), 0, s, parts, n_chunks, G,
-                       qv->diag_signs, out);
+    (void)out;
 }
 
 }  // namespace
@@ -331,14 +356,29 @@ int launch_scores(const tq_quantizer* q, const tq_packed* k, int64_t n_keys, con
 }
 
 int launch_decode(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
-                  const tq_packed* v, int64_t n_streams, int64_t T, int G, const float* qr,
-                  const float* p, float scale, float* out, float* parts, hipStream_t s)
+                  const tq_packed* v, int64_t n_streams, int64_t T, int G, const DecodePlan& plan,
+                  void* ws, float scale, float* out, hipStream_t s)
 {
-    const int n_chunks = decode_chunks(T);
+    const float* qr = (const float*)((char*)ws + plan.off_qr);
+    const float* p = (const float*)((char*)ws + plan.off_p);
+    float* parts = (float*)((char*)ws + plan.off_parts);
+    const float zscale = scale * 1.4426950408889634f;  // scores in log2 units
+    if (plan.mfma) {
+        int rc = launch_decode_mfma(qk, qv, k, v, n_streams, T, G, qr, p, zscale, (char*)ws + plan.off_frag,
+                                    parts, plan.n_chunks, (int)plan.tc, s);
+        if (rc != TQ_OK) return rc;
+    } else {
+        switch (qk->d) {
+            case 64: decode_d<64>(qk, qv, k, v, n_streams, T, G, qr, p, zscale, out, parts, plan.n_chunks, s); break;
+            case 128: decode_d<128>(qk, qv, k, v, n_streams, T, G, qr, p, zscale, out, parts, plan.n_chunks, s); break;
+            default: decode_d<256>(qk, qv, k, v, n_streams, T, G, qr, p, zscale, out, parts, plan.n_chunks, s); break;
+        }
+    }
+    const dim3 cg((unsigned)(n_streams * G));
     switch (qk->d) {
-        case 64: decode_d<64>(qk, qv, k, v, n_streams, T, G, qr, p, scale, out, parts, n_chunks, s); break;
-        case 128: decode_d<128>(qk, qv, k, v, n_streams, T, G, qr, p, scale, out, parts, n_chunks, s); break;
-        default: decode_d<256>(qk, qv, k, v, n_streams, T, G, qr, p, scale, out, parts, n_chunks, s); break;
+        case 64: hipLaunchKernelGGL((k_combine<64>), cg, dim3(256), 0, s, parts, plan.n_chunks, G, qv->diag_signs, out); break;
+        case 128: hipLaunchKernelGGL((k_combine<128>), cg, dim3(256), 0, s, parts, plan.n_chunks, G, qv->diag_signs, out); break;
+        default: hipLaunchKernelGGL((k_combine<256>), cg, dim3(256), 0, s, parts, plan.n_chunks, G, qv->diag_signs, out); break;
     }
     return device_status("tq_decode_attn");
 }

@@ -1,0 +1,395 @@
+// Fused decode attention over compressed K/V on MFMA (d = 128, up to 8 query
+// heads per KV head).
+//
+// The per-token work is three small dense contractions over the G heads of a
+// KV stream: sum_i q'_i c(k_i), sum_j p_j (+-1)_j (the QJL correction of
+// "[Benchmark] TurboQuant 實測：KV Cache 3-bit 壓縮，真的零損失？", section
+// "TurboQuant 是什麼：30 秒懶人包"), and sum_t w_t n_t c(v_t). All of them run
+// on 16x16x32 f16 MFMAs with exact operands: key and value codes expand to
+// fp16 centroids (fp16-representable by construction) and signs to +-1 via
+// small LDS tables; the fp32 side (rotated query, its projection, the softmax
+// weights) is split into an fp16 hi part and an fp16 lo part carried in two
+// halves of the 16 output columns (query side) or rows (weight side), so the
+// products are exact and only the fp32 accumulation rounds.
+//
+// Work split: a block owns a chunk of one stream's tokens, each of its four
+// waves a contiguous quarter, processed 32 tokens at a time:
+//   scores  16 tokens x 16 columns (8 heads x hi/lo) per MFMA tile, K = 256
+//           (128 code slots + 128 sign slots, in group-major order);
+//   softmax exact max per 32-token block; the running max moves (and the
+//           accumulators are rescaled) only when a block beats it by 2^8;
+//   values  16 rows (8 heads x hi/lo) x 16 coordinates per tile, K = 32 tokens.
+// The four waves merge in LDS; one partial (max, sum, rotated-domain
+// accumulator) per block goes to the workspace, and the combine kernel merges
+// the partials of a stream and undoes the value rotation.
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+__device__ __forceinline__ float xor8(float x)
+{
+    // lane i <-> lane i ^ 8 inside each row of 16 lanes (DPP row rotate by 8)
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
+template <int D, bool QJL>
+__global__ __launch_bounds__(256) void k_qfrag(const float* __restrict__ qr, const float* __restrict__ p,
+                                               int64_t n_streams, int G, half8_t* __restrict__ frags)
+{
+    constexpr int KS = D / 32, KSTEPS = KS * (QJL ? 2 : 1);
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n_streams * KSTEPS * 64) return;
+    const int l = (int)(idx & 63);
+    const int t = (int)((idx >> 6) % KSTEPS);
+    const int64_t s = idx / (64 * KSTEPS);
+    const int col = l & 15, g = l >> 4, head = col & 7;
+    const bool lo = col >= 8, sgn = t >= KS;
+    const int grp = g * KS + (sgn ? t - KS : t);
+    half8_t f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float val = 0.f;
+        if (head < G) {
+            const int c = grp + (D / 8) * e;
+            val = sgn ? p[(s * G + head) * D + c] : qr[(s * G + head) * D + c];
+        }
+        const _Float16 hi = (_Float16)val;
+        f[e] = lo ? (_Float16)(val - (float)hi) : hi;
+    }
+    frags[idx] = f;
+}
+
+template <int BV>
+__device__ __forceinline__ uint32_t vfield(const uint32_t* __restrict__ rec, int col)
+{
+    constexpr int VW = BV * 4;  // words per token at d = 128
+    if constexpr (BV == 4) {
+        return rec[col];
+    } else if constexpr (BV == 3) {
+        const int bit = 24 * col, w = bit >> 5, sh = bit & 31;
+        const uint32_t w0 = rec[w];
+        const uint32_t w1 = (w + 1 < VW) ? rec[w + 1] : 0u;
+        return __builtin_amdgcn_alignbit(w1, w0, sh) & 0xFFFFFFu;
+    } else {
+        const int bit = 8 * BV * col;
+        return (rec[bit >> 5] >> (bit & 31)) & ((1u << (8 * BV)) - 1u);
+    }
+}
+
+template <int D, int BK, bool QJL, int BV>
+__global__ __launch_bounds__(256) void k_decode_mfma(const uint32_t* __restrict__ kcodes,
+                                                     const uint32_t* __restrict__ ksigns,
+                                                     const uint16_t* __restrict__ knorm,
+                                                     const uint16_t* __restrict__ krnorm,
+                                                     const uint32_t* __restrict__ vcodes,
+                                                     const uint16_t* __restrict__ vnorm, int64_t T, int G,
+                                                     const half8_t* __restrict__ frags,
+                                                     const float* __restrict__ kcent,
+                                                     const float* __restrict__ vcent, float zscale,
+                                                     float* __restrict__ parts, int n_chunks, int tc)
+{
+    static_assert(D == 128, "MFMA decode is laid out for d = 128");
+    constexpr int KS = D / 32;                 // 4 code groups per lane per token
+    constexpr int KSTEPS = KS * (QJL ? 2 : 1);
+    constexpr int CT = D / 16;                 // value coordinate tiles
+    constexpr int KW = BK * D / 32, VW = BV * D / 32, SWN = D / 32;
+    constexpr bool K4 = BK <= 2;               // one key table entry = 4 codes (else 2)
+    constexpr int KLUT = K4 ? (1 << (4 * BK)) : (1 << (2 * BK));
+    constexpr int VLUT = 1 << (2 * BV);
+    constexpr float kappa = 1.2533141373155003f / D;  // sqrt(pi/2) / m
+
+    __shared__ uint2 klut4[K4 ? KLUT : 1];
+    __shared__ uint32_t klut2[K4 ? 1 : KLUT];
+    __shared__ uint4 slut[QJL ? 256 : 1];
+    __shared__ uint32_t vlut[VLUT];
+    __shared__ float tokv[4][3][32];
+    __shared__ float mrg_m[4][8], mrg_l[4][8];
+    __shared__ float mrg_o[4][8][D];
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int col = lane & 15, g = lane >> 4;
+
+    // ---- lookup tables: codes -> fp16 centroids, sign bytes -> +-1
+    for (int i = tid; i < KLUT; i += 256) {
+        if constexpr (K4) {
+            uint32_t h[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) h[j] = f2h(kcent[(i >> (BK * j)) & ((1 << BK) - 1)]);
+            klut4[i] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        } else {
+            klut2[i] = (uint32_t)f2h(kcent[i & ((1 << BK) - 1)]) | ((uint32_t)f2h(kcent[i >> BK]) << 16);
+        }
+    }
+    if constexpr (QJL)
+        for (int i = tid; i < 256; i += 256) {
+            uint32_t w[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                w[j] = (((i >> (2 * j)) & 1) ? 0x3C00u : 0xBC00u) | ((((i >> (2 * j + 1)) & 1) ? 0x3C00u : 0xBC00u) << 16);
+            slut[i] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    for (int i = tid; i < VLUT; i += 256)
+        vlut[i] = (uint32_t)f2h(vcent[i & ((1 << BV) - 1)]) | ((uint32_t)f2h(vcent[i >> BV]) << 16);
+    __syncthreads();
+
+    const int64_t s = blockIdx.y;
+    const int chunk = blockIdx.x;
+    const int64_t base = s * T;
+    const int64_t c0 = (int64_t)chunk * tc;
+    const int64_t c1 = c0 + tc < T ? c0 + tc : T;
+    const int64_t w0 = c0 + (int64_t)wid * (tc / 4);
+    const int64_t w1 = w0 + tc / 4 < c1 ? w0 + tc / 4 : c1;
+
+    half8_t bq[KSTEPS];
+#pragma unroll
+    for (int k = 0; k < KSTEPS; ++k) bq[k] = frags[(s * KSTEPS + k) * 64 + lane];
+
+    // fixed weight scale for this wave: max weight * norm stays below 2^15 in fp16
+    float nmax = 0.f;
+    for (int64_t t = w0 + lane; t < w1; t += 64) nmax = fmaxf(nmax, h2f(vnorm[base + t]));
+    nmax = wave_max(nmax);
+    int ex = 0;
+    (void)frexpf(nmax, &ex);
+    const float wscale = nmax > 0.f ? ldexpf(1.0f, 7 - ex) : 1.0f;
+
+    float M = -INFINITY, lsum = 0.f;
+    float4_t acc[CT];
+#pragma unroll
+    for (int c = 0; c < CT; ++c) acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int64_t tb = w0; tb < w1; tb += 32) {
+        if (lane < 32) {
+            const int64_t t = tb + lane;
+            const bool ok = t < w1;
+            tokv[wid][0][lane] = ok ? h2f(knorm[base + t]) * zscale : 0.f;
+            tokv[wid][1][lane] = (ok && QJL) ? h2f(krnorm[base + t]) * kappa : 0.f;
+            tokv[wid][2][lane] = ok ? h2f(vnorm[base + t]) * wscale : 0.f;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // ---- scores for two 16-token tiles
+        float zz[8];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int64_t tA = tb + 16 * u + col;
+            const bool vA = tA < w1;
+            uint32_t kf[BK];
+#pragma unroll
+            for (int w = 0; w < BK; ++w) kf[w] = vA ? kcodes[(base + tA) * KW + BK * g + w] : 0u;
+            const uint32_t sf = (QJL && vA) ? ksigns[(base + tA) * SWN + g] : 0u;
+            float4_t am = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < KS; ++t) {
+                // code group t of this lane: 8*BK bits at bit 8*BK*t of kf
+                constexpr int FB = 8 * BK;
+                const int bit = FB * t;
+                uint32_t field;
+                if constexpr (BK == 4) field = kf[t];
+                else {
+                    const uint64_t cat = (bit >> 5) + 1 < BK
+                                             ? ((uint64_t)kf[(bit >> 5) + 1] << 32) | kf[bit >> 5]
+                                             : (uint64_t)kf[bit >> 5];
+                    field = (uint32_t)(cat >> (bit & 31)) & ((1u << FB) - 1u);
+                }
+                half8_t a;
+                if constexpr (K4) {
+                    const uint2 e0 = klut4[field & ((1u << (4 * BK)) - 1u)];
+                    const uint2 e1 = klut4[field >> (4 * BK)];
+                    const uint32_t wds[4] = {e0.x, e0.y, e1.x, e1.y};
+                    a = __builtin_bit_cast(half8_t, wds);
+                } else {
+                    uint32_t wds[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) wds[j] = klut2[(field >> (2 * BK * j)) & ((1u << (2 * BK)) - 1u)];
+                    a = __builtin_bit_cast(half8_t, wds);
+                }
+                am = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[t], am, 0, 0, 0);
+                if constexpr (QJL) {
+                    const uint4 sv = slut[(sf >> (8 * t)) & 0xFFu];
+                    const half8_t sa = __builtin_bit_cast(half8_t, sv);
+                    aq = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, bq[KS + t], aq, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * u + 4 * g + r;
+                const float zm = am[r] + xor8(am[r]);
+                const float zq = QJL ? aq[r] + xor8(aq[r]) : 0.f;
+                const float z = tokv[wid][0][row] * (zm + tokv[wid][1][row] * zq);
+                zz[4 * u + r] = (tb + row < w1) ? z : -INFINITY;
+            }
+        }
+
+        // ---- block max per head column; rescale only when it beats the running max by 2^8
+        float bm = zz[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) bm = fmaxf(bm, zz[e]);
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        if (__ballot(bm > M + 8.0f)) {
+            const float nM = fmaxf(M, bm);
+            const float f = exp2f(M - nM);
+            lsum *= f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float fr = __shfl(f, (4 * g + r) & 7);
+#pragma unroll
+                for (int c = 0; c < CT; ++c) acc[c][r] *= fr;
+            }
+            M = nM;
+        }
+
+        // ---- weights as the A operand (row = head column, K slot = token)
+        half8_t aw;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float w = exp2f(zz[e] - M);
+            lsum += w;
+            const float W = w * tokv[wid][2][16 * (e >> 2) + 4 * g + (e & 3)];
+            const _Float16 hi = (_Float16)W;
+            aw[e] = col < 8 ? hi : (_Float16)(W - (float)hi);
+        }
+
+        // ---- value codes: lane column = code group, slot e = token 4g+e (tile 0) / 16+4g+e-4 (tile 1)
+        uint32_t X[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int64_t t = tb + 16 * (e >> 2) + 4 * g + (e & 3);
+            X[e] = t < w1 ? vfield<BV>(vcodes + (base + t) * VW, col) : 0u;
+        }
+        if constexpr (BV == 3) {
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+                uint32_t bw[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t ia = (X[2 * j] >> (3 * c)) & 7u, ib = (X[2 * j + 1] >> (3 * c)) & 7u;
+                    bw[j] = vlut[ia | (ib << 3)];
+                }
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, bw), acc[c], 0, 0, 0);
+            }
+        } else {
+            // interleave the two tokens' fields: slot k of y0 (2*BV bits) is the index for
+            // tile 2k, slot k of y1 the index for tile 2k+1
+            constexpr uint32_t MSK = BV == 4 ? 0x0F0F0F0Fu : (BV == 2 ? 0x33333333u : 0x55555555u);
+            uint32_t y0[4], y1[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t xa = X[2 * j], xb = X[2 * j + 1];
+                y0[j] = (xa & MSK) | ((xb << BV) & ~MSK);
+                y1[j] = ((xa >> BV) & MSK) | (xb & ~MSK);
+            }
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+                uint32_t bw[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t y = (c & 1) ? y1[j] : y0[j];
+                    bw[j] = vlut[(y >> (2 * BV * (c >> 1))) & ((1u << (2 * BV)) - 1u)];
+                }
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, bw), acc[c], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- per-wave results: sum over row groups, hi rows + lo rows
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    const float inv = 1.0f / wscale;
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float o = acc[c][r] + __shfl_xor(acc[c][r], 32);
+            const int h = 4 * g + r;
+            if (g < 2 && h < G) mrg_o[wid][h][col + 16 * c] = o * inv;
+        }
+    if (lane < 8) {
+        mrg_m[wid][lane] = M;
+        mrg_l[wid][lane] = lsum;
+    }
+    __syncthreads();
+
+    // ---- merge the four waves into one partial per head
+    float* part0 = parts + ((s * n_chunks + chunk) * G) * (D + 2);
+    for (int e = tid; e < G * D; e += 256) {
+        const int h = e / D, i = e % D;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) mx = fmaxf(mx, mrg_m[w][h]);
+        float o = 0.f;
+        if (mx != -INFINITY)
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                if (mrg_m[w][h] != -INFINITY) o += exp2f(mrg_m[w][h] - mx) * mrg_o[w][h][i];
+        part0[h * (D + 2) + 2 + i] = o;
+        if (i == 0) {
+            float l = 0.f;
+            if (mx != -INFINITY)
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    if (mrg_m[w][h] != -INFINITY) l += exp2f(mrg_m[w][h] - mx) * mrg_l[w][h];
+            part0[h * (D + 2)] = mx;
+            part0[h * (D + 2) + 1] = l;
+        }
+    }
+}
+
+template <int D, int BK, bool QJL, int BV>
+void launch_mfma(const tq_packed* k, const tq_packed* v, int64_t n_streams, int64_t T, int G,
+                 const half8_t* frags, const tq_quantizer* qk, const tq_quantizer* qv, float zscale,
+                 float* parts, int n_chunks, int tc, hipStream_t s)
+{
+    hipLaunchKernelGGL((k_decode_mfma<D, BK, QJL, BV>), dim3((unsigned)n_chunks, (unsigned)n_streams), dim3(256),
+                       0, s, k->codes, k->signs, k->norm, k->rnorm, v->codes, v->norm, T, G, frags,
+                       qk->centroids, qv->centroids, zscale, parts, n_chunks, tc);
+}
+
+template <int D, int BK, bool QJL>
+void launch_bv(int bv, const tq_packed* k, const tq_packed* v, int64_t ns, int64_t T, int G, const half8_t* fr,
+               const tq_quantizer* qk, const tq_quantizer* qv, float zs, float* parts, int nc, int tc,
+               hipStream_t s)
+{
+    switch (bv) {
+        case 1: launch_mfma<D, BK, QJL, 1>(k, v, ns, T, G, fr, qk, qv, zs, parts, nc, tc, s); break;
+        case 2: launch_mfma<D, BK, QJL, 2>(k, v, ns, T, G, fr, qk, qv, zs, parts, nc, tc, s); break;
+        case 3: launch_mfma<D, BK, QJL, 3>(k, v, ns, T, G, fr, qk, qv, zs, parts, nc, tc, s); break;
+        default: launch_mfma<D, BK, QJL, 4>(k, v, ns, T, G, fr, qk, qv, zs, parts, nc, tc, s); break;
+    }
+}
+
+}  // namespace
+
+int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
+                       const tq_packed* v, int64_t n_streams, int64_t T, int G, const float* qr,
+                       const float* p, float zscale, void* frags, float* parts, int n_chunks, int tc,
+                       hipStream_t s)
+{
+    constexpr int D = 128;
+    const bool qjl = qk->qjl_m != 0;
+    const int ksteps = (D / 32) * (qjl ? 2 : 1);
+    const int64_t nf = n_streams * ksteps * 64;
+    const unsigned fb = (unsigned)((nf + 255) / 256);
+    if (qjl) hipLaunchKernelGGL((k_qfrag<D, true>), dim3(fb), dim3(256), 0, s, qr, p, n_streams, G, (half8_t*)frags);
+    else hipLaunchKernelGGL((k_qfrag<D, false>), dim3(fb), dim3(256), 0, s, qr, p, n_streams, G, (half8_t*)frags);
+    const half8_t* fr = (const half8_t*)frags;
+    switch (qk->mse_bits) {
+        case 1: qjl ? launch_bv<D, 1, true>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
+                    : launch_bv<D, 1, false>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
+        case 2: qjl ? launch_bv<D, 2, true>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
+                    : launch_bv<D, 2, false>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
+        case 3: qjl ? launch_bv<D, 3, true>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
+                    : launch_bv<D, 3, false>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
+        default: qjl ? launch_bv<D, 4, true>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
+                     : launch_bv<D, 4, false>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "tq_decode_attn: %s", hipGetErrorString(e));
+    return TQ_OK;
+}
+
+}  // namespace tq

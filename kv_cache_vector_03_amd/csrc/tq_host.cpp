@@ -185,18 +185,28 @@ size_t scores_ws(const tq_quantizer* q, int64_t n_q)
     return up256((size_t)n_q * q->d * 4) + up256((size_t)n_q * (q->qjl_m ? q->qjl_m : 1) * 4);
 }
 
-int decode_chunks(int64_t T)
+DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G)
 {
-    int64_t tc = decode_chunk_tokens(T);
-    return (int)((T + tc - 1) / tc);
-}
-
-size_t decode_ws(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G)
-{
-    size_t nq = (size_t)n_streams * G;
-    size_t prep = scores_ws(qk, (int64_t)nq);
-    size_t parts = (size_t)n_streams * decode_chunks(T) * G * (qk->d + 2) * 4;
-    return prep + up256(parts);
+    DecodePlan p{};
+    p.mfma = qk->d == 128 && G <= 8;
+    if (p.mfma) {
+        // about 1024 blocks in total, 128..2048 tokens each (a power of two)
+        int64_t want = (n_streams * T) / 1024;
+        int64_t tc = 128;
+        while (tc * 2 <= want && tc < 2048) tc *= 2;
+        p.tc = tc;
+    } else {
+        p.tc = 256;  // the scalar kernel handles one token per thread
+    }
+    p.n_chunks = (int)((T + p.tc - 1) / p.tc);
+    const size_t nq = (size_t)n_streams * G;
+    const int ksteps = (qk->d / 32) * (qk->qjl_m ? 2 : 1);
+    p.off_qr = 0;
+    p.off_p = up256(nq * qk->d * 4);
+    p.off_frag = p.off_p + up256(nq * (qk->qjl_m ? qk->qjl_m : 1) * 4);
+    p.off_parts = p.off_frag + (p.mfma ? up256((size_t)n_streams * ksteps * 64 * 16) : 0);
+    p.total = p.off_parts + up256((size_t)n_streams * p.n_chunks * G * (qk->d + 2) * 4);
+    return p;
 }
 
 }  // namespace tq
@@ -217,7 +227,7 @@ size_t tq_workspace_size(int op, const tq_quantizer* qk, int64_t n_a, int64_t n_
     if (op == TQ_OP_SCORES) return tq::scores_ws(qk, n_a);
     if (op == TQ_OP_DECODE_ATTN) {
         if (G < 1 || G > 16 || n_b < 1) return 0;
-        return tq::decode_ws(qk, n_a, n_b, G);
+        return tq::decode_plan(qk, n_a, n_b, G).total;
     }
     return 0;
 }

@@ -19,15 +19,16 @@ int check_packed(const tq_quantizer* q, const tq_packed* p, const char* who, con
 int check_dense(const void* p, int dtype, const char* who, const char* what);
 
 size_t scores_ws(const tq_quantizer* q, int64_t n_q);
-size_t decode_ws(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G);
-int decode_chunks(int64_t T);
 
-// tokens per split-K chunk of the decode-attention kernel
-inline int64_t decode_chunk_tokens(int64_t T)
-{
-    (void)T;
-    return 256;
-}
+// Decode-attention work split and workspace layout (offsets in bytes from
+// the workspace base, each 256-byte aligned).
+struct DecodePlan {
+    bool mfma;          // MFMA kernel (d = 128, G <= 8); else the scalar kernel
+    int64_t tc;         // tokens per block
+    int n_chunks;       // blocks per stream
+    size_t off_qr, off_p, off_frag, off_parts, total;
+};
+DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G);
 
 // kernel launchers (tq_*.hip); each returns TQ_OK or TQ_ERR_DEVICE
 int launch_quantize(const tq_quantizer* q, const void* x, int dtype, int64_t n,
@@ -39,8 +40,12 @@ int launch_scores(const tq_quantizer* q, const tq_packed* k, int64_t n_keys, con
 int launch_dequantize(const tq_quantizer* q, const tq_packed* in, int64_t n, int include_qjl,
                       void* out, int dtype, hipStream_t s);
 int launch_decode(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
-                  const tq_packed* v, int64_t n_streams, int64_t T, int G, const float* qr,
-                  const float* p, float scale, float* out, float* parts, hipStream_t s);
+                  const tq_packed* v, int64_t n_streams, int64_t T, int G, const DecodePlan& plan,
+                  void* ws, float scale, float* out, hipStream_t s);
+int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
+                       const tq_packed* v, int64_t n_streams, int64_t T, int G, const float* qr,
+                       const float* p, float zscale, void* frags, float* parts, int n_chunks, int tc,
+                       hipStream_t s);
 
 }  // namespace tq
 
