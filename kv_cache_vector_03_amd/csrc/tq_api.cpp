@@ -96,11 +96,8 @@ int tq_decode_attn(const tq_quantizer* qk, const tq_quantizer* qv,
         return fail(TQ_ERR_WORKSPACE, "tq_decode_attn: workspace %zu bytes < %zu", ws_bytes, plan.total);
     if ((uintptr_t)ws % 256) return fail(TQ_ERR_INVALID, "tq_decode_attn: workspace must be 256-byte aligned");
     if (scale == 0.0f) scale = 1.0f / std::sqrt((float)qk->d);
-    const int64_t nq = n_streams * G;
-    float* qr = (float*)((char*)ws + plan.off_qr);
-    float* p = (float*)((char*)ws + plan.off_p);
-    if ((rc = launch_qprep(qk, q, q_dtype, nq, qr, p, (hipStream_t)stream)) != TQ_OK) return rc;
-    return launch_decode(qk, qv, k, v, n_streams, T, G, plan, ws, scale, out, (hipStream_t)stream);
+    return launch_decode(qk, qv, k, v, n_streams, T, G, q, q_dtype, plan, ws, scale, out,
+                         (hipStream_t)stream);
 }
 
 }  // extern "C"

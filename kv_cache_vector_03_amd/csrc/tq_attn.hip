@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void k_decode(const uint32_t* __restrict__ kco
         l = wave_sum(l);
         if (lane == 0) {
             smax[h] = m;
-            float* part = parts + (((int64_t)s * n_chunks + chunk) * G + h) * (D + 2);
+            float* part = parts + (((int64_t)s * n_chunks + chunk) * G + h) * part_stride(D);
             part[0] = m;
             part[1] = l;
         }
@@ -212,66 +212,74 @@ __global__ __launch_bounds__(256) void k_decode(const uint32_t* __restrict__ kco
             }
             acc += z[h][tt] * vn[tt] * vc[idx];
         }
-        parts[(((int64_t)s * n_chunks + chunk) * G + h) * (D + 2) + 2 + i] = acc;
+        parts[(((int64_t)s * n_chunks + chunk) * G + h) * part_stride(D) + kPartAcc + i] = acc;
     }
 }
 
 // Merge the chunk partials of one (stream, head) and rotate back to the value
-// domain. Partials hold (max, sum, accumulator) with max in log2 units. Four
-// waves each merge a strided subset of the chunks; wave 0 finishes.
+// domain. Partials hold (max, sum, accumulator) with max in log2 units.
+// Thread (lane c, slot i) sums chunks c, c + CL, ... of float4 slot i; the
+// loop is unrolled so that many chunks' loads are in flight at once.
 template <int D>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ parts, int n_chunks, int G,
                                                  const uint32_t* __restrict__ vdiag,
                                                  float* __restrict__ out)
 {
-    constexpr int R = D / 64;
-    __shared__ float wm[4], wl[4];
-    __shared__ float wo[4][D];
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    constexpr int R = D / 64, NV = D / 4, CL = 256 / NV, PS = part_stride(D);
+    __shared__ float red[4];
+    __shared__ float4 om[CL][NV];
+    __shared__ float ol[CL];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t sh = blockIdx.x;  // s * G + h
     const int64_t s = sh / G, h = sh % G;
-    float M = -INFINITY;
-    for (int c = wid; c < n_chunks; c += 4) M = fmaxf(M, parts[((s * n_chunks + c) * G + h) * (D + 2)]);
-    float acc[R], l = 0.f;
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.f;
-    for (int c = wid; c < n_chunks; c += 4) {
-        const float* part = parts + ((s * n_chunks + c) * G + h) * (D + 2);
-        const float m = part[0];
-        if (m == -INFINITY) continue;
-        const float f = exp2f(m - M);
-        l += f * part[1];
-#pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] += f * part[2 + 64 * r + lane];
+    const int64_t stride = (int64_t)G * PS;
+    const float* p0 = parts + ((s * n_chunks) * G + h) * PS;
+
+    float m = -INFINITY;
+    for (int c = tid; c < n_chunks; c += 256) m = fmaxf(m, p0[c * stride]);
+    m = wave_max(m);
+    if (lane == 0) red[wid] = m;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+    const int cl = tid / NV, i = tid % NV;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float l = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll 8
+        for (int c = cl; c < n_chunks; c += CL) {
+            const float* pc = p0 + c * stride;
+            const float2 ml = *reinterpret_cast<const float2*>(pc);
+            const float4 a = reinterpret_cast<const float4*>(pc + kPartAcc)[i];
+            const float f = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
+            acc.x += f * a.x;
+            acc.y += f * a.y;
+            acc.z += f * a.z;
+            acc.w += f * a.w;
+            l += f * ml.y;
+        }
     }
-    if (lane == 0) {
-        wm[wid] = M;
-        wl[wid] = l;
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) wo[wid][64 * r + lane] = acc[r];
+    om[cl][i] = acc;
+    if (i == 0) ol[cl] = l;
     __syncthreads();
     if (wid != 0) return;
-    float Mx = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) Mx = fmaxf(Mx, wm[w]);
+    const float* omf = reinterpret_cast<const float*>(&om[0][0]);
+    float v[R];
     float L = 0.f;
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    for (int q = 0; q < CL; ++q) L += ol[q];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        if (wm[w] == -INFINITY) continue;
-        const float f = exp2f(wm[w] - Mx);
-        L += f * wl[w];
+    for (int r = 0; r < R; ++r) {
+        v[r] = 0.f;
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] += f * wo[w][64 * r + lane];
+        for (int q = 0; q < CL; ++q) v[r] += omf[q * D + 64 * r + lane];
     }
-    fwht_wave<R>(acc, lane);
+    fwht_wave<R>(v, lane);
     uint32_t dm[R];
     load_diag<R>(vdiag, lane, dm);
     const float sc = 1.0f / (sqrtf((float)D) * L);
 #pragma unroll
-    for (int r = 0; r < R; ++r) out[sh * D + 64 * r + lane] = flip(acc[r], dm[r]) * sc;
+    for (int r = 0; r < R; ++r) out[sh * D + 64 * r + lane] = flip(v[r], dm[r]) * sc;
 }
 
 int device_status(const char* who)
@@ -356,18 +364,20 @@ int launch_scores(const tq_quantizer* q, const tq_packed* k, int64_t n_keys, con
 }
 
 int launch_decode(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
-                  const tq_packed* v, int64_t n_streams, int64_t T, int G, const DecodePlan& plan,
-                  void* ws, float scale, float* out, hipStream_t s)
+                  const tq_packed* v, int64_t n_streams, int64_t T, int G, const void* q, int q_dtype,
+                  const DecodePlan& plan, void* ws, float scale, float* out, hipStream_t s)
 {
-    const float* qr = (const float*)((char*)ws + plan.off_qr);
-    const float* p = (const float*)((char*)ws + plan.off_p);
+    float* qr = (float*)((char*)ws + plan.off_qr);
+    float* p = (float*)((char*)ws + plan.off_p);
     float* parts = (float*)((char*)ws + plan.off_parts);
     const float zscale = scale * 1.4426950408889634f;  // scores in log2 units
     if (plan.mfma) {
-        int rc = launch_decode_mfma(qk, qv, k, v, n_streams, T, G, qr, p, zscale, (char*)ws + plan.off_frag,
-                                    parts, plan.n_chunks, (int)plan.tc, s);
+        int rc = launch_decode_mfma(qk, qv, k, v, n_streams, T, G, q, q_dtype, zscale,
+                                    (char*)ws + plan.off_frag, parts, plan.n_chunks, (int)plan.tc, s);
         if (rc != TQ_OK) return rc;
     } else {
+        int rc = launch_qprep(qk, q, q_dtype, n_streams * G, qr, p, s);
+        if (rc != TQ_OK) return rc;
         switch (qk->d) {
             case 64: decode_d<64>(qk, qv, k, v, n_streams, T, G, qr, p, zscale, out, parts, plan.n_chunks, s); break;
             case 128: decode_d<128>(qk, qv, k, v, n_streams, T, G, qr, p, zscale, out, parts, plan.n_chunks, s); break;

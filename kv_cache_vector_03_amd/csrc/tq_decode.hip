@@ -34,52 +34,127 @@ __device__ __forceinline__ float xor8(float x)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
 }
 
-template <int D, bool QJL>
-__global__ __launch_bounds__(256) void k_qfrag(const float* __restrict__ qr, const float* __restrict__ p,
-                                               int64_t n_streams, int G, half8_t* __restrict__ frags)
+// Query preparation, grid (stream, k-step t < d/32). Every block rotates the
+// stream's G <= 8 queries in double (q' = H D q / sqrt(d)); block t then
+// projects them onto the d/4 rows of S with index = t (mod d/32), one dot
+// product per thread (p = S q'), and writes two score-GEMM B fragments: code
+// k-step t and sign k-step d/32 + t. Column c < 8 carries the fp16 rounding of
+// head c's value, column c + 8 the fp16 rounding of the remainder. Lane
+// (g, col) element e of k-step t maps to coordinate (or projection row)
+// (4 g + t) + (d/8) e, the group-major order the key codes arrive in.
+template <int D, bool QJL, bool F16>
+__global__ __launch_bounds__(256) void k_qprep_frag(const void* __restrict__ q, int G,
+                                                    const uint32_t* __restrict__ diag,
+                                                    const uint16_t* __restrict__ S,
+                                                    half8_t* __restrict__ frags)
 {
-    constexpr int KS = D / 32, KSTEPS = KS * (QJL ? 2 : 1);
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= n_streams * KSTEPS * 64) return;
-    const int l = (int)(idx & 63);
-    const int t = (int)((idx >> 6) % KSTEPS);
-    const int64_t s = idx / (64 * KSTEPS);
-    const int col = l & 15, g = l >> 4, head = col & 7;
-    const bool lo = col >= 8, sgn = t >= KS;
-    const int grp = g * KS + (sgn ? t - KS : t);
-    half8_t f;
+    static_assert(D == 128, "fragment layout is laid out for d = 128");
+    constexpr int R = D / 64, KS = D / 32, KSTEPS = KS * (QJL ? 2 : 1);
+    __shared__ double qs[8][D];
+    __shared__ double ps[QJL ? 8 : 1][32];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int64_t s = blockIdx.x;
+    const int tt = blockIdx.y;
+    // thread (h, i) projects row j = tt + (d/32) i of S onto head h; its row is
+    // fetched first so the load overlaps the rotation
+    const int ph = tid >> 5, pi = tid & 31;
+    uint4 srow[QJL ? D / 8 : 1];
+    if constexpr (QJL) {
+        const uint4* row = reinterpret_cast<const uint4*>(S + (int64_t)(tt + KS * pi) * D);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        float val = 0.f;
-        if (head < G) {
-            const int c = grp + (D / 8) * e;
-            val = sgn ? p[(s * G + head) * D + c] : qr[(s * G + head) * D + c];
-        }
-        const _Float16 hi = (_Float16)val;
-        f[e] = lo ? (_Float16)(val - (float)hi) : hi;
+        for (int c = 0; c < D / 8; ++c) srow[c] = row[c];
     }
-    frags[idx] = f;
+    uint32_t dm[R];
+    load_diag<R>(diag, lane, dm);
+    const double inv_sqrt_d = 1.0 / sqrt((double)D);
+    for (int h = wid; h < 8; h += 4) {
+        double y[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            y[r] = h < G ? (double)flip(load_elem<F16>(q, (s * G + h) * D + 64 * r + lane), dm[r]) : 0.0;
+        fwht_wave<R>(y, lane);
+#pragma unroll
+        for (int r = 0; r < R; ++r) qs[h][64 * r + lane] = y[r] * inv_sqrt_d;
+    }
+    __syncthreads();
+    if constexpr (QJL) {
+        // four partial sums shorten the dependent chain of double FMAs
+        double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) {
+            const uint32_t w4[4] = {srow[c].x, srow[c].y, srow[c].z, srow[c].w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                acc[k & 3] += (double)h2f((uint16_t)(w4[k >> 1] >> (16 * (k & 1)))) * qs[ph][8 * c + k];
+        }
+        ps[ph][pi] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        __syncthreads();
+    }
+    if (tid < (QJL ? 128 : 64)) {
+        const bool sgn = tid >= 64;
+        const int l = tid & 63;
+        const int col = l & 15, g = l >> 4, head = col & 7;
+        const bool lo = col >= 8;
+        half8_t f;
+#pragma unroll
+        for (int ee = 0; ee < 8; ++ee) {
+            // coordinate (row) 4 g + tt + (d/8) ee; as a row of this block: i = g + 4 ee
+            double val = 0.0;
+            if (head < G) val = sgn ? ps[QJL ? head : 0][(g + 4 * ee) & 31] : qs[head][KS * g + tt + (D / 8) * ee];
+            const _Float16 hi = (_Float16)val;
+            f[ee] = lo ? (_Float16)(val - (double)hi) : hi;
+        }
+        frags[(s * KSTEPS + (sgn ? KS + tt : tt)) * 64 + l] = f;
+    }
 }
 
-template <int BV>
-__device__ __forceinline__ uint32_t vfield(const uint32_t* __restrict__ rec, int col)
+// One 32-token step's packed inputs for one lane (prefetched a step ahead).
+template <int BK, int BV>
+struct Step {
+    uint32_t kf[2][BK];   // key code words of this lane's 4 groups, tiles 0 and 1
+    uint32_t sf[2];       // key sign bytes of this lane's 4 groups
+    uint32_t x0[8], x1[8];// value field words (x1: second word, 3-bit codes only)
+    uint16_t nk, ng, nv;  // token (tb + lane) norms, lanes < 32
+};
+
+template <int D, int BK, bool QJL, int BV>
+__device__ __forceinline__ void load_step(Step<BK, BV>& st, int64_t tb, int64_t w1, int64_t base, int lane,
+                                          const uint32_t* __restrict__ kcodes,
+                                          const uint32_t* __restrict__ ksigns,
+                                          const uint16_t* __restrict__ knorm,
+                                          const uint16_t* __restrict__ krnorm,
+                                          const uint32_t* __restrict__ vcodes,
+                                          const uint16_t* __restrict__ vnorm)
 {
-    constexpr int VW = BV * 4;  // words per token at d = 128
-    if constexpr (BV == 4) {
-        return rec[col];
-    } else if constexpr (BV == 3) {
-        const int bit = 24 * col, w = bit >> 5, sh = bit & 31;
-        const uint32_t w0 = rec[w];
-        const uint32_t w1 = (w + 1 < VW) ? rec[w + 1] : 0u;
-        return __builtin_amdgcn_alignbit(w1, w0, sh) & 0xFFFFFFu;
-    } else {
-        const int bit = 8 * BV * col;
-        return (rec[bit >> 5] >> (bit & 31)) & ((1u << (8 * BV)) - 1u);
+    constexpr int KW = BK * D / 32, VW = BV * D / 32, SWN = D / 32;
+    const int col = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t tA = tb + 16 * u + col;
+        const bool vA = tA < w1;
+#pragma unroll
+        for (int w = 0; w < BK; ++w) st.kf[u][w] = vA ? kcodes[(base + tA) * KW + BK * g + w] : 0u;
+        st.sf[u] = (QJL && vA) ? ksigns[(base + tA) * SWN + g] : 0u;
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int64_t t = tb + 16 * (e >> 2) + 4 * g + (e & 3);
+        const bool ok = t < w1;
+        const uint32_t* rec = vcodes + (base + t) * VW;
+        const int w = (8 * BV * col) >> 5;
+        st.x0[e] = ok ? rec[w] : 0u;
+        if constexpr (BV == 3) st.x1[e] = (ok && w + 1 < VW) ? rec[w + 1] : 0u;
+        else st.x1[e] = 0u;
+    }
+    const int64_t t = tb + (lane & 31);
+    const bool ok = t < w1;
+    st.nk = ok ? knorm[base + t] : (uint16_t)0;
+    st.ng = (ok && QJL) ? krnorm[base + t] : (uint16_t)0;
+    st.nv = ok ? vnorm[base + t] : (uint16_t)0;
 }
 
 template <int D, int BK, bool QJL, int BV>
-__global__ __launch_bounds__(256) void k_decode_mfma(const uint32_t* __restrict__ kcodes,
+__global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restrict__ kcodes,
                                                      const uint32_t* __restrict__ ksigns,
                                                      const uint16_t* __restrict__ knorm,
                                                      const uint16_t* __restrict__ krnorm,
@@ -88,13 +163,13 @@ __global__ __launch_bounds__(256) void k_decode_mfma(const uint32_t* __restrict_
                                                      const half8_t* __restrict__ frags,
                                                      const float* __restrict__ kcent,
                                                      const float* __restrict__ vcent, float zscale,
-                                                     float* __restrict__ parts, int n_chunks, int tc)
+                                                     float* __restrict__ parts, int n_chunks, int tc,
+                                                     int64_t n_items)
 {
     static_assert(D == 128, "MFMA decode is laid out for d = 128");
     constexpr int KS = D / 32;                 // 4 code groups per lane per token
     constexpr int KSTEPS = KS * (QJL ? 2 : 1);
     constexpr int CT = D / 16;                 // value coordinate tiles
-    constexpr int KW = BK * D / 32, VW = BV * D / 32, SWN = D / 32;
     constexpr bool K4 = BK <= 2;               // one key table entry = 4 codes (else 2)
     constexpr int KLUT = K4 ? (1 << (4 * BK)) : (1 << (2 * BK));
     constexpr int VLUT = 1 << (2 * BV);
@@ -111,7 +186,7 @@ __global__ __launch_bounds__(256) void k_decode_mfma(const uint32_t* __restrict_
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int col = lane & 15, g = lane >> 4;
 
-    // ---- lookup tables: codes -> fp16 centroids, sign bytes -> +-1
+    // ---- lookup tables: codes -> fp16 centroids, sign bytes -> +-1 (built once per block)
     for (int i = tid; i < KLUT; i += 256) {
         if constexpr (K4) {
             uint32_t h[4];
@@ -134,208 +209,211 @@ __global__ __launch_bounds__(256) void k_decode_mfma(const uint32_t* __restrict_
         vlut[i] = (uint32_t)f2h(vcent[i & ((1 << BV) - 1)]) | ((uint32_t)f2h(vcent[i >> BV]) << 16);
     __syncthreads();
 
-    const int64_t s = blockIdx.y;
-    const int chunk = blockIdx.x;
-    const int64_t base = s * T;
-    const int64_t c0 = (int64_t)chunk * tc;
-    const int64_t c1 = c0 + tc < T ? c0 + tc : T;
-    const int64_t w0 = c0 + (int64_t)wid * (tc / 4);
-    const int64_t w1 = w0 + tc / 4 < c1 ? w0 + tc / 4 : c1;
+    for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int64_t s = item / n_chunks;
+        const int chunk = (int)(item % n_chunks);
+        const int64_t base = s * T;
+        const int64_t c0 = (int64_t)chunk * tc;
+        const int64_t c1 = c0 + tc < T ? c0 + tc : T;
+        const int64_t w0 = c0 + (int64_t)wid * (tc / 4);
+        const int64_t w1 = w0 + tc / 4 < c1 ? w0 + tc / 4 : c1;
 
-    half8_t bq[KSTEPS];
+        half8_t bq[KSTEPS];
 #pragma unroll
-    for (int k = 0; k < KSTEPS; ++k) bq[k] = frags[(s * KSTEPS + k) * 64 + lane];
+        for (int k = 0; k < KSTEPS; ++k) bq[k] = frags[(s * KSTEPS + k) * 64 + lane];
 
-    // fixed weight scale for this wave: max weight * norm stays below 2^15 in fp16
-    float nmax = 0.f;
-    for (int64_t t = w0 + lane; t < w1; t += 64) nmax = fmaxf(nmax, h2f(vnorm[base + t]));
-    nmax = wave_max(nmax);
-    int ex = 0;
-    (void)frexpf(nmax, &ex);
-    const float wscale = nmax > 0.f ? ldexpf(1.0f, 7 - ex) : 1.0f;
+        // fixed weight scale for this wave: max weight * norm stays below 2^15 in fp16
+        float nmax = 0.f;
+        for (int64_t t = w0 + lane; t < w1; t += 64) nmax = fmaxf(nmax, h2f(vnorm[base + t]));
+        nmax = wave_max(nmax);
+        int ex = 0;
+        (void)frexpf(nmax, &ex);
+        const float wscale = nmax > 0.f ? ldexpf(1.0f, 7 - ex) : 1.0f;
 
-    float M = -INFINITY, lsum = 0.f;
-    float4_t acc[CT];
+        float M = -INFINITY, lsum = 0.f;
+        float4_t acc[CT];
 #pragma unroll
-    for (int c = 0; c < CT; ++c) acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < CT; ++c) acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t tb = w0; tb < w1; tb += 32) {
-        if (lane < 32) {
-            const int64_t t = tb + lane;
-            const bool ok = t < w1;
-            tokv[wid][0][lane] = ok ? h2f(knorm[base + t]) * zscale : 0.f;
-            tokv[wid][1][lane] = (ok && QJL) ? h2f(krnorm[base + t]) * kappa : 0.f;
-            tokv[wid][2][lane] = ok ? h2f(vnorm[base + t]) * wscale : 0.f;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        Step<BK, BV> cur, nxt;
+        if (w0 < w1) load_step<D, BK, QJL, BV>(cur, w0, w1, base, lane, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
 
-        // ---- scores for two 16-token tiles
-        float zz[8];
+        for (int64_t tb = w0; tb < w1; tb += 32) {
+            if (tb + 32 < w1)
+                load_step<D, BK, QJL, BV>(nxt, tb + 32, w1, base, lane, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
+            if (lane < 32) {
+                tokv[wid][0][lane] = h2f(cur.nk) * zscale;
+                tokv[wid][1][lane] = h2f(cur.ng) * kappa;
+                tokv[wid][2][lane] = h2f(cur.nv) * wscale;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+            // ---- scores for two 16-token tiles
+            float zz[8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int64_t tA = tb + 16 * u + col;
-            const bool vA = tA < w1;
-            uint32_t kf[BK];
+            for (int u = 0; u < 2; ++u) {
+                float4_t am = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int w = 0; w < BK; ++w) kf[w] = vA ? kcodes[(base + tA) * KW + BK * g + w] : 0u;
-            const uint32_t sf = (QJL && vA) ? ksigns[(base + tA) * SWN + g] : 0u;
-            float4_t am = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+                for (int t = 0; t < KS; ++t) {
+                    // code group t of this lane: 8*BK bits at bit 8*BK*t of kf
+                    constexpr int FB = 8 * BK;
+                    const int bit = FB * t;
+                    uint32_t field;
+                    if constexpr (BK == 4) field = cur.kf[u][t];
+                    else {
+                        const uint64_t cat = (bit >> 5) + 1 < BK
+                                                 ? ((uint64_t)cur.kf[u][(bit >> 5) + 1] << 32) | cur.kf[u][bit >> 5]
+                                                 : (uint64_t)cur.kf[u][bit >> 5];
+                        field = (uint32_t)(cat >> (bit & 31)) & ((1u << FB) - 1u);
+                    }
+                    half8_t a;
+                    if constexpr (K4) {
+                        const uint2 e0 = klut4[field & ((1u << (4 * BK)) - 1u)];
+                        const uint2 e1 = klut4[field >> (4 * BK)];
+                        const uint32_t wds[4] = {e0.x, e0.y, e1.x, e1.y};
+                        a = __builtin_bit_cast(half8_t, wds);
+                    } else {
+                        uint32_t wds[4];
 #pragma unroll
-            for (int t = 0; t < KS; ++t) {
-                // code group t of this lane: 8*BK bits at bit 8*BK*t of kf
-                constexpr int FB = 8 * BK;
-                const int bit = FB * t;
-                uint32_t field;
-                if constexpr (BK == 4) field = kf[t];
-                else {
-                    const uint64_t cat = (bit >> 5) + 1 < BK
-                                             ? ((uint64_t)kf[(bit >> 5) + 1] << 32) | kf[bit >> 5]
-                                             : (uint64_t)kf[bit >> 5];
-                    field = (uint32_t)(cat >> (bit & 31)) & ((1u << FB) - 1u);
+                        for (int j = 0; j < 4; ++j) wds[j] = klut2[(field >> (2 * BK * j)) & ((1u << (2 * BK)) - 1u)];
+                        a = __builtin_bit_cast(half8_t, wds);
+                    }
+                    am = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[t], am, 0, 0, 0);
+                    if constexpr (QJL) {
+                        const uint4 sv = slut[(cur.sf[u] >> (8 * t)) & 0xFFu];
+                        aq = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, sv), bq[KS + t], aq,
+                                                                    0, 0, 0);
+                    }
                 }
-                half8_t a;
-                if constexpr (K4) {
-                    const uint2 e0 = klut4[field & ((1u << (4 * BK)) - 1u)];
-                    const uint2 e1 = klut4[field >> (4 * BK)];
-                    const uint32_t wds[4] = {e0.x, e0.y, e1.x, e1.y};
-                    a = __builtin_bit_cast(half8_t, wds);
-                } else {
-                    uint32_t wds[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) wds[j] = klut2[(field >> (2 * BK * j)) & ((1u << (2 * BK)) - 1u)];
-                    a = __builtin_bit_cast(half8_t, wds);
-                }
-                am = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[t], am, 0, 0, 0);
-                if constexpr (QJL) {
-                    const uint4 sv = slut[(sf >> (8 * t)) & 0xFFu];
-                    const half8_t sa = __builtin_bit_cast(half8_t, sv);
-                    aq = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, bq[KS + t], aq, 0, 0, 0);
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * u + 4 * g + r;
+                    const float zm = am[r] + xor8(am[r]);
+                    const float zq = QJL ? aq[r] + xor8(aq[r]) : 0.f;
+                    const float z = tokv[wid][0][row] * (zm + tokv[wid][1][row] * zq);
+                    zz[4 * u + r] = (tb + row < w1) ? z : -INFINITY;
                 }
             }
+
+            // ---- block max per head column; rescale only when it beats the running max by 2^8
+            float bm = zz[0];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * u + 4 * g + r;
-                const float zm = am[r] + xor8(am[r]);
-                const float zq = QJL ? aq[r] + xor8(aq[r]) : 0.f;
-                const float z = tokv[wid][0][row] * (zm + tokv[wid][1][row] * zq);
-                zz[4 * u + r] = (tb + row < w1) ? z : -INFINITY;
+            for (int e = 1; e < 8; ++e) bm = fmaxf(bm, zz[e]);
+            bm = fmaxf(bm, __shfl_xor(bm, 16));
+            bm = fmaxf(bm, __shfl_xor(bm, 32));
+            if (__ballot(bm > M + 8.0f)) {
+                const float nM = fmaxf(M, bm);
+                const float f = exp2f(M - nM);
+                lsum *= f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float fr = __shfl(f, (4 * g + r) & 7);
+#pragma unroll
+                    for (int c = 0; c < CT; ++c) acc[c][r] *= fr;
+                }
+                M = nM;
             }
-        }
 
-        // ---- block max per head column; rescale only when it beats the running max by 2^8
-        float bm = zz[0];
+            // ---- weights as the A operand (row = head column, K slot = token)
+            half8_t aw;
 #pragma unroll
-        for (int e = 1; e < 8; ++e) bm = fmaxf(bm, zz[e]);
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        if (__ballot(bm > M + 8.0f)) {
-            const float nM = fmaxf(M, bm);
-            const float f = exp2f(M - nM);
-            lsum *= f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float fr = __shfl(f, (4 * g + r) & 7);
-#pragma unroll
-                for (int c = 0; c < CT; ++c) acc[c][r] *= fr;
+            for (int e = 0; e < 8; ++e) {
+                const float w = exp2f(zz[e] - M);
+                lsum += w;
+                const float W = w * tokv[wid][2][16 * (e >> 2) + 4 * g + (e & 3)];
+                const _Float16 hi = (_Float16)W;
+                aw[e] = col < 8 ? hi : (_Float16)(W - (float)hi);
             }
-            M = nM;
-        }
 
-        // ---- weights as the A operand (row = head column, K slot = token)
-        half8_t aw;
+            // ---- value codes: lane column = code group, slot e = token 4g+e (tile 0) / 16+4g+e-4 (tile 1)
+            uint32_t X[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float w = exp2f(zz[e] - M);
-            lsum += w;
-            const float W = w * tokv[wid][2][16 * (e >> 2) + 4 * g + (e & 3)];
-            const _Float16 hi = (_Float16)W;
-            aw[e] = col < 8 ? hi : (_Float16)(W - (float)hi);
-        }
-
-        // ---- value codes: lane column = code group, slot e = token 4g+e (tile 0) / 16+4g+e-4 (tile 1)
-        uint32_t X[8];
+            for (int e = 0; e < 8; ++e) {
+                if constexpr (BV == 3) X[e] = __builtin_amdgcn_alignbit(cur.x1[e], cur.x0[e], (24 * col) & 31) & 0xFFFFFFu;
+                else if constexpr (BV == 4) X[e] = cur.x0[e];
+                else X[e] = (cur.x0[e] >> ((8 * BV * col) & 31)) & ((1u << (8 * BV)) - 1u);
+            }
+            if constexpr (BV == 3) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int64_t t = tb + 16 * (e >> 2) + 4 * g + (e & 3);
-            X[e] = t < w1 ? vfield<BV>(vcodes + (base + t) * VW, col) : 0u;
-        }
-        if constexpr (BV == 3) {
+                for (int c = 0; c < CT; ++c) {
+                    uint32_t bw[4];
 #pragma unroll
-            for (int c = 0; c < CT; ++c) {
-                uint32_t bw[4];
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t ia = (X[2 * j] >> (3 * c)) & 7u, ib = (X[2 * j + 1] >> (3 * c)) & 7u;
+                        bw[j] = vlut[ia | (ib << 3)];
+                    }
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, bw), acc[c], 0, 0, 0);
+                }
+            } else {
+                // interleave the two tokens' fields: slot k of y0 (2*BV bits) is the index for
+                // tile 2k, slot k of y1 the index for tile 2k+1
+                constexpr uint32_t MSK = BV == 4 ? 0x0F0F0F0Fu : (BV == 2 ? 0x33333333u : 0x55555555u);
+                uint32_t y0[4], y1[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const uint32_t ia = (X[2 * j] >> (3 * c)) & 7u, ib = (X[2 * j + 1] >> (3 * c)) & 7u;
-                    bw[j] = vlut[ia | (ib << 3)];
+                    const uint32_t xa = X[2 * j], xb = X[2 * j + 1];
+                    y0[j] = (xa & MSK) | ((xb << BV) & ~MSK);
+                    y1[j] = ((xa >> BV) & MSK) | (xb & ~MSK);
                 }
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, bw), acc[c], 0, 0, 0);
-            }
-        } else {
-            // interleave the two tokens' fields: slot k of y0 (2*BV bits) is the index for
-            // tile 2k, slot k of y1 the index for tile 2k+1
-            constexpr uint32_t MSK = BV == 4 ? 0x0F0F0F0Fu : (BV == 2 ? 0x33333333u : 0x55555555u);
-            uint32_t y0[4], y1[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t xa = X[2 * j], xb = X[2 * j + 1];
-                y0[j] = (xa & MSK) | ((xb << BV) & ~MSK);
-                y1[j] = ((xa >> BV) & MSK) | (xb & ~MSK);
-            }
+                for (int c = 0; c < CT; ++c) {
+                    uint32_t bw[4];
 #pragma unroll
-            for (int c = 0; c < CT; ++c) {
-                uint32_t bw[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t y = (c & 1) ? y1[j] : y0[j];
-                    bw[j] = vlut[(y >> (2 * BV * (c >> 1))) & ((1u << (2 * BV)) - 1u)];
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t y = (c & 1) ? y1[j] : y0[j];
+                        bw[j] = vlut[(y >> (2 * BV * (c >> 1))) & ((1u << (2 * BV)) - 1u)];
+                    }
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, bw), acc[c], 0, 0, 0);
                 }
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, bw), acc[c], 0, 0, 0);
             }
+            cur = nxt;
         }
-    }
 
-    // ---- per-wave results: sum over row groups, hi rows + lo rows
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    const float inv = 1.0f / wscale;
+        // ---- per-wave results: sum over row groups, hi rows + lo rows
+        lsum += __shfl_xor(lsum, 16);
+        lsum += __shfl_xor(lsum, 32);
+        const float inv = 1.0f / wscale;
 #pragma unroll
-    for (int c = 0; c < CT; ++c)
+        for (int c = 0; c < CT; ++c)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float o = acc[c][r] + __shfl_xor(acc[c][r], 32);
-            const int h = 4 * g + r;
-            if (g < 2 && h < G) mrg_o[wid][h][col + 16 * c] = o * inv;
+            for (int r = 0; r < 4; ++r) {
+                const float o = acc[c][r] + __shfl_xor(acc[c][r], 32);
+                const int h = 4 * g + r;
+                if (g < 2 && h < G) mrg_o[wid][h][col + 16 * c] = o * inv;
+            }
+        if (lane < 8) {
+            mrg_m[wid][lane] = M;
+            mrg_l[wid][lane] = lsum;
         }
-    if (lane < 8) {
-        mrg_m[wid][lane] = M;
-        mrg_l[wid][lane] = lsum;
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // ---- merge the four waves into one partial per head
-    float* part0 = parts + ((s * n_chunks + chunk) * G) * (D + 2);
-    for (int e = tid; e < G * D; e += 256) {
-        const int h = e / D, i = e % D;
-        float mx = -INFINITY;
+        // ---- merge the four waves into one partial per head
+        constexpr int PS = part_stride(D);
+        float* part0 = parts + ((s * n_chunks + chunk) * G) * PS;
+        for (int e = tid; e < G * D; e += 256) {
+            const int h = e / D, i = e % D;
+            float mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) mx = fmaxf(mx, mrg_m[w][h]);
-        float o = 0.f;
-        if (mx != -INFINITY)
-#pragma unroll
-            for (int w = 0; w < 4; ++w)
-                if (mrg_m[w][h] != -INFINITY) o += exp2f(mrg_m[w][h] - mx) * mrg_o[w][h][i];
-        part0[h * (D + 2) + 2 + i] = o;
-        if (i == 0) {
-            float l = 0.f;
+            for (int w = 0; w < 4; ++w) mx = fmaxf(mx, mrg_m[w][h]);
+            float o = 0.f;
             if (mx != -INFINITY)
 #pragma unroll
                 for (int w = 0; w < 4; ++w)
-                    if (mrg_m[w][h] != -INFINITY) l += exp2f(mrg_m[w][h] - mx) * mrg_l[w][h];
-            part0[h * (D + 2)] = mx;
-            part0[h * (D + 2) + 1] = l;
+                    if (mrg_m[w][h] != -INFINITY) o += exp2f(mrg_m[w][h] - mx) * mrg_o[w][h][i];
+            part0[h * PS + kPartAcc + i] = o;
+            if (i == 0) {
+                float l = 0.f;
+                if (mx != -INFINITY)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w)
+                        if (mrg_m[w][h] != -INFINITY) l += exp2f(mrg_m[w][h] - mx) * mrg_l[w][h];
+                part0[h * PS] = mx;
+                part0[h * PS + 1] = l;
+            }
         }
+        __syncthreads();
     }
 }
 
@@ -344,9 +422,12 @@ void launch_mfma(const tq_packed* k, const tq_packed* v, int64_t n_streams, int6
                  const half8_t* frags, const tq_quantizer* qk, const tq_quantizer* qv, float zscale,
                  float* parts, int n_chunks, int tc, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_decode_mfma<D, BK, QJL, BV>), dim3((unsigned)n_chunks, (unsigned)n_streams), dim3(256),
-                       0, s, k->codes, k->signs, k->norm, k->rnorm, v->codes, v->norm, T, G, frags,
-                       qk->centroids, qv->centroids, zscale, parts, n_chunks, tc);
+    const int64_t n_items = n_streams * n_chunks;
+    const int64_t cap = (int64_t)device_cus() * 2;
+    const unsigned grid = (unsigned)(n_items < cap ? n_items : cap);
+    hipLaunchKernelGGL((k_decode_mfma<D, BK, QJL, BV>), dim3(grid), dim3(256), 0, s, k->codes, k->signs, k->norm,
+                       k->rnorm, v->codes, v->norm, T, G, frags, qk->centroids, qv->centroids, zscale, parts,
+                       n_chunks, tc, n_items);
 }
 
 template <int D, int BK, bool QJL>
@@ -364,18 +445,35 @@ void launch_bv(int bv, const tq_packed* k, const tq_packed* v, int64_t ns, int64
 
 }  // namespace
 
+int device_cus()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
-                       const tq_packed* v, int64_t n_streams, int64_t T, int G, const float* qr,
-                       const float* p, float zscale, void* frags, float* parts, int n_chunks, int tc,
+                       const tq_packed* v, int64_t n_streams, int64_t T, int G, const void* q,
+                       int q_dtype, float zscale, void* frags, float* parts, int n_chunks, int tc,
                        hipStream_t s)
 {
     constexpr int D = 128;
     const bool qjl = qk->qjl_m != 0;
-    const int ksteps = (D / 32) * (qjl ? 2 : 1);
-    const int64_t nf = n_streams * ksteps * 64;
-    const unsigned fb = (unsigned)((nf + 255) / 256);
-    if (qjl) hipLaunchKernelGGL((k_qfrag<D, true>), dim3(fb), dim3(256), 0, s, qr, p, n_streams, G, (half8_t*)frags);
-    else hipLaunchKernelGGL((k_qfrag<D, false>), dim3(fb), dim3(256), 0, s, qr, p, n_streams, G, (half8_t*)frags);
+    half8_t* fw = (half8_t*)frags;
+    const dim3 pg((unsigned)n_streams, (unsigned)(D / 32)), pb(256);
+    if (q_dtype == TQ_F16) {
+        if (qjl) hipLaunchKernelGGL((k_qprep_frag<D, true, true>), pg, pb, 0, s, q, G, qk->diag_signs, qk->S, fw);
+        else hipLaunchKernelGGL((k_qprep_frag<D, false, true>), pg, pb, 0, s, q, G, qk->diag_signs, qk->S, fw);
+    } else {
+        if (qjl) hipLaunchKernelGGL((k_qprep_frag<D, true, false>), pg, pb, 0, s, q, G, qk->diag_signs, qk->S, fw);
+        else hipLaunchKernelGGL((k_qprep_frag<D, false, false>), pg, pb, 0, s, q, G, qk->diag_signs, qk->S, fw);
+    }
     const half8_t* fr = (const half8_t*)frags;
     switch (qk->mse_bits) {
         case 1: qjl ? launch_bv<D, 1, true>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)

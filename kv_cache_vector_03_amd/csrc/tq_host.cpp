@@ -190,10 +190,12 @@ DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int
     DecodePlan p{};
     p.mfma = qk->d == 128 && G <= 8;
     if (p.mfma) {
-        // about 1024 blocks in total, 128..2048 tokens each (a power of two)
-        int64_t want = (n_streams * T) / 1024;
-        int64_t tc = 128;
-        while (tc * 2 <= want && tc < 2048) tc *= 2;
+        // spread the n_streams * T tokens over at most kDecodeSlots equal chunks
+        // (multiples of 128 tokens: four waves of 32-token steps)
+        int64_t per = kDecodeSlots / n_streams;
+        if (per < 1) per = 1;
+        int64_t tc = (T + per - 1) / per;
+        tc = (tc + 127) / 128 * 128;
         p.tc = tc;
     } else {
         p.tc = 256;  // the scalar kernel handles one token per thread
@@ -205,7 +207,7 @@ DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int
     p.off_p = up256(nq * qk->d * 4);
     p.off_frag = p.off_p + up256(nq * (qk->qjl_m ? qk->qjl_m : 1) * 4);
     p.off_parts = p.off_frag + (p.mfma ? up256((size_t)n_streams * ksteps * 64 * 16) : 0);
-    p.total = p.off_parts + up256((size_t)n_streams * p.n_chunks * G * (qk->d + 2) * 4);
+    p.total = p.off_parts + up256((size_t)n_streams * p.n_chunks * G * part_stride(qk->d) * 4);
     return p;
 }
 

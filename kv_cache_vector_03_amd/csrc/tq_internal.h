@@ -22,6 +22,16 @@ size_t scores_ws(const tq_quantizer* q, int64_t n_q);
 
 // Decode-attention work split and workspace layout (offsets in bytes from
 // the workspace base, each 256-byte aligned).
+// One decode partial (per stream, chunk, head): max (log2 units), sum of
+// weights, two pad words, then the d-float rotated-domain accumulator (16-byte
+// aligned for vector loads).
+constexpr int part_stride(int d) { return d + 4; }
+constexpr int kPartAcc = 4;
+
+// Blocks the MFMA decode plans for: two resident 256-thread blocks on each of
+// the 256 compute units of an MI355X.
+constexpr int kDecodeSlots = 512;
+
 struct DecodePlan {
     bool mfma;          // MFMA kernel (d = 128, G <= 8); else the scalar kernel
     int64_t tc;         // tokens per block
@@ -29,6 +39,9 @@ struct DecodePlan {
     size_t off_qr, off_p, off_frag, off_parts, total;
 };
 DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G);
+
+// compute units of the current device (cached per device)
+int device_cus();
 
 // kernel launchers (tq_*.hip); each returns TQ_OK or TQ_ERR_DEVICE
 int launch_quantize(const tq_quantizer* q, const void* x, int dtype, int64_t n,
@@ -40,11 +53,11 @@ int launch_scores(const tq_quantizer* q, const tq_packed* k, int64_t n_keys, con
 int launch_dequantize(const tq_quantizer* q, const tq_packed* in, int64_t n, int include_qjl,
                       void* out, int dtype, hipStream_t s);
 int launch_decode(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
-                  const tq_packed* v, int64_t n_streams, int64_t T, int G, const DecodePlan& plan,
-                  void* ws, float scale, float* out, hipStream_t s);
+                  const tq_packed* v, int64_t n_streams, int64_t T, int G, const void* q, int q_dtype,
+                  const DecodePlan& plan, void* ws, float scale, float* out, hipStream_t s);
 int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
-                       const tq_packed* v, int64_t n_streams, int64_t T, int G, const float* qr,
-                       const float* p, float zscale, void* frags, float* parts, int n_chunks, int tc,
+                       const tq_packed* v, int64_t n_streams, int64_t T, int G, const void* q,
+                       int q_dtype, float zscale, void* frags, float* parts, int n_chunks, int tc,
                        hipStream_t s);
 
 }  // namespace tq
