@@ -31,7 +31,8 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-ffp-contract=off", "-Wall", f"-I{INCLUDE}",
               f"-I{CSRC}"]
 
-SOURCES = ["tq_host.cpp", "tq_api.cpp", "tq_quantize.hip", "tq_attn.hip", "tq_decode.hip"]
+SOURCES = ["tq_host.cpp", "tq_api.cpp", "tq_quantize.hip", "tq_quantize_m128.hip", "tq_attn.hip",
+           "tq_decode.hip"]
 
 
 def _run(cmd):

@@ -133,6 +133,27 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 // sqrt(pi/2)
 constexpr float kSqrtHalfPi = 1.2533141373155003f;
 
+int device_cus();
+
+// Grid for a grid-stride kernel of 256-thread blocks: enough blocks to cover
+// n units (units_per_block each), but no more than fit on the device at once,
+// so every block is resident and the work divides evenly.
+template <typename Kern>
+int resident_grid(Kern kern, int64_t units_per_block, int64_t n)
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (!cached[dev]) {
+        int nb = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 256, 0) != hipSuccess || nb < 1) nb = 1;
+        cached[dev] = nb * device_cus();
+    }
+    int64_t want = (n + units_per_block - 1) / units_per_block;
+    if (want < 1) want = 1;
+    return (int)(want < cached[dev] ? want : cached[dev]);
+}
+
 }  // namespace tq
 
 #endif

@@ -44,6 +44,8 @@ DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int
 int device_cus();
 
 // kernel launchers (tq_*.hip); each returns TQ_OK or TQ_ERR_DEVICE
+void launch_quantize_m128(const tq_quantizer* q, const void* x, int64_t n, const tq_packed* out,
+                          hipStream_t s);
 int launch_quantize(const tq_quantizer* q, const void* x, int dtype, int64_t n,
                     const tq_packed* out, hipStream_t s);
 int launch_qprep(const tq_quantizer* q, const void* queries, int dtype, int64_t nq,

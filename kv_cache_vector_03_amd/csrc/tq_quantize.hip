@@ -559,13 +559,19 @@ void quantize_d_b(const tq_quantizer* q, const void* x, int dtype, int64_t n, co
 {
     dim3 block(256);
     if constexpr (D <= 128) {
-        dim3 grid(grid_for(n, kWavesPerBlock * 16, 1024));
-        if (dtype == TQ_F16)
-            hipLaunchKernelGGL((k_quantize_quad<D, B, QJL, true>), grid, block, 0, s, x, n, q->centroids,
-                               q->boundaries, q->diag_signs, q->S, o->codes, o->signs, o->norm, o->rnorm);
-        else
-            hipLaunchKernelGGL((k_quantize_quad<D, B, QJL, false>), grid, block, 0, s, x, n, q->centroids,
-                               q->boundaries, q->diag_signs, q->S, o->codes, o->signs, o->norm, o->rnorm);
+        if (D == 128 && dtype == TQ_F16) {
+            launch_quantize_m128(q, x, n, o, s);
+        } else if (dtype == TQ_F16) {
+            auto kern = k_quantize_quad<D, B, QJL, true>;
+            hipLaunchKernelGGL(kern, dim3(resident_grid(kern, kWavesPerBlock * 16, n)), block, 0, s, x, n,
+                               q->centroids, q->boundaries, q->diag_signs, q->S, o->codes, o->signs, o->norm,
+                               o->rnorm);
+        } else {
+            auto kern = k_quantize_quad<D, B, QJL, false>;
+            hipLaunchKernelGGL(kern, dim3(resident_grid(kern, kWavesPerBlock * 16, n)), block, 0, s, x, n,
+                               q->centroids, q->boundaries, q->diag_signs, q->S, o->codes, o->signs, o->norm,
+                               o->rnorm);
+        }
     } else {
         dim3 grid(grid_for(n, kWavesPerBlock));
         if (dtype == TQ_F16)

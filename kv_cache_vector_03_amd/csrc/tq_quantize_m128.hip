@@ -1,0 +1,371 @@
+// Quantizer for d = 128 with fp16 input: the rotation runs on MFMA.
+//
+// Same method as the quad kernel ("[Benchmark] TurboQuant 實測：KV Cache 3-bit
+// 壓縮，真的零損失？", section "TurboQuant 是什麼：30 秒懶人包": random
+// rotation, stored norm, per-coordinate Lloyd-Max codes, and for keys a 1-bit
+// sketch of the residual plus its norm); only the data movement differs.
+//
+// Rotation. Sylvester's H_128 factors as H_4 (x) H_32 over the coordinate
+// bits: H_128[i][j] = (-1)^popcount(i & j) = H_4[i >> 5][j >> 5] H_32[i & 31][j & 31].
+// A wave takes 16 vectors at a time, four lanes per vector: lane (v, q) with
+// v = lane % 16 and q = lane / 16. For each 32-coordinate chunk a' of the
+// input the lane loads coordinates 32 a' + 8 q .. + 7 (sign-flipped by the
+// random diagonal) -- the B operand of a 16x16x32 MFMA whose 16 columns are
+// the vectors. The A operand is a constant 16-row slab of H_32 (two slabs,
+// tau = 0, 1), so each MFMA applies H_32 to one chunk of 16 vectors. Output
+// row rho = 4 q + r of slab tau lands in lane (v, q), register r, which
+// therefore holds chunk outputs b = 16 tau + 4 q + r for all four chunks; the
+// H_4 factor is two butterfly stages across those registers. Coordinate
+// 32 a + 16 tau + 4 q + r is group n = 4 q + r, member t = 2 a + tau of the
+// group-major layout, so lane (v, q) ends up holding the four complete groups
+// 4 q .. 4 q + 3 of vector v, i.e. code words B q .. B q + B - 1.
+//
+// Codes and the QJL projection then follow the quad kernel: sign-bit code
+// arithmetic with thresholds scaled by sqrt(d) ||x||, residual split into
+// exact fp16 hi + lo operands, projection on MFMA against S with the rows
+// permuted so each ballot is two bytes of the sign stream. The projection's
+// A operand is the residual with rows = vectors (lane % 16) and k-block q:
+// k-step r, element t is coordinate 4 q + r + 16 t, which this lane holds.
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr int kD = 128;
+
+// S row feeding column c of n-tile nu (sign stream bits 16 nu .. 16 nu + 15)
+__host__ __device__ constexpr int m128_proj_row(int nu, int c) { return 2 * nu + c / 8 + 16 * (c % 8); }
+
+// Codes of the 32 coordinates a lane holds by sign-bit arithmetic: with the
+// symmetric codebook the top code bit is [Y > 0] and the lower bits are the
+// count #{M_j s < |Y|} (XOR-folded from the signs of M_j s - |Y|), complemented
+// for Y <= 0. Local stream bit 8 B r + B t + p is shifted in from the top. For
+// keys the residual Y - c replaces y and its squared norm goes to g2.
+template <int B, bool QJL, int K = (1 << B) / 2 - 1>
+__device__ __forceinline__ void codes_compare(float (&y)[8][4], const float (&Ms)[K > 0 ? K : 1],
+                                              const float (&Cs)[K + 1], const float* __restrict__ ctab, float s,
+                                              uint32_t (&W)[B], float& g2)
+{
+#pragma unroll
+    for (int w = 0; w < B; ++w) W[w] = 0;
+#pragma unroll
+    for (int r = 3; r >= 0; --r)
+#pragma unroll
+        for (int t = 7; t >= 0; --t) {
+            const float Y = y[t][r];
+            const uint32_t d2 = __float_as_uint(0.0f - Y);  // sign bit = [Y > 0]
+            uint32_t e[K > 0 ? K : 1];
+#pragma unroll
+            for (int j = 0; j < K; ++j) e[j] = __float_as_uint(Ms[j] - fabsf(Y));  // [|Y| > M_j s]
+#pragma unroll
+            for (int p = B - 1; p >= 0; --p) {
+                uint32_t val;
+                if (p == B - 1) {
+                    val = d2;
+                } else {
+                    uint32_t xq = 0;
+#pragma unroll
+                    for (int j = 1; j <= K; ++j)
+                        if (j % (1 << p) == 0) xq ^= e[j - 1];
+                    val = ~(xq ^ d2);
+                }
+                const int P = 8 * B * r + B * t + p;
+                W[P >> 5] = __builtin_amdgcn_alignbit(W[P >> 5], val, 31);
+            }
+            if constexpr (QJL) {
+                float mag;
+                if constexpr (K <= 1) {
+                    mag = Cs[0];
+#pragma unroll
+                    for (int j = 0; j < K; ++j) mag = fabsf(Y) > Ms[j] ? Cs[j + 1] : mag;
+                } else {
+                    // magnitude level from the comparison signs, value from the table
+                    uint32_t cnt = 0;
+#pragma unroll
+                    for (int j = 0; j < K; ++j) cnt += e[j] >> 31;
+                    mag = ctab[(1 << B) / 2 + cnt] * s;
+                }
+                // c = +mag for Y > 0, -mag otherwise (y = 0 maps to the level just below 0)
+                const float c = __uint_as_float((__float_as_uint(mag) & 0x7FFFFFFFu) | (~d2 & 0x80000000u));
+                const float rr = Y - c;
+                g2 += rr * rr;
+                y[t][r] = rr;
+            }
+        }
+}
+
+// Code lookup grid. Cell c of the table covers the rotated unit coordinate
+// y in [(c - NC - 1/2) / NC, (c - NC + 1/2) / NC); its entry holds the number
+// of boundaries below the cell start and the first boundary at or above it.
+// The code of Y = sqrt(d) ||x|| y is then base + [Y > next * sqrt(d) ||x||],
+// the same strict comparison the codebook defines, as long as no window of two
+// cells holds two boundaries (the cell index itself may be off by one where
+// rounding puts y on a cell edge). The table is checked for that when built.
+constexpr int kLutCells = 256;
+constexpr int kLutEntries = 2 * kLutCells + 2;
+constexpr uint32_t kMagicBits = 0x4B000000u;  // bit pattern of 2^23
+
+template <int B, bool QJL>
+__device__ __forceinline__ void codes_lut(float (&y)[8][4], const uint2* __restrict__ lut,
+                                          const float* __restrict__ ctab, float s, float rs, uint32_t (&W)[B],
+                                          float& g2)
+{
+    constexpr float magic = 8388608.0f + kLutCells;  // 2^23 + NC: rounds to an integer index
+    uint32_t Gr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        uint32_t g = 0;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float Y = y[t][r];
+            uint32_t bits = __float_as_uint(fmaf(Y, rs, magic));
+            bits = min(max(bits, kMagicBits), kMagicBits + (uint32_t)(kLutEntries - 1));
+            const uint2 ent = lut[bits - kMagicBits];
+            const float e = fmaf(__uint_as_float(ent.x), s, -Y);  // < 0 iff Y > next boundary
+            const uint32_t code = ent.y - (uint32_t)((int32_t)__float_as_uint(e) >> 31);
+            g = __builtin_amdgcn_alignbit(code, g, B);  // code t ends at bits 32 - 8B + B t
+            if constexpr (QJL) {
+                const float rr = fmaf(-ctab[code & ((1u << B) - 1u)], s, Y);
+                g2 += rr * rr;
+                y[t][r] = rr;
+            }
+        }
+        Gr[r] = g;  // group r in its top 8 B bits
+    }
+    if constexpr (B == 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) W[r] = Gr[r];
+    } else if constexpr (B == 3) {
+        W[0] = (Gr[0] >> 8) | (Gr[1] << 16);
+        W[1] = (Gr[1] >> 16) | (Gr[2] << 8);
+        W[2] = (Gr[2] >> 24) | Gr[3];
+    } else if constexpr (B == 2) {
+        W[0] = (Gr[0] >> 16) | (Gr[1] & 0xFFFF0000u);
+        W[1] = (Gr[2] >> 16) | (Gr[3] & 0xFFFF0000u);
+    } else {
+        W[0] = (Gr[0] >> 24) | ((Gr[1] >> 16) & 0xFF00u) | ((Gr[2] >> 8) & 0xFF0000u) | (Gr[3] & 0xFF000000u);
+    }
+}
+
+template <int B, bool QJL>
+__global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restrict__ x, int64_t n,
+                                                       const float* __restrict__ cent,
+                                                       const float* __restrict__ bnd,
+                                                       const uint32_t* __restrict__ diag,
+                                                       const uint16_t* __restrict__ S,
+                                                       uint32_t* __restrict__ codes,
+                                                       uint32_t* __restrict__ signs,
+                                                       uint16_t* __restrict__ norm,
+                                                       uint16_t* __restrict__ rnorm)
+{
+    constexpr int L = 1 << B, K = L / 2 - 1;
+    constexpr int CW = B * kD / 32;  // code words per vector
+    constexpr int NT = 8, KS = 4;    // projection n-tiles (m = 128) and k-steps
+    constexpr bool LUT = B >= 3;
+    __shared__ __align__(16) half8_t bfrag[QJL ? KS * NT * 64 : 1];
+    __shared__ uint2 lut[LUT ? kLutEntries : 1];
+    __shared__ float ctab[LUT ? L : 1];
+    __shared__ int lut_bad;
+
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int v = lane & 15, q = lane >> 4;
+
+    float Mth[K > 0 ? K : 1], Cm[K + 1];
+#pragma unroll
+    for (int j = 1; j <= K; ++j) Mth[j - 1] = bnd[L / 2 - 1 + j];
+#pragma unroll
+    for (int m = 0; m <= K; ++m) Cm[m] = cent[L / 2 + m];
+
+    // H_32 slabs as A operands: lane (row rho = v, k-block q), element e is
+    // H_32[16 tau + rho][8 q + e]
+    half8_t hA[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            hA[tau][e] = (__builtin_popcount((16 * tau + v) & (8 * q + e)) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
+
+    // diagonal sign flips of the lane's input halves: chunk a', word w holds
+    // coordinates 32 a' + 8 q + 2 w (low half) and + 1 (high half)
+    uint32_t dm[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const uint32_t word = diag[a] >> (8 * q);
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            dm[a][w] = (((word >> (2 * w)) & 1u) << 15) | (((word >> (2 * w + 1)) & 1u) << 31);
+    }
+
+    if constexpr (LUT) {
+        if (threadIdx.x == 0) lut_bad = 0;
+        __syncthreads();
+        for (int c = threadIdx.x; c < kLutEntries; c += 256) {
+            const float lo = ((float)(c - kLutCells) - 0.5f) / kLutCells;  // exact
+            const float win = lo + 2.0f / kLutCells;
+            uint32_t base = 0;
+            int inwin = 0;
+            float next = INFINITY;
+            for (int j = 0; j < L - 1; ++j) {
+                const float b = bnd[j];
+                base += b < lo ? 1u : 0u;
+                if (b >= lo && b < next) next = b;
+                inwin += (b >= lo && b < win) ? 1 : 0;
+            }
+            if (inwin > 1) lut_bad = 1;
+            lut[c] = make_uint2(__float_as_uint(next), base);
+        }
+        if (threadIdx.x < L) ctab[threadIdx.x] = cent[threadIdx.x];
+        __syncthreads();
+    }
+    const bool use_lut = LUT && !lut_bad;
+
+    if constexpr (QJL) {
+        // B fragments: lane (k-block kb, column c) of fragment (ks, nu), element e
+        // holds S[proj_row(nu, c)][4 kb + ks + 16 e]
+        for (int e = threadIdx.x; e < KS * NT * 64; e += 256) {
+            const int ks = e / (NT * 64), nu = (e / 64) % NT, ln = e & 63;
+            const int kb = ln >> 4, c = ln & 15;
+            const uint16_t* row = S + (int64_t)m128_proj_row(nu, c) * kD;
+            half8_t f;
+#pragma unroll
+            for (int ee = 0; ee < 8; ++ee) f[ee] = __builtin_bit_cast(_Float16, row[4 * kb + ks + 16 * ee]);
+            bfrag[(ks * NT + nu) * 64 + ln] = f;
+        }
+        __syncthreads();
+    }
+
+    const float inv_sqrt_d = 0.08838834764831845f;  // 1 / sqrt(128)
+    for (int64_t base = ((int64_t)blockIdx.x * 4 + wid) * 16; base < n; base += (int64_t)gridDim.x * 64) {
+        const int64_t vec = base + v;
+        const bool live = vec < n;
+
+        // ---- rotation: H_32 per chunk on MFMA, then H_4 across chunks
+        float4_t z[2][4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            uint4 u = make_uint4(0u, 0u, 0u, 0u);
+            if (live) u = *reinterpret_cast<const uint4*>(x + vec * kD + 32 * a + 8 * q);
+            const uint32_t w4[4] = {u.x ^ dm[a][0], u.y ^ dm[a][1], u.z ^ dm[a][2], u.w ^ dm[a][3]};
+            const half8_t bx = __builtin_bit_cast(half8_t, w4);
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau)
+                z[tau][a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hA[tau], bx, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        }
+        // y[t][r]: coordinate 4 q + r + 16 t, t = 2 a + tau
+        float y[8][4];
+        float ss = 0.f;
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float s01 = z[tau][0][r] + z[tau][1][r], d01 = z[tau][0][r] - z[tau][1][r];
+                const float s23 = z[tau][2][r] + z[tau][3][r], d23 = z[tau][2][r] - z[tau][3][r];
+                y[0 + tau][r] = s01 + s23;
+                y[2 + tau][r] = d01 + d23;
+                y[4 + tau][r] = s01 - s23;
+                y[6 + tau][r] = d01 - d23;
+            }
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ss += y[t][r] * y[t][r];
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        const float sr = sqrtf(ss);                 // sqrt(d) ||x||
+        const float nrm = sr * inv_sqrt_d;
+        const float s = sr > 0.f ? sr : 1.0f;
+        float Ms[K > 0 ? K : 1], Cs[K + 1];
+#pragma unroll
+        for (int j = 0; j < K; ++j) Ms[j] = Mth[j] * s;
+#pragma unroll
+        for (int m = 0; m <= K; ++m) Cs[m] = Cm[m] * s;
+
+        // ---- codes (and for keys the residual)
+        uint32_t W[B];
+        float g2 = 0.f;
+        if (use_lut) codes_lut<B, QJL>(y, lut, ctab, s, (float)kLutCells / s, W, g2);
+        else codes_compare<B, QJL>(y, Ms, Cs, ctab, s, W, g2);
+        if (live) {
+            uint32_t* dst = codes + vec * CW + B * q;
+#pragma unroll
+            for (int w = 0; w < B; ++w) dst[w] = W[w];
+        }
+
+        if constexpr (QJL) {
+            g2 += __shfl_xor(g2, 16);
+            g2 += __shfl_xor(g2, 32);
+            // residual in units of 1/(1024 s) (fp16 range), split into exact fp16 hi + lo
+            const float sc = 1024.0f / s;
+            half8_t ahi[KS], alo[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const float rs = y[t][ks] * sc;
+                    const _Float16 hi = (_Float16)rs;
+                    ahi[ks][t] = hi;
+                    alo[ks][t] = (_Float16)(rs - (float)hi);
+                }
+            uint32_t SW[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) SW[w] = 0;
+#pragma unroll
+            for (int nu = 0; nu < NT; nu += 2) {
+                uint64_t mk[2][4];
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const half8_t bf = bfrag[(ks * NT + nu + hh) * 64 + lane];
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[ks], bf, acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[ks], bf, acc, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) mk[hh][r4] = __ballot(acc[r4] >= 0.f);
+                }
+                // output row 4 g + r4 is vector 4 g + r4 of the batch; its 16 bits in
+                // each ballot are bits 16 g .. 16 g + 15
+                uint32_t sw = SW[nu >> 1];
+                static_for<0, 16>([&](auto k) {
+                    constexpr int g = decltype(k)::value / 4, r4 = decltype(k)::value % 4;
+                    const uint32_t lo = (uint32_t)(mk[0][r4] >> (16 * g)) & 0xFFFFu;
+                    const uint32_t hi = (uint32_t)(mk[1][r4] >> (16 * g)) & 0xFFFFu;
+                    sw = write_lane<4 * g + r4>(sw, lo | (hi << 16));
+                });
+                SW[nu >> 1] = sw;
+            }
+            if (live && q == 0) {
+                *reinterpret_cast<uint4*>(signs + vec * 4) = make_uint4(SW[0], SW[1], SW[2], SW[3]);
+                rnorm[vec] = f2h(sqrtf(g2) / s);
+            }
+        }
+        if (live && q == 0) norm[vec] = f2h(nrm);
+    }
+}
+
+template <int B, bool QJL>
+void launch_b(const tq_quantizer* q, const uint16_t* x, int64_t n, const tq_packed* o, hipStream_t s)
+{
+    auto kern = k_quantize_m128<B, QJL>;
+    const int grid = resident_grid(kern, 64, n);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, x, n, q->centroids, q->boundaries, q->diag_signs,
+                       q->S, o->codes, o->signs, o->norm, o->rnorm);
+}
+
+}  // namespace
+
+void launch_quantize_m128(const tq_quantizer* q, const void* x, int64_t n, const tq_packed* out, hipStream_t s)
+{
+    const uint16_t* xh = static_cast<const uint16_t*>(x);
+    const bool qjl = q->qjl_m != 0;
+    switch (q->mse_bits) {
+        case 1: qjl ? launch_b<1, true>(q, xh, n, out, s) : launch_b<1, false>(q, xh, n, out, s); break;
+        case 2: qjl ? launch_b<2, true>(q, xh, n, out, s) : launch_b<2, false>(q, xh, n, out, s); break;
+        case 3: qjl ? launch_b<3, true>(q, xh, n, out, s) : launch_b<3, false>(q, xh, n, out, s); break;
+        default: qjl ? launch_b<4, true>(q, xh, n, out, s) : launch_b<4, false>(q, xh, n, out, s); break;
+    }
+}
+
+}  // namespace tq

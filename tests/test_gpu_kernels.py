@@ -193,3 +193,29 @@ def test_synth_gpu_twin_matches_host():
     u = torch.empty((50, 64), dtype=torch.float32, device=DEV)
     gpu.unit_f32(u, 5, synth.ROLE_DATA_K, first_vec=1000)
     assert np.array_equal(u.cpu().numpy(), synth.unit_vectors_f32(5, synth.ROLE_DATA_K, 50, 64, first=1000))
+
+
+@pytest.mark.parametrize("m", [0, 128])
+def test_quantize_crowded_codebook(m):
+    """A symmetric 3-bit codebook with two boundaries 0.0075 apart near zero
+    (closer than the lookup grid of the d = 128 fp16 kernel resolves), and one
+    with well-spread levels: both must give the codebook's codes exactly. The
+    crowded one exercises the comparison path that the grid check falls back to."""
+    import dataclasses
+    tq = tqmod()
+    d = 128
+    diag = synth.diag_signs(7, synth.ROLE_DIAG_K, d)
+    S = synth.proj_matrix_f16(7, synth.ROLE_PROJ_K, d, d) if m else None
+    for cent in ([-0.3, -0.2, -0.01, -0.005, 0.005, 0.01, 0.2, 0.3],
+                 [-0.25, -0.15, -0.08, -0.02, 0.02, 0.08, 0.15, 0.25]):
+        cent = np.asarray(cent, np.float32)
+        bnd = ((cent[1:].astype(np.float64) + cent[:-1]) / 2).astype(np.float32)
+        base = oracle.codebook(d, 3)
+        cb = dataclasses.replace(base, c_exact=cent.astype(np.float64), centroids=cent, boundaries=bnd)
+        qo = oracle.Quantizer(d, 3, m, diag, S, cb=cb)
+        qg = tq.Quantizer(d, 3, m, diag, S, DEV)
+        qg.centroids.copy_(torch.from_numpy(cent))
+        qg.boundaries[:7].copy_(torch.from_numpy(bnd))
+        n = 700
+        x = synth.to_f16(synth.normals(23, synth.ROLE_DATA_K, np.arange(n * d)).reshape(n, d) * 2.0)
+        check_quantize(qo, x.astype(np.float64), gpu_quantize(qg, x).to_host())
