@@ -42,6 +42,10 @@ def parse():
     ap.add_argument("--replicas", type=int, default=5, help="8k workload: cache replicas")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=0, help="override layer count (debug)")
+    ap.add_argument("--cpu-streams", type=int, default=8,
+                    help="streams of the first batch the oracle baseline runs on")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (profiler byte-counter calibration)")
     return ap.parse_args()
 
 
@@ -61,9 +65,10 @@ def source_sha(paths):
 
 
 KERNEL_SOURCES = {
-    "quantize": ["kv_cache_vector_03_amd/csrc/tq_quantize.hip", "kv_cache_vector_03_amd/csrc/tq_device.h"],
-    "decode_attn": ["kv_cache_vector_03_amd/csrc/tq_attn.hip", "kv_cache_vector_03_amd/csrc/tq_quantize.hip",
-                    "kv_cache_vector_03_amd/csrc/tq_device.h"],
+    "quantize_k": ["kv_cache_vector_03_amd/csrc/tq_quantize_m128.hip", "kv_cache_vector_03_amd/csrc/tq_device.h"],
+    "quantize_v": ["kv_cache_vector_03_amd/csrc/tq_quantize_m128.hip", "kv_cache_vector_03_amd/csrc/tq_device.h"],
+    "decode_attn": ["kv_cache_vector_03_amd/csrc/tq_decode.hip", "kv_cache_vector_03_amd/csrc/tq_attn.hip",
+                    "kv_cache_vector_03_amd/csrc/tq_device.h", "kv_cache_vector_03_amd/csrc/tq_host.cpp"],
 }
 
 
@@ -80,10 +85,12 @@ def traffic_for(op, launch_alg_bytes, workload):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU; the method's data-parallel path "
-                                   "is measured per GPU (see DESIGN.md for how it would shard)",
-                          "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark measures the data-parallel path on one GPU; "
+                                   "runs on several GPUs are not part of it", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import numpy as np
@@ -190,10 +197,10 @@ def main():
     step_bytes = sum(per_launch[o] * launches[o] // args.steps for o in ops)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dom = max(ops, key=lambda o: kern[o]["time_share"])
-    dom_key = "quantize" if dom.startswith("quantize") else "decode_attn"
+    for o in ops:
+        kern[o]["traffic"] = traffic_for(o, per_launch[o], args.workload)
     roof = {"kernel": dom, "bound": "hbm", "achieved": kern[dom]["GB_per_s"], "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"],
-            "traffic": traffic_for(dom_key, per_launch[dom], args.workload)}
+            "unit": "GB/s", "frac": kern[dom]["frac_hbm_peak"], "traffic": kern[dom]["traffic"]}
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -213,37 +220,50 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, diag_k, S, diag_v, kb, vb)
+        u = units[0]
+        result["cpu_baseline"] = cpu_baseline(cfg, diag_k, S, diag_v, kb, vb, u["K"], u["V"], u["Q"], u["ns"],
+                                              args.cpu_streams)
     print(json.dumps(result))
 
 
-def cpu_baseline(cfg, diag_k, S, diag_v, kb, vb):
-    """The oracle on a bounded sample of the same workload: one stream's first
-    ``n`` tokens quantized (K and V) and decoded with its G query heads."""
-    import numpy as np
-
+def cpu_baseline(cfg, diag_k, S, diag_v, kb, vb, K_dev, V_dev, Q_dev, ns, max_streams):
+    """The oracle on a bounded sample of the same workload: the first streams
+    of the first batch (the same fp16 inputs the GPU quantizes), quantized (K
+    and V) and decoded with their G query heads."""
     import oracle
-    import synth
-    from synth import workloads as W
-    d, G = cfg.d, cfg.G
-    n = min(cfg.tokens, 32768)
-    toks = np.arange(n)
-    K = W.kv_vectors_host(cfg, 0, synth.ROLE_DATA_K, 0, toks).astype(np.float64)
-    V = W.kv_vectors_host(cfg, 0, synth.ROLE_DATA_V, 0, toks).astype(np.float64)
-    Q = W.kv_queries_host(cfg, 0)[0:1].astype(np.float64)
+    d, G, T = cfg.d, cfg.G, cfg.tokens
+    s = min(ns, max_streams)
+    n = s * T
+    K = K_dev[:n].cpu().numpy().astype("float64")
+    V = V_dev[:n].cpu().numpy().astype("float64")
+    Q = Q_dev[:s].cpu().numpy().astype("float64")
     qko = oracle.Quantizer(d, cfg.k_mse_bits, d, diag_k, S)
     qvo = oracle.Quantizer(d, cfg.v_bits, 0, diag_v, None)
     oracle.quantize(qko, K[:256])
     t0 = time.perf_counter()
     pk = oracle.quantize(qko, K)
     pv = oracle.quantize(qvo, V)
-    oracle.decode_attn(qko, qvo, pk, pv, 1, n, G, Q)
+    oracle.decode_attn(qko, qvo, pk, pv, s, T, G, Q)
     dt = time.perf_counter() - t0
-    alg = n * (2 * d + kb) + n * (2 * d + vb) + n * (kb + vb) + G * d * 6
+    alg = n * (2 * d + kb) + n * (2 * d + vb) + n * (kb + vb) + s * G * d * 6
     return {"value": round(alg / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(),
             "kind": "oracle",
-            "sample": f"one stream (layer 0, KV head 0), first {n} tokens: quantize K and V, "
-                      f"decode with its {G} query heads; {dt:.2f} s"}
+            "sample": f"first {s} streams ({n} tokens) of the first batch: quantize K and V, "
+                      f"decode with {G} query heads per stream; {dt:.2f} s"}
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters (FETCH_SIZE, WRITE_SIZE) of a profiler run."""
+    import torch
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 2, dtype=torch.float16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                      "launches": 3}))
 
 
 if __name__ == "__main__":

@@ -31,6 +31,10 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-ffp-contract=off", "-Wall", f"-I{INCLUDE}",
               f"-I{CSRC}"]
 
+# per-source extra hipcc flags: keep MFMA results in ordinary VGPRs (no AGPR
+# copies) where the results feed VALU code right away
+EXTRA_FLAGS = {"tq_quantize_m128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 SOURCES = ["tq_host.cpp", "tq_api.cpp", "tq_quantize.hip", "tq_quantize_m128.hip", "tq_attn.hip",
            "tq_decode.hip"]
 
@@ -47,7 +51,7 @@ def _compile(src: str) -> str:
     path = os.path.join(CSRC, src)
     obj = os.path.join(BUILD, src + ".o")
     if src.endswith(".hip"):
-        cmd = [HIPCC, *HIP_FLAGS, "-x", "hip", "-c", path, "-o", obj]
+        cmd = [HIPCC, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", path, "-o", obj]
     else:
         cmd = ["g++", *HOST_FLAGS, "-c", path, "-o", obj]
     _run(cmd)

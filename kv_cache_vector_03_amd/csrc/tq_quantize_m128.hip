@@ -12,20 +12,23 @@
 // input the lane loads coordinates 32 a' + 8 q .. + 7 (sign-flipped by the
 // random diagonal) -- the B operand of a 16x16x32 MFMA whose 16 columns are
 // the vectors. The A operand is a constant 16-row slab of H_32 (two slabs,
-// tau = 0, 1), so each MFMA applies H_32 to one chunk of 16 vectors. Output
-// row rho = 4 q + r of slab tau lands in lane (v, q), register r, which
-// therefore holds chunk outputs b = 16 tau + 4 q + r for all four chunks; the
-// H_4 factor is two butterfly stages across those registers. Coordinate
-// 32 a + 16 tau + 4 q + r is group n = 4 q + r, member t = 2 a + tau of the
-// group-major layout, so lane (v, q) ends up holding the four complete groups
-// 4 q .. 4 q + 3 of vector v, i.e. code words B q .. B q + B - 1.
+// tau = 0, 1) or its negation, and output chunk a accumulates the four input
+// chunks with the signs H_4[a][a'], so each accumulator holds finished
+// rotated coordinates: row rho = 4 q + r of slab tau, output chunk a lands in
+// lane (v, q), register r, as coordinate 32 a + 16 tau + 4 q + r -- group
+// n = 4 q + r, member t = 2 a + tau of the group-major layout. Lane (v, q)
+// thus holds the four complete groups 4 q .. 4 q + 3 of vector v, i.e. code
+// words B q .. B q + B - 1. The next batch's input is fetched while the
+// current one is processed.
 //
-// Codes and the QJL projection then follow the quad kernel: sign-bit code
-// arithmetic with thresholds scaled by sqrt(d) ||x||, residual split into
-// exact fp16 hi + lo operands, projection on MFMA against S with the rows
-// permuted so each ballot is two bytes of the sign stream. The projection's
-// A operand is the residual with rows = vectors (lane % 16) and k-block q:
-// k-step r, element t is coordinate 4 q + r + 16 t, which this lane holds.
+// Codes follow the quad kernel (sign-bit arithmetic for 1- and 2-bit codes)
+// or a lookup grid (3 and 4 bits). For keys the residual is formed directly in
+// units of 1/(1024 s) (s = sqrt(d) ||x||, keeping it in fp16 range), split
+// into exact fp16 hi + lo operands and projected on MFMA against S, with the
+// rows of S permuted so each ballot is two bytes of the sign stream. The
+// projection's A operand is the residual with rows = vectors (lane % 16) and
+// k-block q: k-step r, element t is coordinate 4 q + r + 16 t, which this
+// lane holds.
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -33,6 +36,7 @@ namespace tq {
 namespace {
 
 constexpr int kD = 128;
+constexpr float kResUnit = 1024.0f;  // residual scale for the projection operands
 
 // S row feeding column c of n-tile nu (sign stream bits 16 nu .. 16 nu + 15)
 __host__ __device__ constexpr int m128_proj_row(int nu, int c) { return 2 * nu + c / 8 + 16 * (c % 8); }
@@ -41,10 +45,11 @@ __host__ __device__ constexpr int m128_proj_row(int nu, int c) { return 2 * nu +
 // symmetric codebook the top code bit is [Y > 0] and the lower bits are the
 // count #{M_j s < |Y|} (XOR-folded from the signs of M_j s - |Y|), complemented
 // for Y <= 0. Local stream bit 8 B r + B t + p is shifted in from the top. For
-// keys the residual Y - c replaces y and its squared norm goes to g2.
+// keys, y is replaced by the scaled residual (Y - c s) * sc and its squared
+// norm accumulates in g2 (Cq: centroid magnitudes times kResUnit).
 template <int B, bool QJL, int K = (1 << B) / 2 - 1>
 __device__ __forceinline__ void codes_compare(float (&y)[8][4], const float (&Ms)[K > 0 ? K : 1],
-                                              const float (&Cs)[K + 1], const float* __restrict__ ctab, float s,
+                                              const float (&Cq)[K + 1], const float* __restrict__ ctab, float sc,
                                               uint32_t (&W)[B], float& g2)
 {
 #pragma unroll
@@ -76,21 +81,21 @@ __device__ __forceinline__ void codes_compare(float (&y)[8][4], const float (&Ms
             if constexpr (QJL) {
                 float mag;
                 if constexpr (K <= 1) {
-                    mag = Cs[0];
+                    mag = Cq[0];
 #pragma unroll
-                    for (int j = 0; j < K; ++j) mag = fabsf(Y) > Ms[j] ? Cs[j + 1] : mag;
+                    for (int j = 0; j < K; ++j) mag = (int32_t)e[j] < 0 ? Cq[j + 1] : mag;
                 } else {
                     // magnitude level from the comparison signs, value from the table
                     uint32_t cnt = 0;
 #pragma unroll
                     for (int j = 0; j < K; ++j) cnt += e[j] >> 31;
-                    mag = ctab[(1 << B) / 2 + cnt] * s;
+                    mag = ctab[(1 << B) / 2 + cnt];
                 }
                 // c = +mag for Y > 0, -mag otherwise (y = 0 maps to the level just below 0)
                 const float c = __uint_as_float((__float_as_uint(mag) & 0x7FFFFFFFu) | (~d2 & 0x80000000u));
-                const float rr = Y - c;
-                g2 += rr * rr;
-                y[t][r] = rr;
+                const float rs = fmaf(Y, sc, -c);
+                g2 = fmaf(rs, rs, g2);
+                y[t][r] = rs;
             }
         }
 }
@@ -108,8 +113,8 @@ constexpr uint32_t kMagicBits = 0x4B000000u;  // bit pattern of 2^23
 
 template <int B, bool QJL>
 __device__ __forceinline__ void codes_lut(float (&y)[8][4], const uint2* __restrict__ lut,
-                                          const float* __restrict__ ctab, float s, float rs, uint32_t (&W)[B],
-                                          float& g2)
+                                          const float* __restrict__ ctab, float s, float rs_cells, float sc,
+                                          uint32_t (&W)[B], float& g2)
 {
     constexpr float magic = 8388608.0f + kLutCells;  // 2^23 + NC: rounds to an integer index
     uint32_t Gr[4];
@@ -119,15 +124,15 @@ __device__ __forceinline__ void codes_lut(float (&y)[8][4], const uint2* __restr
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const float Y = y[t][r];
-            uint32_t bits = __float_as_uint(fmaf(Y, rs, magic));
+            uint32_t bits = __float_as_uint(fmaf(Y, rs_cells, magic));
             bits = min(max(bits, kMagicBits), kMagicBits + (uint32_t)(kLutEntries - 1));
             const uint2 ent = lut[bits - kMagicBits];
             const float e = fmaf(__uint_as_float(ent.x), s, -Y);  // < 0 iff Y > next boundary
             const uint32_t code = ent.y - (uint32_t)((int32_t)__float_as_uint(e) >> 31);
             g = __builtin_amdgcn_alignbit(code, g, B);  // code t ends at bits 32 - 8B + B t
             if constexpr (QJL) {
-                const float rr = fmaf(-ctab[code & ((1u << B) - 1u)], s, Y);
-                g2 += rr * rr;
+                const float rr = fmaf(Y, sc, -ctab[code & ((1u << B) - 1u)]);
+                g2 = fmaf(rr, rr, g2);
                 y[t][r] = rr;
             }
         }
@@ -148,6 +153,16 @@ __device__ __forceinline__ void codes_lut(float (&y)[8][4], const uint2* __restr
     }
 }
 
+__device__ __forceinline__ void load_batch(uint4 (&u)[4], const uint16_t* __restrict__ x, int64_t vec, int64_t n,
+                                           int q)
+{
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        u[a] = make_uint4(0u, 0u, 0u, 0u);
+        if (vec < n) u[a] = *reinterpret_cast<const uint4*>(x + vec * kD + 32 * a + 8 * q);
+    }
+}
+
 template <int B, bool QJL>
 __global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restrict__ x, int64_t n,
                                                        const float* __restrict__ cent,
@@ -165,26 +180,29 @@ __global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restric
     constexpr bool LUT = B >= 3;
     __shared__ __align__(16) half8_t bfrag[QJL ? KS * NT * 64 : 1];
     __shared__ uint2 lut[LUT ? kLutEntries : 1];
-    __shared__ float ctab[LUT ? L : 1];
+    __shared__ float ctab[L];  // centroids (times kResUnit for keys)
     __shared__ int lut_bad;
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int v = lane & 15, q = lane >> 4;
 
-    float Mth[K > 0 ? K : 1], Cm[K + 1];
+    float Mth[K > 0 ? K : 1], Cq[K + 1];
 #pragma unroll
     for (int j = 1; j <= K; ++j) Mth[j - 1] = bnd[L / 2 - 1 + j];
 #pragma unroll
-    for (int m = 0; m <= K; ++m) Cm[m] = cent[L / 2 + m];
+    for (int m = 0; m <= K; ++m) Cq[m] = cent[L / 2 + m] * kResUnit;
 
-    // H_32 slabs as A operands: lane (row rho = v, k-block q), element e is
-    // H_32[16 tau + rho][8 q + e]
-    half8_t hA[2];
+    // H_32 slabs and their negations as A operands: lane (row rho = v,
+    // k-block q), element e is +-H_32[16 tau + rho][8 q + e]
+    half8_t hA[2][2];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            hA[tau][e] = (__builtin_popcount((16 * tau + v) & (8 * q + e)) & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
+        for (int e = 0; e < 8; ++e) {
+            const bool neg = __builtin_popcount((16 * tau + v) & (8 * q + e)) & 1;
+            hA[tau][0][e] = neg ? (_Float16)-1.0f : (_Float16)1.0f;
+            hA[tau][1][e] = neg ? (_Float16)1.0f : (_Float16)-1.0f;
+        }
 
     // diagonal sign flips of the lane's input halves: chunk a', word w holds
     // coordinates 32 a' + 8 q + 2 w (low half) and + 1 (high half)
@@ -197,9 +215,10 @@ __global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restric
             dm[a][w] = (((word >> (2 * w)) & 1u) << 15) | (((word >> (2 * w + 1)) & 1u) << 31);
     }
 
+    if (threadIdx.x == 0) lut_bad = 0;
+    if (threadIdx.x < L) ctab[threadIdx.x] = cent[threadIdx.x] * (QJL ? kResUnit : 1.0f);
+    __syncthreads();
     if constexpr (LUT) {
-        if (threadIdx.x == 0) lut_bad = 0;
-        __syncthreads();
         for (int c = threadIdx.x; c < kLutEntries; c += 256) {
             const float lo = ((float)(c - kLutCells) - 0.5f) / kLutCells;  // exact
             const float win = lo + 2.0f / kLutCells;
@@ -215,11 +234,7 @@ __global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restric
             if (inwin > 1) lut_bad = 1;
             lut[c] = make_uint2(__float_as_uint(next), base);
         }
-        if (threadIdx.x < L) ctab[threadIdx.x] = cent[threadIdx.x];
-        __syncthreads();
     }
-    const bool use_lut = LUT && !lut_bad;
-
     if constexpr (QJL) {
         // B fragments: lane (k-block kb, column c) of fragment (ks, nu), element e
         // holds S[proj_row(nu, c)][4 kb + ks + 16 e]
@@ -232,60 +247,69 @@ __global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restric
             for (int ee = 0; ee < 8; ++ee) f[ee] = __builtin_bit_cast(_Float16, row[4 * kb + ks + 16 * ee]);
             bfrag[(ks * NT + nu) * 64 + ln] = f;
         }
-        __syncthreads();
     }
+    __syncthreads();
+    const bool use_lut = LUT && !lut_bad;
 
-    const float inv_sqrt_d = 0.08838834764831845f;  // 1 / sqrt(128)
-    for (int64_t base = ((int64_t)blockIdx.x * 4 + wid) * 16; base < n; base += (int64_t)gridDim.x * 64) {
+    const float sqrt_d = 11.313708498984761f;  // sqrt(128)
+    const int64_t stride = (int64_t)gridDim.x * 64;
+    int64_t base = ((int64_t)blockIdx.x * 4 + wid) * 16;
+    uint4 cur[4];
+    load_batch(cur, x, base + v, n, q);
+    for (; base < n; base += stride) {
         const int64_t vec = base + v;
         const bool live = vec < n;
+        uint4 nxt[4];
+        load_batch(nxt, x, base + stride + v, n, q);
 
-        // ---- rotation: H_32 per chunk on MFMA, then H_4 across chunks
-        float4_t z[2][4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            uint4 u = make_uint4(0u, 0u, 0u, 0u);
-            if (live) u = *reinterpret_cast<const uint4*>(x + vec * kD + 32 * a + 8 * q);
-            const uint32_t w4[4] = {u.x ^ dm[a][0], u.y ^ dm[a][1], u.z ^ dm[a][2], u.w ^ dm[a][3]};
-            const half8_t bx = __builtin_bit_cast(half8_t, w4);
-#pragma unroll
-            for (int tau = 0; tau < 2; ++tau)
-                z[tau][a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(hA[tau], bx, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        }
-        // y[t][r]: coordinate 4 q + r + 16 t, t = 2 a + tau
-        float y[8][4];
-        float ss = 0.f;
+        // ---- rotation: H_32 per chunk on MFMA with the H_4 signs, accumulated
+        // into the output chunks; ||x||^2 from the fp16 input
+        float4_t acc[2][4];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float s01 = z[tau][0][r] + z[tau][1][r], d01 = z[tau][0][r] - z[tau][1][r];
-                const float s23 = z[tau][2][r] + z[tau][3][r], d23 = z[tau][2][r] - z[tau][3][r];
-                y[0 + tau][r] = s01 + s23;
-                y[2 + tau][r] = d01 + d23;
-                y[4 + tau][r] = s01 - s23;
-                y[6 + tau][r] = d01 - d23;
+            for (int a = 0; a < 4; ++a) acc[tau][a] = float4_t{0.f, 0.f, 0.f, 0.f};
+        float ss = 0.f;
+#pragma unroll
+        for (int ap = 0; ap < 4; ++ap) {
+            const uint32_t w4[4] = {cur[ap].x ^ dm[ap][0], cur[ap].y ^ dm[ap][1], cur[ap].z ^ dm[ap][2],
+                                    cur[ap].w ^ dm[ap][3]};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const auto h2 = __builtin_bit_cast(__attribute__((ext_vector_type(2))) _Float16, w4[w]);
+                ss = __builtin_amdgcn_fdot2(h2, h2, ss, false);
             }
+            const half8_t bx = __builtin_bit_cast(half8_t, w4);
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
+            for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ss += y[t][r] * y[t][r];
+                for (int a = 0; a < 4; ++a)
+                    acc[tau][a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        hA[tau][__builtin_popcount(a & ap) & 1], bx, acc[tau][a], 0, 0, 0);
+        }
+        // y[t][r]: coordinate 4 q + r + 16 t, t = 2 a + tau
+        float y[8][4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) y[2 * a + tau][r] = acc[tau][a][r];
         ss += __shfl_xor(ss, 16);
         ss += __shfl_xor(ss, 32);
-        const float sr = sqrtf(ss);                 // sqrt(d) ||x||
-        const float nrm = sr * inv_sqrt_d;
+        const float nrm = sqrtf(ss);
+        const float sr = nrm * sqrt_d;  // sqrt(d) ||x||
         const float s = sr > 0.f ? sr : 1.0f;
-        float Ms[K > 0 ? K : 1], Cs[K + 1];
+        const float sc = kResUnit / s;
+        float Ms[K > 0 ? K : 1];
 #pragma unroll
         for (int j = 0; j < K; ++j) Ms[j] = Mth[j] * s;
-#pragma unroll
-        for (int m = 0; m <= K; ++m) Cs[m] = Cm[m] * s;
 
-        // ---- codes (and for keys the residual)
+        // ---- codes (and for keys the scaled residual)
         uint32_t W[B];
         float g2 = 0.f;
-        if (use_lut) codes_lut<B, QJL>(y, lut, ctab, s, (float)kLutCells / s, W, g2);
-        else codes_compare<B, QJL>(y, Ms, Cs, ctab, s, W, g2);
+        if (use_lut) codes_lut<B, QJL>(y, lut, ctab, s, (float)kLutCells / s, sc, W, g2);
+        else codes_compare<B, QJL>(y, Ms, Cq, ctab, sc, W, g2);
         if (live) {
             uint32_t* dst = codes + vec * CW + B * q;
 #pragma unroll
@@ -295,14 +319,13 @@ __global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restric
         if constexpr (QJL) {
             g2 += __shfl_xor(g2, 16);
             g2 += __shfl_xor(g2, 32);
-            // residual in units of 1/(1024 s) (fp16 range), split into exact fp16 hi + lo
-            const float sc = 1024.0f / s;
+            // exact fp16 hi + lo split of the scaled residual
             half8_t ahi[KS], alo[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
-                    const float rs = y[t][ks] * sc;
+                    const float rs = y[t][ks];
                     const _Float16 hi = (_Float16)rs;
                     ahi[ks][t] = hi;
                     alo[ks][t] = (_Float16)(rs - (float)hi);
@@ -315,15 +338,15 @@ __global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restric
                 uint64_t mk[2][4];
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
-                    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+                    float4_t pa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
                         const half8_t bf = bfrag[(ks * NT + nu + hh) * 64 + lane];
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[ks], bf, acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[ks], bf, acc, 0, 0, 0);
+                        pa = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[ks], bf, pa, 0, 0, 0);
+                        pa = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[ks], bf, pa, 0, 0, 0);
                     }
 #pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) mk[hh][r4] = __ballot(acc[r4] >= 0.f);
+                    for (int r4 = 0; r4 < 4; ++r4) mk[hh][r4] = __ballot(pa[r4] >= 0.f);
                 }
                 // output row 4 g + r4 is vector 4 g + r4 of the batch; its 16 bits in
                 // each ballot are bits 16 g .. 16 g + 15
@@ -338,10 +361,12 @@ __global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restric
             }
             if (live && q == 0) {
                 *reinterpret_cast<uint4*>(signs + vec * 4) = make_uint4(SW[0], SW[1], SW[2], SW[3]);
-                rnorm[vec] = f2h(sqrtf(g2) / s);
+                rnorm[vec] = f2h(sqrtf(g2) * (1.0f / kResUnit));
             }
         }
         if (live && q == 0) norm[vec] = f2h(nrm);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) cur[a] = nxt[a];
     }
 }
 

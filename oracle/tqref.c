@@ -19,7 +19,7 @@
  *       scalar quantizer, a 1-bit QJL residual corrects inner-product bias.
  *  [P1] WHT rotation to "Gaussianize", then scalar quantization.
  *
- * Readings where the pages are silent (each one listed in the design doc):
+ * Readings where the pages are silent:
  *  - codebook law N(0, 1/d); centroids stored rounded to fp16-representable
  *    values, boundaries = fp32 midpoints of the stored centroids;
  *  - rotation y = H (D .* x) / (sqrt(d) * ||x||), H the natural-order
