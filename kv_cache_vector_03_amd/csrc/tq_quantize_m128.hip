@@ -22,10 +22,11 @@
 // current one is processed.
 //
 // Codes follow the quad kernel (sign-bit arithmetic for 1- and 2-bit codes)
-// or a lookup grid (3 and 4 bits). For keys the residual is formed directly in
-// units of 1/(1024 s) (s = sqrt(d) ||x||, keeping it in fp16 range), split
-// into exact fp16 hi + lo operands and projected on MFMA against S, with the
-// rows of S permuted so each ballot is two bytes of the sign stream. The
+// or a lookup grid (3 and 4 bits). For keys the residual is formed, negated,
+// directly in units of 1/(1024 s) (s = sqrt(d) ||x||, keeping it in fp16
+// range), split into exact fp16 hi + lo operands and projected on MFMA against
+// S, with the rows of S permuted so each ballot is two bytes of the sign
+// stream. The
 // projection's A operand is the residual with rows = vectors (lane % 16) and
 // k-block q: k-step r, element t is coordinate 4 q + r + 16 t, which this
 // lane holds.
@@ -45,8 +46,8 @@ __host__ __device__ constexpr int m128_proj_row(int nu, int c) { return 2 * nu +
 // symmetric codebook the top code bit is [Y > 0] and the lower bits are the
 // count #{M_j s < |Y|} (XOR-folded from the signs of M_j s - |Y|), complemented
 // for Y <= 0. Local stream bit 8 B r + B t + p is shifted in from the top. For
-// keys, y is replaced by the scaled residual (Y - c s) * sc and its squared
-// norm accumulates in g2 (Cq: centroid magnitudes times kResUnit).
+// keys, y is replaced by the negated scaled residual (c s - Y) * sc and its
+// squared norm accumulates in g2 (Cq: centroid magnitudes times kResUnit).
 template <int B, bool QJL, int K = (1 << B) / 2 - 1>
 __device__ __forceinline__ void codes_compare(float (&y)[8][4], const float (&Ms)[K > 0 ? K : 1],
                                               const float (&Cq)[K + 1], const float* __restrict__ ctab, float sc,
@@ -59,43 +60,51 @@ __device__ __forceinline__ void codes_compare(float (&y)[8][4], const float (&Ms
 #pragma unroll
         for (int t = 7; t >= 0; --t) {
             const float Y = y[t][r];
-            const uint32_t d2 = __float_as_uint(0.0f - Y);  // sign bit = [Y > 0]
-            uint32_t e[K > 0 ? K : 1];
+            const float d2f = 0.0f - Y;  // sign bit = [Y > 0]
+            const uint32_t d2 = __float_as_uint(d2f);
+            const int P = 8 * B * r + B * t;
+            float mag = Cq[0];
+            if constexpr (K == 0) {
+                W[P >> 5] = __builtin_amdgcn_alignbit(W[P >> 5], d2, 31);
+            } else if constexpr (K == 1) {
+                const bool outer = fabsf(Y) > Ms[0];
+                // bit 0 = [|Y| > M s] for Y > 0, its complement otherwise
+                const float b0 = outer ? d2f : -d2f;
+                W[(P + 1) >> 5] = __builtin_amdgcn_alignbit(W[(P + 1) >> 5], d2, 31);
+                W[P >> 5] = __builtin_amdgcn_alignbit(W[P >> 5], __float_as_uint(b0), 31);
+                if constexpr (QJL) mag = outer ? Cq[1] : Cq[0];
+            } else {
+                uint32_t e[K];
 #pragma unroll
-            for (int j = 0; j < K; ++j) e[j] = __float_as_uint(Ms[j] - fabsf(Y));  // [|Y| > M_j s]
+                for (int j = 0; j < K; ++j) e[j] = __float_as_uint(Ms[j] - fabsf(Y));  // [|Y| > M_j s]
 #pragma unroll
-            for (int p = B - 1; p >= 0; --p) {
-                uint32_t val;
-                if (p == B - 1) {
-                    val = d2;
-                } else {
-                    uint32_t xq = 0;
+                for (int p = B - 1; p >= 0; --p) {
+                    uint32_t val;
+                    if (p == B - 1) {
+                        val = d2;
+                    } else {
+                        uint32_t xq = 0;
 #pragma unroll
-                    for (int j = 1; j <= K; ++j)
-                        if (j % (1 << p) == 0) xq ^= e[j - 1];
-                    val = ~(xq ^ d2);
+                        for (int j = 1; j <= K; ++j)
+                            if (j % (1 << p) == 0) xq ^= e[j - 1];
+                        val = ~(xq ^ d2);
+                    }
+                    W[(P + p) >> 5] = __builtin_amdgcn_alignbit(W[(P + p) >> 5], val, 31);
                 }
-                const int P = 8 * B * r + B * t + p;
-                W[P >> 5] = __builtin_amdgcn_alignbit(W[P >> 5], val, 31);
-            }
-            if constexpr (QJL) {
-                float mag;
-                if constexpr (K <= 1) {
-                    mag = Cq[0];
-#pragma unroll
-                    for (int j = 0; j < K; ++j) mag = (int32_t)e[j] < 0 ? Cq[j + 1] : mag;
-                } else {
+                if constexpr (QJL) {
                     // magnitude level from the comparison signs, value from the table
                     uint32_t cnt = 0;
 #pragma unroll
                     for (int j = 0; j < K; ++j) cnt += e[j] >> 31;
                     mag = ctab[(1 << B) / 2 + cnt];
                 }
+            }
+            if constexpr (QJL) {
                 // c = +mag for Y > 0, -mag otherwise (y = 0 maps to the level just below 0)
-                const float c = __uint_as_float((__float_as_uint(mag) & 0x7FFFFFFFu) | (~d2 & 0x80000000u));
-                const float rs = fmaf(Y, sc, -c);
-                g2 = fmaf(rs, rs, g2);
-                y[t][r] = rs;
+                const float c = __uint_as_float(__float_as_uint(mag) ^ (~d2 & 0x80000000u));
+                const float rn = fmaf(-Y, sc, c);  // negated scaled residual
+                g2 = fmaf(rn, rn, g2);
+                y[t][r] = rn;
             }
         }
 }
@@ -131,9 +140,9 @@ __device__ __forceinline__ void codes_lut(float (&y)[8][4], const uint2* __restr
             const uint32_t code = ent.y - (uint32_t)((int32_t)__float_as_uint(e) >> 31);
             g = __builtin_amdgcn_alignbit(code, g, B);  // code t ends at bits 32 - 8B + B t
             if constexpr (QJL) {
-                const float rr = fmaf(Y, sc, -ctab[code & ((1u << B) - 1u)]);
-                g2 = fmaf(rr, rr, g2);
-                y[t][r] = rr;
+                const float rn = fmaf(-Y, sc, ctab[code & ((1u << B) - 1u)]);  // negated residual
+                g2 = fmaf(rn, rn, g2);
+                y[t][r] = rn;
             }
         }
         Gr[r] = g;  // group r in its top 8 B bits
@@ -151,6 +160,17 @@ __device__ __forceinline__ void codes_lut(float (&y)[8][4], const uint2* __restr
     } else {
         W[0] = (Gr[0] >> 24) | ((Gr[1] >> 16) & 0xFF00u) | ((Gr[2] >> 8) & 0xFF0000u) | (Gr[3] & 0xFF000000u);
     }
+}
+
+// Half H (0: low, 1: high) of two wave-uniform words packed into one:
+// half H of a in bits 0..15, half H of b in bits 16..31 (one scalar op).
+template <int H>
+__device__ __forceinline__ uint32_t pack_half(uint32_t a, uint32_t b)
+{
+    uint32_t w;
+    if constexpr (H == 0) asm("s_pack_ll_b32_b16 %0, %1, %2" : "=s"(w) : "s"(a), "s"(b));
+    else asm("s_pack_hh_b32_b16 %0, %1, %2" : "=s"(w) : "s"(a), "s"(b));
+    return w;
 }
 
 __device__ __forceinline__ void load_batch(uint4 (&u)[4], const uint16_t* __restrict__ x, int64_t vec, int64_t n,
@@ -300,7 +320,7 @@ __global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restric
         const float nrm = sqrtf(ss);
         const float sr = nrm * sqrt_d;  // sqrt(d) ||x||
         const float s = sr > 0.f ? sr : 1.0f;
-        const float sc = kResUnit / s;
+        const float sc = kResUnit * __builtin_amdgcn_rcpf(s);  // any uniform scale near 1024 / s
         float Ms[K > 0 ? K : 1];
 #pragma unroll
         for (int j = 0; j < K; ++j) Ms[j] = Mth[j] * s;
@@ -319,17 +339,25 @@ __global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restric
         if constexpr (QJL) {
             g2 += __shfl_xor(g2, 16);
             g2 += __shfl_xor(g2, 32);
-            // exact fp16 hi + lo split of the scaled residual
+            // exact fp16 hi + lo split of the scaled residual: hi rounds toward zero, lo is
+            // the fp32 remainder (hi taken straight from its fp16 half) rounded once more
             half8_t ahi[KS], alo[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks) {
+                uint32_t hw[4], lw[4];
 #pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const float rs = y[t][ks];
-                    const _Float16 hi = (_Float16)rs;
-                    ahi[ks][t] = hi;
-                    alo[ks][t] = (_Float16)(rs - (float)hi);
+                for (int j = 0; j < 4; ++j) {
+                    const float r0 = y[2 * j][ks], r1 = y[2 * j + 1][ks];
+                    hw[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+                    float l0, l1;
+                    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(l0) : "v"(hw[j]), "v"(r0));
+                    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+                        : "=v"(l1) : "v"(hw[j]), "v"(r1));
+                    lw[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(l0, l1));
                 }
+                ahi[ks] = __builtin_bit_cast(half8_t, hw);
+                alo[ks] = __builtin_bit_cast(half8_t, lw);
+            }
             uint32_t SW[4];
 #pragma unroll
             for (int w = 0; w < 4; ++w) SW[w] = 0;
@@ -346,16 +374,17 @@ __global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restric
                         pa = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[ks], bf, pa, 0, 0, 0);
                     }
 #pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) mk[hh][r4] = __ballot(pa[r4] >= 0.f);
+                    // pa = -(S r) in scaled units: sign bit [S r >= 0] = [pa <= 0]
+                    for (int r4 = 0; r4 < 4; ++r4) mk[hh][r4] = __ballot(pa[r4] <= 0.f);
                 }
                 // output row 4 g + r4 is vector 4 g + r4 of the batch; its 16 bits in
                 // each ballot are bits 16 g .. 16 g + 15
                 uint32_t sw = SW[nu >> 1];
                 static_for<0, 16>([&](auto k) {
                     constexpr int g = decltype(k)::value / 4, r4 = decltype(k)::value % 4;
-                    const uint32_t lo = (uint32_t)(mk[0][r4] >> (16 * g)) & 0xFFFFu;
-                    const uint32_t hi = (uint32_t)(mk[1][r4] >> (16 * g)) & 0xFFFFu;
-                    sw = write_lane<4 * g + r4>(sw, lo | (hi << 16));
+                    const uint32_t a = (uint32_t)(mk[0][r4] >> (32 * (g / 2)));
+                    const uint32_t b = (uint32_t)(mk[1][r4] >> (32 * (g / 2)));
+                    sw = write_lane<4 * g + r4>(sw, pack_half<g % 2>(a, b));
                 });
                 SW[nu >> 1] = sw;
             }
