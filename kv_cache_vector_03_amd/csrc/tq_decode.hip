@@ -445,19 +445,6 @@ void launch_bv(int bv, const tq_packed* k, const tq_packed* v, int64_t ns, int64
 
 }  // namespace
 
-int device_cus()
-{
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cached[dev]) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
 int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
                        const tq_packed* v, int64_t n_streams, int64_t T, int G, const void* q,
                        int q_dtype, float zscale, void* frags, float* parts, int n_chunks, int tc,

@@ -138,20 +138,15 @@ int device_cus();
 // Grid for a grid-stride kernel of 256-thread blocks: enough blocks to cover
 // n units (units_per_block each), but no more than fit on the device at once,
 // so every block is resident and the work divides evenly.
+int resident_blocks(const void* kern);
+
 template <typename Kern>
 int resident_grid(Kern kern, int64_t units_per_block, int64_t n)
 {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (!cached[dev]) {
-        int nb = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 256, 0) != hipSuccess || nb < 1) nb = 1;
-        cached[dev] = nb * device_cus();
-    }
+    const int cap = resident_blocks(reinterpret_cast<const void*>(kern));
     int64_t want = (n + units_per_block - 1) / units_per_block;
     if (want < 1) want = 1;
-    return (int)(want < cached[dev] ? want : cached[dev]);
+    return (int)(want < cap ? want : cap);
 }
 
 }  // namespace tq

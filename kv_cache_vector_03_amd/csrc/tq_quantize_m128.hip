@@ -48,15 +48,16 @@ __host__ __device__ constexpr int m128_proj_row(int nu, int c) { return 2 * nu +
 // for Y <= 0. Local stream bit 8 B r + B t + p is shifted in from the top. For
 // keys, y is replaced by the negated scaled residual (c s - Y) * sc and its
 // squared norm accumulates in g2 (Cq: centroid magnitudes times kResUnit).
-template <int B, bool QJL, int K = (1 << B) / 2 - 1>
+template <int B, bool QJL, int K = (1 << B) / 2 - 1, typename Pre, typename Post>
 __device__ __forceinline__ void codes_compare(float (&y)[8][4], const float (&Ms)[K > 0 ? K : 1],
                                               const float (&Cq)[K + 1], const float* __restrict__ ctab, float sc,
-                                              uint32_t (&W)[B], float& g2)
+                                              uint32_t (&W)[B], float& g2, Pre&& pre, Post&& post)
 {
 #pragma unroll
     for (int w = 0; w < B; ++w) W[w] = 0;
 #pragma unroll
-    for (int r = 3; r >= 0; --r)
+    for (int r = 3; r >= 0; --r) {
+        pre(r);
 #pragma unroll
         for (int t = 7; t >= 0; --t) {
             const float Y = y[t][r];
@@ -107,6 +108,8 @@ __device__ __forceinline__ void codes_compare(float (&y)[8][4], const float (&Ms
                 y[t][r] = rn;
             }
         }
+        post(r);
+    }
 }
 
 // Code lookup grid. Cell c of the table covers the rotated unit coordinate
@@ -120,15 +123,16 @@ constexpr int kLutCells = 256;
 constexpr int kLutEntries = 2 * kLutCells + 2;
 constexpr uint32_t kMagicBits = 0x4B000000u;  // bit pattern of 2^23
 
-template <int B, bool QJL>
+template <int B, bool QJL, typename Pre, typename Post>
 __device__ __forceinline__ void codes_lut(float (&y)[8][4], const uint2* __restrict__ lut,
                                           const float* __restrict__ ctab, float s, float rs_cells, float sc,
-                                          uint32_t (&W)[B], float& g2)
+                                          uint32_t (&W)[B], float& g2, Pre&& pre, Post&& post)
 {
     constexpr float magic = 8388608.0f + kLutCells;  // 2^23 + NC: rounds to an integer index
     uint32_t Gr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
+        pre(r);
         uint32_t g = 0;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -146,6 +150,7 @@ __device__ __forceinline__ void codes_lut(float (&y)[8][4], const uint2* __restr
             }
         }
         Gr[r] = g;  // group r in its top 8 B bits
+        post(r);
     }
     if constexpr (B == 4) {
 #pragma unroll
@@ -171,6 +176,29 @@ __device__ __forceinline__ uint32_t pack_half(uint32_t a, uint32_t b)
     if constexpr (H == 0) asm("s_pack_ll_b32_b16 %0, %1, %2" : "=s"(w) : "s"(a), "s"(b));
     else asm("s_pack_hh_b32_b16 %0, %1, %2" : "=s"(w) : "s"(a), "s"(b));
     return w;
+}
+
+// Sign word of n-tiles (2p, 2p+1) for the 16 vectors of a batch, from the
+// projection accumulators t0, t1 (values -(S r) in scaled units, so the sign
+// bit [S r >= 0] is [t <= 0]). Output row 4 g + r4 is vector 4 g + r4; its 16
+// bits in each ballot are bits 16 g .. 16 g + 15. Lane v < 16 receives the
+// word of vector v.
+__device__ __forceinline__ uint32_t sign_word(const float4_t& t0, const float4_t& t1)
+{
+    uint64_t m0[4], m1[4];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+        m0[r4] = __ballot(t0[r4] <= 0.f);
+        m1[r4] = __ballot(t1[r4] <= 0.f);
+    }
+    uint32_t sw = 0;
+    static_for<0, 16>([&](auto k) {
+        constexpr int g = decltype(k)::value / 4, r4 = decltype(k)::value % 4;
+        const uint32_t a = (uint32_t)(m0[r4] >> (32 * (g / 2)));
+        const uint32_t b = (uint32_t)(m1[r4] >> (32 * (g / 2)));
+        sw = write_lane<4 * g + r4>(sw, pack_half<g % 2>(a, b));
+    });
+    return sw;
 }
 
 __device__ __forceinline__ void load_batch(uint4 (&u)[4], const uint16_t* __restrict__ x, int64_t vec, int64_t n,
@@ -272,16 +300,12 @@ __global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restric
     const bool use_lut = LUT && !lut_bad;
 
     const float sqrt_d = 11.313708498984761f;  // sqrt(128)
-    const int64_t stride = (int64_t)gridDim.x * 64;
-    int64_t base = ((int64_t)blockIdx.x * 4 + wid) * 16;
-    uint4 cur[4];
-    load_batch(cur, x, base + v, n, q);
-    for (; base < n; base += stride) {
-        const int64_t vec = base + v;
-        const bool live = vec < n;
-        uint4 nxt[4];
-        load_batch(nxt, x, base + stride + v, n, q);
+    auto none = [](int) {};
 
+    // One 16-vector batch: rotation, norm and codes (stored), and for keys the
+    // residual norm (stored) and the scaled residual split into exact fp16
+    // hi + lo projection operands (k-step r = group r of the lane).
+    auto batch = [&](const uint4(&xin)[4], int64_t vec, bool live, half8_t(&ahi)[KS], half8_t(&alo)[KS]) {
         // ---- rotation: H_32 per chunk on MFMA with the H_4 signs, accumulated
         // into the output chunks; ||x||^2 from the fp16 input
         float4_t acc[2][4];
@@ -292,8 +316,8 @@ __global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restric
         float ss = 0.f;
 #pragma unroll
         for (int ap = 0; ap < 4; ++ap) {
-            const uint32_t w4[4] = {cur[ap].x ^ dm[ap][0], cur[ap].y ^ dm[ap][1], cur[ap].z ^ dm[ap][2],
-                                    cur[ap].w ^ dm[ap][3]};
+            const uint32_t w4[4] = {xin[ap].x ^ dm[ap][0], xin[ap].y ^ dm[ap][1], xin[ap].z ^ dm[ap][2],
+                                    xin[ap].w ^ dm[ap][3]};
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const auto h2 = __builtin_bit_cast(__attribute__((ext_vector_type(2))) _Float16, w4[w]);
@@ -325,29 +349,28 @@ __global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restric
 #pragma unroll
         for (int j = 0; j < K; ++j) Ms[j] = Mth[j] * s;
 
-        // ---- codes (and for keys the scaled residual)
+        // ---- codes (and for keys the negated scaled residual)
         uint32_t W[B];
         float g2 = 0.f;
-        if (use_lut) codes_lut<B, QJL>(y, lut, ctab, s, (float)kLutCells / s, sc, W, g2);
-        else codes_compare<B, QJL>(y, Ms, Cq, ctab, sc, W, g2);
+        if (use_lut) codes_lut<B, QJL>(y, lut, ctab, s, (float)kLutCells / s, sc, W, g2, none, none);
+        else codes_compare<B, QJL>(y, Ms, Cq, ctab, sc, W, g2, none, none);
         if (live) {
             uint32_t* dst = codes + vec * CW + B * q;
 #pragma unroll
             for (int w = 0; w < B; ++w) dst[w] = W[w];
         }
-
         if constexpr (QJL) {
             g2 += __shfl_xor(g2, 16);
             g2 += __shfl_xor(g2, 32);
-            // exact fp16 hi + lo split of the scaled residual: hi rounds toward zero, lo is
-            // the fp32 remainder (hi taken straight from its fp16 half) rounded once more
-            half8_t ahi[KS], alo[KS];
+            if (live && q == 0) rnorm[vec] = f2h(sqrtf(g2) * (1.0f / kResUnit));
+            // hi rounds toward zero; lo is the fp32 remainder (hi taken straight from
+            // its fp16 half) rounded once more
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
+            for (int r = 0; r < KS; ++r) {
                 uint32_t hw[4], lw[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float r0 = y[2 * j][ks], r1 = y[2 * j + 1][ks];
+                    const float r0 = y[2 * j][r], r1 = y[2 * j + 1][r];
                     hw[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
                     float l0, l1;
                     asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(l0) : "v"(hw[j]), "v"(r0));
@@ -355,47 +378,65 @@ __global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restric
                         : "=v"(l1) : "v"(hw[j]), "v"(r1));
                     lw[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(l0, l1));
                 }
-                ahi[ks] = __builtin_bit_cast(half8_t, hw);
-                alo[ks] = __builtin_bit_cast(half8_t, lw);
-            }
-            uint32_t SW[4];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) SW[w] = 0;
-#pragma unroll
-            for (int nu = 0; nu < NT; nu += 2) {
-                uint64_t mk[2][4];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    float4_t pa = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        const half8_t bf = bfrag[(ks * NT + nu + hh) * 64 + lane];
-                        pa = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[ks], bf, pa, 0, 0, 0);
-                        pa = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[ks], bf, pa, 0, 0, 0);
-                    }
-#pragma unroll
-                    // pa = -(S r) in scaled units: sign bit [S r >= 0] = [pa <= 0]
-                    for (int r4 = 0; r4 < 4; ++r4) mk[hh][r4] = __ballot(pa[r4] <= 0.f);
-                }
-                // output row 4 g + r4 is vector 4 g + r4 of the batch; its 16 bits in
-                // each ballot are bits 16 g .. 16 g + 15
-                uint32_t sw = SW[nu >> 1];
-                static_for<0, 16>([&](auto k) {
-                    constexpr int g = decltype(k)::value / 4, r4 = decltype(k)::value % 4;
-                    const uint32_t a = (uint32_t)(mk[0][r4] >> (32 * (g / 2)));
-                    const uint32_t b = (uint32_t)(mk[1][r4] >> (32 * (g / 2)));
-                    sw = write_lane<4 * g + r4>(sw, pack_half<g % 2>(a, b));
-                });
-                SW[nu >> 1] = sw;
-            }
-            if (live && q == 0) {
-                *reinterpret_cast<uint4*>(signs + vec * 4) = make_uint4(SW[0], SW[1], SW[2], SW[3]);
-                rnorm[vec] = f2h(sqrtf(g2) * (1.0f / kResUnit));
+                ahi[r] = __builtin_bit_cast(half8_t, hw);
+                alo[r] = __builtin_bit_cast(half8_t, lw);
             }
         }
         if (live && q == 0) norm[vec] = f2h(nrm);
+    };
+
+    const int64_t step = (int64_t)gridDim.x * 64;  // vectors between a wave's batches
+    int64_t base = ((int64_t)blockIdx.x * 4 + wid) * 16;
+    uint4 cur[4];
+    load_batch(cur, x, base + v, n, q);
+    if constexpr (!QJL) {
+        half8_t nh[KS], nl[KS];  // unused for values
+        for (; base < n; base += step) {
+            uint4 nxt[4];
+            load_batch(nxt, x, base + step + v, n, q);
+            batch(cur, base + v, base + v < n, nh, nl);
 #pragma unroll
-        for (int a = 0; a < 4; ++a) cur[a] = nxt[a];
+            for (int a = 0; a < 4; ++a) cur[a] = nxt[a];
+        }
+    } else {
+        // keys: two batches per iteration, then one projection pass in which each
+        // S fragment read from LDS feeds four MFMAs (both batches, hi and lo)
+        for (; base < n; base += 2 * step) {
+            const int64_t baseB = base + step;
+            uint4 nxt[4];
+            load_batch(nxt, x, baseB + v, n, q);
+            half8_t ahiA[KS], aloA[KS], ahiB[KS], aloB[KS];
+            batch(cur, base + v, base + v < n, ahiA, aloA);
+            load_batch(cur, x, base + 2 * step + v, n, q);
+            batch(nxt, baseB + v, baseB + v < n, ahiB, aloB);
+
+            uint32_t SWA[4], SWB[4];
+#pragma unroll
+            for (int p = 0; p < NT / 2; ++p) {
+                float4_t pA0 = {0.f, 0.f, 0.f, 0.f}, pA1 = pA0, pB0 = pA0, pB1 = pA0;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const half8_t b0 = bfrag[(ks * NT + 2 * p) * 64 + lane];
+                    const half8_t b1 = bfrag[(ks * NT + 2 * p + 1) * 64 + lane];
+                    pA0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahiA[ks], b0, pA0, 0, 0, 0);
+                    pA1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahiA[ks], b1, pA1, 0, 0, 0);
+                    pB0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahiB[ks], b0, pB0, 0, 0, 0);
+                    pB1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahiB[ks], b1, pB1, 0, 0, 0);
+                    pA0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aloA[ks], b0, pA0, 0, 0, 0);
+                    pA1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aloA[ks], b1, pA1, 0, 0, 0);
+                    pB0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aloB[ks], b0, pB0, 0, 0, 0);
+                    pB1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aloB[ks], b1, pB1, 0, 0, 0);
+                }
+                SWA[p] = sign_word(pA0, pA1);
+                SWB[p] = sign_word(pB0, pB1);
+            }
+            if (q == 0) {
+                if (base + v < n)
+                    *reinterpret_cast<uint4*>(signs + (base + v) * 4) = make_uint4(SWA[0], SWA[1], SWA[2], SWA[3]);
+                if (baseB + v < n)
+                    *reinterpret_cast<uint4*>(signs + (baseB + v) * 4) = make_uint4(SWB[0], SWB[1], SWB[2], SWB[3]);
+            }
+        }
     }
 }
 
