@@ -1,6 +1,4 @@
 // Launch geometry helpers: compute-unit count and resident blocks per kernel.
-#include <stdio.h>
-#include <stdlib.h>
 #include <mutex>
 #include <unordered_map>
 
@@ -36,10 +34,6 @@ int resident_blocks(const void* kern)
     if (it != cache[dev].end()) return it->second;
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 256, 0) != hipSuccess || nb < 1) nb = 1;
-    hipFuncAttributes fa{};
-    hipFuncGetAttributes(&fa, kern);
-    fprintf(stderr, "OCC api=%d regs=%d lds=%zu\n", nb, fa.numRegs, fa.sharedSizeBytes);
-    if (getenv("TQ_OCC")) nb = atoi(getenv("TQ_OCC"));
     const int blocks = nb * device_cus();
     cache[dev][kern] = blocks;
     return blocks;
