@@ -36,8 +36,8 @@ METRIC = "packed-KV GB/s & % HBM peak (quantize, score, decode-attn); keys/s"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", choices=["128k", "8k"], default="128k")
     ap.add_argument("--replicas", type=int, default=5, help="8k workload: cache replicas")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -35,13 +35,14 @@ __device__ __forceinline__ float xor8(float x)
 }
 
 // Query preparation, grid (stream, k-step t < d/32). Every block rotates the
-// stream's G <= 8 queries in double (q' = H D q / sqrt(d)); block t then
-// projects them onto the d/4 rows of S with index = t (mod d/32), one dot
-// product per thread (p = S q'), and writes two score-GEMM B fragments: code
-// k-step t and sign k-step d/32 + t. Column c < 8 carries the fp16 rounding of
-// head c's value, column c + 8 the fp16 rounding of the remainder. Lane
-// (g, col) element e of k-step t maps to coordinate (or projection row)
-// (4 g + t) + (d/8) e, the group-major order the key codes arrive in.
+// stream's G <= 8 queries (q' = H D q / sqrt(d)); block t then projects them
+// onto the d/4 rows of S with index = t (mod d/32), one dot product per thread
+// (p = S q'), and writes two score-GEMM B fragments: code k-step t and sign
+// k-step d/32 + t. Column c < 8 carries the fp16 rounding of head c's value,
+// column c + 8 the fp16 rounding of the remainder. Lane (g, col) element e of
+// k-step t maps to coordinate (or projection row) (4 g + t) + (d/8) e, the
+// group-major order the key codes arrive in. Arithmetic is fp32: its relative
+// error (~1e-7) is far below what the hi/lo operands carry into the scores.
 template <int D, bool QJL, bool F16>
 __global__ __launch_bounds__(256) void k_qprep_frag(const void* __restrict__ q, int G,
                                                     const uint32_t* __restrict__ diag,
@@ -50,8 +51,8 @@ __global__ __launch_bounds__(256) void k_qprep_frag(const void* __restrict__ q, 
 {
     static_assert(D == 128, "fragment layout is laid out for d = 128");
     constexpr int R = D / 64, KS = D / 32, KSTEPS = KS * (QJL ? 2 : 1);
-    __shared__ double qs[8][D];
-    __shared__ double ps[QJL ? 8 : 1][32];
+    __shared__ float qs[8][D];
+    __shared__ float ps[QJL ? 8 : 1][32];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t s = blockIdx.x;
     const int tt = blockIdx.y;
@@ -66,26 +67,28 @@ __global__ __launch_bounds__(256) void k_qprep_frag(const void* __restrict__ q, 
     }
     uint32_t dm[R];
     load_diag<R>(diag, lane, dm);
-    const double inv_sqrt_d = 1.0 / sqrt((double)D);
+    const float inv_sqrt_d = 0.08838834764831845f;  // 1 / sqrt(128)
     for (int h = wid; h < 8; h += 4) {
-        double y[R];
+        float y[R];
 #pragma unroll
         for (int r = 0; r < R; ++r)
-            y[r] = h < G ? (double)flip(load_elem<F16>(q, (s * G + h) * D + 64 * r + lane), dm[r]) : 0.0;
+            y[r] = h < G ? flip(load_elem<F16>(q, (s * G + h) * D + 64 * r + lane), dm[r]) : 0.f;
         fwht_wave<R>(y, lane);
 #pragma unroll
         for (int r = 0; r < R; ++r) qs[h][64 * r + lane] = y[r] * inv_sqrt_d;
     }
     __syncthreads();
     if constexpr (QJL) {
-        // four partial sums shorten the dependent chain of double FMAs
-        double acc[4] = {0.0, 0.0, 0.0, 0.0};
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < D / 8; ++c) {
             const uint32_t w4[4] = {srow[c].x, srow[c].y, srow[c].z, srow[c].w};
+            const float4 qa = *reinterpret_cast<const float4*>(&qs[ph][8 * c]);
+            const float4 qb = *reinterpret_cast<const float4*>(&qs[ph][8 * c + 4]);
+            const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
 #pragma unroll
             for (int k = 0; k < 8; ++k)
-                acc[k & 3] += (double)h2f((uint16_t)(w4[k >> 1] >> (16 * (k & 1)))) * qs[ph][8 * c + k];
+                acc[k & 3] = fmaf(h2f((uint16_t)(w4[k >> 1] >> (16 * (k & 1)))), qv[k], acc[k & 3]);
         }
         ps[ph][pi] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
         __syncthreads();
@@ -99,10 +102,10 @@ __global__ __launch_bounds__(256) void k_qprep_frag(const void* __restrict__ q, 
 #pragma unroll
         for (int ee = 0; ee < 8; ++ee) {
             // coordinate (row) 4 g + tt + (d/8) ee; as a row of this block: i = g + 4 ee
-            double val = 0.0;
+            float val = 0.f;
             if (head < G) val = sgn ? ps[QJL ? head : 0][(g + 4 * ee) & 31] : qs[head][KS * g + tt + (D / 8) * ee];
             const _Float16 hi = (_Float16)val;
-            f[ee] = lo ? (_Float16)(val - (double)hi) : hi;
+            f[ee] = lo ? (_Float16)(val - (float)hi) : hi;
         }
         frags[(s * KSTEPS + (sgn ? KS + tt : tt)) * 64 + l] = f;
     }
@@ -117,6 +120,10 @@ struct Step {
     uint16_t nk, ng, nv;  // token (tb + lane) norms, lanes < 32
 };
 
+// Loads of one step. Token indices are clamped to the last token of the
+// wave's range (w1 - 1 >= tb), so every load is unconditional and in bounds;
+// tokens past the range get a score of -inf and a weight of 0 later, so the
+// values read for them never reach the result.
 template <int D, int BK, bool QJL, int BV>
 __device__ __forceinline__ void load_step(Step<BK, BV>& st, int64_t tb, int64_t w1, int64_t base, int lane,
                                           const uint32_t* __restrict__ kcodes,
@@ -128,29 +135,28 @@ __device__ __forceinline__ void load_step(Step<BK, BV>& st, int64_t tb, int64_t 
 {
     constexpr int KW = BK * D / 32, VW = BV * D / 32, SWN = D / 32;
     const int col = lane & 15, g = lane >> 4;
+    const int64_t last = w1 - 1;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int64_t tA = tb + 16 * u + col;
-        const bool vA = tA < w1;
+        const int64_t tA = base + min(tb + 16 * u + col, last);
 #pragma unroll
-        for (int w = 0; w < BK; ++w) st.kf[u][w] = vA ? kcodes[(base + tA) * KW + BK * g + w] : 0u;
-        st.sf[u] = (QJL && vA) ? ksigns[(base + tA) * SWN + g] : 0u;
+        for (int w = 0; w < BK; ++w) st.kf[u][w] = kcodes[tA * KW + BK * g + w];
+        st.sf[u] = QJL ? ksigns[tA * SWN + g] : 0u;
     }
+    const int w = (8 * BV * col) >> 5;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const int64_t t = tb + 16 * (e >> 2) + 4 * g + (e & 3);
-        const bool ok = t < w1;
-        const uint32_t* rec = vcodes + (base + t) * VW;
-        const int w = (8 * BV * col) >> 5;
-        st.x0[e] = ok ? rec[w] : 0u;
-        if constexpr (BV == 3) st.x1[e] = (ok && w + 1 < VW) ? rec[w + 1] : 0u;
+        const int64_t t = base + min(tb + 16 * (e >> 2) + 4 * g + (e & 3), last);
+        const uint32_t* rec = vcodes + t * VW;
+        st.x0[e] = rec[w];
+        // 3-bit fields may straddle two words; the last field of a token does not
+        if constexpr (BV == 3) st.x1[e] = rec[w + 1 < VW ? w + 1 : w];
         else st.x1[e] = 0u;
     }
-    const int64_t t = tb + (lane & 31);
-    const bool ok = t < w1;
-    st.nk = ok ? knorm[base + t] : (uint16_t)0;
-    st.ng = (ok && QJL) ? krnorm[base + t] : (uint16_t)0;
-    st.nv = ok ? vnorm[base + t] : (uint16_t)0;
+    const int64_t t = base + min(tb + (lane & 31), last);
+    st.nk = knorm[t];
+    st.ng = QJL ? krnorm[t] : (uint16_t)0;
+    st.nv = vnorm[t];
 }
 
 template <int D, int BK, bool QJL, int BV>
@@ -222,9 +228,17 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
 #pragma unroll
         for (int k = 0; k < KSTEPS; ++k) bq[k] = frags[(s * KSTEPS + k) * 64 + lane];
 
-        // fixed weight scale for this wave: max weight * norm stays below 2^15 in fp16
+        // fixed weight scale for this wave: max weight * norm stays below 2^15 in fp16.
+        // The norms of the wave's range are read 512 at a time with all loads in
+        // flight together (indices clamped into the range, as for the steps).
         float nmax = 0.f;
-        for (int64_t t = w0 + lane; t < w1; t += 64) nmax = fmaxf(nmax, h2f(vnorm[base + t]));
+        for (int64_t t0 = w0; t0 < w1; t0 += 512) {
+            uint16_t hv[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) hv[k] = vnorm[base + min(t0 + lane + 64 * k, w1 - 1)];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) nmax = fmaxf(nmax, h2f(hv[k]));
+        }
         nmax = wave_max(nmax);
         int ex = 0;
         (void)frexpf(nmax, &ex);
