@@ -219,6 +219,8 @@ def main():
         "setup_s": round(t_gen, 2),
     }
 
+    result["small_keyset"] = small_keyset(tq, qk, dev)
+
     if not args.no_cpu_baseline:
         nb = args.cpu_batches or (5 if args.workload == "128k" else 8)
         result["cpu_baseline"] = cpu_baseline(cfg, diag_k, S, diag_v, kb, vb, units, nb)
@@ -257,6 +259,37 @@ def cpu_baseline(cfg, diag_k, S, diag_v, kb, vb, units, n_batches):
             "kind": "oracle",
             "sample": f"{n_batches} batches of the step ({toks} tokens in all): quantize K and V, decode "
                       f"with {G} query heads per stream; {dt:.1f} s of oracle time"}
+
+
+def small_keyset(tq, qk, dev, reps=50):
+    """The score path on the pages' small benchmark shape (GB10 section of the
+    GX10 page): quantize 8192 fp16 keys (prod 2+1, d = 128, four outlier
+    channels), then score 64 queries against all of them. Both are single
+    launches of a few MB, so they are latency-bound; reported in microseconds
+    beside the page's PyTorch timings (31.04 ms and 11.16 ms on a GB10)."""
+    import torch
+    from synth import workloads as W
+    keys, qs = W.config2_host()
+    x = torch.from_numpy(keys).to(dev)
+    q = torch.from_numpy(qs).to(dev)
+    pk = tq.Packed.empty(qk, x.shape[0], dev)
+    scores = torch.empty((q.shape[0], x.shape[0]), dtype=torch.float32, device=dev)
+    ws = tq.workspace(tq.tq_workspace_size(tq.TQ_OP_SCORES, qk, q.shape[0], x.shape[0]), dev)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, fn in (("quantize_8192_keys", lambda: tq.tq_quantize(qk, x, pk)),
+                     ("scores_64x8192", lambda: tq.tq_scores(qk, pk, x.shape[0], q, scores, ws=ws))):
+        for _ in range(5):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        out[name + "_us"] = round(a.elapsed_time(b) / reps * 1e3, 2)
+    out["page_gb10_ms"] = {"quantize_8192_keys": 31.04, "scores_64x8192": 11.16}
+    return out
 
 
 def calibrate_copy():

@@ -49,7 +49,8 @@ __global__ __launch_bounds__(256) void k_scores(const uint32_t* __restrict__ cod
         nk = (double)h2f(norm[key]);
         if (QJL) gk = (double)h2f(rnorm[key]) * (1.2533141373155003 / D);
     }
-    for (int64_t q0 = 0; q0 < n_q; q0 += kQT) {
+    // query tiles are spread over grid.y so that small key sets still fill the device
+    for (int64_t q0 = (int64_t)blockIdx.y * kQT; q0 < n_q; q0 += (int64_t)gridDim.y * kQT) {
         __syncthreads();
         for (int e = threadIdx.x; e < kQT * D; e += 256) {
             const int qi = e / D, i = e % D;
@@ -293,7 +294,8 @@ template <int D, int B, bool QJL>
 void scores_d_b(const tq_quantizer* q, const tq_packed* k, int64_t n_keys, const float* qr,
                 const float* p, int64_t n_q, float* scores, hipStream_t s)
 {
-    dim3 grid((unsigned)((n_keys + 255) / 256)), block(256);
+    const int64_t qt = (n_q + kQT - 1) / kQT;
+    dim3 grid((unsigned)((n_keys + 255) / 256), (unsigned)(qt < 65535 ? qt : 65535)), block(256);
     hipLaunchKernelGGL((k_scores<D, B, QJL>), grid, block, 0, s, k->codes, k->signs, k->norm,
                        k->rnorm, n_keys, qr, p, n_q, q->centroids, scores);
 }

@@ -34,6 +34,13 @@ __device__ __forceinline__ float xor8(float x)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
 }
 
+// Value of lane (lane & ~3) + R within each quad of lanes (DPP quad_perm).
+template <int R>
+__device__ __forceinline__ float quad_bcast(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), R * 0x55, 0xF, 0xF, false));
+}
+
 // Query preparation, grid (stream, k-step t < d/32). Every block rotates the
 // stream's G <= 8 queries (q' = H D q / sqrt(d)); block t then projects them
 // onto the d/4 rows of S with index = t (mod d/32), one dot product per thread
@@ -117,7 +124,7 @@ struct Step {
     uint32_t kf[2][BK];   // key code words of this lane's 4 groups, tiles 0 and 1
     uint32_t sf[2];       // key sign bytes of this lane's 4 groups
     uint32_t x0[8], x1[8];// value field words (x1: second word, 3-bit codes only)
-    uint16_t nk, ng, nv;  // token (tb + lane) norms, lanes < 32
+    uint16_t nk[2], ng[2], nv[2];  // norms of token tb + 16 u + 4 g + (col & 3), u = 0, 1
 };
 
 // Loads of one step. Token indices are clamped to the last token of the
@@ -153,10 +160,13 @@ __device__ __forceinline__ void load_step(Step<BK, BV>& st, int64_t tb, int64_t 
         if constexpr (BV == 3) st.x1[e] = rec[w + 1 < VW ? w + 1 : w];
         else st.x1[e] = 0u;
     }
-    const int64_t t = base + min(tb + (lane & 31), last);
-    st.nk = knorm[t];
-    st.ng = QJL ? krnorm[t] : (uint16_t)0;
-    st.nv = vnorm[t];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t t = base + min(tb + 16 * u + 4 * g + (col & 3), last);
+        st.nk[u] = knorm[t];
+        st.ng[u] = QJL ? krnorm[t] : (uint16_t)0;
+        st.nv[u] = vnorm[t];
+    }
 }
 
 template <int D, int BK, bool QJL, int BV>
@@ -185,7 +195,6 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
     __shared__ uint32_t klut2[K4 ? 1 : KLUT];
     __shared__ uint4 slut[QJL ? 256 : 1];
     __shared__ uint32_t vlut[VLUT];
-    __shared__ float tokv[4][3][32];
     __shared__ float mrg_m[4][8], mrg_l[4][8];
     __shared__ float mrg_o[4][8][D];
 
@@ -255,14 +264,14 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
         for (int64_t tb = w0; tb < w1; tb += 32) {
             if (tb + 32 < w1)
                 load_step<D, BK, QJL, BV>(nxt, tb + 32, w1, base, lane, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
-            if (lane < 32) {
-                tokv[wid][0][lane] = h2f(cur.nk) * zscale;
-                tokv[wid][1][lane] = h2f(cur.ng) * kappa;
-                tokv[wid][2][lane] = h2f(cur.nv) * wscale;
+            // per-token factors of this lane's quad: row 16 u + 4 g + r sits in quad lane r
+            float fk[2], fq[2], fv[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                fk[u] = h2f(cur.nk[u]) * zscale;
+                fq[u] = fk[u] * (h2f(cur.ng[u]) * kappa);
+                fv[u] = h2f(cur.nv[u]) * wscale;
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
             // ---- scores for two 16-token tiles
             float zz[8];
@@ -301,14 +310,14 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                                                                     0, 0, 0);
                     }
                 }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
+                static_for<0, 4>([&](auto rr) {
+                    constexpr int r = decltype(rr)::value;
                     const int row = 16 * u + 4 * g + r;
                     const float zm = am[r] + xor8(am[r]);
-                    const float zq = QJL ? aq[r] + xor8(aq[r]) : 0.f;
-                    const float z = tokv[wid][0][row] * (zm + tokv[wid][1][row] * zq);
+                    float z = quad_bcast<r>(fk[u]) * zm;
+                    if constexpr (QJL) z = fmaf(quad_bcast<r>(fq[u]), aq[r] + xor8(aq[r]), z);
                     zz[4 * u + r] = (tb + row < w1) ? z : -INFINITY;
-                }
+                });
             }
 
             // ---- block max per head column; rescale only when it beats the running max by 2^8
@@ -332,14 +341,14 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
 
             // ---- weights as the A operand (row = head column, K slot = token)
             half8_t aw;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            static_for<0, 8>([&](auto ee) {
+                constexpr int e = decltype(ee)::value;
                 const float w = exp2f(zz[e] - M);
                 lsum += w;
-                const float W = w * tokv[wid][2][16 * (e >> 2) + 4 * g + (e & 3)];
+                const float W = w * quad_bcast<e & 3>(fv[e >> 2]);
                 const _Float16 hi = (_Float16)W;
                 aw[e] = col < 8 ? hi : (_Float16)(W - (float)hi);
-            }
+            });
 
             // ---- value codes: lane column = code group, slot e = token 4g+e (tile 0) / 16+4g+e-4 (tile 1)
             uint32_t X[8];
