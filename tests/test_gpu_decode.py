@@ -62,6 +62,10 @@ SMALL = [
     (64, 2, 3, 3, 600, 8, True),
     (256, 2, 4, 2, 300, 5, True),
     (256, 1, 1, 1, 260, 2, True),
+    # more (stream, chunk) items than resident blocks: blocks loop over items
+    (128, 2, 4, 600, 130, 8, True),
+    # one long stream split into many chunks
+    (128, 2, 3, 1, 70000, 8, True),
 ]
 
 
@@ -93,6 +97,30 @@ def test_decode_small(d, kb, vb, ns, T, G, k_qjl):
     check_close(out3, oracle.decode_attn(qko, qvo, opacked(qko, pk.to_host()), opacked(qvo, pv.to_host()),
                                          ns, T, G, Q.astype(np.float64), scale=0.03))
     assert np.array_equal(out, run_decode(qkg, qvg, pk, pv, ns, T, G, qd))
+
+
+def test_decode_zero_and_large_norm_tokens():
+    """Zero vectors (n = 0) and tokens with norms near 10^4 in the same
+    stream: the weight scaling must keep every product in fp16 range."""
+    tq = tqmod()
+    d, ns, T, G = 128, 2, 700, 8
+    qkg, qvg, qko, qvo = make(d, 2, 4)
+    K = synth.normals(41, synth.ROLE_DATA_K, np.arange(ns * T * d)).reshape(ns * T, d)
+    V = synth.normals(41, synth.ROLE_DATA_V, np.arange(ns * T * d)).reshape(ns * T, d)
+    K[::7] = 0.0
+    V[::11] = 0.0
+    V[5::13] *= 900.0   # ||v|| ~ 1e4
+    K[3::17] *= 3.0
+    K, V = synth.to_f16(K), synth.to_f16(V)
+    Q = synth.to_f16(synth.normals(41, synth.ROLE_QUERY, np.arange(ns * G * d)).reshape(ns, G, d) * 0.5)
+    pk, pv = tq.Packed.empty(qkg, ns * T, DEV), tq.Packed.empty(qvg, ns * T, DEV)
+    tq.tq_quantize(qkg, torch.from_numpy(K).to(DEV), pk)
+    tq.tq_quantize(qvg, torch.from_numpy(V).to(DEV), pv)
+    out = run_decode(qkg, qvg, pk, pv, ns, T, G, torch.from_numpy(Q).to(DEV))
+    ref = oracle.decode_attn(qko, qvo, opacked(qko, pk.to_host()), opacked(qvo, pv.to_host()), ns, T, G,
+                             Q.astype(np.float64))
+    # outputs reach ~10^3 here; the bound is relative to the output scale
+    check_close(out, ref, tol=1e-4 * max(1.0, float(np.abs(ref).max())), what="zero / large-norm tokens")
 
 
 def _kv_case(cfg, layers, sample):
