@@ -135,15 +135,15 @@ constexpr float kSqrtHalfPi = 1.2533141373155003f;
 
 int device_cus();
 
-// Grid for a grid-stride kernel of 256-thread blocks: enough blocks to cover
-// n units (units_per_block each), but no more than fit on the device at once,
-// so every block is resident and the work divides evenly.
-int resident_blocks(const void* kern);
+// Grid for a grid-stride kernel of `threads`-thread blocks: enough blocks to
+// cover n units (units_per_block each), but no more than fit on the device at
+// once, so every block is resident and the work divides evenly.
+int resident_blocks(const void* kern, int threads = 256);
 
 template <typename Kern>
-int resident_grid(Kern kern, int64_t units_per_block, int64_t n)
+int resident_grid(Kern kern, int64_t units_per_block, int64_t n, int threads = 256)
 {
-    const int cap = resident_blocks(reinterpret_cast<const void*>(kern));
+    const int cap = resident_blocks(reinterpret_cast<const void*>(kern), threads);
     int64_t want = (n + units_per_block - 1) / units_per_block;
     if (want < 1) want = 1;
     return (int)(want < cap ? want : cap);

@@ -20,10 +20,10 @@ int device_cus()
     return cached[dev];
 }
 
-// Blocks of 256 threads of kern that are resident on the current device at
-// once (occupancy per compute unit times compute units), cached per
-// (kernel, device).
-int resident_blocks(const void* kern)
+// Blocks of kern (launched with `threads` threads each) that are resident on
+// the current device at once (occupancy per compute unit times compute units),
+// cached per (kernel, device): each kernel is launched with one block size.
+int resident_blocks(const void* kern, int threads)
 {
     static std::mutex mu;
     static std::unordered_map<const void*, int> cache[64];
@@ -33,7 +33,7 @@ int resident_blocks(const void* kern)
     auto it = cache[dev].find(kern);
     if (it != cache[dev].end()) return it->second;
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 256, 0) != hipSuccess || nb < 1) nb = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, threads, 0) != hipSuccess || nb < 1) nb = 1;
     const int blocks = nb * device_cus();
     cache[dev][kern] = blocks;
     return blocks;

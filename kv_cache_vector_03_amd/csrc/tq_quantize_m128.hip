@@ -25,11 +25,11 @@
 // or a lookup grid (3 and 4 bits). For keys the residual is formed, negated,
 // directly in units of 1/(1024 s) (s = sqrt(d) ||x||, keeping it in fp16
 // range), split into exact fp16 hi + lo operands and projected on MFMA against
-// S, with the rows of S permuted so each ballot is two bytes of the sign
-// stream. The
-// projection's A operand is the residual with rows = vectors (lane % 16) and
-// k-block q: k-step r, element t is coordinate 4 q + r + 16 t, which this
-// lane holds.
+// S. The projection's B operand is the residual with columns = vectors
+// (lane % 16) and k-block q: k-step r, element t is coordinate 4 q + r + 16 t,
+// which this lane holds. The A operand is S with its rows permuted so that
+// lane (v, q) receives the 32 projections of sign word q of vector v, which
+// it packs from their sign bits and stores itself.
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -39,15 +39,23 @@ namespace {
 constexpr int kD = 128;
 constexpr float kResUnit = 1024.0f;  // residual scale for the projection operands
 
-// S row feeding column c of n-tile nu (sign stream bits 16 nu .. 16 nu + 15)
-__host__ __device__ constexpr int m128_proj_row(int nu, int c) { return 2 * nu + c / 8 + 16 * (c % 8); }
+// S row feeding row c of m-tile nu. The projection lands in lane (v, c / 4),
+// register c % 4, as bit 4 nu + c % 4 of sign word c / 4, i.e. stream bit
+// j = 32 (c / 4) + 4 nu + c % 4; group-major, that bit is row j / 8 + 16 (j % 8).
+__host__ __device__ constexpr int m128_proj_row(int nu, int c)
+{
+    return (32 * (c / 4) + 4 * nu + c % 4) / 8 + 16 * ((32 * (c / 4) + 4 * nu + c % 4) % 8);
+}
 
-// Codes of the 32 coordinates a lane holds by sign-bit arithmetic: with the
-// symmetric codebook the top code bit is [Y > 0] and the lower bits are the
-// count #{M_j s < |Y|} (XOR-folded from the signs of M_j s - |Y|), complemented
-// for Y <= 0. Local stream bit 8 B r + B t + p is shifted in from the top. For
-// keys, y is replaced by the negated scaled residual (c s - Y) * sc and its
-// squared norm accumulates in g2 (Cq: centroid magnitudes times kResUnit).
+// Codes of the 32 coordinates a lane holds by sign-bit arithmetic. The lane
+// holds Z = -Y (the rotation produces the negated coordinates, so the sign bit
+// of Z is [Y > 0] with Y = 0 below zero, as a rotated exact zero comes out as
+// +0). With the symmetric codebook the top code bit is [Y > 0] and the lower
+// bits are the count #{M_j s < |Y|} (XOR-folded from the signs of
+// M_j s - |Y|), complemented for Y <= 0. Local stream bit 8 B r + B t + p is
+// shifted in from the top. For keys, y is replaced by the negated scaled
+// residual (c s - Y) * sc and its squared norm accumulates in g2 (Cq: centroid
+// magnitudes times kResUnit).
 template <int B, bool QJL, int K = (1 << B) / 2 - 1, typename Pre, typename Post>
 __device__ __forceinline__ void codes_compare(float (&y)[8][4], const float (&Ms)[K > 0 ? K : 1],
                                               const float (&Cq)[K + 1], const float* __restrict__ ctab, float sc,
@@ -60,24 +68,23 @@ __device__ __forceinline__ void codes_compare(float (&y)[8][4], const float (&Ms
         pre(r);
 #pragma unroll
         for (int t = 7; t >= 0; --t) {
-            const float Y = y[t][r];
-            const float d2f = 0.0f - Y;  // sign bit = [Y > 0]
-            const uint32_t d2 = __float_as_uint(d2f);
+            const float Z = y[t][r];                 // -Y
+            const uint32_t d2 = __float_as_uint(Z);  // sign bit = [Y > 0]
             const int P = 8 * B * r + B * t;
             float mag = Cq[0];
             if constexpr (K == 0) {
                 W[P >> 5] = __builtin_amdgcn_alignbit(W[P >> 5], d2, 31);
             } else if constexpr (K == 1) {
-                const bool outer = fabsf(Y) > Ms[0];
+                const bool outer = fabsf(Z) > Ms[0];
                 // bit 0 = [|Y| > M s] for Y > 0, its complement otherwise
-                const float b0 = outer ? d2f : -d2f;
+                const float b0 = outer ? Z : -Z;
                 W[(P + 1) >> 5] = __builtin_amdgcn_alignbit(W[(P + 1) >> 5], d2, 31);
                 W[P >> 5] = __builtin_amdgcn_alignbit(W[P >> 5], __float_as_uint(b0), 31);
                 if constexpr (QJL) mag = outer ? Cq[1] : Cq[0];
             } else {
                 uint32_t e[K];
 #pragma unroll
-                for (int j = 0; j < K; ++j) e[j] = __float_as_uint(Ms[j] - fabsf(Y));  // [|Y| > M_j s]
+                for (int j = 0; j < K; ++j) e[j] = __float_as_uint(Ms[j] - fabsf(Z));  // [|Y| > M_j s]
 #pragma unroll
                 for (int p = B - 1; p >= 0; --p) {
                     uint32_t val;
@@ -103,7 +110,7 @@ __device__ __forceinline__ void codes_compare(float (&y)[8][4], const float (&Ms
             if constexpr (QJL) {
                 // c = +mag for Y > 0, -mag otherwise (y = 0 maps to the level just below 0)
                 const float c = __uint_as_float(__float_as_uint(mag) ^ (~d2 & 0x80000000u));
-                const float rn = fmaf(-Y, sc, c);  // negated scaled residual
+                const float rn = fmaf(Z, sc, c);  // negated scaled residual
                 g2 = fmaf(rn, rn, g2);
                 y[t][r] = rn;
             }
@@ -119,6 +126,7 @@ __device__ __forceinline__ void codes_compare(float (&y)[8][4], const float (&Ms
 // the same strict comparison the codebook defines, as long as no window of two
 // cells holds two boundaries (the cell index itself may be off by one where
 // rounding puts y on a cell edge). The table is checked for that when built.
+// As for the sign-bit codes, the lane holds Z = -Y.
 constexpr int kLutCells = 256;
 constexpr int kLutEntries = 2 * kLutCells + 2;
 constexpr uint32_t kMagicBits = 0x4B000000u;  // bit pattern of 2^23
@@ -136,15 +144,15 @@ __device__ __forceinline__ void codes_lut(float (&y)[8][4], const uint2* __restr
         uint32_t g = 0;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const float Y = y[t][r];
-            uint32_t bits = __float_as_uint(fmaf(Y, rs_cells, magic));
+            const float Z = y[t][r];  // -Y
+            uint32_t bits = __float_as_uint(fmaf(Z, -rs_cells, magic));
             bits = min(max(bits, kMagicBits), kMagicBits + (uint32_t)(kLutEntries - 1));
             const uint2 ent = lut[bits - kMagicBits];
-            const float e = fmaf(__uint_as_float(ent.x), s, -Y);  // < 0 iff Y > next boundary
+            const float e = fmaf(__uint_as_float(ent.x), s, Z);  // < 0 iff Y > next boundary
             const uint32_t code = ent.y - (uint32_t)((int32_t)__float_as_uint(e) >> 31);
             g = __builtin_amdgcn_alignbit(code, g, B);  // code t ends at bits 32 - 8B + B t
             if constexpr (QJL) {
-                const float rn = fmaf(-Y, sc, ctab[code & ((1u << B) - 1u)]);  // negated residual
+                const float rn = fmaf(Z, sc, ctab[code & ((1u << B) - 1u)]);  // negated residual
                 g2 = fmaf(rn, rn, g2);
                 y[t][r] = rn;
             }
@@ -167,38 +175,14 @@ __device__ __forceinline__ void codes_lut(float (&y)[8][4], const uint2* __restr
     }
 }
 
-// Half H (0: low, 1: high) of two wave-uniform words packed into one:
-// half H of a in bits 0..15, half H of b in bits 16..31 (one scalar op).
-template <int H>
-__device__ __forceinline__ uint32_t pack_half(uint32_t a, uint32_t b)
+// Shift the sign bits of the four projections t[3], .., t[0] into w from
+// below. The projections are negated (t = -(S r)), so the sign bit of t is
+// the stored bit [S r >= 0] everywhere except at S r = 0 exactly.
+__device__ __forceinline__ uint32_t shift_signs(uint32_t w, const float4_t& t)
 {
-    uint32_t w;
-    if constexpr (H == 0) asm("s_pack_ll_b32_b16 %0, %1, %2" : "=s"(w) : "s"(a), "s"(b));
-    else asm("s_pack_hh_b32_b16 %0, %1, %2" : "=s"(w) : "s"(a), "s"(b));
-    return w;
-}
-
-// Sign word of n-tiles (2p, 2p+1) for the 16 vectors of a batch, from the
-// projection accumulators t0, t1 (values -(S r) in scaled units, so the sign
-// bit [S r >= 0] is [t <= 0]). Output row 4 g + r4 is vector 4 g + r4; its 16
-// bits in each ballot are bits 16 g .. 16 g + 15. Lane v < 16 receives the
-// word of vector v.
-__device__ __forceinline__ uint32_t sign_word(const float4_t& t0, const float4_t& t1)
-{
-    uint64_t m0[4], m1[4];
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-        m0[r4] = __ballot(t0[r4] <= 0.f);
-        m1[r4] = __ballot(t1[r4] <= 0.f);
-    }
-    uint32_t sw = 0;
-    static_for<0, 16>([&](auto k) {
-        constexpr int g = decltype(k)::value / 4, r4 = decltype(k)::value % 4;
-        const uint32_t a = (uint32_t)(m0[r4] >> (32 * (g / 2)));
-        const uint32_t b = (uint32_t)(m1[r4] >> (32 * (g / 2)));
-        sw = write_lane<4 * g + r4>(sw, pack_half<g % 2>(a, b));
-    });
-    return sw;
+    for (int r4 = 3; r4 >= 0; --r4) w = __builtin_amdgcn_alignbit(w, __float_as_uint(t[r4]), 31);
+    return w;
 }
 
 __device__ __forceinline__ void load_batch(uint4 (&u)[4], const uint16_t* __restrict__ x, int64_t vec, int64_t n,
@@ -211,63 +195,96 @@ __device__ __forceinline__ void load_batch(uint4 (&u)[4], const uint16_t* __rest
     }
 }
 
-template <int B, bool QJL>
-__global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restrict__ x, int64_t n,
-                                                       const float* __restrict__ cent,
-                                                       const float* __restrict__ bnd,
-                                                       const uint32_t* __restrict__ diag,
-                                                       const uint16_t* __restrict__ S,
-                                                       uint32_t* __restrict__ codes,
-                                                       uint32_t* __restrict__ signs,
-                                                       uint16_t* __restrict__ norm,
-                                                       uint16_t* __restrict__ rnorm)
-{
-    constexpr int L = 1 << B, K = L / 2 - 1;
-    constexpr int CW = B * kD / 32;  // code words per vector
-    constexpr int NT = 8, KS = 4;    // projection n-tiles (m = 128) and k-steps
-    constexpr bool LUT = B >= 3;
-    __shared__ __align__(16) half8_t bfrag[QJL ? KS * NT * 64 : 1];
-    __shared__ uint2 lut[LUT ? kLutEntries : 1];
-    __shared__ float ctab[L];  // centroids (times kResUnit for keys)
-    __shared__ int lut_bad;
-
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int v = lane & 15, q = lane >> 4;
-
-    float Mth[K > 0 ? K : 1], Cq[K + 1];
-#pragma unroll
-    for (int j = 1; j <= K; ++j) Mth[j - 1] = bnd[L / 2 - 1 + j];
-#pragma unroll
-    for (int m = 0; m <= K; ++m) Cq[m] = cent[L / 2 + m] * kResUnit;
-
-    // H_32 slabs and their negations as A operands: lane (row rho = v,
-    // k-block q), element e is +-H_32[16 tau + rho][8 q + e]
+// Per-lane constants of the rotation: the negated H_32 slabs and the slabs as A
+// operands (lane (row rho = v, k-block q), element e of hA[tau][0] is
+// -H_32[16 tau + rho][8 q + e], of hA[tau][1] +H_32[..]), so the rotation yields -Y,
+// and the random diagonal's sign flips of the lane's input halves (chunk a',
+// word w holds coordinates 32 a' + 8 q + 2 w in its low half and + 1 in its high half).
+struct RotConsts {
     half8_t hA[2][2];
+    uint32_t dm[4][4];
+};
+
+__device__ __forceinline__ void rot_consts(RotConsts& rc, const uint32_t* __restrict__ diag, int v, int q)
+{
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const bool neg = __builtin_popcount((16 * tau + v) & (8 * q + e)) & 1;
-            hA[tau][0][e] = neg ? (_Float16)-1.0f : (_Float16)1.0f;
-            hA[tau][1][e] = neg ? (_Float16)1.0f : (_Float16)-1.0f;
+            rc.hA[tau][0][e] = neg ? (_Float16)1.0f : (_Float16)-1.0f;
+            rc.hA[tau][1][e] = neg ? (_Float16)-1.0f : (_Float16)1.0f;
         }
-
-    // diagonal sign flips of the lane's input halves: chunk a', word w holds
-    // coordinates 32 a' + 8 q + 2 w (low half) and + 1 (high half)
-    uint32_t dm[4][4];
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
         const uint32_t word = diag[a] >> (8 * q);
 #pragma unroll
         for (int w = 0; w < 4; ++w)
-            dm[a][w] = (((word >> (2 * w)) & 1u) << 15) | (((word >> (2 * w + 1)) & 1u) << 31);
+            rc.dm[a][w] = (((word >> (2 * w)) & 1u) << 15) | (((word >> (2 * w + 1)) & 1u) << 31);
     }
+}
 
-    if (threadIdx.x == 0) lut_bad = 0;
-    if (threadIdx.x < L) ctab[threadIdx.x] = cent[threadIdx.x] * (QJL ? kResUnit : 1.0f);
+// Rotation of one 16-vector batch: H_32 of each input chunk on MFMA with the
+// H_4 signs, accumulated into the output chunks (acc[tau][a] register r is
+// coordinate 32 a + 16 tau + 4 q + r, negated), and the lane's share of ||x||^2
+// from the fp16 input.
+__device__ __forceinline__ void rotate_batch(const uint4 (&xin)[4], const RotConsts& rc, float4_t (&acc)[2][4],
+                                             float& ss)
+{
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) acc[tau][a] = float4_t{0.f, 0.f, 0.f, 0.f};
+    ss = 0.f;
+#pragma unroll
+    for (int ap = 0; ap < 4; ++ap) {
+        const uint32_t w4[4] = {xin[ap].x ^ rc.dm[ap][0], xin[ap].y ^ rc.dm[ap][1], xin[ap].z ^ rc.dm[ap][2],
+                                xin[ap].w ^ rc.dm[ap][3]};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const auto h2 = __builtin_bit_cast(__attribute__((ext_vector_type(2))) _Float16, w4[w]);
+            ss = __builtin_amdgcn_fdot2(h2, h2, ss, false);
+        }
+        const half8_t bx = __builtin_bit_cast(half8_t, w4);
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                acc[tau][a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(rc.hA[tau][__builtin_popcount(a & ap) & 1], bx,
+                                                                     acc[tau][a], 0, 0, 0);
+    }
+}
+
+// Codebook state: boundaries and centroid magnitudes in registers (sign-bit
+// arithmetic), the centroid table and the lookup grid in LDS.
+template <int B>
+struct CodeConsts {
+    static constexpr int L = 1 << B, K = L / 2 - 1;
+    float Mth[K > 0 ? K : 1];
+    float Cq[K + 1];
+    const float* ctab;
+    const uint2* lut;
+    bool use_lut;
+};
+
+// Fill the block's centroid table (times `unit`) and, for 3 and 4 bits, the
+// lookup grid, and set up cc; the grid is used only if it resolves the
+// codebook. Ends with a barrier.
+template <int B>
+__device__ void build_tables(CodeConsts<B>& cc, const float* __restrict__ cent, const float* __restrict__ bnd,
+                             float unit, float* ctab, uint2* lut, int* lut_bad)
+{
+    constexpr int L = 1 << B, K = L / 2 - 1;
+    constexpr bool LUT = B >= 3;
+#pragma unroll
+    for (int j = 1; j <= K; ++j) cc.Mth[j - 1] = bnd[L / 2 - 1 + j];
+#pragma unroll
+    for (int m = 0; m <= K; ++m) cc.Cq[m] = cent[L / 2 + m] * unit;
+    if (threadIdx.x == 0) *lut_bad = 0;
+    if (threadIdx.x < L) ctab[threadIdx.x] = cent[threadIdx.x] * unit;
     __syncthreads();
     if constexpr (LUT) {
-        for (int c = threadIdx.x; c < kLutEntries; c += 256) {
+        for (int c = threadIdx.x; c < kLutEntries; c += blockDim.x) {
             const float lo = ((float)(c - kLutCells) - 0.5f) / kLutCells;  // exact
             const float win = lo + 2.0f / kLutCells;
             uint32_t base = 0;
@@ -279,174 +296,257 @@ __global__ __launch_bounds__(256) void k_quantize_m128(const uint16_t* __restric
                 if (b >= lo && b < next) next = b;
                 inwin += (b >= lo && b < win) ? 1 : 0;
             }
-            if (inwin > 1) lut_bad = 1;
+            if (inwin > 1) *lut_bad = 1;
             lut[c] = make_uint2(__float_as_uint(next), base);
         }
     }
-    if constexpr (QJL) {
-        // B fragments: lane (k-block kb, column c) of fragment (ks, nu), element e
-        // holds S[proj_row(nu, c)][4 kb + ks + 16 e]
-        for (int e = threadIdx.x; e < KS * NT * 64; e += 256) {
-            const int ks = e / (NT * 64), nu = (e / 64) % NT, ln = e & 63;
-            const int kb = ln >> 4, c = ln & 15;
-            const uint16_t* row = S + (int64_t)m128_proj_row(nu, c) * kD;
-            half8_t f;
-#pragma unroll
-            for (int ee = 0; ee < 8; ++ee) f[ee] = __builtin_bit_cast(_Float16, row[4 * kb + ks + 16 * ee]);
-            bfrag[(ks * NT + nu) * 64 + ln] = f;
-        }
-    }
     __syncthreads();
-    const bool use_lut = LUT && !lut_bad;
+    cc.ctab = ctab;
+    cc.lut = lut;
+    cc.use_lut = LUT && !*lut_bad;
+}
 
-    const float sqrt_d = 11.313708498984761f;  // sqrt(128)
+// Code one rotated batch (pure register work): norm, code words, and for keys
+// the residual norm and the negated scaled residual split into exact fp16
+// hi + lo projection operands (k-step r = group r of the lane). Lane (v, q)
+// returns code words B q .. B q + B - 1 of vector v; every lane gets the norms.
+template <int B, bool QJL, typename Pre = void (*)(int)>
+__device__ __forceinline__ void code_batch(const float4_t (&acc)[2][4], float ss, const CodeConsts<B>& cc,
+                                           uint32_t (&W)[B], float& nrm, float& gam, half8_t (&ahi)[4],
+                                           half8_t (&alo)[4], Pre&& pre = [](int) {})
+{
+    constexpr int K = (1 << B) / 2 - 1;
+    constexpr float sqrt_d = 11.313708498984761f;  // sqrt(128)
     auto none = [](int) {};
-
-    // One 16-vector batch: rotation, norm and codes (stored), and for keys the
-    // residual norm (stored) and the scaled residual split into exact fp16
-    // hi + lo projection operands (k-step r = group r of the lane).
-    auto batch = [&](const uint4(&xin)[4], int64_t vec, bool live, half8_t(&ahi)[KS], half8_t(&alo)[KS]) {
-        // ---- rotation: H_32 per chunk on MFMA with the H_4 signs, accumulated
-        // into the output chunks; ||x||^2 from the fp16 input
-        float4_t acc[2][4];
+    // y[t][r]: coordinate 4 q + r + 16 t, t = 2 a + tau
+    float y[8][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-            for (int a = 0; a < 4; ++a) acc[tau][a] = float4_t{0.f, 0.f, 0.f, 0.f};
-        float ss = 0.f;
+            for (int r = 0; r < 4; ++r) y[2 * a + tau][r] = acc[tau][a][r];
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    // hardware square root (within an ulp of fp32); the stored value is fp16
+    nrm = __builtin_amdgcn_sqrtf(ss);
+    const float sr = nrm * sqrt_d;  // sqrt(d) ||x||
+    const float s = sr > 0.f ? sr : 1.0f;
+    const float sc = kResUnit * __builtin_amdgcn_rcpf(s);  // any uniform scale near 1024 / s
+    float Ms[K > 0 ? K : 1];
 #pragma unroll
-        for (int ap = 0; ap < 4; ++ap) {
-            const uint32_t w4[4] = {xin[ap].x ^ dm[ap][0], xin[ap].y ^ dm[ap][1], xin[ap].z ^ dm[ap][2],
-                                    xin[ap].w ^ dm[ap][3]};
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const auto h2 = __builtin_bit_cast(__attribute__((ext_vector_type(2))) _Float16, w4[w]);
-                ss = __builtin_amdgcn_fdot2(h2, h2, ss, false);
-            }
-            const half8_t bx = __builtin_bit_cast(half8_t, w4);
-#pragma unroll
-            for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-                    acc[tau][a] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        hA[tau][__builtin_popcount(a & ap) & 1], bx, acc[tau][a], 0, 0, 0);
-        }
-        // y[t][r]: coordinate 4 q + r + 16 t, t = 2 a + tau
-        float y[8][4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) y[2 * a + tau][r] = acc[tau][a][r];
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
-        const float nrm = sqrtf(ss);
-        const float sr = nrm * sqrt_d;  // sqrt(d) ||x||
-        const float s = sr > 0.f ? sr : 1.0f;
-        const float sc = kResUnit * __builtin_amdgcn_rcpf(s);  // any uniform scale near 1024 / s
-        float Ms[K > 0 ? K : 1];
-#pragma unroll
-        for (int j = 0; j < K; ++j) Ms[j] = Mth[j] * s;
+    for (int j = 0; j < K; ++j) Ms[j] = cc.Mth[j] * s;
 
-        // ---- codes (and for keys the negated scaled residual)
-        uint32_t W[B];
-        float g2 = 0.f;
-        if (use_lut) codes_lut<B, QJL>(y, lut, ctab, s, (float)kLutCells / s, sc, W, g2, none, none);
-        else codes_compare<B, QJL>(y, Ms, Cq, ctab, sc, W, g2, none, none);
-        if (live) {
-            uint32_t* dst = codes + vec * CW + B * q;
+    float g2 = 0.f;
+    if (cc.use_lut) codes_lut<B, QJL>(y, cc.lut, cc.ctab, s, (float)kLutCells / s, sc, W, g2, pre, none);
+    else codes_compare<B, QJL>(y, Ms, cc.Cq, cc.ctab, sc, W, g2, pre, none);
+    gam = 0.f;
+    if constexpr (QJL) {
+        g2 += __shfl_xor(g2, 16);
+        g2 += __shfl_xor(g2, 32);
+        gam = __builtin_amdgcn_sqrtf(g2) * (1.0f / kResUnit);
+        // hi rounds toward zero; lo is the remainder r - hi (exact in fp32, hi
+        // taken straight from its fp16 half) rounded once to fp16, written
+        // straight into its half of the packed word
 #pragma unroll
-            for (int w = 0; w < B; ++w) dst[w] = W[w];
-        }
-        if constexpr (QJL) {
-            g2 += __shfl_xor(g2, 16);
-            g2 += __shfl_xor(g2, 32);
-            if (live && q == 0) rnorm[vec] = f2h(sqrtf(g2) * (1.0f / kResUnit));
-            // hi rounds toward zero; lo is the fp32 remainder (hi taken straight from
-            // its fp16 half) rounded once more
+        for (int r = 0; r < 4; ++r) {
+            uint32_t hw[4], lw[4];
 #pragma unroll
-            for (int r = 0; r < KS; ++r) {
-                uint32_t hw[4], lw[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float r0 = y[2 * j][r], r1 = y[2 * j + 1][r];
-                    hw[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
-                    float l0, l1;
-                    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(l0) : "v"(hw[j]), "v"(r0));
-                    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-                        : "=v"(l1) : "v"(hw[j]), "v"(r1));
-                    lw[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(l0, l1));
-                }
-                ahi[r] = __builtin_bit_cast(half8_t, hw);
-                alo[r] = __builtin_bit_cast(half8_t, lw);
+            for (int j = 0; j < 4; ++j) {
+                const float r0 = y[2 * j][r], r1 = y[2 * j + 1][r];
+                hw[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+                uint32_t l = 0;
+                asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "+v"(l) : "v"(hw[j]), "v"(r0));
+                asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+                    : "+v"(l) : "v"(hw[j]), "v"(r1));
+                lw[j] = l;
             }
-        }
-        if (live && q == 0) norm[vec] = f2h(nrm);
-    };
-
-    const int64_t step = (int64_t)gridDim.x * 64;  // vectors between a wave's batches
-    int64_t base = ((int64_t)blockIdx.x * 4 + wid) * 16;
-    uint4 cur[4];
-    load_batch(cur, x, base + v, n, q);
-    if constexpr (!QJL) {
-        half8_t nh[KS], nl[KS];  // unused for values
-        for (; base < n; base += step) {
-            uint4 nxt[4];
-            load_batch(nxt, x, base + step + v, n, q);
-            batch(cur, base + v, base + v < n, nh, nl);
-#pragma unroll
-            for (int a = 0; a < 4; ++a) cur[a] = nxt[a];
-        }
-    } else {
-        // keys: two batches per iteration, then one projection pass in which each
-        // S fragment read from LDS feeds four MFMAs (both batches, hi and lo)
-        for (; base < n; base += 2 * step) {
-            const int64_t baseB = base + step;
-            uint4 nxt[4];
-            load_batch(nxt, x, baseB + v, n, q);
-            half8_t ahiA[KS], aloA[KS], ahiB[KS], aloB[KS];
-            batch(cur, base + v, base + v < n, ahiA, aloA);
-            load_batch(cur, x, base + 2 * step + v, n, q);
-            batch(nxt, baseB + v, baseB + v < n, ahiB, aloB);
-
-            uint32_t SWA[4], SWB[4];
-#pragma unroll
-            for (int p = 0; p < NT / 2; ++p) {
-                float4_t pA0 = {0.f, 0.f, 0.f, 0.f}, pA1 = pA0, pB0 = pA0, pB1 = pA0;
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const half8_t b0 = bfrag[(ks * NT + 2 * p) * 64 + lane];
-                    const half8_t b1 = bfrag[(ks * NT + 2 * p + 1) * 64 + lane];
-                    pA0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahiA[ks], b0, pA0, 0, 0, 0);
-                    pA1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahiA[ks], b1, pA1, 0, 0, 0);
-                    pB0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahiB[ks], b0, pB0, 0, 0, 0);
-                    pB1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahiB[ks], b1, pB1, 0, 0, 0);
-                    pA0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aloA[ks], b0, pA0, 0, 0, 0);
-                    pA1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aloA[ks], b1, pA1, 0, 0, 0);
-                    pB0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aloB[ks], b0, pB0, 0, 0, 0);
-                    pB1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(aloB[ks], b1, pB1, 0, 0, 0);
-                }
-                SWA[p] = sign_word(pA0, pA1);
-                SWB[p] = sign_word(pB0, pB1);
-            }
-            if (q == 0) {
-                if (base + v < n)
-                    *reinterpret_cast<uint4*>(signs + (base + v) * 4) = make_uint4(SWA[0], SWA[1], SWA[2], SWA[3]);
-                if (baseB + v < n)
-                    *reinterpret_cast<uint4*>(signs + (baseB + v) * 4) = make_uint4(SWB[0], SWB[1], SWB[2], SWB[3]);
-            }
+            ahi[r] = __builtin_bit_cast(half8_t, hw);
+            alo[r] = __builtin_bit_cast(half8_t, lw);
         }
     }
 }
 
+// Store lane (v, q)'s code words of vector vec and, from lanes q = 0, its norm
+// (and residual norm), if vec < n.
 template <int B, bool QJL>
+__device__ __forceinline__ void store_coded(const uint32_t (&W)[B], float nrm, float gam, int64_t vec, int64_t n,
+                                            int q, uint32_t* __restrict__ codes, uint16_t* __restrict__ norm,
+                                            uint16_t* __restrict__ rnorm)
+{
+    constexpr int CW = B * kD / 32;  // code words per vector
+    if (vec < n) {
+        uint32_t* dst = codes + vec * CW + B * q;
+        if constexpr (B == 2) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(W[0], W[1]);
+        } else if constexpr (B == 4) {
+            *reinterpret_cast<uint4*>(dst) = make_uint4(W[0], W[1], W[2], W[3]);
+        } else {
+#pragma unroll
+            for (int w = 0; w < B; ++w) dst[w] = W[w];
+        }
+        if (q == 0) {
+            norm[vec] = f2h(nrm);
+            if constexpr (QJL) rnorm[vec] = f2h(gam);
+        }
+    }
+}
+
+// Input of one batch for lane (v, q); rows past the end repeat the last row
+// (their results are not stored), so the loads need no branch.
+__device__ __forceinline__ void load_clamped(uint4 (&u)[4], const uint16_t* __restrict__ x, int64_t vec, int64_t n,
+                                             int q)
+{
+    const uint16_t* row = x + (vec < n ? vec : n - 1) * kD + 8 * q;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) u[a] = *reinterpret_cast<const uint4*>(row + 32 * a);
+}
+
+// Values (MSE codes only). A wave takes one 16-vector batch at a time and
+// fetches the next batch while it processes the current one.
+template <int B>
+__global__ __launch_bounds__(256) void k_quantize_values_m128(const uint16_t* __restrict__ x, int64_t n,
+                                                              const float* __restrict__ cent,
+                                                              const float* __restrict__ bnd,
+                                                              const uint32_t* __restrict__ diag,
+                                                              uint32_t* __restrict__ codes,
+                                                              uint16_t* __restrict__ norm)
+{
+    __shared__ uint2 lut[B >= 3 ? kLutEntries : 1];
+    __shared__ float ctab[1 << B];
+    __shared__ int lut_bad;
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int v = lane & 15, q = lane >> 4;
+    RotConsts rc;
+    rot_consts(rc, diag, v, q);
+    CodeConsts<B> cc;
+    build_tables<B>(cc, cent, bnd, 1.0f, ctab, lut, &lut_bad);
+
+    const int64_t step = (int64_t)gridDim.x * 64;  // vectors between a wave's batches
+    int64_t base = ((int64_t)blockIdx.x * 4 + wid) * 16;
+    if (base >= n) return;
+    uint4 cur[4];
+    load_clamped(cur, x, base + v, n, q);
+    half8_t nh[4], nl[4];  // unused for values
+    for (; base < n; base += step) {
+        uint4 nxt[4];
+        load_clamped(nxt, x, base + step + v, n, q);
+        float4_t acc[2][4];
+        float ss, nrm, gam;
+        uint32_t W[B];
+        rotate_batch(cur, rc, acc, ss);
+        code_batch<B, false>(acc, ss, cc, W, nrm, gam, nh, nl);
+        store_coded<B, false>(W, nrm, gam, base + v, n, q, codes, norm, nullptr);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) cur[a] = nxt[a];
+    }
+}
+
+// Keys (codes + QJL sketch). A wave codes two 16-vector batches, then projects
+// both residuals against S in one pass in which each S fragment read from LDS
+// (A-fragment order) feeds four MFMAs (both batches, hi and lo). The next pair
+// of batches is fetched while the current pair is processed.
+template <int B>
+__global__ __launch_bounds__(256) void k_quantize_keys_m128(const uint16_t* __restrict__ x, int64_t n,
+                                                            const float* __restrict__ cent,
+                                                            const float* __restrict__ bnd,
+                                                            const uint32_t* __restrict__ diag,
+                                                            const uint16_t* __restrict__ S,
+                                                            uint32_t* __restrict__ codes,
+                                                            uint32_t* __restrict__ signs,
+                                                            uint16_t* __restrict__ norm,
+                                                            uint16_t* __restrict__ rnorm)
+{
+    constexpr int NT = 8, KS = 4;  // projection m-tiles (m = 128) and k-steps
+    __shared__ __align__(16) half8_t sfrag[KS * NT * 64];  // 32 KiB
+    __shared__ uint2 lut[B >= 3 ? kLutEntries : 1];
+    __shared__ float ctab[1 << B];
+    __shared__ int lut_bad;
+
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const int v = lane & 15, q = lane >> 4;
+    CodeConsts<B> cc;
+    build_tables<B>(cc, cent, bnd, kResUnit, ctab, lut, &lut_bad);
+    // A fragments: lane (row c, k-block kb) of fragment (ks, nu), element e
+    // holds S[proj_row(nu, c)][4 kb + ks + 16 e]
+    for (int e = threadIdx.x; e < KS * NT * 64; e += 256) {
+        const int ks = e / (NT * 64), nu = (e / 64) % NT, ln = e & 63;
+        const int kb = ln >> 4, c = ln & 15;
+        const uint16_t* row = S + (int64_t)m128_proj_row(nu, c) * kD;
+        half8_t f;
+#pragma unroll
+        for (int ee = 0; ee < 8; ++ee) f[ee] = __builtin_bit_cast(_Float16, row[4 * kb + ks + 16 * ee]);
+        sfrag[(ks * NT + nu) * 64 + ln] = f;
+    }
+    __syncthreads();
+    RotConsts rc;
+    rot_consts(rc, diag, v, q);
+
+    const int64_t step = (int64_t)gridDim.x * 64;  // vectors between a wave's batches
+    int64_t base = ((int64_t)blockIdx.x * 4 + wid) * 16;
+    if (base >= n) return;
+    // one batch: rotation, codes and norms (stored), residual operands
+    auto batch = [&](const uint4(&in)[4], int64_t b0, half8_t(&hi)[KS], half8_t(&lo)[KS]) {
+        float4_t acc[2][4];
+        float ss, nrm, gam;
+        uint32_t W[B];
+        rotate_batch(in, rc, acc, ss);
+        code_batch<B, true>(acc, ss, cc, W, nrm, gam, hi, lo);
+        store_coded<B, true>(W, nrm, gam, b0 + v, n, q, codes, norm, rnorm);
+    };
+    uint4 inA[4], inB[4];
+    load_clamped(inA, x, base + v, n, q);
+    load_clamped(inB, x, base + step + v, n, q);
+    for (; base < n; base += 2 * step) {
+        const int64_t baseB = base + step;
+        half8_t hiA[KS], loA[KS], hiB[KS], loB[KS];
+        batch(inA, base, hiA, loA);
+        load_clamped(inA, x, base + 2 * step + v, n, q);
+        batch(inB, baseB, hiB, loB);
+        load_clamped(inB, x, base + 3 * step + v, n, q);
+
+        // m-tiles from the top so the sign bits enter the words from bit 31 down
+        uint32_t swA = 0, swB = 0;
+#pragma unroll
+        for (int pt = NT / 2 - 1; pt >= 0; --pt) {
+            float4_t pA0 = {0.f, 0.f, 0.f, 0.f}, pA1 = pA0, pB0 = pA0, pB1 = pA0;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const half8_t s0 = sfrag[(ks * NT + 2 * pt) * 64 + lane];
+                const half8_t s1 = sfrag[(ks * NT + 2 * pt + 1) * 64 + lane];
+                pA0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(s0, hiA[ks], pA0, 0, 0, 0);
+                pA1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(s1, hiA[ks], pA1, 0, 0, 0);
+                pB0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(s0, hiB[ks], pB0, 0, 0, 0);
+                pB1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(s1, hiB[ks], pB1, 0, 0, 0);
+                pA0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(s0, loA[ks], pA0, 0, 0, 0);
+                pA1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(s1, loA[ks], pA1, 0, 0, 0);
+                pB0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(s0, loB[ks], pB0, 0, 0, 0);
+                pB1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(s1, loB[ks], pB1, 0, 0, 0);
+            }
+            swA = shift_signs(shift_signs(swA, pA1), pA0);
+            swB = shift_signs(shift_signs(swB, pB1), pB0);
+        }
+        if (base + v < n) signs[(base + v) * 4 + q] = swA;
+        if (baseB + v < n) signs[(baseB + v) * 4 + q] = swB;
+    }
+}
+
+template <int B>
 void launch_b(const tq_quantizer* q, const uint16_t* x, int64_t n, const tq_packed* o, hipStream_t s)
 {
-    auto kern = k_quantize_m128<B, QJL>;
-    const int grid = resident_grid(kern, 64, n);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, x, n, q->centroids, q->boundaries, q->diag_signs,
-                       q->S, o->codes, o->signs, o->norm, o->rnorm);
+    if (q->qjl_m != 0) {
+        auto kern = k_quantize_keys_m128<B>;
+        const int grid = resident_grid(kern, 64, n);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, x, n, q->centroids, q->boundaries, q->diag_signs,
+                           q->S, o->codes, o->signs, o->norm, o->rnorm);
+    } else {
+        auto kern = k_quantize_values_m128<B>;
+        const int grid = resident_grid(kern, 64, n);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, x, n, q->centroids, q->boundaries, q->diag_signs,
+                           o->codes, o->norm);
+    }
 }
 
 }  // namespace
@@ -454,12 +554,11 @@ void launch_b(const tq_quantizer* q, const uint16_t* x, int64_t n, const tq_pack
 void launch_quantize_m128(const tq_quantizer* q, const void* x, int64_t n, const tq_packed* out, hipStream_t s)
 {
     const uint16_t* xh = static_cast<const uint16_t*>(x);
-    const bool qjl = q->qjl_m != 0;
     switch (q->mse_bits) {
-        case 1: qjl ? launch_b<1, true>(q, xh, n, out, s) : launch_b<1, false>(q, xh, n, out, s); break;
-        case 2: qjl ? launch_b<2, true>(q, xh, n, out, s) : launch_b<2, false>(q, xh, n, out, s); break;
-        case 3: qjl ? launch_b<3, true>(q, xh, n, out, s) : launch_b<3, false>(q, xh, n, out, s); break;
-        default: qjl ? launch_b<4, true>(q, xh, n, out, s) : launch_b<4, false>(q, xh, n, out, s); break;
+        case 1: launch_b<1>(q, xh, n, out, s); break;
+        case 2: launch_b<2>(q, xh, n, out, s); break;
+        case 3: launch_b<3>(q, xh, n, out, s); break;
+        default: launch_b<4>(q, xh, n, out, s); break;
     }
 }
 

@@ -70,6 +70,17 @@ def test_quantize_ragged_counts(n):
     check_quantize(qo, x.astype(np.float64), gpu_quantize(qg, x).to_host())
 
 
+@pytest.mark.parametrize("bits,m", [(2, 128), (3, 128), (4, 0)])
+def test_quantize_many_rounds_full(bits, m):
+    """Enough fp16 vectors that every resident block loops over several rounds
+    of batches (and a ragged last round); every output is checked."""
+    d = 128
+    qg, qo = quantizers(d, bits, m)
+    n = 3 * 256 * 64 + 4 * 64 + 37
+    x = synth.to_f16(synth.normals(23, synth.ROLE_DATA_K, np.arange(n * d)).reshape(n, d) * 2.0)
+    check_quantize(qo, x.astype(np.float64), gpu_quantize(qg, x).to_host())
+
+
 def test_quantize_zero_and_one_hot_vectors():
     d = 128
     qg, qo = quantizers(d, 2, d)
