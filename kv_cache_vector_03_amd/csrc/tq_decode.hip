@@ -169,6 +169,62 @@ __device__ __forceinline__ void load_step(Step<BK, BV>& st, int64_t tb, int64_t 
     }
 }
 
+// Per-lane element offsets of a step's loads, relative to the step's first
+// token (the same for every step).
+struct LaneOff {
+    int k, s, v, v1, n;
+};
+
+template <int D, int BK, int BV>
+__device__ __forceinline__ LaneOff lane_offsets(int lane)
+{
+    constexpr int KW = BK * D / 32, VW = BV * D / 32, SWN = D / 32;
+    const int col = lane & 15, g = lane >> 4;
+    const int w = (8 * BV * col) >> 5;
+    LaneOff o;
+    o.k = col * KW + BK * g;
+    o.s = col * SWN + g;
+    o.v = 4 * g * VW + w;
+    o.v1 = 4 * g * VW + (w + 1 < VW ? w + 1 : w);
+    o.n = 4 * g + (col & 3);
+    return o;
+}
+
+// Loads of a step whose 32 tokens all lie in the wave's range: wave-uniform
+// row pointers (t0 = first token of the step) plus the fixed lane offsets, so
+// no per-load address arithmetic. Same values as load_step.
+template <int D, int BK, bool QJL, int BV>
+__device__ __forceinline__ void load_full(Step<BK, BV>& st, int64_t t0, const LaneOff& lo,
+                                          const uint32_t* __restrict__ kcodes,
+                                          const uint32_t* __restrict__ ksigns,
+                                          const uint16_t* __restrict__ knorm,
+                                          const uint16_t* __restrict__ krnorm,
+                                          const uint32_t* __restrict__ vcodes,
+                                          const uint16_t* __restrict__ vnorm)
+{
+    constexpr int KW = BK * D / 32, VW = BV * D / 32, SWN = D / 32;
+    const uint32_t* kc = kcodes + t0 * KW;
+    const uint32_t* vc = vcodes + t0 * VW;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int w = 0; w < BK; ++w) st.kf[u][w] = kc[lo.k + 16 * u * KW + w];
+        st.sf[u] = QJL ? ksigns[t0 * SWN + lo.s + 16 * u * SWN] : 0u;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        st.x0[e] = vc[lo.v + (16 * (e >> 2) + (e & 3)) * VW];
+        if constexpr (BV == 3) st.x1[e] = vc[lo.v1 + (16 * (e >> 2) + (e & 3)) * VW];
+        else st.x1[e] = 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        st.nk[u] = knorm[t0 + lo.n + 16 * u];
+        st.ng[u] = QJL ? krnorm[t0 + lo.n + 16 * u] : (uint16_t)0;
+        st.nv[u] = vnorm[t0 + lo.n + 16 * u];
+    }
+}
+
 template <int D, int BK, bool QJL, int BV>
 __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restrict__ kcodes,
                                                      const uint32_t* __restrict__ ksigns,
@@ -194,12 +250,14 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
     __shared__ uint2 klut4[K4 ? KLUT : 1];
     __shared__ uint32_t klut2[K4 ? 1 : KLUT];
     __shared__ uint4 slut[QJL ? 256 : 1];
-    __shared__ uint32_t vlut[VLUT];
+    __shared__ uint32_t vlut[VLUT][32];  // one copy per bank: lane l reads copy l % 32
     __shared__ float mrg_m[4][8], mrg_l[4][8];
     __shared__ float mrg_o[4][8][D];
 
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int col = lane & 15, g = lane >> 4;
+    const LaneOff loff = lane_offsets<D, BK, BV>(lane);
 
     // ---- lookup tables: codes -> fp16 centroids, sign bytes -> +-1 (built once per block)
     for (int i = tid; i < KLUT; i += 256) {
@@ -220,8 +278,10 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                 w[j] = (((i >> (2 * j)) & 1) ? 0x3C00u : 0xBC00u) | ((((i >> (2 * j + 1)) & 1) ? 0x3C00u : 0xBC00u) << 16);
             slut[i] = make_uint4(w[0], w[1], w[2], w[3]);
         }
-    for (int i = tid; i < VLUT; i += 256)
-        vlut[i] = (uint32_t)f2h(vcent[i & ((1 << BV) - 1)]) | ((uint32_t)f2h(vcent[i >> BV]) << 16);
+    for (int i = tid; i < VLUT * 32; i += 256) {
+        const int e = i >> 5;
+        vlut[e][i & 31] = (uint32_t)f2h(vcent[e & ((1 << BV) - 1)]) | ((uint32_t)f2h(vcent[e >> BV]) << 16);
+    }
     __syncthreads();
 
     for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
@@ -258,19 +318,15 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
 #pragma unroll
         for (int c = 0; c < CT; ++c) acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-        Step<BK, BV> cur, nxt;
-        if (w0 < w1) load_step<D, BK, QJL, BV>(cur, w0, w1, base, lane, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
-
-        for (int64_t tb = w0; tb < w1; tb += 32) {
-            if (tb + 32 < w1)
-                load_step<D, BK, QJL, BV>(nxt, tb + 32, w1, base, lane, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
+        // one 32-token step from tb; MASK: the step runs past the wave's range
+        auto compute = [&](const Step<BK, BV>& st, int64_t tb, auto MASK) {
             // per-token factors of this lane's quad: row 16 u + 4 g + r sits in quad lane r
             float fk[2], fq[2], fv[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                fk[u] = h2f(cur.nk[u]) * zscale;
-                fq[u] = fk[u] * (h2f(cur.ng[u]) * kappa);
-                fv[u] = h2f(cur.nv[u]) * wscale;
+                fk[u] = h2f(st.nk[u]) * zscale;
+                fq[u] = fk[u] * (h2f(st.ng[u]) * kappa);
+                fv[u] = h2f(st.nv[u]) * wscale;
             }
 
             // ---- scores for two 16-token tiles
@@ -284,11 +340,11 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                     constexpr int FB = 8 * BK;
                     const int bit = FB * t;
                     uint32_t field;
-                    if constexpr (BK == 4) field = cur.kf[u][t];
+                    if constexpr (BK == 4) field = st.kf[u][t];
                     else {
                         const uint64_t cat = (bit >> 5) + 1 < BK
-                                                 ? ((uint64_t)cur.kf[u][(bit >> 5) + 1] << 32) | cur.kf[u][bit >> 5]
-                                                 : (uint64_t)cur.kf[u][bit >> 5];
+                                                 ? ((uint64_t)st.kf[u][(bit >> 5) + 1] << 32) | st.kf[u][bit >> 5]
+                                                 : (uint64_t)st.kf[u][bit >> 5];
                         field = (uint32_t)(cat >> (bit & 31)) & ((1u << FB) - 1u);
                     }
                     half8_t a;
@@ -305,7 +361,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                     }
                     am = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[t], am, 0, 0, 0);
                     if constexpr (QJL) {
-                        const uint4 sv = slut[(cur.sf[u] >> (8 * t)) & 0xFFu];
+                        const uint4 sv = slut[(st.sf[u] >> (8 * t)) & 0xFFu];
                         aq = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, sv), bq[KS + t], aq,
                                                                     0, 0, 0);
                     }
@@ -316,7 +372,8 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                     const float zm = am[r] + xor8(am[r]);
                     float z = quad_bcast<r>(fk[u]) * zm;
                     if constexpr (QJL) z = fmaf(quad_bcast<r>(fq[u]), aq[r] + xor8(aq[r]), z);
-                    zz[4 * u + r] = (tb + row < w1) ? z : -INFINITY;
+                    if constexpr (decltype(MASK)::value) zz[4 * u + r] = (tb + row < w1) ? z : -INFINITY;
+                    else zz[4 * u + r] = z;
                 });
             }
 
@@ -328,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
             bm = fmaxf(bm, __shfl_xor(bm, 32));
             if (__ballot(bm > M + 8.0f)) {
                 const float nM = fmaxf(M, bm);
-                const float f = exp2f(M - nM);
+                const float f = __builtin_amdgcn_exp2f(M - nM);
                 lsum *= f;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -340,23 +397,33 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
             }
 
             // ---- weights as the A operand (row = head column, K slot = token)
-            half8_t aw;
-            static_for<0, 8>([&](auto ee) {
-                constexpr int e = decltype(ee)::value;
-                const float w = exp2f(zz[e] - M);
-                lsum += w;
-                const float W = w * quad_bcast<e & 3>(fv[e >> 2]);
-                const _Float16 hi = (_Float16)W;
-                aw[e] = col < 8 ? hi : (_Float16)(W - (float)hi);
+            uint32_t awd[4];
+            static_for<0, 4>([&](auto jj) {
+                constexpr int j = decltype(jj)::value;
+                float W[2];
+                static_for<0, 2>([&](auto hh) {
+                    constexpr int e = 2 * j + decltype(hh)::value;
+                    const float w = __builtin_amdgcn_exp2f(zz[e] - M);
+                    lsum += w;
+                    W[decltype(hh)::value] = w * quad_bcast<e & 3>(fv[e >> 2]);
+                });
+                // fp16(W) for head rows, fp16(W - fp16(W)) for remainder rows
+                const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)W[0]);
+                const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)W[1]);
+                uint32_t lw = 0;
+                asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "+v"(lw) : "v"(h0), "v"(W[0]));
+                asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "+v"(lw) : "v"(h1), "v"(W[1]));
+                awd[j] = col < 8 ? (h0 | (h1 << 16)) : lw;
             });
+            const half8_t aw = __builtin_bit_cast(half8_t, awd);
 
             // ---- value codes: lane column = code group, slot e = token 4g+e (tile 0) / 16+4g+e-4 (tile 1)
             uint32_t X[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                if constexpr (BV == 3) X[e] = __builtin_amdgcn_alignbit(cur.x1[e], cur.x0[e], (24 * col) & 31) & 0xFFFFFFu;
-                else if constexpr (BV == 4) X[e] = cur.x0[e];
-                else X[e] = (cur.x0[e] >> ((8 * BV * col) & 31)) & ((1u << (8 * BV)) - 1u);
+                if constexpr (BV == 3) X[e] = __builtin_amdgcn_alignbit(st.x1[e], st.x0[e], (24 * col) & 31) & 0xFFFFFFu;
+                else if constexpr (BV == 4) X[e] = st.x0[e];
+                else X[e] = (st.x0[e] >> ((8 * BV * col) & 31)) & ((1u << (8 * BV)) - 1u);
             }
             if constexpr (BV == 3) {
 #pragma unroll
@@ -365,7 +432,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const uint32_t ia = (X[2 * j] >> (3 * c)) & 7u, ib = (X[2 * j + 1] >> (3 * c)) & 7u;
-                        bw[j] = vlut[ia | (ib << 3)];
+                        bw[j] = vlut[ia | (ib << 3)][lane & 31];
                     }
                     acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, bw), acc[c], 0, 0, 0);
                 }
@@ -386,12 +453,33 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const uint32_t y = (c & 1) ? y1[j] : y0[j];
-                        bw[j] = vlut[(y >> (2 * BV * (c >> 1))) & ((1u << (2 * BV)) - 1u)];
+                        bw[j] = vlut[(y >> (2 * BV * (c >> 1))) & ((1u << (2 * BV)) - 1u)][lane & 31];
                     }
                     acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, bw), acc[c], 0, 0, 0);
                 }
             }
-            cur = nxt;
+        };
+        // full steps (no masking, uniform-base loads, next step in flight),
+        // then at most one partial step with clamped loads and masked scores
+        using Full = std::integral_constant<bool, false>;
+        using Tail = std::integral_constant<bool, true>;
+        const int64_t nfull = w1 > w0 ? (w1 - w0) >> 5 : 0;  // a wave past the chunk's end has none
+        Step<BK, BV> sa, sb;
+        if (nfull > 0) load_full<D, BK, QJL, BV>(sa, base + w0, loff, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
+        int64_t i = 0;
+        for (; i + 2 <= nfull; i += 2) {
+            const int64_t tb = w0 + 32 * i;
+            load_full<D, BK, QJL, BV>(sb, base + tb + 32, loff, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
+            compute(sa, tb, Full{});
+            if (i + 2 < nfull)
+                load_full<D, BK, QJL, BV>(sa, base + tb + 64, loff, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
+            compute(sb, tb + 32, Full{});
+        }
+        if (i < nfull) compute(sa, w0 + 32 * i, Full{});
+        const int64_t tt = w0 + 32 * nfull;
+        if (tt < w1) {
+            load_step<D, BK, QJL, BV>(sa, tt, w1, base, lane, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
+            compute(sa, tt, Tail{});
         }
 
         // ---- per-wave results: sum over row groups, hi rows + lo rows
