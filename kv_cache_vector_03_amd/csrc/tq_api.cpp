@@ -43,6 +43,7 @@ int tq_scores(const tq_quantizer* q, const tq_packed* keys, int64_t n_keys,
     if (!ws || ws_bytes < need)
         return fail(TQ_ERR_WORKSPACE, "tq_scores: workspace %zu bytes < %zu", ws_bytes, need);
     if ((uintptr_t)ws % 256) return fail(TQ_ERR_INVALID, "tq_scores: workspace must be 256-byte aligned");
+    if (q->d == 128) return launch_scores_mfma(q, keys, n_keys, queries, q_dtype, n_q, scores, ws, (hipStream_t)stream);
     float* qr = (float*)ws;
     float* p = (float*)((char*)ws + up256((size_t)n_q * q->d * 4));
     if ((rc = launch_qprep(q, queries, q_dtype, n_q, qr, p, (hipStream_t)stream)) != TQ_OK) return rc;

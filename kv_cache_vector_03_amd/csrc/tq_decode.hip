@@ -42,7 +42,8 @@ __device__ __forceinline__ float quad_bcast(float x)
 }
 
 // Query preparation, grid (stream, k-step t < d/32). Every block rotates the
-// stream's G <= 8 queries (q' = H D q / sqrt(d)); block t then projects them
+// stream's G <= 8 queries (q' = H D q / sqrt(d); rows at or past `total` of
+// the query array count as zero); block t then projects them
 // onto the d/4 rows of S with index = t (mod d/32), one dot product per thread
 // (p = S q'), and writes two score-GEMM B fragments: code k-step t and sign
 // k-step d/32 + t. Column c < 8 carries the fp16 rounding of head c's value,
@@ -51,7 +52,7 @@ __device__ __forceinline__ float quad_bcast(float x)
 // group-major order the key codes arrive in. Arithmetic is fp32: its relative
 // error (~1e-7) is far below what the hi/lo operands carry into the scores.
 template <int D, bool QJL, bool F16>
-__global__ __launch_bounds__(256) void k_qprep_frag(const void* __restrict__ q, int G,
+__global__ __launch_bounds__(256) void k_qprep_frag(const void* __restrict__ q, int G, int64_t total,
                                                     const uint32_t* __restrict__ diag,
                                                     const uint16_t* __restrict__ S,
                                                     half8_t* __restrict__ frags)
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(256) void k_qprep_frag(const void* __restrict__ q, 
         float y[R];
 #pragma unroll
         for (int r = 0; r < R; ++r)
-            y[r] = h < G ? flip(load_elem<F16>(q, (s * G + h) * D + 64 * r + lane), dm[r]) : 0.f;
+            y[r] = h < G && s * G + h < total ? flip(load_elem<F16>(q, (s * G + h) * D + 64 * r + lane), dm[r]) : 0.f;
         fwht_wave<R>(y, lane);
 #pragma unroll
         for (int r = 0; r < R; ++r) qs[h][64 * r + lane] = y[r] * inv_sqrt_d;
@@ -115,6 +116,63 @@ __global__ __launch_bounds__(256) void k_qprep_frag(const void* __restrict__ q, 
             f[ee] = lo ? (_Float16)(val - (float)hi) : hi;
         }
         frags[(s * KSTEPS + (sgn ? KS + tt : tt)) * 64 + l] = f;
+    }
+}
+
+// Key lookup tables of a block: for up to 2-bit codes one entry maps a byte of
+// four codes to four fp16 centroids (klut4), else a field of two codes to two
+// (klut2); slut maps a byte of sign bits to eight fp16 +-1 values.
+template <int BK, bool QJL>
+__device__ void fill_key_luts(uint2* klut4, uint32_t* klut2, uint4* slut, const float* __restrict__ kcent)
+{
+    constexpr bool K4 = BK <= 2;
+    constexpr int KLUT = K4 ? (1 << (4 * BK)) : (1 << (2 * BK));
+    for (int i = threadIdx.x; i < KLUT; i += blockDim.x) {
+        if constexpr (K4) {
+            uint32_t h[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) h[j] = f2h(kcent[(i >> (BK * j)) & ((1 << BK) - 1)]);
+            klut4[i] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        } else {
+            klut2[i] = (uint32_t)f2h(kcent[i & ((1 << BK) - 1)]) | ((uint32_t)f2h(kcent[i >> BK]) << 16);
+        }
+    }
+    if constexpr (QJL)
+        for (int i = threadIdx.x; i < 256; i += blockDim.x) {
+            uint32_t w[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                w[j] = (((i >> (2 * j)) & 1) ? 0x3C00u : 0xBC00u) | ((((i >> (2 * j + 1)) & 1) ? 0x3C00u : 0xBC00u) << 16);
+            slut[i] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+}
+
+// A operand of code group t of a key (8 codes, 8 BK bits at bit 8 BK t of
+// the lane's BK code words) as fp16 centroids.
+template <int BK>
+__device__ __forceinline__ half8_t key_codes_a(const uint32_t (&kf)[BK], int t, const uint2* klut4,
+                                               const uint32_t* klut2)
+{
+    constexpr bool K4 = BK <= 2;
+    constexpr int FB = 8 * BK;
+    const int bit = FB * t;
+    uint32_t field;
+    if constexpr (BK == 4) field = kf[t];
+    else {
+        const uint64_t cat = (bit >> 5) + 1 < BK ? ((uint64_t)kf[(bit >> 5) + 1] << 32) | kf[bit >> 5]
+                                                 : (uint64_t)kf[bit >> 5];
+        field = (uint32_t)(cat >> (bit & 31)) & ((1u << FB) - 1u);
+    }
+    if constexpr (K4) {
+        const uint2 e0 = klut4[field & ((1u << (4 * BK)) - 1u)];
+        const uint2 e1 = klut4[field >> (4 * BK)];
+        const uint32_t wds[4] = {e0.x, e0.y, e1.x, e1.y};
+        return __builtin_bit_cast(half8_t, wds);
+    } else {
+        uint32_t wds[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wds[j] = klut2[(field >> (2 * BK * j)) & ((1u << (2 * BK)) - 1u)];
+        return __builtin_bit_cast(half8_t, wds);
     }
 }
 
@@ -260,24 +318,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
     const LaneOff loff = lane_offsets<D, BK, BV>(lane);
 
     // ---- lookup tables: codes -> fp16 centroids, sign bytes -> +-1 (built once per block)
-    for (int i = tid; i < KLUT; i += 256) {
-        if constexpr (K4) {
-            uint32_t h[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) h[j] = f2h(kcent[(i >> (BK * j)) & ((1 << BK) - 1)]);
-            klut4[i] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-        } else {
-            klut2[i] = (uint32_t)f2h(kcent[i & ((1 << BK) - 1)]) | ((uint32_t)f2h(kcent[i >> BK]) << 16);
-        }
-    }
-    if constexpr (QJL)
-        for (int i = tid; i < 256; i += 256) {
-            uint32_t w[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                w[j] = (((i >> (2 * j)) & 1) ? 0x3C00u : 0xBC00u) | ((((i >> (2 * j + 1)) & 1) ? 0x3C00u : 0xBC00u) << 16);
-            slut[i] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
+    fill_key_luts<BK, QJL>(klut4, klut2, slut, kcent);
     for (int i = tid; i < VLUT * 32; i += 256) {
         const int e = i >> 5;
         vlut[e][i & 31] = (uint32_t)f2h(vcent[e & ((1 << BV) - 1)]) | ((uint32_t)f2h(vcent[e >> BV]) << 16);
@@ -336,29 +377,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                 float4_t am = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int t = 0; t < KS; ++t) {
-                    // code group t of this lane: 8*BK bits at bit 8*BK*t of kf
-                    constexpr int FB = 8 * BK;
-                    const int bit = FB * t;
-                    uint32_t field;
-                    if constexpr (BK == 4) field = st.kf[u][t];
-                    else {
-                        const uint64_t cat = (bit >> 5) + 1 < BK
-                                                 ? ((uint64_t)st.kf[u][(bit >> 5) + 1] << 32) | st.kf[u][bit >> 5]
-                                                 : (uint64_t)st.kf[u][bit >> 5];
-                        field = (uint32_t)(cat >> (bit & 31)) & ((1u << FB) - 1u);
-                    }
-                    half8_t a;
-                    if constexpr (K4) {
-                        const uint2 e0 = klut4[field & ((1u << (4 * BK)) - 1u)];
-                        const uint2 e1 = klut4[field >> (4 * BK)];
-                        const uint32_t wds[4] = {e0.x, e0.y, e1.x, e1.y};
-                        a = __builtin_bit_cast(half8_t, wds);
-                    } else {
-                        uint32_t wds[4];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) wds[j] = klut2[(field >> (2 * BK * j)) & ((1u << (2 * BK)) - 1u)];
-                        a = __builtin_bit_cast(half8_t, wds);
-                    }
+                    const half8_t a = key_codes_a<BK>(st.kf[u], t, klut4, klut2);
                     am = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[t], am, 0, 0, 0);
                     if constexpr (QJL) {
                         const uint4 sv = slut[(st.sf[u] >> (8 * t)) & 0xFFu];
@@ -554,6 +573,117 @@ void launch_bv(int bv, const tq_packed* k, const tq_packed* v, int64_t ns, int64
     }
 }
 
+// Score fragments of `tiles` groups of G query rows (rows at or past `total`
+// count as zero).
+void launch_qprep_frag(const tq_quantizer* qk, const void* q, int q_dtype, int64_t tiles, int G, int64_t total,
+                       half8_t* frags, hipStream_t s)
+{
+    constexpr int D = 128;
+    const bool qjl = qk->qjl_m != 0;
+    const dim3 pg((unsigned)tiles, (unsigned)(D / 32)), pb(256);
+    if (q_dtype == TQ_F16) {
+        if (qjl) hipLaunchKernelGGL((k_qprep_frag<D, true, true>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags);
+        else hipLaunchKernelGGL((k_qprep_frag<D, false, true>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags);
+    } else {
+        if (qjl) hipLaunchKernelGGL((k_qprep_frag<D, true, false>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags);
+        else hipLaunchKernelGGL((k_qprep_frag<D, false, false>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags);
+    }
+}
+
+// Estimated inner products (the score formula of "[Benchmark] TurboQuant
+// 實測：KV Cache 3-bit 壓縮，真的零損失？", section "TurboQuant 是什麼：30 秒懶人包")
+// for d = 128 on MFMA, with the same exact operands as the decode step: a
+// 16-key tile (rows) against a tile of 8 queries whose fp32 rotated values and
+// projections are split into fp16 hi and lo columns. Grid (key-tile groups,
+// query tiles); each wave walks 16-key tiles. scores[q][key], fp32.
+template <int D, int BK, bool QJL>
+__global__ __launch_bounds__(256) void k_scores_mfma(const uint32_t* __restrict__ kcodes,
+                                                     const uint32_t* __restrict__ ksigns,
+                                                     const uint16_t* __restrict__ knorm,
+                                                     const uint16_t* __restrict__ krnorm, int64_t N,
+                                                     const half8_t* __restrict__ frags, int64_t n_q,
+                                                     const float* __restrict__ kcent, float* __restrict__ scores)
+{
+    static_assert(D == 128, "MFMA scores are laid out for d = 128");
+    constexpr int KS = D / 32, KSTEPS = KS * (QJL ? 2 : 1);
+    constexpr int KW = BK * D / 32, SWN = D / 32;
+    constexpr bool K4 = BK <= 2;
+    constexpr int KLUT = K4 ? (1 << (4 * BK)) : (1 << (2 * BK));
+    constexpr float kappa = 1.2533141373155003f / D;  // sqrt(pi/2) / m
+    __shared__ uint2 klut4[K4 ? KLUT : 1];
+    __shared__ uint32_t klut2[K4 ? 1 : KLUT];
+    __shared__ uint4 slut[QJL ? 256 : 1];
+    fill_key_luts<BK, QJL>(klut4, klut2, slut, kcent);
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 15, g = lane >> 4;
+    const int64_t n_qt = (n_q + 7) / 8, n_kt = (N + 15) / 16;
+    for (int64_t qt = blockIdx.y; qt < n_qt; qt += gridDim.y) {
+        half8_t bq[KSTEPS];
+#pragma unroll
+        for (int k = 0; k < KSTEPS; ++k) bq[k] = frags[(qt * KSTEPS + k) * 64 + lane];
+        const int64_t qrow = qt * 8 + (col & 7);
+        for (int64_t kt = (int64_t)blockIdx.x * 4 + wid; kt < n_kt; kt += (int64_t)gridDim.x * 4) {
+            const int64_t k0 = kt * 16;
+            const int64_t ka = min(k0 + col, N - 1);  // A row of this lane (clamped)
+            uint32_t kf[BK];
+#pragma unroll
+            for (int w = 0; w < BK; ++w) kf[w] = kcodes[ka * KW + BK * g + w];
+            const uint32_t sf = QJL ? ksigns[ka * SWN + g] : 0u;
+            float fk[4], fq[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t kr = min(k0 + 4 * g + r, N - 1);
+                fk[r] = h2f(knorm[kr]);
+                fq[r] = QJL ? fk[r] * h2f(krnorm[kr]) * kappa : 0.f;
+            }
+            float4_t am = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < KS; ++t) {
+                am = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_codes_a<BK>(kf, t, klut4, klut2), bq[t], am, 0, 0, 0);
+                if constexpr (QJL)
+                    aq = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, slut[(sf >> (8 * t)) & 0xFFu]),
+                                                                bq[KS + t], aq, 0, 0, 0);
+            }
+            // hi + lo columns, then row (key) 4 g + r of query column col & 7
+            float z[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                z[r] = fk[r] * (am[r] + xor8(am[r]));
+                if constexpr (QJL) z[r] = fmaf(fq[r], aq[r] + xor8(aq[r]), z[r]);
+            }
+            if (col < 8 && qrow < n_q) {
+                float* dst = scores + qrow * N + k0 + 4 * g;
+                if ((N & 3) == 0 && k0 + 4 * g + 3 < N) {
+                    *reinterpret_cast<float4*>(dst) = make_float4(z[0], z[1], z[2], z[3]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (k0 + 4 * g + r < N) dst[r] = z[r];
+                }
+            }
+        }
+    }
+}
+
+template <int D, int BK, bool QJL>
+void launch_scores_k(const tq_packed* k, int64_t n_keys, const half8_t* fr, int64_t n_q, const tq_quantizer* q,
+                     float* scores, hipStream_t s)
+{
+    auto kern = k_scores_mfma<D, BK, QJL>;
+    const int64_t n_kt = (n_keys + 15) / 16, n_qt = (n_q + 7) / 8;
+    // enough 4-wave blocks along the keys to fill the device twice over with all query tiles
+    int64_t gx = (n_kt + 3) / 4;
+    const int64_t want = (int64_t)device_cus() * 8;
+    const int64_t per_q = (want + n_qt - 1) / n_qt;
+    if (gx > per_q) gx = per_q < 1 ? 1 : per_q;
+    const dim3 grid((unsigned)gx, (unsigned)(n_qt < 65535 ? n_qt : 65535));
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, k->codes, k->signs, k->norm, k->rnorm, n_keys, fr, n_q,
+                       q->centroids, scores);
+}
+
 }  // namespace
 
 int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
@@ -563,15 +693,7 @@ int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_
 {
     constexpr int D = 128;
     const bool qjl = qk->qjl_m != 0;
-    half8_t* fw = (half8_t*)frags;
-    const dim3 pg((unsigned)n_streams, (unsigned)(D / 32)), pb(256);
-    if (q_dtype == TQ_F16) {
-        if (qjl) hipLaunchKernelGGL((k_qprep_frag<D, true, true>), pg, pb, 0, s, q, G, qk->diag_signs, qk->S, fw);
-        else hipLaunchKernelGGL((k_qprep_frag<D, false, true>), pg, pb, 0, s, q, G, qk->diag_signs, qk->S, fw);
-    } else {
-        if (qjl) hipLaunchKernelGGL((k_qprep_frag<D, true, false>), pg, pb, 0, s, q, G, qk->diag_signs, qk->S, fw);
-        else hipLaunchKernelGGL((k_qprep_frag<D, false, false>), pg, pb, 0, s, q, G, qk->diag_signs, qk->S, fw);
-    }
+    launch_qprep_frag(qk, q, q_dtype, n_streams, G, n_streams * G, (half8_t*)frags, s);
     const half8_t* fr = (const half8_t*)frags;
     switch (qk->mse_bits) {
         case 1: qjl ? launch_bv<D, 1, true>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
@@ -585,6 +707,25 @@ int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "tq_decode_attn: %s", hipGetErrorString(e));
+    return TQ_OK;
+}
+
+int launch_scores_mfma(const tq_quantizer* q, const tq_packed* k, int64_t n_keys, const void* queries,
+                       int q_dtype, int64_t n_q, float* scores, void* frags, hipStream_t s)
+{
+    constexpr int D = 128;
+    const int64_t n_qt = (n_q + 7) / 8;
+    launch_qprep_frag(q, queries, q_dtype, n_qt, 8, n_q, (half8_t*)frags, s);
+    const half8_t* fr = (const half8_t*)frags;
+    const bool qjl = q->qjl_m != 0;
+    switch (q->mse_bits) {
+        case 1: qjl ? launch_scores_k<D, 1, true>(k, n_keys, fr, n_q, q, scores, s) : launch_scores_k<D, 1, false>(k, n_keys, fr, n_q, q, scores, s); break;
+        case 2: qjl ? launch_scores_k<D, 2, true>(k, n_keys, fr, n_q, q, scores, s) : launch_scores_k<D, 2, false>(k, n_keys, fr, n_q, q, scores, s); break;
+        case 3: qjl ? launch_scores_k<D, 3, true>(k, n_keys, fr, n_q, q, scores, s) : launch_scores_k<D, 3, false>(k, n_keys, fr, n_q, q, scores, s); break;
+        default: qjl ? launch_scores_k<D, 4, true>(k, n_keys, fr, n_q, q, scores, s) : launch_scores_k<D, 4, false>(k, n_keys, fr, n_q, q, scores, s); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "tq_scores: %s", hipGetErrorString(e));
     return TQ_OK;
 }
 

@@ -179,9 +179,19 @@ int check_dense(const void* p, int dtype, const char* who, const char* what)
 // workspace layout helpers (sizes in bytes, each region 256-byte aligned)
 static size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+size_t scores_frag_bytes(const tq_quantizer* q, int64_t n_q)
+{
+    // d = 128: per tile of 8 queries, d/32 code and (QJL) d/32 sign k-steps of
+    // 64 lanes x 16 bytes
+    const size_t ksteps = (size_t)(q->d / 32) * (q->qjl_m ? 2 : 1);
+    return up256((size_t)((n_q + 7) / 8) * ksteps * 64 * 16);
+}
+
 size_t scores_ws(const tq_quantizer* q, int64_t n_q)
 {
-    // prepared queries: fp32 q' [n_q][d] and p = S q' [n_q][m]
+    // d = 128: MFMA query fragments; else prepared queries: fp32 q' [n_q][d]
+    // and p = S q' [n_q][m]
+    if (q->d == 128) return scores_frag_bytes(q, n_q);
     return up256((size_t)n_q * q->d * 4) + up256((size_t)n_q * (q->qjl_m ? q->qjl_m : 1) * 4);
 }
 

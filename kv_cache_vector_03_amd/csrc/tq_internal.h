@@ -19,6 +19,7 @@ int check_packed(const tq_quantizer* q, const tq_packed* p, const char* who, con
 int check_dense(const void* p, int dtype, const char* who, const char* what);
 
 size_t scores_ws(const tq_quantizer* q, int64_t n_q);
+size_t scores_frag_bytes(const tq_quantizer* q, int64_t n_q);
 
 // Decode-attention work split and workspace layout (offsets in bytes from
 // the workspace base, each 256-byte aligned).
@@ -57,6 +58,9 @@ int launch_dequantize(const tq_quantizer* q, const tq_packed* in, int64_t n, int
 int launch_decode(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
                   const tq_packed* v, int64_t n_streams, int64_t T, int G, const void* q, int q_dtype,
                   const DecodePlan& plan, void* ws, float scale, float* out, hipStream_t s);
+// d = 128: query fragments into `frags` (scores_frag_bytes(q, n_q)), then the MFMA score kernel
+int launch_scores_mfma(const tq_quantizer* q, const tq_packed* k, int64_t n_keys, const void* queries,
+                       int q_dtype, int64_t n_q, float* scores, void* frags, hipStream_t s);
 int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
                        const tq_packed* v, int64_t n_streams, int64_t T, int G, const void* q,
                        int q_dtype, float zscale, void* frags, float* parts, int n_chunks, int tc,
