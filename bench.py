@@ -220,6 +220,8 @@ def main():
     }
 
     result["small_keyset"] = small_keyset(tq, qk, dev)
+    if args.workload == "128k":
+        result["prefill_scores"] = prefill_scores(tq, qk, units[0]["PK"], T, dev)
 
     if not args.no_cpu_baseline:
         nb = args.cpu_batches or (5 if args.workload == "128k" else 8)
@@ -290,6 +292,40 @@ def small_keyset(tq, qk, dev, reps=50):
         out[name + "_us"] = round(a.elapsed_time(b) / reps * 1e3, 2)
     out["page_gb10_ms"] = {"quantize_8192_keys": 31.04, "scores_64x8192": 11.16}
     return out
+
+
+def prefill_scores(tq, qk, pk, T, dev, n_q=2048, reps=5):
+    """Multi-query scoring at prefill scale: a 256-token chunk of queries for
+    one KV head (256 x 8 query heads = 2048 queries, seeded N(0, 1) fp16)
+    against that head's whole compressed 128K prefix (the first stream of a
+    quantized layer), scores[2048][131072] in fp32 (1 GiB). Reported as
+    scores/s, output GB/s and the MFMA rate it implies (1024 executed flop
+    per score: eight 16x16x32 fp16 MFMAs per 8-query x 16-key tile)."""
+    import numpy as np
+    import torch
+    import synth
+    keys = tq.Packed(pk.codes[:T], pk.signs[:T], pk.norm[:T], pk.rnorm[:T])
+    qh = synth.to_f16(synth.normals(97, synth.ROLE_QUERY, np.arange(n_q * qk.d)).reshape(n_q, qk.d))
+    q = torch.from_numpy(qh).to(dev)
+    scores = torch.empty((n_q, T), dtype=torch.float32, device=dev)
+    ws = tq.workspace(tq.tq_workspace_size(tq.TQ_OP_SCORES, qk, n_q, T), dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        tq.tq_scores(qk, keys, T, q, scores, ws=ws)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        tq.tq_scores(qk, keys, T, q, scores, ws=ws)
+    b.record(stream)
+    torch.cuda.synchronize()
+    s = a.elapsed_time(b) / reps * 1e-3
+    n = n_q * T
+    out_bytes = n * 4
+    in_bytes = T * packed_bytes_per_vector(qk.d, qk.mse_bits, True) + n_q * qk.d * 2
+    return {"queries": n_q, "keys": T, "us": round(s * 1e6, 1), "scores_per_s": round(n / s, 1),
+            "GB_per_s": round((out_bytes + in_bytes) / s / 1e9, 1),
+            "frac_hbm_peak": round((out_bytes + in_bytes) / s / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_TFLOP_per_s": round(n * 1024 / s / 1e12, 1)}
 
 
 def calibrate_copy():

@@ -593,16 +593,22 @@ void launch_qprep_frag(const tq_quantizer* qk, const void* q, int q_dtype, int64
 // Estimated inner products (the score formula of "[Benchmark] TurboQuant
 // 實測：KV Cache 3-bit 壓縮，真的零損失？", section "TurboQuant 是什麼：30 秒懶人包")
 // for d = 128 on MFMA, with the same exact operands as the decode step: a
-// 16-key tile (rows) against a tile of 8 queries whose fp32 rotated values and
-// projections are split into fp16 hi and lo columns. Grid (key-tile groups,
-// query tiles); each wave walks 16-key tiles. scores[q][key], fp32.
+// 16-key tile (rows) against tiles of 8 queries whose fp32 rotated values and
+// projections are split into fp16 hi and lo columns. A wave holds the
+// fragments of kScoreQT query tiles and walks 16-key tiles, building each
+// tile's key operands once for all of them and fetching the next tile's
+// packed keys while it works. Grid (key-tile groups, query-tile groups);
+// scores[q][key], fp32.
+constexpr int kScoreQT = 4;
+
 template <int D, int BK, bool QJL>
-__global__ __launch_bounds__(256) void k_scores_mfma(const uint32_t* __restrict__ kcodes,
-                                                     const uint32_t* __restrict__ ksigns,
-                                                     const uint16_t* __restrict__ knorm,
-                                                     const uint16_t* __restrict__ krnorm, int64_t N,
-                                                     const half8_t* __restrict__ frags, int64_t n_q,
-                                                     const float* __restrict__ kcent, float* __restrict__ scores)
+__global__ __launch_bounds__(256, 2) void k_scores_mfma(const uint32_t* __restrict__ kcodes,
+                                                        const uint32_t* __restrict__ ksigns,
+                                                        const uint16_t* __restrict__ knorm,
+                                                        const uint16_t* __restrict__ krnorm, int64_t N,
+                                                        const half8_t* __restrict__ frags, int64_t n_q,
+                                                        const float* __restrict__ kcent,
+                                                        float* __restrict__ scores)
 {
     static_assert(D == 128, "MFMA scores are laid out for d = 128");
     constexpr int KS = D / 32, KSTEPS = KS * (QJL ? 2 : 1);
@@ -619,51 +625,86 @@ __global__ __launch_bounds__(256) void k_scores_mfma(const uint32_t* __restrict_
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15, g = lane >> 4;
-    const int64_t n_qt = (n_q + 7) / 8, n_kt = (N + 15) / 16;
-    for (int64_t qt = blockIdx.y; qt < n_qt; qt += gridDim.y) {
-        half8_t bq[KSTEPS];
+    const int64_t n_qt = (n_q + 7) / 8, n_qg = (n_qt + kScoreQT - 1) / kScoreQT, n_kt = (N + 15) / 16;
+    // packed inputs of one key tile for this lane: A row ka = k0 + col (clamped),
+    // norms of rows k0 + 4 g + r (clamped)
+    struct KT {
+        uint32_t kf[BK];
+        uint32_t sf;
+        uint16_t nk[4], ng[4];
+    };
+    auto load_kt = [&](KT& t, int64_t k0) {
+        const int64_t ka = min(k0 + col, N - 1);
 #pragma unroll
-        for (int k = 0; k < KSTEPS; ++k) bq[k] = frags[(qt * KSTEPS + k) * 64 + lane];
-        const int64_t qrow = qt * 8 + (col & 7);
-        for (int64_t kt = (int64_t)blockIdx.x * 4 + wid; kt < n_kt; kt += (int64_t)gridDim.x * 4) {
+        for (int w = 0; w < BK; ++w) t.kf[w] = kcodes[ka * KW + BK * g + w];
+        t.sf = QJL ? ksigns[ka * SWN + g] : 0u;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t kr = min(k0 + 4 * g + r, N - 1);
+            t.nk[r] = knorm[kr];
+            t.ng[r] = QJL ? krnorm[kr] : (uint16_t)0;
+        }
+    };
+    for (int64_t qg = blockIdx.y; qg < n_qg; qg += gridDim.y) {
+        half8_t bq[kScoreQT][KSTEPS];
+#pragma unroll
+        for (int j = 0; j < kScoreQT; ++j) {
+            const int64_t qt = min(qg * kScoreQT + j, n_qt - 1);  // past the end: repeat, not stored
+#pragma unroll
+            for (int k = 0; k < KSTEPS; ++k) bq[j][k] = frags[(qt * KSTEPS + k) * 64 + lane];
+        }
+        // the wave takes key tiles in adjacent pairs (2 pr, 2 pr + 1), so the two
+        // 64-byte halves of each 128-byte line of a score row are written back to back
+        const int64_t pstep = (int64_t)gridDim.x * 4;
+        auto next_kt = [&](int64_t kt) { return (kt & 1) ? kt - 1 + 2 * pstep : kt + 1; };
+        int64_t kt = 2 * ((int64_t)blockIdx.x * 4 + wid);
+        KT cur;
+        if (kt < n_kt) load_kt(cur, kt * 16);
+        for (; kt < n_kt; kt = next_kt(kt)) {
             const int64_t k0 = kt * 16;
-            const int64_t ka = min(k0 + col, N - 1);  // A row of this lane (clamped)
-            uint32_t kf[BK];
+            KT nxt;
+            if (next_kt(kt) < n_kt) load_kt(nxt, next_kt(kt) * 16);
+            half8_t ac[KS], as[QJL ? KS : 1];
 #pragma unroll
-            for (int w = 0; w < BK; ++w) kf[w] = kcodes[ka * KW + BK * g + w];
-            const uint32_t sf = QJL ? ksigns[ka * SWN + g] : 0u;
+            for (int t = 0; t < KS; ++t) {
+                ac[t] = key_codes_a<BK>(cur.kf, t, klut4, klut2);
+                if constexpr (QJL) as[t] = __builtin_bit_cast(half8_t, slut[(cur.sf >> (8 * t)) & 0xFFu]);
+            }
             float fk[4], fq[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t kr = min(k0 + 4 * g + r, N - 1);
-                fk[r] = h2f(knorm[kr]);
-                fq[r] = QJL ? fk[r] * h2f(krnorm[kr]) * kappa : 0.f;
+                fk[r] = h2f(cur.nk[r]);
+                fq[r] = QJL ? fk[r] * h2f(cur.ng[r]) * kappa : 0.f;
             }
-            float4_t am = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < KS; ++t) {
-                am = __builtin_amdgcn_mfma_f32_16x16x32_f16(key_codes_a<BK>(kf, t, klut4, klut2), bq[t], am, 0, 0, 0);
-                if constexpr (QJL)
-                    aq = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, slut[(sf >> (8 * t)) & 0xFFu]),
-                                                                bq[KS + t], aq, 0, 0, 0);
-            }
-            // hi + lo columns, then row (key) 4 g + r of query column col & 7
-            float z[4];
+            for (int j = 0; j < kScoreQT; ++j) {
+                float4_t am = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                z[r] = fk[r] * (am[r] + xor8(am[r]));
-                if constexpr (QJL) z[r] = fmaf(fq[r], aq[r] + xor8(aq[r]), z[r]);
-            }
-            if (col < 8 && qrow < n_q) {
-                float* dst = scores + qrow * N + k0 + 4 * g;
-                if ((N & 3) == 0 && k0 + 4 * g + 3 < N) {
-                    *reinterpret_cast<float4*>(dst) = make_float4(z[0], z[1], z[2], z[3]);
-                } else {
+                for (int t = 0; t < KS; ++t) {
+                    am = __builtin_amdgcn_mfma_f32_16x16x32_f16(ac[t], bq[j][t], am, 0, 0, 0);
+                    if constexpr (QJL) aq = __builtin_amdgcn_mfma_f32_16x16x32_f16(as[t], bq[j][KS + t], aq, 0, 0, 0);
+                }
+                // hi + lo columns, then row (key) 4 g + r of query column col & 7
+                float z[4];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (k0 + 4 * g + r < N) dst[r] = z[r];
+                for (int r = 0; r < 4; ++r) {
+                    z[r] = fk[r] * (am[r] + xor8(am[r]));
+                    if constexpr (QJL) z[r] = fmaf(fq[r], aq[r] + xor8(aq[r]), z[r]);
+                }
+                const int64_t qrow = (qg * kScoreQT + j) * 8 + (col & 7);
+                if (col < 8 && qrow < n_q) {
+                    float* dst = scores + qrow * N + k0 + 4 * g;
+                    if ((N & 3) == 0 && k0 + 4 * g + 3 < N) {
+                        // write-once output: streamed past the caches
+                        __builtin_nontemporal_store(float4_t{z[0], z[1], z[2], z[3]}, reinterpret_cast<float4_t*>(dst));
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (k0 + 4 * g + r < N) dst[r] = z[r];
+                    }
                 }
             }
+            cur = nxt;
         }
     }
 }
@@ -673,13 +714,13 @@ void launch_scores_k(const tq_packed* k, int64_t n_keys, const half8_t* fr, int6
                      float* scores, hipStream_t s)
 {
     auto kern = k_scores_mfma<D, BK, QJL>;
-    const int64_t n_kt = (n_keys + 15) / 16, n_qt = (n_q + 7) / 8;
-    // enough 4-wave blocks along the keys to fill the device twice over with all query tiles
-    int64_t gx = (n_kt + 3) / 4;
-    const int64_t want = (int64_t)device_cus() * 8;
-    const int64_t per_q = (want + n_qt - 1) / n_qt;
+    const int64_t n_kt = (n_keys + 15) / 16, n_qg = ((n_q + 7) / 8 + kScoreQT - 1) / kScoreQT;
+    // about two resident 4-wave blocks per compute unit in all
+    int64_t gx = (n_kt + 7) / 8;
+    const int64_t want = (int64_t)device_cus() * 2;
+    const int64_t per_q = (want + n_qg - 1) / n_qg;
     if (gx > per_q) gx = per_q < 1 ? 1 : per_q;
-    const dim3 grid((unsigned)gx, (unsigned)(n_qt < 65535 ? n_qt : 65535));
+    const dim3 grid((unsigned)gx, (unsigned)(n_qg < 65535 ? n_qg : 65535));
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, k->codes, k->signs, k->norm, k->rnorm, n_keys, fr, n_q,
                        q->centroids, scores);
 }

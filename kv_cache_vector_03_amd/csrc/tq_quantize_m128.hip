@@ -368,7 +368,8 @@ __device__ __forceinline__ void code_batch(const float4_t (&acc)[2][4], float ss
 }
 
 // Store lane (v, q)'s code words of vector vec and, from lanes q = 0, its norm
-// (and residual norm), if vec < n.
+// (and residual norm), if vec < n. The packed output is written once and not
+// read back by this launch, so it is streamed past the caches.
 template <int B, bool QJL>
 __device__ __forceinline__ void store_coded(const uint32_t (&W)[B], float nrm, float gam, int64_t vec, int64_t n,
                                             int q, uint32_t* __restrict__ codes, uint16_t* __restrict__ norm,
@@ -377,17 +378,19 @@ __device__ __forceinline__ void store_coded(const uint32_t (&W)[B], float nrm, f
     constexpr int CW = B * kD / 32;  // code words per vector
     if (vec < n) {
         uint32_t* dst = codes + vec * CW + B * q;
+        typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+        typedef uint32_t u4v __attribute__((ext_vector_type(4)));
         if constexpr (B == 2) {
-            *reinterpret_cast<uint2*>(dst) = make_uint2(W[0], W[1]);
+            __builtin_nontemporal_store(u2v{W[0], W[1]}, reinterpret_cast<u2v*>(dst));
         } else if constexpr (B == 4) {
-            *reinterpret_cast<uint4*>(dst) = make_uint4(W[0], W[1], W[2], W[3]);
+            __builtin_nontemporal_store(u4v{W[0], W[1], W[2], W[3]}, reinterpret_cast<u4v*>(dst));
         } else {
 #pragma unroll
-            for (int w = 0; w < B; ++w) dst[w] = W[w];
+            for (int w = 0; w < B; ++w) __builtin_nontemporal_store(W[w], dst + w);
         }
         if (q == 0) {
-            norm[vec] = f2h(nrm);
-            if constexpr (QJL) rnorm[vec] = f2h(gam);
+            __builtin_nontemporal_store(f2h(nrm), norm + vec);
+            if constexpr (QJL) __builtin_nontemporal_store(f2h(gam), rnorm + vec);
         }
     }
 }
@@ -528,8 +531,8 @@ __global__ __launch_bounds__(256) void k_quantize_keys_m128(const uint16_t* __re
             swA = shift_signs(shift_signs(swA, pA1), pA0);
             swB = shift_signs(shift_signs(swB, pB1), pB0);
         }
-        if (base + v < n) signs[(base + v) * 4 + q] = swA;
-        if (baseB + v < n) signs[(baseB + v) * 4 + q] = swB;
+        if (base + v < n) __builtin_nontemporal_store(swA, signs + (base + v) * 4 + q);
+        if (baseB + v < n) __builtin_nontemporal_store(swB, signs + (baseB + v) * 4 + q);
     }
 }
 

@@ -169,6 +169,46 @@ def test_scores_shapes(d, bits, m, n_q, n_keys):
     check_close(sc.cpu().numpy(), oracle.scores(qo, to_oracle_packed(qo, p.to_host()), q.astype(np.float64)))
 
 
+@pytest.mark.parametrize("bits,m", [(2, 128), (3, 0), (1, 128)])
+def test_scores_many_query_tiles_full(bits, m):
+    """Ragged query tiles (203 = 25 x 8 + 3) against a ragged key count (not a
+    multiple of 16 or 4); every score is checked."""
+    tq = tqmod()
+    d, n_q, n_keys = 128, 203, 20011
+    qg, qo = quantizers(d, bits, m)
+    x = synth.to_f16(synth.normals(29, synth.ROLE_DATA_K, np.arange(n_keys * d)).reshape(n_keys, d))
+    q = synth.to_f16(synth.normals(29, synth.ROLE_QUERY, np.arange(n_q * d)).reshape(n_q, d))
+    p = gpu_quantize(qg, x)
+    sc = torch.empty((n_q, n_keys), dtype=torch.float32, device=DEV)
+    tq.tq_scores(qg, p, n_keys, torch.from_numpy(q).to(DEV), sc)
+    torch.cuda.synchronize()
+    check_close(sc.cpu().numpy(), oracle.scores(qo, to_oracle_packed(qo, p.to_host()), q.astype(np.float64)))
+
+
+def test_scores_prefill_scale_sampled():
+    """The prefill-scale shape the benchmark times: 2048 queries against a
+    131072-key compressed prefix (1 GiB of scores). Checked on whole sampled
+    query rows and on sampled key columns over all queries."""
+    tq = tqmod()
+    d, n_q, n_keys = 128, 2048, 131072
+    qg, qo = quantizers(d, 2, 128)
+    x = torch.randn((n_keys, d), generator=torch.Generator().manual_seed(31)).to(torch.float16).to(DEV)
+    q = synth.to_f16(synth.normals(31, synth.ROLE_QUERY, np.arange(n_q * d)).reshape(n_q, d))
+    p = tq.Packed.empty(qg, n_keys, DEV)
+    tq.tq_quantize(qg, x, p)
+    sc = torch.empty((n_q, n_keys), dtype=torch.float32, device=DEV)
+    tq.tq_scores(qg, p, n_keys, torch.from_numpy(q).to(DEV), sc)
+    torch.cuda.synchronize()
+    host = to_oracle_packed(qo, p.to_host())
+    rows = np.array([0, 7, 8, 1000, 2047])
+    ref_rows = oracle.scores(qo, host, q[rows].astype(np.float64))
+    check_close(sc[torch.from_numpy(rows).to(DEV)].cpu().numpy(), ref_rows, what="sampled query rows")
+    cols = np.unique(np.linspace(0, n_keys - 1, 48).astype(np.int64))
+    ref_cols = oracle.scores(qo, host.take(cols), q.astype(np.float64))
+    check_close(sc[:, torch.from_numpy(cols).to(DEV)].cpu().numpy(), ref_cols, what="sampled key columns")
+    del sc
+
+
 @pytest.mark.parametrize("d,bits,m", [(64, 2, 64), (128, 2, 128), (128, 4, 0), (256, 3, 256)])
 @pytest.mark.parametrize("include_qjl", [True, False])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.float16])
