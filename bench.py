@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="override layer count (debug)")
     ap.add_argument("--cpu-batches", type=int, default=0,
                     help="batches the oracle baseline runs on (default 5 for 128k, 8 for 8k)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the small-keyset and prefill-scale score measurements")
+    ap.add_argument("--scores-only", action="store_true",
+                    help="only the small-keyset and prefill-scale score measurements (one JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (profiler byte-counter calibration)")
     return ap.parse_args()
@@ -87,6 +91,9 @@ def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.scores_only:
+        scores_only()
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark measures the data-parallel path on one GPU; "
@@ -219,9 +226,10 @@ def main():
         "setup_s": round(t_gen, 2),
     }
 
-    result["small_keyset"] = small_keyset(tq, qk, dev)
-    if args.workload == "128k":
-        result["prefill_scores"] = prefill_scores(tq, qk, units[0]["PK"], T, dev)
+    if not args.no_extras:
+        result["small_keyset"] = small_keyset(tq, qk, dev)
+        if args.workload == "128k":
+            result["prefill_scores"] = prefill_scores(tq, qk, units[0]["PK"], T, dev)
 
     if not args.no_cpu_baseline:
         nb = args.cpu_batches or (5 if args.workload == "128k" else 8)
@@ -326,6 +334,29 @@ def prefill_scores(tq, qk, pk, T, dev, n_q=2048, reps=5):
             "GB_per_s": round((out_bytes + in_bytes) / s / 1e9, 1),
             "frac_hbm_peak": round((out_bytes + in_bytes) / s / 1e9 / HBM_PEAK_GBS, 4),
             "mfma_TFLOP_per_s": round(n * 1024 / s / 1e12, 1)}
+
+
+def scores_only():
+    """The two score workloads on their own: the small keyset, and the
+    prefill-scale scores over one stream of a quantized 128K layer (layer 0,
+    KV head 0, quantized here)."""
+    import torch
+    import kv_cache_vector_03_amd as tq
+    import synth
+    from synth import gpu as sgpu
+    from synth import workloads as W
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = W.CONFIG5
+    d, T = cfg.d, cfg.tokens
+    diag_k, S, _ = W.quantizer_inputs(d)
+    qk = tq.Quantizer(d, cfg.k_mse_bits, d, diag_k, S, dev)
+    per = cfg.kv_heads * T
+    K = torch.empty((per, d), dtype=torch.float16, device=dev)
+    W.kv_layer_device(cfg, 0, synth.ROLE_DATA_K, K, sgpu.scales_to_device(W.kv_seed_scales(cfg, 0, synth.ROLE_DATA_K), dev))
+    pk = tq.Packed.empty(qk, T, dev)
+    tq.tq_quantize(qk, K[:T], pk)
+    print(json.dumps({"small_keyset": small_keyset(tq, qk, dev), "prefill_scores": prefill_scores(tq, qk, pk, T, dev)}))
 
 
 def calibrate_copy():
