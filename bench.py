@@ -227,6 +227,8 @@ def main():
     }
 
     if not args.no_extras:
+        result["decode_step"] = decode_step(tq, qk, qv, units, T, G, d, kern["decode_attn"]["us_per_launch"],
+                                            kb + vb, dev)
         result["small_keyset"] = small_keyset(tq, qk, dev)
         if args.workload == "128k":
             result["prefill_scores"] = prefill_scores(tq, qk, units[0]["PK"], T, dev)
@@ -300,6 +302,43 @@ def small_keyset(tq, qk, dev, reps=50):
         out[name + "_us"] = round(a.elapsed_time(b) / reps * 1e3, 2)
     out["page_gb10_ms"] = {"quantize_8192_keys": 31.04, "scores_64x8192": 11.16}
     return out
+
+
+def decode_step(tq, qk, qv, units, T, G, d, attn_us, tok_bytes, dev, passes=3):
+    """The fused append + attend step (tq_decode_step) on the same caches: each
+    stream's last token is re-quantized from its fp16 K and V into slot T - 1
+    (the append), then the attention runs over all T tokens. Reported per
+    call (one call per batch, as decode_attn), beside decode_attn alone."""
+    import torch
+    apps = []
+    for u in units:
+        ns = u["ns"]
+        apps.append((u["K"].view(ns, T, d)[:, T - 1].contiguous(), u["V"].view(ns, T, d)[:, T - 1].contiguous()))
+    max_ns = max(u["ns"] for u in units)
+    ws = tq.workspace(tq.tq_workspace_size(tq.TQ_OP_DECODE_ATTN, qk, max_ns, T, G), dev)
+    stream = torch.cuda.current_stream()
+
+    def one_pass(ev):
+        for u, (kn, vn) in zip(units, apps):
+            a = b = None
+            if ev is not None:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+            tq.tq_decode_step(qk, qv, u["PK"], u["PV"], u["ns"], T - 1, T, G, kn, vn, u["Q"], u["out"], ws=ws)
+            if ev is not None:
+                b.record(stream)
+                ev.append((a, b))
+    one_pass(None)
+    ev = []
+    for _ in range(passes):
+        one_pass(ev)
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e3
+    ns = units[0]["ns"]
+    alg = ns * T * tok_bytes + ns * G * d * 6 + ns * 2 * d * 2
+    return {"us_per_launch": round(us, 2), "decode_attn_us_per_launch": attn_us,
+            "append_overhead_us": round(us - attn_us, 2), "GB_per_s": round(alg / (us * 1e-6) / 1e9, 1),
+            "note": "append of one new token per stream fused into the decode launch"}
 
 
 def prefill_scores(tq, qk, pk, T, dev, n_q=2048, reps=5):

@@ -164,6 +164,29 @@ int tq_decode_attn(const tq_quantizer* qk, const tq_quantizer* qv,
                    void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * tq_decode_step -- append one token to every stream's compressed cache, then
+ * one decode step of attention over the grown caches: the per-token
+ * quantization that generation pays ("Google把32B模型壓到5GB顯存，實測后我發現3個坑",
+ * section "結果：省顯存是真的，慢也是真的") fused into the decode step.
+ * The caches hold stream s at packed vectors s*cap .. s*cap + cap - 1, with
+ * tokens 0..T-1 valid. k_new, v_new: [n_streams][d] (new_dtype TQ_F32 or
+ * TQ_F16), the new token's key and value per stream; they are quantized
+ * (as tq_quantize, with qk and qv) into vector s*cap + T of k and v, which is
+ * the only cache memory written. Then, as tq_decode_attn, out_{s,h} is the
+ * attention of q_{s,h} over tokens 0..T of stream s (T + 1 tokens, the new
+ * one included). 0 <= T < cap; G in 1..16. ws: at least
+ * tq_workspace_size(TQ_OP_DECODE_ATTN, qk, n_streams, T + 1, G) bytes.
+ * Errors as tq_decode_attn (TQ_ERR_INVALID also for T < 0 or T >= cap).
+ * Asynchronous on stream.
+ */
+int tq_decode_step(const tq_quantizer* qk, const tq_quantizer* qv,
+                   const tq_packed* k, const tq_packed* v,
+                   int64_t n_streams, int64_t T, int64_t cap, int G,
+                   const void* k_new, const void* v_new, int new_dtype,
+                   const void* q, int q_dtype, float scale, float* out,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
  * tq_workspace_size -- device workspace bytes for op:
  *   TQ_OP_SCORES:      n_a = n_q, n_b = n_keys, G ignored;
  *   TQ_OP_DECODE_ATTN: n_a = n_streams, n_b = T, G = heads per stream.

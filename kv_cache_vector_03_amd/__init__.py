@@ -44,7 +44,7 @@ class tq_packed(C.Structure):
 
 
 EXPORTS = ("tq_codebook", "tq_quantize", "tq_scores", "tq_dequantize", "tq_decode_attn",
-           "tq_workspace_size", "tq_last_error")
+           "tq_decode_step", "tq_workspace_size", "tq_last_error")
 
 _lib = None
 
@@ -69,6 +69,9 @@ def lib() -> C.CDLL:
         L.tq_decode_attn.argtypes = [qp, qp, pp, pp, C.c_int64, C.c_int64, C.c_int, vp, C.c_int,
                                      C.c_float, vp, vp, C.c_size_t, vp]
         L.tq_decode_attn.restype = C.c_int
+        L.tq_decode_step.argtypes = [qp, qp, pp, pp, C.c_int64, C.c_int64, C.c_int64, C.c_int, vp, vp,
+                                     C.c_int, vp, C.c_int, C.c_float, vp, vp, C.c_size_t, vp]
+        L.tq_decode_step.restype = C.c_int
         L.tq_workspace_size.argtypes = [C.c_int, qp, C.c_int64, C.c_int64, C.c_int]
         L.tq_workspace_size.restype = C.c_size_t
         L.tq_last_error.argtypes = []
@@ -229,3 +232,18 @@ def tq_decode_attn(qk: Quantizer, qv: Quantizer, k: Packed, v: Packed, n_streams
     _check(lib().tq_decode_attn(C.byref(qk.struct), C.byref(qv.struct), C.byref(k.struct),
                                 C.byref(v.struct), n_streams, T, G, _ptr(q), _dtype_code(q),
                                 float(scale), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def tq_decode_step(qk: Quantizer, qv: Quantizer, k: Packed, v: Packed, n_streams: int, T: int, cap: int,
+                   G: int, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor, out: torch.Tensor,
+                   scale: float = 0.0, ws: torch.Tensor | None = None, stream=None) -> None:
+    """Append each stream's new token (k_new, v_new: [n_streams][d]) at position T
+    of caches laid out with `cap` vectors per stream, then attend over T + 1 tokens."""
+    if k_new.dtype != v_new.dtype:
+        raise TypeError("k_new and v_new must have the same dtype")
+    if ws is None:
+        ws = workspace(tq_workspace_size(TQ_OP_DECODE_ATTN, qk, n_streams, T + 1, G), q.device)
+    _check(lib().tq_decode_step(C.byref(qk.struct), C.byref(qv.struct), C.byref(k.struct),
+                                C.byref(v.struct), n_streams, T, cap, G, _ptr(k_new), _ptr(v_new),
+                                _dtype_code(k_new), _ptr(q), _dtype_code(q), float(scale), _ptr(out),
+                                _ptr(ws), ws.numel(), _stream(stream)))

@@ -97,7 +97,44 @@ int tq_decode_attn(const tq_quantizer* qk, const tq_quantizer* qv,
         return fail(TQ_ERR_WORKSPACE, "tq_decode_attn: workspace %zu bytes < %zu", ws_bytes, plan.total);
     if ((uintptr_t)ws % 256) return fail(TQ_ERR_INVALID, "tq_decode_attn: workspace must be 256-byte aligned");
     if (scale == 0.0f) scale = 1.0f / std::sqrt((float)qk->d);
-    return launch_decode(qk, qv, k, v, n_streams, T, G, q, q_dtype, plan, ws, scale, out,
+    return launch_decode(qk, qv, k, v, n_streams, T, T, G, q, q_dtype, plan, ws, scale, out, nullptr,
+                         (hipStream_t)stream);
+}
+
+int tq_decode_step(const tq_quantizer* qk, const tq_quantizer* qv,
+                   const tq_packed* k, const tq_packed* v,
+                   int64_t n_streams, int64_t T, int64_t cap, int G,
+                   const void* k_new, const void* v_new, int new_dtype,
+                   const void* q, int q_dtype, float scale, float* out,
+                   void* ws, size_t ws_bytes, void* stream)
+{
+    clear_error();
+    int rc;
+    if ((rc = check_quantizer(qk, "tq_decode_step", "key")) != TQ_OK) return rc;
+    if ((rc = check_quantizer(qv, "tq_decode_step", "value")) != TQ_OK) return rc;
+    if (qv->d != qk->d) return fail(TQ_ERR_UNSUPPORTED, "tq_decode_step: key d=%d != value d=%d", qk->d, qv->d);
+    if (qv->qjl_m != 0)
+        return fail(TQ_ERR_UNSUPPORTED, "tq_decode_step: value quantizer must be codes-only (qjl_m=0)");
+    if (n_streams < 0) return fail(TQ_ERR_INVALID, "tq_decode_step: n_streams < 0");
+    if (G < 1 || G > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_decode_step: G=%d not in 1..16", G);
+    if (n_streams == 0) return TQ_OK;
+    if (T < 0 || cap <= T)
+        return fail(TQ_ERR_INVALID, "tq_decode_step: need 0 <= T < cap (T=%lld, cap=%lld)", (long long)T,
+                    (long long)cap);
+    if (!std::isfinite(scale) || scale < 0) return fail(TQ_ERR_INVALID, "tq_decode_step: bad scale");
+    if ((rc = check_packed(qk, k, "tq_decode_step", "k")) != TQ_OK) return rc;
+    if ((rc = check_packed(qv, v, "tq_decode_step", "v")) != TQ_OK) return rc;
+    if ((rc = check_dense(k_new, new_dtype, "tq_decode_step", "k_new")) != TQ_OK) return rc;
+    if ((rc = check_dense(v_new, new_dtype, "tq_decode_step", "v_new")) != TQ_OK) return rc;
+    if ((rc = check_dense(q, q_dtype, "tq_decode_step", "q")) != TQ_OK) return rc;
+    if ((rc = check_dense(out, TQ_F32, "tq_decode_step", "out")) != TQ_OK) return rc;
+    const DecodePlan plan = decode_plan(qk, n_streams, T + 1, G);
+    if (!ws || ws_bytes < plan.total)
+        return fail(TQ_ERR_WORKSPACE, "tq_decode_step: workspace %zu bytes < %zu", ws_bytes, plan.total);
+    if ((uintptr_t)ws % 256) return fail(TQ_ERR_INVALID, "tq_decode_step: workspace must be 256-byte aligned");
+    if (scale == 0.0f) scale = 1.0f / std::sqrt((float)qk->d);
+    const AppendArgs app{k_new, v_new, new_dtype, T};
+    return launch_decode(qk, qv, k, v, n_streams, T + 1, cap, G, q, q_dtype, plan, ws, scale, out, &app,
                          (hipStream_t)stream);
 }
 

@@ -12,6 +12,7 @@
 // and applies the inverse value rotation D_v H / sqrt(d) once per head.
 #include <float.h>
 
+#include "tq_append.h"
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -97,8 +98,8 @@ __global__ __launch_bounds__(256) void k_decode(const uint32_t* __restrict__ kco
                                                 const uint16_t* __restrict__ knorm,
                                                 const uint16_t* __restrict__ krnorm,
                                                 const uint32_t* __restrict__ vcodes,
-                                                const uint16_t* __restrict__ vnorm, int64_t T, int G,
-                                                const float* __restrict__ qr,
+                                                const uint16_t* __restrict__ vnorm, int64_t T, int64_t stride,
+                                                int G, const float* __restrict__ qr,
                                                 const float* __restrict__ p,
                                                 const float* __restrict__ kcent,
                                                 const float* __restrict__ vcent, float scale,
@@ -127,11 +128,11 @@ __global__ __launch_bounds__(256) void k_decode(const uint32_t* __restrict__ kco
     for (int e = tid; e < kTC * BV * W; e += 256) {
         const int tt = e / (BV * W), j = e % (BV * W);
         const int64_t t = t0 + tt;
-        vw[tt][j] = t < T ? vcodes[(s * T + t) * (BV * W) + j] : 0u;
+        vw[tt][j] = t < T ? vcodes[(s * stride + t) * (BV * W) + j] : 0u;
     }
     {
         const int64_t t = t0 + tid;
-        vn[tid] = t < T ? h2f(vnorm[s * T + t]) : 0.f;
+        vn[tid] = t < T ? h2f(vnorm[s * stride + t]) : 0.f;
     }
     __syncthreads();
 
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(256) void k_decode(const uint32_t* __restrict__ kco
 #pragma unroll
         for (int h = 0; h < kMaxG; ++h) am[h] = aj[h] = 0.f;
         if (t < T) {
-            const int64_t v = s * T + t;
+            const int64_t v = s * stride + t;
             uint32_t cw[BK * W], sw[W];
 #pragma unroll
             for (int w = 0; w < BK * W; ++w) cw[w] = kcodes[v * (BK * W) + w];
@@ -283,6 +284,19 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ parts
     for (int r = 0; r < R; ++r) out[sh * D + 64 * r + lane] = flip(v[r], dm[r]) * sc;
 }
 
+// The decode step's append for the shapes without the MFMA path: block
+// (s, 0) quantizes stream s's new key, block (s, 1) its new value.
+template <int D>
+__global__ __launch_bounds__(256) void k_append(tq_quantizer qk, tq_quantizer qv, tq_packed k, tq_packed v,
+                                                const void* __restrict__ k_new, const void* __restrict__ v_new,
+                                                int dtype, int64_t stride, int64_t pos)
+{
+    __shared__ float sm[append_smem_floats(D)];
+    const int64_t s = blockIdx.x;
+    const bool val = blockIdx.y == 1;
+    quantize_one<D>(val ? qv : qk, val ? v : k, val ? v_new : k_new, dtype, s, s * stride + pos, sm);
+}
+
 int device_status(const char* who)
 {
     hipError_t e = hipGetLastError();
@@ -315,39 +329,39 @@ void scores_d(const tq_quantizer* q, const tq_packed* k, int64_t n_keys, const f
 
 template <int D, int BK, bool QJL, int BV>
 void decode_kernel(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k, const tq_packed* v,
-                   int64_t n_streams, int64_t T, int G, const float* qr, const float* p, float scale,
-                   float* parts, int n_chunks, hipStream_t s)
+                   int64_t n_streams, int64_t T, int64_t stride, int G, const float* qr, const float* p,
+                   float scale, float* parts, int n_chunks, hipStream_t s)
 {
     dim3 grid((unsigned)n_chunks, (unsigned)n_streams), block(256);
     hipLaunchKernelGGL((k_decode<D, BK, QJL, BV>), grid, block, 0, s, k->codes, k->signs, k->norm,
-                       k->rnorm, v->codes, v->norm, T, G, qr, p, qk->centroids, qv->centroids, scale,
-                       parts, n_chunks);
+                       k->rnorm, v->codes, v->norm, T, stride, G, qr, p, qk->centroids, qv->centroids,
+                       scale, parts, n_chunks);
 }
 
 template <int D, int BK, bool QJL>
 void decode_bv(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k, const tq_packed* v,
-               int64_t n_streams, int64_t T, int G, const float* qr, const float* p, float scale,
-               float* parts, int n_chunks, hipStream_t s)
+               int64_t n_streams, int64_t T, int64_t stride, int G, const float* qr, const float* p,
+               float scale, float* parts, int n_chunks, hipStream_t s)
 {
     switch (qv->mse_bits) {
-        case 1: decode_kernel<D, BK, QJL, 1>(qk, qv, k, v, n_streams, T, G, qr, p, scale, parts, n_chunks, s); break;
-        case 2: decode_kernel<D, BK, QJL, 2>(qk, qv, k, v, n_streams, T, G, qr, p, scale, parts, n_chunks, s); break;
-        case 3: decode_kernel<D, BK, QJL, 3>(qk, qv, k, v, n_streams, T, G, qr, p, scale, parts, n_chunks, s); break;
-        default: decode_kernel<D, BK, QJL, 4>(qk, qv, k, v, n_streams, T, G, qr, p, scale, parts, n_chunks, s); break;
+        case 1: decode_kernel<D, BK, QJL, 1>(qk, qv, k, v, n_streams, T, stride, G, qr, p, scale, parts, n_chunks, s); break;
+        case 2: decode_kernel<D, BK, QJL, 2>(qk, qv, k, v, n_streams, T, stride, G, qr, p, scale, parts, n_chunks, s); break;
+        case 3: decode_kernel<D, BK, QJL, 3>(qk, qv, k, v, n_streams, T, stride, G, qr, p, scale, parts, n_chunks, s); break;
+        default: decode_kernel<D, BK, QJL, 4>(qk, qv, k, v, n_streams, T, stride, G, qr, p, scale, parts, n_chunks, s); break;
     }
 }
 
 template <int D>
 void decode_d(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k, const tq_packed* v,
-              int64_t n_streams, int64_t T, int G, const float* qr, const float* p, float scale,
-              float* out, float* parts, int n_chunks, hipStream_t s)
+              int64_t n_streams, int64_t T, int64_t stride, int G, const float* qr, const float* p,
+              float scale, float* out, float* parts, int n_chunks, hipStream_t s)
 {
     const bool qjl = qk->qjl_m != 0;
     switch (qk->mse_bits) {
-        case 1: qjl ? decode_bv<D, 1, true>(qk, qv, k, v, n_streams, T, G, qr, p, scale, parts, n_chunks, s) : decode_bv<D, 1, false>(qk, qv, k, v, n_streams, T, G, qr, p, scale, parts, n_chunks, s); break;
-        case 2: qjl ? decode_bv<D, 2, true>(qk, qv, k, v, n_streams, T, G, qr, p, scale, parts, n_chunks, s) : decode_bv<D, 2, false>(qk, qv, k, v, n_streams, T, G, qr, p, scale, parts, n_chunks, s); break;
-        case 3: qjl ? decode_bv<D, 3, true>(qk, qv, k, v, n_streams, T, G, qr, p, scale, parts, n_chunks, s) : decode_bv<D, 3, false>(qk, qv, k, v, n_streams, T, G, qr, p, scale, parts, n_chunks, s); break;
-        default: qjl ? decode_bv<D, 4, true>(qk, qv, k, v, n_streams, T, G, qr, p, scale, parts, n_chunks, s) : decode_bv<D, 4, false>(qk, qv, k, v, n_streams, T, G, qr, p, scale, parts, n_chunks, s); break;
+        case 1: qjl ? decode_bv<D, 1, true>(qk, qv, k, v, n_streams, T, stride, G, qr, p, scale, parts, n_chunks, s) : decode_bv<D, 1, false>(qk, qv, k, v, n_streams, T, stride, G, qr, p, scale, parts, n_chunks, s); break;
+        case 2: qjl ? decode_bv<D, 2, true>(qk, qv, k, v, n_streams, T, stride, G, qr, p, scale, parts, n_chunks, s) : decode_bv<D, 2, false>(qk, qv, k, v, n_streams, T, stride, G, qr, p, scale, parts, n_chunks, s); break;
+        case 3: qjl ? decode_bv<D, 3, true>(qk, qv, k, v, n_streams, T, stride, G, qr, p, scale, parts, n_chunks, s) : decode_bv<D, 3, false>(qk, qv, k, v, n_streams, T, stride, G, qr, p, scale, parts, n_chunks, s); break;
+        default: qjl ? decode_bv<D, 4, true>(qk, qv, k, v, n_streams, T, stride, G, qr, p, scale, parts, n_chunks, s) : decode_bv<D, 4, false>(qk, qv, k, v, n_streams, T, stride, G, qr, p, scale, parts, n_chunks, s); break;
     }
     (void)out;
 }
@@ -366,24 +380,33 @@ int launch_scores(const tq_quantizer* q, const tq_packed* k, int64_t n_keys, con
 }
 
 int launch_decode(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
-                  const tq_packed* v, int64_t n_streams, int64_t T, int G, const void* q, int q_dtype,
-                  const DecodePlan& plan, void* ws, float scale, float* out, hipStream_t s)
+                  const tq_packed* v, int64_t n_streams, int64_t T, int64_t stride, int G, const void* q,
+                  int q_dtype, const DecodePlan& plan, void* ws, float scale, float* out,
+                  const AppendArgs* app, hipStream_t s)
 {
     float* qr = (float*)((char*)ws + plan.off_qr);
     float* p = (float*)((char*)ws + plan.off_p);
     float* parts = (float*)((char*)ws + plan.off_parts);
     const float zscale = scale * 1.4426950408889634f;  // scores in log2 units
     if (plan.mfma) {
-        int rc = launch_decode_mfma(qk, qv, k, v, n_streams, T, G, q, q_dtype, zscale,
-                                    (char*)ws + plan.off_frag, parts, plan.n_chunks, (int)plan.tc, s);
+        int rc = launch_decode_mfma(qk, qv, k, v, n_streams, T, stride, G, q, q_dtype, zscale,
+                                    (char*)ws + plan.off_frag, parts, plan.n_chunks, (int)plan.tc, app, s);
         if (rc != TQ_OK) return rc;
     } else {
+        if (app) {
+            const dim3 ag((unsigned)n_streams, 2u);
+            switch (qk->d) {
+                case 64: hipLaunchKernelGGL((k_append<64>), ag, dim3(256), 0, s, *qk, *qv, *k, *v, app->k_new, app->v_new, app->dtype, stride, app->pos); break;
+                case 128: hipLaunchKernelGGL((k_append<128>), ag, dim3(256), 0, s, *qk, *qv, *k, *v, app->k_new, app->v_new, app->dtype, stride, app->pos); break;
+                default: hipLaunchKernelGGL((k_append<256>), ag, dim3(256), 0, s, *qk, *qv, *k, *v, app->k_new, app->v_new, app->dtype, stride, app->pos); break;
+            }
+        }
         int rc = launch_qprep(qk, q, q_dtype, n_streams * G, qr, p, s);
         if (rc != TQ_OK) return rc;
         switch (qk->d) {
-            case 64: decode_d<64>(qk, qv, k, v, n_streams, T, G, qr, p, zscale, out, parts, plan.n_chunks, s); break;
-            case 128: decode_d<128>(qk, qv, k, v, n_streams, T, G, qr, p, zscale, out, parts, plan.n_chunks, s); break;
-            default: decode_d<256>(qk, qv, k, v, n_streams, T, G, qr, p, zscale, out, parts, plan.n_chunks, s); break;
+            case 64: decode_d<64>(qk, qv, k, v, n_streams, T, stride, G, qr, p, zscale, out, parts, plan.n_chunks, s); break;
+            case 128: decode_d<128>(qk, qv, k, v, n_streams, T, stride, G, qr, p, zscale, out, parts, plan.n_chunks, s); break;
+            default: decode_d<256>(qk, qv, k, v, n_streams, T, stride, G, qr, p, zscale, out, parts, plan.n_chunks, s); break;
         }
     }
     const dim3 cg((unsigned)(n_streams * G));
@@ -392,7 +415,7 @@ int launch_decode(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packe
         case 128: hipLaunchKernelGGL((k_combine<128>), cg, dim3(256), 0, s, parts, plan.n_chunks, G, qv->diag_signs, out); break;
         default: hipLaunchKernelGGL((k_combine<256>), cg, dim3(256), 0, s, parts, plan.n_chunks, G, qv->diag_signs, out); break;
     }
-    return device_status("tq_decode_attn");
+    return device_status(app ? "tq_decode_step" : "tq_decode_attn");
 }
 
 }  // namespace tq

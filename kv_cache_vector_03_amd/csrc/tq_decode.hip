@@ -22,6 +22,7 @@
 // The four waves merge in LDS; one partial (max, sum, rotated-domain
 // accumulator) per block goes to the workspace, and the combine kernel merges
 // the partials of a stream and undoes the value rotation.
+#include "tq_append.h"
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -51,19 +52,39 @@ __device__ __forceinline__ float quad_bcast(float x)
 // k-step t maps to coordinate (or projection row) (4 g + t) + (d/8) e, the
 // group-major order the key codes arrive in. Arithmetic is fp32: its relative
 // error (~1e-7) is far below what the hi/lo operands carry into the scores.
+//
+// With the decode step's append, grid.y has two more blocks per stream: they
+// quantize the stream's new key (y = d/32) and value (y = d/32 + 1) into the
+// caches, beside the fragment blocks and in the same launch.
+struct AppendDev {
+    tq_quantizer qk, qv;
+    tq_packed k, v;
+    const void* k_new;
+    const void* v_new;
+    int dtype;
+    int64_t stride, pos;
+};
+
 template <int D, bool QJL, bool F16>
 __global__ __launch_bounds__(256) void k_qprep_frag(const void* __restrict__ q, int G, int64_t total,
                                                     const uint32_t* __restrict__ diag,
                                                     const uint16_t* __restrict__ S,
-                                                    half8_t* __restrict__ frags)
+                                                    half8_t* __restrict__ frags, AppendDev app)
 {
     static_assert(D == 128, "fragment layout is laid out for d = 128");
+    static_assert(8 * D >= append_smem_floats(D), "append scratch reuses the query buffer");
     constexpr int R = D / 64, KS = D / 32, KSTEPS = KS * (QJL ? 2 : 1);
     __shared__ float qs[8][D];
     __shared__ float ps[QJL ? 8 : 1][32];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t s = blockIdx.x;
     const int tt = blockIdx.y;
+    if (tt >= KS) {
+        const bool val = tt == KS + 1;
+        quantize_one<D>(val ? app.qv : app.qk, val ? app.v : app.k, val ? app.v_new : app.k_new, app.dtype, s,
+                        s * app.stride + app.pos, &qs[0][0]);
+        return;
+    }
     // thread (h, i) projects row j = tt + (d/32) i of S onto head h; its row is
     // fetched first so the load overlaps the rotation
     const int ph = tid >> 5, pi = tid & 31;
@@ -289,8 +310,8 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                                                      const uint16_t* __restrict__ knorm,
                                                      const uint16_t* __restrict__ krnorm,
                                                      const uint32_t* __restrict__ vcodes,
-                                                     const uint16_t* __restrict__ vnorm, int64_t T, int G,
-                                                     const half8_t* __restrict__ frags,
+                                                     const uint16_t* __restrict__ vnorm, int64_t T,
+                                                     int64_t stride, int G, const half8_t* __restrict__ frags,
                                                      const float* __restrict__ kcent,
                                                      const float* __restrict__ vcent, float zscale,
                                                      float* __restrict__ parts, int n_chunks, int tc,
@@ -328,7 +349,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
     for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int64_t s = item / n_chunks;
         const int chunk = (int)(item % n_chunks);
-        const int64_t base = s * T;
+        const int64_t base = s * stride;
         const int64_t c0 = (int64_t)chunk * tc;
         const int64_t c1 = c0 + tc < T ? c0 + tc : T;
         const int64_t w0 = c0 + (int64_t)wid * (tc / 4);
@@ -548,7 +569,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
 }
 
 template <int D, int BK, bool QJL, int BV>
-void launch_mfma(const tq_packed* k, const tq_packed* v, int64_t n_streams, int64_t T, int G,
+void launch_mfma(const tq_packed* k, const tq_packed* v, int64_t n_streams, int64_t T, int64_t stride, int G,
                  const half8_t* frags, const tq_quantizer* qk, const tq_quantizer* qv, float zscale,
                  float* parts, int n_chunks, int tc, hipStream_t s)
 {
@@ -556,37 +577,40 @@ void launch_mfma(const tq_packed* k, const tq_packed* v, int64_t n_streams, int6
     const int64_t cap = (int64_t)device_cus() * 2;
     const unsigned grid = (unsigned)(n_items < cap ? n_items : cap);
     hipLaunchKernelGGL((k_decode_mfma<D, BK, QJL, BV>), dim3(grid), dim3(256), 0, s, k->codes, k->signs, k->norm,
-                       k->rnorm, v->codes, v->norm, T, G, frags, qk->centroids, qv->centroids, zscale, parts,
+                       k->rnorm, v->codes, v->norm, T, stride, G, frags, qk->centroids, qv->centroids, zscale, parts,
                        n_chunks, tc, n_items);
 }
 
 template <int D, int BK, bool QJL>
-void launch_bv(int bv, const tq_packed* k, const tq_packed* v, int64_t ns, int64_t T, int G, const half8_t* fr,
+void launch_bv(int bv, const tq_packed* k, const tq_packed* v, int64_t ns, int64_t T, int64_t stride, int G,
+               const half8_t* fr,
                const tq_quantizer* qk, const tq_quantizer* qv, float zs, float* parts, int nc, int tc,
                hipStream_t s)
 {
     switch (bv) {
-        case 1: launch_mfma<D, BK, QJL, 1>(k, v, ns, T, G, fr, qk, qv, zs, parts, nc, tc, s); break;
-        case 2: launch_mfma<D, BK, QJL, 2>(k, v, ns, T, G, fr, qk, qv, zs, parts, nc, tc, s); break;
-        case 3: launch_mfma<D, BK, QJL, 3>(k, v, ns, T, G, fr, qk, qv, zs, parts, nc, tc, s); break;
-        default: launch_mfma<D, BK, QJL, 4>(k, v, ns, T, G, fr, qk, qv, zs, parts, nc, tc, s); break;
+        case 1: launch_mfma<D, BK, QJL, 1>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
+        case 2: launch_mfma<D, BK, QJL, 2>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
+        case 3: launch_mfma<D, BK, QJL, 3>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
+        default: launch_mfma<D, BK, QJL, 4>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
     }
 }
 
 // Score fragments of `tiles` groups of G query rows (rows at or past `total`
-// count as zero).
+// count as zero); with app (one tile per stream), also the append blocks.
 void launch_qprep_frag(const tq_quantizer* qk, const void* q, int q_dtype, int64_t tiles, int G, int64_t total,
-                       half8_t* frags, hipStream_t s)
+                       half8_t* frags, const AppendDev* app, hipStream_t s)
 {
     constexpr int D = 128;
     const bool qjl = qk->qjl_m != 0;
-    const dim3 pg((unsigned)tiles, (unsigned)(D / 32)), pb(256);
+    AppendDev a{};
+    if (app) a = *app;
+    const dim3 pg((unsigned)tiles, (unsigned)(D / 32 + (app ? 2 : 0))), pb(256);
     if (q_dtype == TQ_F16) {
-        if (qjl) hipLaunchKernelGGL((k_qprep_frag<D, true, true>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags);
-        else hipLaunchKernelGGL((k_qprep_frag<D, false, true>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags);
+        if (qjl) hipLaunchKernelGGL((k_qprep_frag<D, true, true>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags, a);
+        else hipLaunchKernelGGL((k_qprep_frag<D, false, true>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags, a);
     } else {
-        if (qjl) hipLaunchKernelGGL((k_qprep_frag<D, true, false>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags);
-        else hipLaunchKernelGGL((k_qprep_frag<D, false, false>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags);
+        if (qjl) hipLaunchKernelGGL((k_qprep_frag<D, true, false>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags, a);
+        else hipLaunchKernelGGL((k_qprep_frag<D, false, false>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags, a);
     }
 }
 
@@ -728,23 +752,25 @@ void launch_scores_k(const tq_packed* k, int64_t n_keys, const half8_t* fr, int6
 }  // namespace
 
 int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
-                       const tq_packed* v, int64_t n_streams, int64_t T, int G, const void* q,
+                       const tq_packed* v, int64_t n_streams, int64_t T, int64_t stride, int G, const void* q,
                        int q_dtype, float zscale, void* frags, float* parts, int n_chunks, int tc,
-                       hipStream_t s)
+                       const AppendArgs* app, hipStream_t s)
 {
     constexpr int D = 128;
     const bool qjl = qk->qjl_m != 0;
-    launch_qprep_frag(qk, q, q_dtype, n_streams, G, n_streams * G, (half8_t*)frags, s);
+    AppendDev ad{};
+    if (app) ad = AppendDev{*qk, *qv, *k, *v, app->k_new, app->v_new, app->dtype, stride, app->pos};
+    launch_qprep_frag(qk, q, q_dtype, n_streams, G, n_streams * G, (half8_t*)frags, app ? &ad : nullptr, s);
     const half8_t* fr = (const half8_t*)frags;
     switch (qk->mse_bits) {
-        case 1: qjl ? launch_bv<D, 1, true>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
-                    : launch_bv<D, 1, false>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
-        case 2: qjl ? launch_bv<D, 2, true>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
-                    : launch_bv<D, 2, false>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
-        case 3: qjl ? launch_bv<D, 3, true>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
-                    : launch_bv<D, 3, false>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
-        default: qjl ? launch_bv<D, 4, true>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
-                     : launch_bv<D, 4, false>(qv->mse_bits, k, v, n_streams, T, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
+        case 1: qjl ? launch_bv<D, 1, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
+                    : launch_bv<D, 1, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
+        case 2: qjl ? launch_bv<D, 2, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
+                    : launch_bv<D, 2, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
+        case 3: qjl ? launch_bv<D, 3, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
+                    : launch_bv<D, 3, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
+        default: qjl ? launch_bv<D, 4, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
+                     : launch_bv<D, 4, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "tq_decode_attn: %s", hipGetErrorString(e));
@@ -756,7 +782,7 @@ int launch_scores_mfma(const tq_quantizer* q, const tq_packed* k, int64_t n_keys
 {
     constexpr int D = 128;
     const int64_t n_qt = (n_q + 7) / 8;
-    launch_qprep_frag(q, queries, q_dtype, n_qt, 8, n_q, (half8_t*)frags, s);
+    launch_qprep_frag(q, queries, q_dtype, n_qt, 8, n_q, (half8_t*)frags, nullptr, s);
     const half8_t* fr = (const half8_t*)frags;
     const bool qjl = q->qjl_m != 0;
     switch (q->mse_bits) {

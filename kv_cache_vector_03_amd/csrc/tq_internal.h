@@ -55,16 +55,28 @@ int launch_scores(const tq_quantizer* q, const tq_packed* k, int64_t n_keys, con
                   const float* p, int64_t n_q, float* scores, hipStream_t s);
 int launch_dequantize(const tq_quantizer* q, const tq_packed* in, int64_t n, int include_qjl,
                       void* out, int dtype, hipStream_t s);
+// The decode step's append: the new token of stream s (row s of k_new and
+// v_new, [n_streams][d]) goes to vector s * stride + pos of the caches.
+struct AppendArgs {
+    const void* k_new;
+    const void* v_new;
+    int dtype;
+    int64_t pos;
+};
+
+// decode over tokens 0..T-1 of each stream; stream s starts at vector s * stride;
+// with app, the new tokens are quantized into the caches first (app->pos < T)
 int launch_decode(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
-                  const tq_packed* v, int64_t n_streams, int64_t T, int G, const void* q, int q_dtype,
-                  const DecodePlan& plan, void* ws, float scale, float* out, hipStream_t s);
+                  const tq_packed* v, int64_t n_streams, int64_t T, int64_t stride, int G, const void* q,
+                  int q_dtype, const DecodePlan& plan, void* ws, float scale, float* out,
+                  const AppendArgs* app, hipStream_t s);
 // d = 128: query fragments into `frags` (scores_frag_bytes(q, n_q)), then the MFMA score kernel
 int launch_scores_mfma(const tq_quantizer* q, const tq_packed* k, int64_t n_keys, const void* queries,
                        int q_dtype, int64_t n_q, float* scores, void* frags, hipStream_t s);
 int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
-                       const tq_packed* v, int64_t n_streams, int64_t T, int G, const void* q,
+                       const tq_packed* v, int64_t n_streams, int64_t T, int64_t stride, int G, const void* q,
                        int q_dtype, float zscale, void* frags, float* parts, int n_chunks, int tc,
-                       hipStream_t s);
+                       const AppendArgs* app, hipStream_t s);
 
 }  // namespace tq
 

@@ -123,6 +123,77 @@ def test_decode_zero_and_large_norm_tokens():
     check_close(out, ref, tol=1e-4 * max(1.0, float(np.abs(ref).max())), what="zero / large-norm tokens")
 
 
+STEP = [
+    # d, kb, vb, ns, T, cap, G, k_qjl, new-token dtype
+    (128, 2, 4, 3, 300, 320, 8, True, np.float16),   # MFMA path: append blocks in the query prep
+    (128, 2, 3, 2, 0, 4, 8, True, np.float32),       # empty caches: attend over the new token only
+    (128, 3, 3, 2, 1000, 1001, 4, False, np.float16),  # last slot; codes-only keys
+    (128, 2, 4, 2, 2047, 4096, 8, True, np.float16),  # T + 1 = 2048: full steps only
+    (64, 2, 3, 2, 200, 260, 8, True, np.float32),    # d = 64: separate append kernel
+    (128, 2, 4, 2, 130, 200, 16, True, np.float16),  # G = 16: separate append kernel
+]
+
+
+@pytest.mark.parametrize("d,kb,vb,ns,T,cap,G,k_qjl,dt", STEP)
+def test_decode_step_append(d, kb, vb, ns, T, cap, G, k_qjl, dt):
+    """tq_decode_step: the new token of each stream is quantized into slot T of
+    a cache with `cap` slots per stream, nothing else in the caches changes,
+    and the output is the attention over tokens 0..T."""
+    tq = tqmod()
+    qkg, qvg, qko, qvo = make(d, kb, vb, k_qjl=k_qjl)
+    K = synth.to_f16(synth.normals(37, synth.ROLE_DATA_K, np.arange(ns * cap * d)).reshape(ns, cap, d) * 2)
+    V = synth.to_f16(synth.normals(37, synth.ROLE_DATA_V, np.arange(ns * cap * d)).reshape(ns, cap, d))
+    Q = synth.to_f16(synth.normals(37, synth.ROLE_QUERY, np.arange(ns * G * d)).reshape(ns, G, d))
+    kn = (synth.normals(41, synth.ROLE_DATA_K, np.arange(ns * d)).reshape(ns, d) * 2).astype(dt)
+    vn = synth.normals(41, synth.ROLE_DATA_V, np.arange(ns * d)).reshape(ns, d).astype(dt)
+    pk, pv = tq.Packed.empty(qkg, ns * cap, DEV), tq.Packed.empty(qvg, ns * cap, DEV)
+    for t in [a for a in (pk.codes, pk.signs, pk.norm, pk.rnorm, pv.codes, pv.norm) if a is not None]:
+        t.fill_(-1)
+    # the caches: tokens 0..T-1 of stream s at slots s*cap + t
+    for st in range(ns):
+        if T == 0:
+            break
+        sl = slice(st * cap, st * cap + T)
+        for qg, pkd, X in ((qkg, pk, K), (qvg, pv, V)):
+            sub = tq.Packed(pkd.codes[sl], pkd.signs[sl] if pkd.signs is not None else None, pkd.norm[sl],
+                            pkd.rnorm[sl] if pkd.rnorm is not None else None)
+            tq.tq_quantize(qg, torch.from_numpy(np.ascontiguousarray(X[st, :T])).to(DEV), sub)
+    torch.cuda.synchronize()
+    before_k, before_v = pk.to_host(), pv.to_host()
+    out = torch.empty((ns, G, d), dtype=torch.float32, device=DEV)
+    tq.tq_decode_step(qkg, qvg, pk, pv, ns, T, cap, G, torch.from_numpy(kn).to(DEV), torch.from_numpy(vn).to(DEV),
+                      torch.from_numpy(Q).to(DEV), out)
+    torch.cuda.synchronize()
+    after_k, after_v = pk.to_host(), pv.to_host()
+    slots = np.arange(ns) * cap + T
+    keep = np.ones(ns * cap, bool)
+    keep[slots] = False
+    for b, a in zip(before_k + before_v, after_k + after_v):
+        if a is not None and a.size:
+            assert np.array_equal(b[keep], a[keep]), "cache changed outside the appended slots"
+    # the appended tokens against the oracle's quantizer
+    check_quantize(qko, kn.astype(np.float64), tuple(a[slots] for a in after_k))
+    check_quantize(qvo, vn.astype(np.float64), tuple(a[slots] for a in after_v))
+    # attention over tokens 0..T of each stream, on the cache as the GPU left it
+    rows = (np.arange(ns)[:, None] * cap + np.arange(T + 1)[None, :]).reshape(-1)
+    gk = opacked(qko, tuple(a[rows] for a in after_k))
+    gv = opacked(qvo, tuple(a[rows] for a in after_v))
+    ref = oracle.decode_attn(qko, qvo, gk, gv, ns, T + 1, G, Q.astype(np.float64))
+    check_close(out.cpu().numpy(), ref, what="decode step after append")
+
+
+def test_decode_step_argument_errors():
+    tq = tqmod()
+    qkg, qvg, _, _ = make(128, 2, 4)
+    pk, pv = tq.Packed.empty(qkg, 8, DEV), tq.Packed.empty(qvg, 8, DEV)
+    z = torch.zeros((2, 128), dtype=torch.float16, device=DEV)
+    q = torch.zeros((2, 8, 128), dtype=torch.float16, device=DEV)
+    out = torch.empty((2, 8, 128), dtype=torch.float32, device=DEV)
+    for T, cap in ((4, 4), (-1, 4)):
+        with pytest.raises(tq.TQError):
+            tq.tq_decode_step(qkg, qvg, pk, pv, 2, T, cap, 8, z, z, q, out)
+
+
 def _kv_case(cfg, layers, sample):
     """Generate, quantize and decode ``layers`` of cfg on the GPU; check sampled streams.
 
