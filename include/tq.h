@@ -76,6 +76,7 @@ extern "C" {
 
 /* codebook laws */
 #define TQ_LAW_GAUSSIAN 0     /* N(0, 1/d) */
+#define TQ_LAW_SPHERE 1       /* exact law of one coordinate of a random unit vector in R^d */
 
 /* Quantizer state. All pointers are device pointers owned by the caller. */
 typedef struct tq_quantizer {
@@ -106,7 +107,12 @@ typedef struct tq_packed {
  * boundaries (host float[2^bits - 1]; fp32 RNE of the exact midpoints of the
  * stored centroids). distortion (nullable) receives the analytic mean squared
  * error per coordinate of the stored codebook under the law.
- * Supports d in 1..65536, bits in 1..8, law TQ_LAW_GAUSSIAN.
+ * law TQ_LAW_SPHERE instead solves for the exact law of one coordinate of a
+ * uniformly random unit vector in R^d, density proportional to
+ * (1 - t^2)^((d-3)/2) on [-1, 1] (Y^2 ~ Beta(1/2, (d-1)/2): the Beta law that
+ * "TurboQuant 是什麼：30 秒懶人包" on the vLLM benchmark summary names; N(0, 1/d)
+ * is its large-d limit); d >= 2 for it.
+ * Supports d in 1..65536, bits in 1..8.
  * Returns TQ_OK, TQ_ERR_INVALID (null output), TQ_ERR_UNSUPPORTED, or
  * TQ_ERR_NOCONV.
  */

@@ -24,6 +24,7 @@ TQ_OK, TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_DEVICE, TQ_E
 TQ_F32, TQ_F16 = 0, 1
 TQ_OP_SCORES, TQ_OP_DECODE_ATTN = 1, 2
 TQ_LAW_GAUSSIAN = 0
+TQ_LAW_SPHERE = 1
 
 
 class TQError(RuntimeError):
@@ -122,9 +123,9 @@ class Quantizer:
     ``S`` the fp16 [qjl_m, d] matrix or None for codes-only (value) quantizers.
     """
 
-    def __init__(self, d: int, mse_bits: int, qjl_m: int, diag, S=None, device="cuda"):
-        self.d, self.mse_bits, self.qjl_m = d, mse_bits, qjl_m
-        cent, bnd, dist = tq_codebook(d, mse_bits)
+    def __init__(self, d: int, mse_bits: int, qjl_m: int, diag, S=None, device="cuda", law: int = 0):
+        self.d, self.mse_bits, self.qjl_m, self.law = d, mse_bits, qjl_m, law
+        cent, bnd, dist = tq_codebook(d, mse_bits, law)
         self.distortion = dist
         self.centroids_host, self.boundaries_host = cent, bnd
         self.centroids = torch.from_numpy(cent).to(device)

@@ -83,12 +83,169 @@ static double gauss_distortion(double sigma, int L, const double* c, const doubl
     return D;
 }
 
+// ---- the exact coordinate law of a random unit vector in R^d (TQ_LAW_SPHERE)
+//
+// With t = cos(theta) the density K (1 - t^2)^((d-3)/2) dt becomes
+// K sin(theta)^(d-2) d(theta), smooth on [0, pi], so cell masses are
+// integrated in theta by composite Gauss-Legendre rules (pieces narrower than
+// the density's width, where a 24-point rule is exact to rounding). K is the
+// inverse of the Wallis integral W(d-2) = int_0^pi sin^(d-2). The first moment
+// has the closed form K (1 - t^2)^((d-1)/2) / (d - 1) between the cell ends.
+
+struct GaussLegendre {
+    double x[24], w[24];
+    GaussLegendre()
+    {
+        const int n = 24;
+        for (int i = 0; i < n; ++i) {
+            double z = std::cos(M_PI * (i + 0.75) / (n + 0.5)), dp = 1.0;
+            for (int it = 0; it < 100; ++it) {
+                double p0 = 1.0, p1 = z;  // Legendre recurrence up to P_n
+                for (int k = 2; k <= n; ++k) {
+                    const double p2 = ((2.0 * k - 1.0) * z * p1 - (k - 1.0) * p0) / k;
+                    p0 = p1;
+                    p1 = p2;
+                }
+                dp = n * (z * p1 - p0) / (z * z - 1.0);
+                const double dz = p1 / dp;
+                z -= dz;
+                if (std::fabs(dz) <= 1e-16) break;
+            }
+            x[i] = z;
+            w[i] = 2.0 / ((1.0 - z * z) * dp * dp);
+        }
+    }
+};
+
+static const GaussLegendre& gauss_legendre()
+{
+    static const GaussLegendre g;
+    return g;
+}
+
+// int_{th0}^{th1} sin(th)^p cos(th)^k d(th), pieces no wider than h
+static double sin_pow_integral(double th0, double th1, double p, int k, double h)
+{
+    if (th1 <= th0) return 0.0;
+    const GaussLegendre& g = gauss_legendre();
+    const int pieces = (int)std::ceil((th1 - th0) / h);
+    const double wdt = (th1 - th0) / pieces;
+    double sum = 0.0;
+    for (int j = 0; j < pieces; ++j) {
+        const double mid = th0 + (j + 0.5) * wdt;
+        double part = 0.0;
+        for (int i = 0; i < 24; ++i) {
+            const double th = mid + 0.5 * wdt * g.x[i];
+            const double sn = std::sin(th);
+            double f = sn > 0 ? std::exp(p * std::log(sn)) : (p == 0 ? 1.0 : 0.0);
+            if (k) f *= std::pow(std::cos(th), k);
+            part += g.w[i] * f;
+        }
+        sum += 0.5 * wdt * part;
+    }
+    return sum;
+}
+
+struct SphereLaw {
+    int d;
+    double K, h;
+    explicit SphereLaw(int dim) : d(dim)
+    {
+        double W = (dim - 2) % 2 ? 2.0 : M_PI;  // Wallis: W(n) = (n - 1) / n W(n - 2)
+        for (int n = (dim - 2) % 2 ? 3 : 2; n <= dim - 2; n += 2) W *= (n - 1.0) / n;
+        K = 1.0 / W;
+        h = std::fmin(0.25, 1.5 / std::sqrt((double)dim));
+    }
+    double mass(double a, double b) const
+    {
+        a = std::fmax(a, -1.0);
+        b = std::fmin(b, 1.0);
+        return b > a ? K * sin_pow_integral(std::acos(b), std::acos(a), d - 2.0, 0, h) : 0.0;
+    }
+    double first(double a, double b) const
+    {
+        a = std::fmax(a, -1.0);
+        b = std::fmin(b, 1.0);
+        if (b <= a) return 0.0;
+        const double e = 0.5 * (d - 1);
+        return K / (d - 1) * (std::pow(1.0 - a * a, e) - std::pow(1.0 - b * b, e));
+    }
+    double second(double a, double b) const
+    {
+        a = std::fmax(a, -1.0);
+        b = std::fmin(b, 1.0);
+        return b > a ? K * sin_pow_integral(std::acos(b), std::acos(a), d - 2.0, 2, h) : 0.0;
+    }
+    // the p-quantile, by bisection on the mass below
+    double quantile(double p) const
+    {
+        double lo = -1.0, hi = 1.0;
+        for (int i = 0; i < 80; ++i) {
+            const double mid = 0.5 * (lo + hi);
+            if (mass(-1.0, mid) < p) lo = mid; else hi = mid;
+        }
+        return 0.5 * (lo + hi);
+    }
+};
+
+static int codebook_sphere(int d, int bits, float* cent, float* bnd, double* dist)
+{
+    if (d < 2) return fail(TQ_ERR_UNSUPPORTED, "tq_codebook: the exact law needs d >= 2 (d=%d)", d);
+    const int L = 1 << bits;
+    const SphereLaw law(d);
+    const double sigma = 1.0 / std::sqrt((double)d);
+    double c[256], t[256], cn[256];
+    for (int l = 0; l < L; ++l) c[l] = law.quantile((l + 0.5) / L);
+    const double tol = (bits <= 4 ? 1e-13 : 1e-12) * sigma;
+    bool done = false;
+    for (int it = 0; it < 200000 && !done; ++it) {
+        for (int l = 0; l + 1 < L; ++l) t[l] = 0.5 * (c[l] + c[l + 1]);
+        for (int l = 0; l < L; ++l) {
+            const double a = l == 0 ? -1.0 : t[l - 1], b = l == L - 1 ? 1.0 : t[l];
+            const double m0 = law.mass(a, b);
+            cn[l] = m0 > 0 ? law.first(a, b) / m0 : c[l];
+        }
+        for (int l = 0; l < L / 2; ++l) {  // symmetric law: keep the solution antisymmetric
+            const double v = 0.5 * (cn[L - 1 - l] - cn[l]);
+            cn[l] = -v;
+            cn[L - 1 - l] = v;
+        }
+        double move = 0;
+        for (int l = 0; l < L; ++l) {
+            move = std::fmax(move, std::fabs(cn[l] - c[l]));
+            c[l] = cn[l];
+        }
+        done = move < tol;
+    }
+    if (!done) return fail(TQ_ERR_NOCONV, "tq_codebook: no convergence for d=%d bits=%d (exact law)", d, bits);
+    double cs[256], ts[256];
+    for (int l = 0; l < L; ++l) {
+        cs[l] = round_to_half(c[l]);
+        cent[l] = (float)cs[l];
+    }
+    for (int l = 0; l + 1 < L; ++l) {
+        bnd[l] = (float)(0.5 * (cs[l] + cs[l + 1]));
+        ts[l] = (double)bnd[l];
+    }
+    if (dist) {
+        double D = 0;
+        for (int l = 0; l < L; ++l) {
+            const double a = l == 0 ? -1.0 : ts[l - 1], b = l == L - 1 ? 1.0 : ts[l];
+            D += law.second(a, b) - 2 * cs[l] * law.first(a, b) + cs[l] * cs[l] * law.mass(a, b);
+        }
+        *dist = D;
+    }
+    return TQ_OK;
+}
+
 int codebook(int d, int bits, int law, float* cent, float* bnd, double* dist)
 {
     if (!cent || !bnd) return fail(TQ_ERR_INVALID, "tq_codebook: null output");
-    if (law != TQ_LAW_GAUSSIAN) return fail(TQ_ERR_UNSUPPORTED, "tq_codebook: law %d unsupported", law);
+    if (law != TQ_LAW_GAUSSIAN && law != TQ_LAW_SPHERE)
+        return fail(TQ_ERR_UNSUPPORTED, "tq_codebook: law %d unsupported", law);
     if (d < 1 || d > 65536) return fail(TQ_ERR_UNSUPPORTED, "tq_codebook: d=%d outside 1..65536", d);
     if (bits < 1 || bits > 8) return fail(TQ_ERR_UNSUPPORTED, "tq_codebook: bits=%d outside 1..8", bits);
+    if (law == TQ_LAW_SPHERE) return codebook_sphere(d, bits, cent, bnd, dist);
     const int L = 1 << bits;
     const double sigma = 1.0 / std::sqrt((double)d);
     double c[256], t[256], cn[256];

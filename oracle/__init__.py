@@ -51,6 +51,10 @@ def lib():
         qp = C.POINTER(_Quantizer)
         L.tqref_codebook.argtypes = [C.c_int, C.c_int, dp, fp, fp, dp, dp]
         L.tqref_codebook.restype = C.c_int
+        L.tqref_codebook_law.argtypes = [C.c_int, C.c_int, C.c_int, dp, fp, fp, dp, dp]
+        L.tqref_codebook_law.restype = C.c_int
+        L.tqref_sphere_moments.argtypes = [C.c_int, C.c_double, C.c_double, dp]
+        L.tqref_sphere_moments.restype = None
         L.tqref_lloyd_discrete.argtypes = [dp, dp, C.c_int, C.c_int, dp, dp]
         L.tqref_lloyd_discrete.restype = C.c_int
         L.tqref_gauss_distortion.argtypes = [C.c_int, C.c_int, dp, dp]
@@ -100,18 +104,30 @@ class Codebook:
     iters: int
 
 
-def codebook(d: int, bits: int) -> Codebook:
+LAW_GAUSSIAN, LAW_SPHERE = 0, 1
+
+
+def codebook(d: int, bits: int, law: int = LAW_GAUSSIAN) -> Codebook:
+    """Lloyd-Max codebook for N(0, 1/d) (law 0) or the exact coordinate law of
+    a random unit vector in R^d (law 1, a Beta law of Y^2)."""
     L = 1 << bits
     ce = np.zeros(L, np.float64)
     cs = np.zeros(L, np.float32)
     ts = np.zeros(max(L - 1, 1), np.float32)
     de = C.c_double()
     ds = C.c_double()
-    it = lib().tqref_codebook(d, bits, _p(ce, C.c_double), _p(cs, C.c_float), _p(ts, C.c_float),
-                              C.byref(de), C.byref(ds))
+    it = lib().tqref_codebook_law(d, bits, law, _p(ce, C.c_double), _p(cs, C.c_float), _p(ts, C.c_float),
+                                  C.byref(de), C.byref(ds))
     if it < 0:
-        raise RuntimeError(f"oracle codebook failed (d={d}, bits={bits}): {it}")
+        raise RuntimeError(f"oracle codebook failed (d={d}, bits={bits}, law={law}): {it}")
     return Codebook(d, bits, ce, cs, ts[:L - 1], de.value, ds.value, it)
+
+
+def sphere_moments(d: int, a: float, b: float) -> np.ndarray:
+    """(mass, first, second moment) of the exact coordinate law over (a, b]."""
+    m = np.zeros(3, np.float64)
+    lib().tqref_sphere_moments(d, a, b, _p(m, C.c_double))
+    return m
 
 
 def lloyd_discrete(x: np.ndarray, w: np.ndarray, levels: int):

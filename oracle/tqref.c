@@ -98,12 +98,77 @@ static int had(int i, int j) { return (__builtin_popcount((unsigned)(i & j)) & 1
 /* ------------------------------------------------------------ laws */
 
 typedef struct {
-    int kind;              /* 0 = N(0, sigma^2); 2 = discrete points */
+    int kind;              /* 0 = N(0, sigma^2); 1 = exact coordinate law in dimension dim; 2 = discrete points */
     double sigma;
     const double* x;       /* discrete: sorted points */
     const double* w;       /* discrete: weights */
     int n;
+    int dim;               /* kind 1 */
 } law_t;
+
+/*
+ * The exact law of one coordinate of a uniformly random unit vector in R^d
+ * ([vLLM] "TurboQuant 是什麼：30 秒懶人包": after the random rotation the
+ * coordinates follow a Beta law): density proportional to (1 - t^2)^((d-3)/2)
+ * on [-1, 1], i.e. Y^2 ~ Beta(1/2, (d-1)/2). Its upper tail is
+ *   P(Y > t) = 1/2 I_{1 - t^2}((d-1)/2, 1/2)  for t >= 0,
+ * with I the regularized incomplete beta function, evaluated here from its
+ * continued fraction (modified Lentz) on the side where it converges.
+ */
+static double ibeta_fraction(double a, double b, double x)
+{
+    /* h = 1 + d1 / (1 + d2 / (1 + ...)) with
+     *   d_{2m+1} = -(a + m)(a + b + m) x / ((a + 2m)(a + 2m + 1)),
+     *   d_{2m}   = m (b - m) x / ((a + 2m - 1)(a + 2m)),
+     * evaluated by the modified Lentz method; I_x(a, b) = front / (a h) */
+    const double tiny = 1e-300;
+    double h = 1.0, C = 1.0, Dd = 0.0;
+    for (int i = 1; i <= 40000; ++i) {
+        double num;
+        if (i % 2 == 0) {
+            int m = i / 2;
+            num = m * (b - m) * x / ((a + 2.0 * m - 1.0) * (a + 2.0 * m));
+        } else {
+            int m = (i - 1) / 2;
+            num = -(a + m) * (a + b + m) * x / ((a + 2.0 * m) * (a + 2.0 * m + 1.0));
+        }
+        Dd = 1.0 + num * Dd;
+        if (fabs(Dd) < tiny) Dd = tiny;
+        Dd = 1.0 / Dd;
+        C = 1.0 + num / C;
+        if (fabs(C) < tiny) C = tiny;
+        double step = C * Dd;
+        h *= step;
+        if (fabs(step - 1.0) < 1e-16) break;
+    }
+    return 1.0 / h;
+}
+
+static double ibeta(double a, double b, double x)
+{
+    if (x <= 0.0) return 0.0;
+    if (x >= 1.0) return 1.0;
+    double lfront = a * log(x) + b * log1p(-x) - (lgamma(a) + lgamma(b) - lgamma(a + b));
+    if (x < (a + 1.0) / (a + b + 2.0)) return exp(lfront) / a * ibeta_fraction(a, b, x);
+    return 1.0 - exp(lfront) / b * ibeta_fraction(b, a, 1.0 - x);
+}
+
+/* P(Y > t) under the coordinate law in dimension d (d >= 2) */
+static double sphere_upper(int d, double t)
+{
+    if (t >= 1.0) return 0.0;
+    if (t <= -1.0) return 1.0;
+    if (t >= 0.0) return 0.5 * ibeta(0.5 * (d - 1), 0.5, 1.0 - t * t);
+    return 1.0 - 0.5 * ibeta(0.5 * (d - 1), 0.5, 1.0 - t * t);
+}
+
+/* P(a < Y <= b), from the nearer tail */
+static double sphere_mass(int d, double a, double b)
+{
+    if (a >= 0) return sphere_upper(d, a) - sphere_upper(d, b);
+    if (b <= 0) return sphere_upper(d, -b) - sphere_upper(d, -a);
+    return 1.0 - sphere_upper(d, -a) - sphere_upper(d, b);
+}
 
 static double phi(double t) { return isinf(t) ? 0.0 : exp(-0.5 * t * t) / sqrt(2.0 * M_PI); }
 
@@ -125,6 +190,20 @@ static void law_moments(const law_t* L, double a, double b, double* m0, double* 
         *m0 = norm_mass(al, be);
         *m1 = s * (phi(al) - phi(be));
         *m2 = s * s * (*m0 + tphi(al) - tphi(be));
+    } else if (L->kind == 1) {
+        /* first moment in closed form: the density times t integrates to
+         * -K (1 - t^2)^((d-1)/2) / (d - 1), K the density's normalizer
+         * 1 / B(1/2, (d-1)/2); the second from t^2 (1-t^2)^k = (1-t^2)^k -
+         * (1-t^2)^(k+1): the law in dimension d minus (d-1)/d times the law in
+         * dimension d + 2 */
+        int d = L->dim;
+        double lo = a < -1.0 ? -1.0 : a, hi = b > 1.0 ? 1.0 : b;
+        if (hi <= lo) { *m0 = *m1 = *m2 = 0.0; return; }
+        double K = exp(lgamma(0.5 * d) - lgamma(0.5 * (d - 1)) - 0.5 * log(M_PI));
+        double e = 0.5 * (d - 1);
+        *m0 = sphere_mass(d, lo, hi);
+        *m1 = K / (d - 1) * (pow(1.0 - lo * lo, e) - pow(1.0 - hi * hi, e));
+        *m2 = *m0 - (double)(d - 1) / d * sphere_mass(d + 2, lo, hi);
     } else {
         double s0 = 0, s1 = 0, s2 = 0;
         for (int i = 0; i < L->n; ++i) {
@@ -137,7 +216,7 @@ static void law_moments(const law_t* L, double a, double b, double* m0, double* 
 
 static double law_sigma(const law_t* L)
 {
-    if (L->kind == 0) return L->sigma;
+    if (L->kind == 0 || L->kind == 1) return L->sigma;
     double s0 = 0, s1 = 0, s2 = 0;
     for (int i = 0; i < L->n; ++i) { s0 += L->w[i]; s1 += L->w[i] * L->x[i]; s2 += L->w[i] * L->x[i] * L->x[i]; }
     double mu = s1 / s0;
@@ -150,8 +229,11 @@ static double law_sigma(const law_t* L)
 static int lloyd(const law_t* L, int nl, double* c, double tol, int maxit, int symmetric)
 {
     double sg = law_sigma(L);
+    /* start spread over +-2.5 sigma (inside the support for the bounded law) */
+    double r = 2.5 * sg;
+    if (L->kind == 1 && r > 1.0 - 1.0 / nl) r = 1.0 - 1.0 / nl;
     for (int l = 0; l < nl; ++l)
-        c[l] = (nl == 1) ? 0.0 : sg * (-2.5 + 5.0 * l / (nl - 1));
+        c[l] = (nl == 1) ? 0.0 : r * (-1.0 + 2.0 * l / (nl - 1));
     double t[TQREF_MAXL + 1], cn[TQREF_MAXL];
     for (int it = 1; it <= maxit; ++it) {
         t[0] = -INFINITY; t[nl] = INFINITY;
@@ -201,17 +283,21 @@ static double law_distortion(const law_t* L, int nl, const double* c, const doub
  * and of the stored codebook. Returns iterations, or -1 if not converged,
  * -2 for bad arguments.
  */
-int tqref_codebook(int d, int bits, double* c_exact, float* c_stored, float* t_stored,
-                   double* dist_exact, double* dist_stored)
+int tqref_codebook_law(int d, int bits, int law, double* c_exact, float* c_stored, float* t_stored,
+                       double* dist_exact, double* dist_stored)
 {
-    if (d < 1 || bits < 1 || bits > 8) return -2;
+    if (d < 1 || bits < 1 || bits > 8 || law < 0 || law > 1) return -2;
+    if (law == 1 && d < 2) return -2;
     int nl = 1 << bits;
-    law_t L = {0, 1.0 / sqrt((double)d), NULL, NULL, 0};
+    law_t L = {law, 1.0 / sqrt((double)d), NULL, NULL, 0, d};
     double c[TQREF_MAXL];
     /* 1e-15 sigma for the widths the cache uses (<= 4 bits); wider codebooks
      * have cells of tiny mass whose conditional means carry more rounding
-     * noise, so they stop at 1e-12 sigma */
-    int it = lloyd(&L, nl, c, bits <= 4 ? 1e-15 : 1e-12, 2000000, 1);
+     * noise, so they stop at 1e-12 sigma. The exact law's masses come from a
+     * continued fraction accurate to a few 1e-15, so it stops at 1e-13 sigma. */
+    double tol = bits <= 4 ? 1e-15 : 1e-12;
+    if (law == 1 && tol < 1e-13) tol = 1e-13;
+    int it = lloyd(&L, nl, c, tol, 2000000, 1);
     if (it < 0) return -1;
     double t[TQREF_MAXL], cs[TQREF_MAXL], ts[TQREF_MAXL];
     for (int l = 0; l < nl; ++l) {
@@ -229,12 +315,25 @@ int tqref_codebook(int d, int bits, double* c_exact, float* c_stored, float* t_s
     return it;
 }
 
+int tqref_codebook(int d, int bits, double* c_exact, float* c_stored, float* t_stored,
+                   double* dist_exact, double* dist_stored)
+{
+    return tqref_codebook_law(d, bits, 0, c_exact, c_stored, t_stored, dist_exact, dist_stored);
+}
+
+/* moments (m0, m1, m2) of the coordinate law in dimension d over (a, b] */
+void tqref_sphere_moments(int d, double a, double b, double* m)
+{
+    law_t L = {1, 1.0 / sqrt((double)d), NULL, NULL, 0, d};
+    law_moments(&L, a, b, &m[0], &m[1], &m[2]);
+}
+
 /* The same Lloyd iteration on a discrete law (sorted points x, weights w);
  * used by the brute-force optimality test. Returns iterations or -1. */
 int tqref_lloyd_discrete(const double* x, const double* w, int n, int nl, double* c_out,
                          double* dist)
 {
-    law_t L = {2, 0, x, w, n};
+    law_t L = {2, 0, x, w, n, 0};
     double c[TQREF_MAXL], t[TQREF_MAXL];
     int it = lloyd(&L, nl, c, 1e-15, 100000, 0);
     for (int l = 0; l < nl; ++l) c_out[l] = c[l];
@@ -246,7 +345,7 @@ int tqref_lloyd_discrete(const double* x, const double* w, int n, int nl, double
 /* analytic distortion of an arbitrary codebook under N(0, 1/d) */
 double tqref_gauss_distortion(int d, int nl, const double* c, const double* t)
 {
-    law_t L = {0, 1.0 / sqrt((double)d), NULL, NULL, 0};
+    law_t L = {0, 1.0 / sqrt((double)d), NULL, NULL, 0, 0};
     return law_distortion(&L, nl, c, t);
 }
 

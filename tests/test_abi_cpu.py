@@ -39,12 +39,25 @@ def test_host_codebook_equals_oracle(d, bits):
     assert abs(dist - ref.dist_stored) <= 1e-12 * ref.dist_stored
 
 
+@pytest.mark.parametrize("d", [2, 3, 4, 64, 128, 256])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_host_sphere_codebook_equals_oracle(d, bits):
+    """The library's exact-law solver (Gauss-Legendre cell masses) against the
+    oracle's (incomplete-beta continued fraction): same stored codebook."""
+    cent, bnd, dist = tq.tq_codebook(d, bits, tq.TQ_LAW_SPHERE)
+    ref = oracle.codebook(d, bits, oracle.LAW_SPHERE)
+    assert np.array_equal(cent, ref.centroids)
+    assert np.array_equal(bnd, ref.boundaries)
+    assert abs(dist - ref.dist_stored) <= 1e-8 * ref.dist_stored
+
+
 def test_codebook_wide_and_errors():
     cent, bnd, _ = tq.tq_codebook(128, 6)
     assert np.array_equal(cent, oracle.codebook(128, 6).centroids)
     L = tq.lib()
     buf = np.zeros(256, np.float32)
-    assert L.tq_codebook(128, 3, 1, buf.ctypes.data, buf.ctypes.data, None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_codebook(128, 3, 2, buf.ctypes.data, buf.ctypes.data, None) == tq.TQ_ERR_UNSUPPORTED
+    assert L.tq_codebook(1, 3, tq.TQ_LAW_SPHERE, buf.ctypes.data, buf.ctypes.data, None) == tq.TQ_ERR_UNSUPPORTED
     assert L.tq_codebook(128, 0, 0, buf.ctypes.data, buf.ctypes.data, None) == tq.TQ_ERR_UNSUPPORTED
     assert L.tq_codebook(128, 9, 0, buf.ctypes.data, buf.ctypes.data, None) == tq.TQ_ERR_UNSUPPORTED
     assert L.tq_codebook(0, 3, 0, buf.ctypes.data, buf.ctypes.data, None) == tq.TQ_ERR_UNSUPPORTED

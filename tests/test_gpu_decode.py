@@ -194,6 +194,32 @@ def test_decode_step_argument_errors():
             tq.tq_decode_step(qkg, qvg, pk, pv, 2, T, cap, 8, z, z, q, out)
 
 
+def test_decode_with_exact_law_codebooks():
+    """Quantize and decode with codebooks solved for the exact coordinate law
+    (keys 2 + 1, values 3-bit); the oracle uses the same codebooks."""
+    tq = tqmod()
+    d, ns, T, G = 128, 3, 777, 8
+    diag_k = synth.diag_signs(7, synth.ROLE_DIAG_K, d)
+    diag_v = synth.diag_signs(7, synth.ROLE_DIAG_V, d)
+    S = synth.proj_matrix_f16(7, synth.ROLE_PROJ_K, d, d)
+    qkg = tq.Quantizer(d, 2, d, diag_k, S, DEV, law=tq.TQ_LAW_SPHERE)
+    qvg = tq.Quantizer(d, 3, 0, diag_v, None, DEV, law=tq.TQ_LAW_SPHERE)
+    qko = oracle.Quantizer(d, 2, d, diag_k, S, cb=oracle.codebook(d, 2, oracle.LAW_SPHERE))
+    qvo = oracle.Quantizer(d, 3, 0, diag_v, None, cb=oracle.codebook(d, 3, oracle.LAW_SPHERE))
+    K = synth.to_f16(synth.normals(43, synth.ROLE_DATA_K, np.arange(ns * T * d)).reshape(ns * T, d) * 2)
+    V = synth.to_f16(synth.normals(43, synth.ROLE_DATA_V, np.arange(ns * T * d)).reshape(ns * T, d))
+    Q = synth.to_f16(synth.normals(43, synth.ROLE_QUERY, np.arange(ns * G * d)).reshape(ns, G, d))
+    pk, pv = tq.Packed.empty(qkg, ns * T, DEV), tq.Packed.empty(qvg, ns * T, DEV)
+    tq.tq_quantize(qkg, torch.from_numpy(K).to(DEV), pk)
+    tq.tq_quantize(qvg, torch.from_numpy(V).to(DEV), pv)
+    hk, hv = pk.to_host(), pv.to_host()
+    check_quantize(qko, K.astype(np.float64), hk)
+    check_quantize(qvo, V.astype(np.float64), hv)
+    out = run_decode(qkg, qvg, pk, pv, ns, T, G, torch.from_numpy(Q).to(DEV))
+    check_close(out, oracle.decode_attn(qko, qvo, opacked(qko, hk), opacked(qvo, hv), ns, T, G,
+                                        Q.astype(np.float64)), what="exact-law codebooks")
+
+
 def _kv_case(cfg, layers, sample):
     """Generate, quantize and decode ``layers`` of cfg on the GPU; check sampled streams.
 
