@@ -229,6 +229,8 @@ def main():
     if not args.no_extras:
         result["decode_step"] = decode_step(tq, qk, qv, units, T, G, d, kern["decode_attn"]["us_per_launch"],
                                             kb + vb, dev)
+        result["unfused_baseline"] = unfused_baseline(tq, qk, qv, units, T, G, d,
+                                                      kern["decode_attn"]["us_per_launch"], dev)
         result["small_keyset"] = small_keyset(tq, qk, dev)
         if args.workload == "128k":
             result["prefill_scores"] = prefill_scores(tq, qk, units[0]["PK"], T, dev)
@@ -339,6 +341,61 @@ def decode_step(tq, qk, qv, units, T, G, d, attn_us, tok_bytes, dev, passes=3):
     return {"us_per_launch": round(us, 2), "decode_attn_us_per_launch": attn_us,
             "append_overhead_us": round(us - attn_us, 2), "GB_per_s": round(alg / (us * 1e-6) / 1e9, 1),
             "note": "append of one new token per stream fused into the decode launch"}
+
+
+def unfused_baseline(tq, qk, qv, units, T, G, d, fused_us, dev, passes=3, n_units=8):
+    """The engines' unfused design on the same caches, for comparison: each
+    batch's packed K and V are dequantized to fp16 (tq_dequantize, keys with
+    the QJL term so scores match the estimator), then dense attention runs
+    with torch (fp16 batched products, fp32 softmax). Timed per batch over up
+    to n_units distinct batches; reported beside the fused decode_attn."""
+    import torch
+    ns = units[0]["ns"]
+    n = ns * T
+    Kd = torch.empty((n, d), dtype=torch.float16, device=dev)
+    Vd = torch.empty((n, d), dtype=torch.float16, device=dev)
+    scale = 1.0 / (d ** 0.5)
+    stream = torch.cuda.current_stream()
+
+    def dequant(u):
+        tq.tq_dequantize(qk, u["PK"], n, True, Kd)
+        tq.tq_dequantize(qv, u["PV"], n, False, Vd)
+
+    def attend(u):
+        K3, V3 = Kd.view(ns, T, d), Vd.view(ns, T, d)
+        qt = u["Q"].to(torch.float16).transpose(1, 2).contiguous()      # [ns, d, G]
+        z = torch.bmm(K3, qt).float() * scale                              # [ns, T, G]
+        w = torch.softmax(z, dim=1).transpose(1, 2).contiguous().to(torch.float16)
+        return torch.bmm(w, V3).float()                                    # [ns, G, d]
+
+    us = [u for u in units if u["ns"] == ns][:n_units]
+    dequant(us[0]); attend(us[0])
+    ev_d, ev_a = [], []
+    for _ in range(passes):
+        for u in us:
+            a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            a.record(stream)
+            dequant(u)
+            b.record(stream)
+            attend(u)
+            c.record(stream)
+            ev_d.append((a, b))
+            ev_a.append((b, c))
+    torch.cuda.synchronize()
+    dq = sum(a.elapsed_time(b) for a, b in ev_d) / len(ev_d) * 1e3
+    at = sum(a.elapsed_time(b) for a, b in ev_a) / len(ev_a) * 1e3
+    # agreement with the fused step on the last batch (fp16 rounding of the dequantized cache)
+    u = us[-1]
+    dequant(u)
+    ref = attend(u)
+    fused = torch.empty((ns, G, d), dtype=torch.float32, device=dev)
+    tq.tq_decode_attn(qk, qv, u["PK"], u["PV"], ns, T, G, u["Q"], fused)
+    torch.cuda.synchronize()
+    diff = float((ref - fused).abs().max())
+    return {"us_per_launch": round(dq + at, 2), "dequantize_us": round(dq, 2), "dense_attention_us": round(at, 2),
+            "fused_decode_attn_us": fused_us, "fused_speedup": round((dq + at) / fused_us, 2),
+            "max_abs_diff_vs_fused": round(diff, 5),
+            "note": "dequantize to fp16 + torch fp16 attention on the same packed caches"}
 
 
 def prefill_scores(tq, qk, pk, T, dev, n_q=2048, reps=5):
