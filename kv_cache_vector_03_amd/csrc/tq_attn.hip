@@ -220,61 +220,69 @@ __global__ __launch_bounds__(256) void k_decode(const uint32_t* __restrict__ kco
 
 // Merge the chunk partials of one (stream, head) and rotate back to the value
 // domain. Partials hold (max, sum, accumulator) with max in log2 units.
-// Thread (lane c, slot i) sums chunks c, c + CL, ... of float4 slot i; the
-// loop is unrolled so that many chunks' loads are in flight at once.
+// Thread (lane c, slot i) folds chunks c, c + CL, ... of float4 slot i into a
+// running (max, sum, accumulator) in a single pass over the partials (the
+// loop is unrolled so that many chunks' loads are in flight at once); wave 0
+// then merges the CL running results.
 template <int D>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ parts, int n_chunks, int G,
                                                  const uint32_t* __restrict__ vdiag,
                                                  float* __restrict__ out)
 {
     constexpr int R = D / 64, NV = D / 4, CL = 256 / NV, PS = part_stride(D);
-    __shared__ float red[4];
     __shared__ float4 om[CL][NV];
-    __shared__ float ol[CL];
+    __shared__ float ol[CL], omx[CL];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t sh = blockIdx.x;  // s * G + h
     const int64_t s = sh / G, h = sh % G;
     const int64_t stride = (int64_t)G * PS;
     const float* p0 = parts + ((s * n_chunks) * G + h) * PS;
 
-    float m = -INFINITY;
-    for (int c = tid; c < n_chunks; c += 256) m = fmaxf(m, p0[c * stride]);
-    m = wave_max(m);
-    if (lane == 0) red[wid] = m;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-
+    // one pass: thread (cl, i) folds chunks cl, cl + CL, ... into a running
+    // (max, sum, accumulator) for coordinates 4 i .. 4 i + 3
     const int cl = tid / NV, i = tid % NV;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float l = 0.f;
-    if (M != -INFINITY) {
+    float l = 0.f, m = -INFINITY;
 #pragma unroll 8
-        for (int c = cl; c < n_chunks; c += CL) {
-            const float* pc = p0 + c * stride;
-            const float2 ml = *reinterpret_cast<const float2*>(pc);
-            const float4 a = reinterpret_cast<const float4*>(pc + kPartAcc)[i];
-            const float f = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
-            acc.x += f * a.x;
-            acc.y += f * a.y;
-            acc.z += f * a.z;
-            acc.w += f * a.w;
-            l += f * ml.y;
-        }
+    for (int c = cl; c < n_chunks; c += CL) {
+        const float* pc = p0 + c * stride;
+        const float2 ml = *reinterpret_cast<const float2*>(pc);
+        const float4 a = reinterpret_cast<const float4*>(pc + kPartAcc)[i];
+        // branch-free, so that the unrolled iterations' loads issue together;
+        // a chunk with no tokens (max -inf) contributes nothing
+        const float nm = fmaxf(m, ml.x);
+        const float fo = m == -INFINITY ? 0.f : exp2f(m - nm);
+        const float fn = ml.x == -INFINITY ? 0.f : exp2f(ml.x - nm);
+        acc.x = acc.x * fo + fn * a.x;
+        acc.y = acc.y * fo + fn * a.y;
+        acc.z = acc.z * fo + fn * a.z;
+        acc.w = acc.w * fo + fn * a.w;
+        l = l * fo + fn * ml.y;
+        m = nm;
     }
     om[cl][i] = acc;
-    if (i == 0) ol[cl] = l;
+    if (i == 0) {
+        ol[cl] = l;
+        omx[cl] = m;
+    }
     __syncthreads();
     if (wid != 0) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < CL; ++q) M = fmaxf(M, omx[q]);
+    float fq[CL];
+#pragma unroll
+    for (int q = 0; q < CL; ++q) fq[q] = omx[q] == -INFINITY ? 0.f : exp2f(omx[q] - M);
     const float* omf = reinterpret_cast<const float*>(&om[0][0]);
     float v[R];
     float L = 0.f;
 #pragma unroll
-    for (int q = 0; q < CL; ++q) L += ol[q];
+    for (int q = 0; q < CL; ++q) L += fq[q] * ol[q];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         v[r] = 0.f;
 #pragma unroll
-        for (int q = 0; q < CL; ++q) v[r] += omf[q * D + 64 * r + lane];
+        for (int q = 0; q < CL; ++q) v[r] += fq[q] * omf[q * D + 64 * r + lane];
     }
     fwht_wave<R>(v, lane);
     uint32_t dm[R];

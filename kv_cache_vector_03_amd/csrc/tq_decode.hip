@@ -355,6 +355,12 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
         const int64_t w0 = c0 + (int64_t)wid * (tc / 4);
         const int64_t w1 = w0 + tc / 4 < c1 ? w0 + tc / 4 : c1;
 
+        // the first full step's loads go out first, so that they are in flight
+        // while the query fragments and the norms of the range arrive
+        const int64_t nfull = w1 > w0 ? (w1 - w0) >> 5 : 0;  // a wave past the chunk's end has none
+        Step<BK, BV> sa, sb;
+        if (nfull > 0) load_full<D, BK, QJL, BV>(sa, base + w0, loff, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
+
         half8_t bq[KSTEPS];
 #pragma unroll
         for (int k = 0; k < KSTEPS; ++k) bq[k] = frags[(s * KSTEPS + k) * 64 + lane];
@@ -503,9 +509,6 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
         // then at most one partial step with clamped loads and masked scores
         using Full = std::integral_constant<bool, false>;
         using Tail = std::integral_constant<bool, true>;
-        const int64_t nfull = w1 > w0 ? (w1 - w0) >> 5 : 0;  // a wave past the chunk's end has none
-        Step<BK, BV> sa, sb;
-        if (nfull > 0) load_full<D, BK, QJL, BV>(sa, base + w0, loff, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
         int64_t i = 0;
         for (; i + 2 <= nfull; i += 2) {
             const int64_t tb = w0 + 32 * i;
