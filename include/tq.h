@@ -27,8 +27,10 @@
  *    failures return TQ_ERR_DEVICE. n == 0 is a no-op returning TQ_OK.
  *  - Alignment: every device buffer must be 16-byte aligned, except norm and
  *    rnorm arrays (2-byte aligned).
- *  - Supported shapes: d in {64, 128, 256}; mse_bits in 1..4;
- *    qjl_m in {0, d}.
+ *  - Supported shapes: d in {64, 128, 256}; mse_bits in 1..8 (widths 5..8,
+ *    such as the 8-bit key / 4-bit value split measured in the vLLM benchmark
+ *    summary, section "vLLM 工程師的實測", run on plain wide-code kernels;
+ *    widths 1..4 on the tuned ones); qjl_m in {0, d}.
  *  - Inputs with ||x|| >= 65504 overflow the fp16 norm and are out of
  *    contract (stored norm becomes inf); non-finite inputs likewise.
  *
@@ -81,7 +83,7 @@ extern "C" {
 /* Quantizer state. All pointers are device pointers owned by the caller. */
 typedef struct tq_quantizer {
     int d;                       /* vector length: 64, 128 or 256 */
-    int mse_bits;                /* bits of the scalar codes: 1..4 */
+    int mse_bits;                /* bits of the scalar codes: 1..8 */
     int qjl_m;                   /* 0: codes only (values); d: codes + QJL signs (keys) */
     const float* centroids;      /* [2^mse_bits], ascending, from tq_codebook */
     const float* boundaries;     /* [2^mse_bits - 1], from tq_codebook */
@@ -195,7 +197,10 @@ int tq_decode_step(const tq_quantizer* qk, const tq_quantizer* qv,
 /*
  * tq_workspace_size -- device workspace bytes for op:
  *   TQ_OP_SCORES:      n_a = n_q, n_b = n_keys, G ignored;
- *   TQ_OP_DECODE_ATTN: n_a = n_streams, n_b = T, G = heads per stream.
+ *   TQ_OP_DECODE_ATTN: n_a = n_streams, n_b = T, G = heads per stream; the
+ *                      value quantizer is not an argument, so the size covers
+ *                      every value width (the wide-code kernels split the
+ *                      tokens into more chunks than the tuned ones).
  * Returns 0 for unknown ops or unsupported quantizers.
  */
 size_t tq_workspace_size(int op, const tq_quantizer* qk, int64_t n_a, int64_t n_b, int G);

@@ -36,7 +36,7 @@ HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-ffp-contract=off", "-Wall", f"-I{I
 EXTRA_FLAGS = {"tq_quantize_m128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 SOURCES = ["tq_host.cpp", "tq_api.cpp", "tq_quantize.hip", "tq_quantize_m128.hip", "tq_attn.hip",
-           "tq_decode.hip", "tq_launch.hip"]
+           "tq_decode.hip", "tq_launch.hip", "tq_wide.hip"]
 
 
 def _run(cmd):

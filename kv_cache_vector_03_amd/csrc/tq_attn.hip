@@ -411,7 +411,10 @@ int launch_decode(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packe
         }
         int rc = launch_qprep(qk, q, q_dtype, n_streams * G, qr, p, s);
         if (rc != TQ_OK) return rc;
-        switch (qk->d) {
+        if (qk->mse_bits > 4 || qv->mse_bits > 4) {
+            rc = launch_decode_wide(qk, qv, k, v, n_streams, T, stride, G, qr, p, zscale, parts, plan.n_chunks, s);
+            if (rc != TQ_OK) return rc;
+        } else switch (qk->d) {
             case 64: decode_d<64>(qk, qv, k, v, n_streams, T, stride, G, qr, p, zscale, out, parts, plan.n_chunks, s); break;
             case 128: decode_d<128>(qk, qv, k, v, n_streams, T, stride, G, qr, p, zscale, out, parts, plan.n_chunks, s); break;
             default: decode_d<256>(qk, qv, k, v, n_streams, T, stride, G, qr, p, zscale, out, parts, plan.n_chunks, s); break;

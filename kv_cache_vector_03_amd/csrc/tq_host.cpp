@@ -296,8 +296,8 @@ int check_quantizer(const tq_quantizer* q, const char* who, const char* role)
     if (!q) return fail(TQ_ERR_INVALID, "%s: %s quantizer is NULL", who, role);
     if (q->d != 64 && q->d != 128 && q->d != 256)
         return fail(TQ_ERR_UNSUPPORTED, "%s: %s d=%d not in {64,128,256}", who, role, q->d);
-    if (q->mse_bits < 1 || q->mse_bits > 4)
-        return fail(TQ_ERR_UNSUPPORTED, "%s: %s mse_bits=%d not in 1..4", who, role, q->mse_bits);
+    if (q->mse_bits < 1 || q->mse_bits > 8)
+        return fail(TQ_ERR_UNSUPPORTED, "%s: %s mse_bits=%d not in 1..8", who, role, q->mse_bits);
     if (q->qjl_m != 0 && q->qjl_m != q->d)
         return fail(TQ_ERR_UNSUPPORTED, "%s: %s qjl_m=%d must be 0 or d", who, role, q->qjl_m);
     if (!q->centroids || !q->boundaries || !q->diag_signs)
@@ -346,16 +346,16 @@ size_t scores_frag_bytes(const tq_quantizer* q, int64_t n_q)
 
 size_t scores_ws(const tq_quantizer* q, int64_t n_q)
 {
-    // d = 128: MFMA query fragments; else prepared queries: fp32 q' [n_q][d]
-    // and p = S q' [n_q][m]
-    if (q->d == 128) return scores_frag_bytes(q, n_q);
+    // d = 128 with codes of at most 4 bits: MFMA query fragments; else
+    // prepared queries: fp32 q' [n_q][d] and p = S q' [n_q][m]
+    if (q->d == 128 && q->mse_bits <= 4) return scores_frag_bytes(q, n_q);
     return up256((size_t)n_q * q->d * 4) + up256((size_t)n_q * (q->qjl_m ? q->qjl_m : 1) * 4);
 }
 
-DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G)
+DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G, bool wide)
 {
     DecodePlan p{};
-    p.mfma = qk->d == 128 && G <= 8;
+    p.mfma = qk->d == 128 && G <= 8 && !wide;
     if (p.mfma) {
         // spread the n_streams * T tokens over at most kDecodeSlots equal chunks
         // (multiples of 128 tokens: four waves of 32-token steps)
@@ -396,7 +396,10 @@ size_t tq_workspace_size(int op, const tq_quantizer* qk, int64_t n_a, int64_t n_
     if (op == TQ_OP_SCORES) return tq::scores_ws(qk, n_a);
     if (op == TQ_OP_DECODE_ATTN) {
         if (G < 1 || G > 16 || n_b < 1) return 0;
-        return tq::decode_plan(qk, n_a, n_b, G).total;
+        // the value width is not an argument: enough for either kernel family
+        const size_t a = tq::decode_plan(qk, n_a, n_b, G, false).total;
+        const size_t b = tq::decode_plan(qk, n_a, n_b, G, true).total;
+        return a > b ? a : b;
     }
     return 0;
 }

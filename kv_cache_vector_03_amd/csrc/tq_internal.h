@@ -34,12 +34,13 @@ constexpr int kPartAcc = 4;
 constexpr int kDecodeSlots = 512;
 
 struct DecodePlan {
-    bool mfma;          // MFMA kernel (d = 128, G <= 8); else the scalar kernel
+    bool mfma;          // MFMA kernel (d = 128, G <= 8, widths <= 4); else a scalar kernel
     int64_t tc;         // tokens per block
     int n_chunks;       // blocks per stream
     size_t off_qr, off_p, off_frag, off_parts, total;
 };
-DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G);
+// wide: a key or value code width above 4 bits (the scalar wide-code kernel)
+DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G, bool wide);
 
 // compute units of the current device (cached per device)
 int device_cus();
@@ -77,6 +78,18 @@ int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_
                        const tq_packed* v, int64_t n_streams, int64_t T, int64_t stride, int G, const void* q,
                        int q_dtype, float zscale, void* frags, float* parts, int n_chunks, int tc,
                        const AppendArgs* app, hipStream_t s);
+
+// code widths 5..8 (tq_wide.hip); scores and decode take prepared queries
+// (launch_qprep) like the scalar narrow kernels
+int launch_quantize_wide(const tq_quantizer* q, const void* x, int dtype, int64_t n, const tq_packed* out,
+                         hipStream_t s);
+int launch_dequantize_wide(const tq_quantizer* q, const tq_packed* in, int64_t n, int include_qjl, void* out,
+                           int dtype, hipStream_t s);
+int launch_scores_wide(const tq_quantizer* q, const tq_packed* k, int64_t n_keys, const float* qr, const float* p,
+                       int64_t n_q, float* scores, hipStream_t s);
+int launch_decode_wide(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k, const tq_packed* v,
+                       int64_t n_streams, int64_t T, int64_t stride, int G, const float* qr, const float* p,
+                       float zscale, float* parts, int n_chunks, hipStream_t s);
 
 }  // namespace tq
 

@@ -640,6 +640,7 @@ void dequant_d(const tq_quantizer* q, const tq_packed* in, int64_t n, int qjl, v
 int launch_quantize(const tq_quantizer* q, const void* x, int dtype, int64_t n, const tq_packed* out,
                     hipStream_t s)
 {
+    if (q->mse_bits > 4) return launch_quantize_wide(q, x, dtype, n, out, s);
     switch (q->d) {
         case 64: quantize_d<64>(q, x, dtype, n, out, s); break;
         case 128: quantize_d<128>(q, x, dtype, n, out, s); break;
@@ -662,6 +663,7 @@ int launch_qprep(const tq_quantizer* q, const void* queries, int dtype, int64_t 
 int launch_dequantize(const tq_quantizer* q, const tq_packed* in, int64_t n, int include_qjl, void* out,
                       int dtype, hipStream_t s)
 {
+    if (q->mse_bits > 4) return launch_dequantize_wide(q, in, n, include_qjl, out, dtype, s);
     switch (q->d) {
         case 64: dequant_d<64>(q, in, n, include_qjl, out, dtype, s); break;
         case 128: dequant_d<128>(q, in, n, include_qjl, out, dtype, s); break;

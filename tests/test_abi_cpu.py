@@ -30,7 +30,7 @@ def test_exports_every_declared_function():
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
-@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_host_codebook_equals_oracle(d, bits):
     cent, bnd, dist = tq.tq_codebook(d, bits)
     ref = oracle.codebook(d, bits)
@@ -89,7 +89,7 @@ def test_quantize_argument_errors():
     assert quantize_rc(qstruct(d=96)) == tq.TQ_ERR_UNSUPPORTED
     assert quantize_rc(qstruct(d=32)) == tq.TQ_ERR_UNSUPPORTED
     assert quantize_rc(qstruct(bits=0)) == tq.TQ_ERR_UNSUPPORTED
-    assert quantize_rc(qstruct(bits=5)) == tq.TQ_ERR_UNSUPPORTED
+    assert quantize_rc(qstruct(bits=9)) == tq.TQ_ERR_UNSUPPORTED
     assert quantize_rc(qstruct(m=64)) == tq.TQ_ERR_UNSUPPORTED
     assert quantize_rc(qstruct(S=False)) == tq.TQ_ERR_INVALID
     assert quantize_rc(qstruct(), n=-1) == tq.TQ_ERR_INVALID
@@ -135,7 +135,10 @@ def test_scores_and_decode_argument_errors():
         return L.tq_decode_attn(C.byref(qk), C.byref(qvv), C.byref(p), C.byref(pv), ns, T, G,
                                 A + 0x8000, tq.TQ_F16, C.c_float(scale), A + 0x9000, ws, wsb, None)
 
-    assert dec(wsb=wsd - 1) == tq.TQ_ERR_WORKSPACE
+    # tq_workspace_size covers either kernel family (the value width is not
+    # an argument); the wide-code plan (8-bit values here) needs all of it
+    assert dec(qvv=qstruct(bits=8, m=0, S=False), wsb=wsd - 1) == tq.TQ_ERR_WORKSPACE
+    assert dec(wsb=4096) == tq.TQ_ERR_WORKSPACE
     assert dec(G=0) == tq.TQ_ERR_UNSUPPORTED
     assert dec(G=17) == tq.TQ_ERR_UNSUPPORTED
     assert dec(T=0) == tq.TQ_ERR_INVALID

@@ -50,7 +50,8 @@ def test_max_table(bits):
     np.testing.assert_allclose(half, MAX_TABLE[bits], atol=6e-4)
 
 
-@pytest.mark.parametrize("d,bits", [(64, 2), (128, 3), (256, 4), (128, 4), (32, 2)])
+@pytest.mark.parametrize("d,bits", [(64, 2), (128, 3), (256, 4), (128, 4), (32, 2), (64, 5), (256, 7),
+                                    (128, 8)])
 def test_stored_codebook_rules(d, bits):
     cb = oracle.codebook(d, bits)
     L = 1 << bits
