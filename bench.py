@@ -232,6 +232,7 @@ def main():
         result["unfused_baseline"] = unfused_baseline(tq, qk, qv, units, T, G, d,
                                                       kern["decode_attn"]["us_per_launch"], dev)
         result["small_keyset"] = small_keyset(tq, qk, dev)
+        result["wide_widths"] = wide_widths(tq, qv, units[0], T, G, d, diag_k, S, diag_v, dev)
         if args.workload == "128k":
             result["prefill_scores"] = prefill_scores(tq, qk, units[0]["PK"], T, dev)
 
@@ -341,6 +342,51 @@ def decode_step(tq, qk, qv, units, T, G, d, attn_us, tok_bytes, dev, passes=3):
     return {"us_per_launch": round(us, 2), "decode_attn_us_per_launch": attn_us,
             "append_overhead_us": round(us - attn_us, 2), "GB_per_s": round(alg / (us * 1e-6) / 1e9, 1),
             "note": "append of one new token per stream fused into the decode launch"}
+
+
+def wide_widths(tq, qv, u, T, G, d, diag_k, S, diag_v, dev, passes=3):
+    """Code widths above 4 bits (the wide-code kernels) on the first batch: 8-bit
+    keys (7-bit codes + the 1-bit sketch) beside the workload's values, and
+    8-bit values; quantize and decode times per launch with their algorithmic
+    GB/s."""
+    import torch
+    ns = u["ns"]
+    nvec = ns * T
+    qk8 = tq.Quantizer(d, 7, d, diag_k, S, dev)
+    qv8 = tq.Quantizer(d, 8, 0, diag_v, None, dev)
+    pk8, pv8 = tq.Packed.empty(qk8, nvec, dev), tq.Packed.empty(qv8, nvec, dev)
+    ws = tq.workspace(tq.tq_workspace_size(tq.TQ_OP_DECODE_ATTN, qk8, ns, T, G), dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        ev = []
+        for _ in range(passes):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e3
+
+    kb8 = packed_bytes_per_vector(d, 7, True)
+    vbw = packed_bytes_per_vector(d, qv.mse_bits, False)
+    vb8 = packed_bytes_per_vector(d, 8, False)
+    res = {}
+    for name, fn, alg in (
+            ("quantize_k8", lambda: tq.tq_quantize(qk8, u["K"], pk8), nvec * (2 * d + kb8)),
+            ("quantize_v8", lambda: tq.tq_quantize(qv8, u["V"], pv8), nvec * (2 * d + vb8)),
+            (f"decode_k8v{qv.mse_bits}",
+             lambda: tq.tq_decode_attn(qk8, qv, pk8, u["PV"], ns, T, G, u["Q"], u["out"], ws=ws),
+             nvec * (kb8 + vbw) + ns * G * d * 6),
+            ("decode_k8v8", lambda: tq.tq_decode_attn(qk8, qv8, pk8, pv8, ns, T, G, u["Q"], u["out"], ws=ws),
+             nvec * (kb8 + vb8) + ns * G * d * 6)):
+        us = timed(fn)
+        res[name] = {"us_per_launch": round(us, 2), "GB_per_s": round(alg / (us * 1e-6) / 1e9, 1),
+                     "frac_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    res["note"] = "plain wide-code kernels (binary-search codes, scalar scores and decode)"
+    return res
 
 
 def unfused_baseline(tq, qk, qv, units, T, G, d, fused_us, dev, passes=3, n_units=8):

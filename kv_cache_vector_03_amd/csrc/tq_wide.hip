@@ -67,12 +67,15 @@ __global__ __launch_bounds__(64 * kWaves) void k_quantize_wide(const void* __res
     __shared__ float tb[kMaxL], cb[kMaxL];
     __shared__ float res[kWaves][D];
     __shared__ unsigned char cidx[kWaves][D];
+    extern __shared__ uint16_t st[];  // QJL: S transposed, st[i * D + j] = S[j][i]
     const int L = 1 << b;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     for (int l = threadIdx.x; l < L; l += blockDim.x) {
         cb[l] = cent[l];
         tb[l] = l < L - 1 ? bnd[l] : INFINITY;
     }
+    if constexpr (QJL)
+        for (int e = threadIdx.x; e < D * D; e += blockDim.x) st[(e % D) * D + e / D] = S[e];
     __syncthreads();
     uint32_t dm[R];
     load_diag<R>(diag, lane, dm);
@@ -117,13 +120,18 @@ __global__ __launch_bounds__(64 * kWaves) void k_quantize_wide(const void* __res
         if constexpr (QJL) {
             g2 = wave_sum(g2);
             uint32_t sb[R];
+            // row j = 64 k + lane of S r: consecutive lanes read consecutive
+            // entries of a row of S^T, the residual entry is a broadcast
+            float u[R];
 #pragma unroll
-            for (int k = 0; k < R; ++k) {
-                const uint16_t* Sj = S + (int64_t)(64 * k + lane) * D;
-                float u = 0.f;
-                for (int i = 0; i < D; ++i) u += h2f(Sj[i]) * res[wid][i];
-                sb[k] = u >= 0.f ? 1u : 0u;
+            for (int k = 0; k < R; ++k) u[k] = 0.f;
+            for (int i = 0; i < D; ++i) {
+                const float ri = res[wid][i];
+#pragma unroll
+                for (int k = 0; k < R; ++k) u[k] = fmaf(h2f(st[i * D + 64 * k + lane]), ri, u[k]);
             }
+#pragma unroll
+            for (int k = 0; k < R; ++k) sb[k] = u[k] >= 0.f ? 1u : 0u;
             __syncthreads();
 #pragma unroll
             for (int k = 0; k < R; ++k) cidx[wid][64 * k + lane] = (unsigned char)sb[k];
@@ -255,11 +263,15 @@ __global__ __launch_bounds__(256) void k_scores_wide(const uint32_t* __restrict_
 }
 
 // Decode attention over one chunk of kTC tokens of one stream (grid: chunks x
-// streams), any key width bk and value width bv in 1..8: phase A scores this
-// thread's token for the G heads, phase B takes the chunk-local softmax per
-// head, phase C accumulates sum_t w_t n_t c_v[idx] in the rotated value domain.
-// Each chunk writes a partial (max, sum, accumulator) that the combine kernel
-// merges.
+// streams), any key width bk and value width bv in 1..8. The chunk's key and
+// value code rows are staged in LDS with coalesced loads (key rows padded to
+// an odd word stride, so the per-token reads of phase A do not collide).
+// Phase A scores this thread's token for the G heads, four coordinates per
+// query read; phase B takes the chunk-local softmax per head and folds the
+// value norms into the weights; phase C gives each thread one coordinate and
+// a set of heads, so one code lookup serves all of them, and accumulates
+// sum_t w_t n_t c_v[idx] in the rotated value domain. Each chunk writes a
+// partial (max, sum, accumulator) that the combine kernel merges.
 template <int D, bool QJL>
 __global__ __launch_bounds__(256) void k_decode_wide(const uint32_t* __restrict__ kcodes,
                                                      const uint32_t* __restrict__ ksigns,
@@ -274,16 +286,20 @@ __global__ __launch_bounds__(256) void k_decode_wide(const uint32_t* __restrict_
                                                      float* __restrict__ parts, int n_chunks)
 {
     constexpr int W = D / 32;
-    __shared__ float sq[kMaxG][D];
-    __shared__ float sp[QJL ? kMaxG : 1][D];
-    __shared__ float z[kMaxG][kTC];
-    __shared__ uint32_t vw[kTC][8 * W];
-    __shared__ float vn[kTC];
+    constexpr int KROW = 8 * W + 1;          // staged key row stride (words)
+    constexpr int TPC = 256 / D;             // phase C threads per coordinate
+    constexpr int HPT = (kMaxG + TPC - 1) / TPC;  // heads per phase C thread (at most)
+    __shared__ __align__(16) float sq[kMaxG][D];
+    __shared__ __align__(16) float sp[QJL ? kMaxG : 1][D];
+    __shared__ float z[kMaxG][kTC];          // scores, then weights times value norms
+    __shared__ uint32_t ks[kTC * KROW];      // key code rows (phase A), value code rows (phase C)
     __shared__ float kc[kMaxL], vc[kMaxL];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t s = blockIdx.y;
     const int chunk = blockIdx.x;
     const int64_t t0 = (int64_t)chunk * kTC;
+    const int64_t row0 = s * stride + t0;     // first vector of the chunk
+    const int nt = (int)(T - t0 < kTC ? T - t0 : kTC);  // tokens in this chunk
     const int kw = bk * W, vwn = bv * W;  // code words per key / value
     for (int l = tid; l < (1 << bk); l += 256) kc[l] = kcent[l];
     for (int l = tid; l < (1 << bv); l += 256) vc[l] = vcent[l];
@@ -292,54 +308,53 @@ __global__ __launch_bounds__(256) void k_decode_wide(const uint32_t* __restrict_
         sq[h][i] = qr[(s * G + h) * D + i];
         if (QJL) sp[h][i] = p[(s * G + h) * D + i];
     }
-    for (int e = tid; e < kTC * vwn; e += 256) {
-        const int tt = e / vwn, j = e % vwn;
-        const int64_t t = t0 + tt;
-        vw[tt][j] = t < T ? vcodes[(s * stride + t) * vwn + j] : 0u;
-    }
-    {
-        const int64_t t = t0 + tid;
-        vn[tid] = t < T ? h2f(vnorm[s * stride + t]) : 0.f;
-    }
+    for (int e = tid; e < nt * kw; e += 256) ks[(e / kw) * KROW + e % kw] = kcodes[row0 * kw + e];
     __syncthreads();
 
     // phase A: scores of this thread's token for all heads
-    {
-        const int64_t t = t0 + tid;
-        if (t < T) {
-            float am[kMaxG], aj[kMaxG];
+    if (tid < nt) {
+        float am[kMaxG], aj[kMaxG];
 #pragma unroll
-            for (int h = 0; h < kMaxG; ++h) am[h] = aj[h] = 0.f;
-            const int64_t v = s * stride + t;
-            const uint32_t* cv = kcodes + v * kw;
-            uint32_t sw[W];
+        for (int h = 0; h < kMaxG; ++h) am[h] = aj[h] = 0.f;
+        const int64_t v = row0 + tid;
+        const uint32_t* cv = ks + tid * KROW;
+        uint32_t sw[W];
 #pragma unroll
-            for (int w = 0; w < W; ++w) sw[w] = QJL ? ksigns[v * W + w] : 0u;
-            for (int i = 0; i < D; ++i) {
-                const float c = kc[wide_code(cv, D, bk, i)];
-                const int SP = sign_bit<D>(i);
-                const float sg = ((sw[SP >> 5] >> (SP & 31)) & 1u) ? 1.f : -1.f;
+        for (int w = 0; w < W; ++w) sw[w] = QJL ? ksigns[v * W + w] : 0u;
+        for (int i0 = 0; i0 < D; i0 += 4) {
+            float c[4], sg[4];
 #pragma unroll
-                for (int h = 0; h < kMaxG; ++h)
-                    if (h < G) {
-                        am[h] += sq[h][i] * c;
-                        if (QJL) aj[h] += sp[h][i] * sg;
-                    }
+            for (int k = 0; k < 4; ++k) {
+                c[k] = kc[wide_code(cv, D, bk, i0 + k)];
+                const int SP = sign_bit<D>(i0 + k);
+                sg[k] = ((sw[SP >> 5] >> (SP & 31)) & 1u) ? 1.f : -1.f;
             }
-            const float nk = h2f(knorm[v]);
-            const float gk = QJL ? h2f(krnorm[v]) * (kSqrtHalfPi / (float)D) : 0.f;
 #pragma unroll
             for (int h = 0; h < kMaxG; ++h)
-                if (h < G) z[h][tid] = nk * (am[h] + gk * aj[h]) * scale;
-        } else {
-#pragma unroll
-            for (int h = 0; h < kMaxG; ++h)
-                if (h < G) z[h][tid] = -INFINITY;
+                if (h < G) {
+                    const float4 q4 = *reinterpret_cast<const float4*>(&sq[h][i0]);
+                    am[h] += q4.x * c[0] + q4.y * c[1] + q4.z * c[2] + q4.w * c[3];
+                    if (QJL) {
+                        const float4 p4 = *reinterpret_cast<const float4*>(&sp[h][i0]);
+                        aj[h] += p4.x * sg[0] + p4.y * sg[1] + p4.z * sg[2] + p4.w * sg[3];
+                    }
+                }
         }
+        const float nk = h2f(knorm[v]);
+        const float gk = QJL ? h2f(krnorm[v]) * (kSqrtHalfPi / (float)D) : 0.f;
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h)
+            if (h < G) z[h][tid] = nk * (am[h] + gk * aj[h]) * scale;
+    } else {
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h)
+            if (h < G) z[h][tid] = -INFINITY;
     }
-    __syncthreads();
+    __syncthreads();  // the key rows are no longer read: the buffer takes the value rows
 
-    // phase B: chunk-local softmax per head (one wave per head, round robin)
+    for (int e = tid; e < nt * vwn; e += 256) ks[(e / vwn) * KROW + e % vwn] = vcodes[row0 * vwn + e];
+    // phase B: chunk-local softmax per head (one wave per head, round robin);
+    // the weights are stored times the token's value norm
     for (int h = wid; h < G; h += 4) {
         float m = -INFINITY;
         for (int tt = lane; tt < kTC; tt += 64) m = fmaxf(m, z[h][tt]);
@@ -347,7 +362,7 @@ __global__ __launch_bounds__(256) void k_decode_wide(const uint32_t* __restrict_
         float l = 0.f;
         for (int tt = lane; tt < kTC; tt += 64) {
             const float w = (z[h][tt] == -INFINITY) ? 0.f : exp2f(z[h][tt] - m);
-            z[h][tt] = w;
+            z[h][tt] = tt < nt ? w * h2f(vnorm[row0 + tt]) : 0.f;
             l += w;
         }
         l = wave_sum(l);
@@ -359,12 +374,30 @@ __global__ __launch_bounds__(256) void k_decode_wide(const uint32_t* __restrict_
     }
     __syncthreads();
 
-    // phase C: rotated-domain value accumulation, one (head, coordinate) per step
-    for (int e = tid; e < G * D; e += 256) {
-        const int h = e / D, i = e % D;
-        float acc = 0.f;
-        for (int tt = 0; tt < kTC; ++tt) acc += z[h][tt] * vn[tt] * vc[wide_code(vw[tt], D, bv, i)];
-        parts[(((int64_t)s * n_chunks + chunk) * G + h) * part_stride(D) + kPartAcc + i] = acc;
+    // phase C: coordinate i = tid % D, heads tid / D, tid / D + TPC, ...
+    {
+        const int i = tid % D, h0 = tid / D;
+        const int start = 8 * bv * (i % (D / 8)) + bv * (i / (D / 8));  // code bit of coordinate i
+        const int w = start >> 5, off = start & 31;
+        const bool two = off + bv > 32;
+        const uint32_t mask = (1u << bv) - 1u;
+        float acc[HPT];
+#pragma unroll
+        for (int k = 0; k < HPT; ++k) acc[k] = 0.f;
+        for (int tt = 0; tt < nt; ++tt) {
+            const uint32_t* row = ks + tt * KROW;
+            uint32_t cw = row[w] >> off;
+            if (two) cw |= row[w + 1] << (32 - off);
+            const float c = vc[cw & mask];
+#pragma unroll
+            for (int k = 0; k < HPT; ++k)
+                if (h0 + TPC * k < G) acc[k] = fmaf(z[h0 + TPC * k][tt], c, acc[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < HPT; ++k) {
+            const int h = h0 + TPC * k;
+            if (h < G) parts[(((int64_t)s * n_chunks + chunk) * G + h) * part_stride(D) + kPartAcc + i] = acc[k];
+        }
     }
 }
 
@@ -381,18 +414,36 @@ unsigned wide_grid(int64_t units, int per_block)
     return (unsigned)(b < 65536 ? b : 65536);
 }
 
+// Launch with the dynamic LDS the kernel needs (S^T for keys) and a grid of
+// resident blocks (each block stages S^T once and loops over vectors).
+template <typename Kern>
+void launch_wide_q(Kern kern, size_t lds, int64_t n, const void* x, int b, const tq_quantizer* q,
+                   const tq_packed* o, hipStream_t s)
+{
+    static int cap = 0;  // resident blocks of this instance (same device for the process's launches)
+    if (!cap) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds);
+        int per = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, 64 * kWaves, lds) != hipSuccess || per < 1)
+            per = 1;
+        cap = per * device_cus();
+    }
+    int64_t want = (n + kWaves - 1) / kWaves;
+    const unsigned grid = (unsigned)(want < cap ? want : cap);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * kWaves), lds, s, x, n, b, q->centroids, q->boundaries,
+                       q->diag_signs, q->S, o->codes, o->signs, o->norm, o->rnorm);
+}
+
 template <int D>
 void quantize_wide_d(const tq_quantizer* q, const void* x, int dtype, int64_t n, const tq_packed* o, hipStream_t s)
 {
     const dim3 grid(wide_grid(n, kWaves)), block(64 * kWaves);
     const int b = q->mse_bits;
     if (q->qjl_m) {
-        if (dtype == TQ_F16)
-            hipLaunchKernelGGL((k_quantize_wide<D, true, true>), grid, block, 0, s, x, n, b, q->centroids,
-                               q->boundaries, q->diag_signs, q->S, o->codes, o->signs, o->norm, o->rnorm);
-        else
-            hipLaunchKernelGGL((k_quantize_wide<D, true, false>), grid, block, 0, s, x, n, b, q->centroids,
-                               q->boundaries, q->diag_signs, q->S, o->codes, o->signs, o->norm, o->rnorm);
+        constexpr size_t lds = (size_t)D * D * 2;
+        if (dtype == TQ_F16) launch_wide_q(k_quantize_wide<D, true, true>, lds, n, x, b, q, o, s);
+        else launch_wide_q(k_quantize_wide<D, true, false>, lds, n, x, b, q, o, s);
     } else {
         if (dtype == TQ_F16)
             hipLaunchKernelGGL((k_quantize_wide<D, false, true>), grid, block, 0, s, x, n, b, q->centroids,
