@@ -85,7 +85,8 @@ def test_one_hot_codes_and_packed_words():
     assert np.allclose(Q3.cent[[2, 5]] * np.sqrt(d), [-0.7560, 0.7560], atol=1e-3)
 
 
-@pytest.mark.parametrize("d,bits", [(128, 3), (64, 2), (256, 4), (128, 1)])
+@pytest.mark.parametrize("d,bits", [(128, 3), (64, 2), (256, 4), (128, 1), (64, 5), (128, 6), (256, 7),
+                                    (128, 8)])
 def test_packing_bit_layout_against_manual_pack(d, bits):
     """Group-major stream: group c = coordinates c + (d/8) t; code t of group c
     at stream bits 8*bits*c + bits*t .. +bits-1; words little-endian."""
@@ -127,6 +128,20 @@ def test_codes_are_the_brute_force_argmin(d, bits):
     for v in range(40):
         err = ((y[v][None, :] - c[allc]) ** 2).sum(1)
         assert np.array_equal(allc[np.argmin(err)], idx[v])
+
+
+@pytest.mark.parametrize("d,bits", [(64, 5), (128, 6), (128, 8), (256, 7)])
+def test_wide_codes_are_the_nearest_centroid(d, bits):
+    """Wide codebooks: the code of each coordinate is its nearest stored
+    centroid (the distortion is separable over coordinates, so this is the
+    argmin over whole code vectors); ties cannot occur on these inputs."""
+    Q = make_q(d, bits, 0)
+    x = synth.normals(12, synth.ROLE_DATA_K, np.arange(64 * d)).reshape(64, d)
+    P, y = oracle.quantize(Q, x, want_y=True)
+    idx = oracle.unpack_codes(Q, P.codes)
+    c = Q.cent.astype(np.float64)
+    dist = np.abs(y[..., None] - c[None, None, :])
+    assert np.array_equal(np.argmin(dist, axis=-1), idx)
 
 
 def test_projection_orientation_with_shift_matrix():
