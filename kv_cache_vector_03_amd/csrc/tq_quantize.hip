@@ -640,7 +640,12 @@ void dequant_d(const tq_quantizer* q, const tq_packed* in, int64_t n, int qjl, v
 int launch_quantize(const tq_quantizer* q, const void* x, int dtype, int64_t n, const tq_packed* out,
                     hipStream_t s)
 {
-    if (q->mse_bits > 4) return launch_quantize_wide(q, x, dtype, n, out, s);
+    if (q->mse_bits > 4) {
+        // widths 5..8: the MFMA quantizer for d = 128 fp16 input, else the wide-code kernel
+        if (q->d != 128 || dtype != TQ_F16) return launch_quantize_wide(q, x, dtype, n, out, s);
+        launch_quantize_m128(q, x, n, out, s);
+        return device_status("tq_quantize");
+    }
     switch (q->d) {
         case 64: quantize_d<64>(q, x, dtype, n, out, s); break;
         case 128: quantize_d<128>(q, x, dtype, n, out, s); break;

@@ -175,6 +175,44 @@ __device__ __forceinline__ void codes_lut(float (&y)[8][4], const uint2* __restr
     }
 }
 
+// Codes of the 32 coordinates a lane holds for widths 5..8: y = -Z / s, its
+// code the number of boundaries strictly below y, found by a branch-free
+// binary search over the boundaries in LDS (tb, padded to 2^B entries).
+// Group r's eight codes form a 64-bit field (code t at bit B t) placed at
+// bit 8 B r of the lane's B code words. For keys, y is replaced by the
+// negated scaled residual and its square accumulates in g2, as in codes_lut.
+template <int B, bool QJL>
+__device__ __forceinline__ void codes_search(float (&y)[8][4], const float* __restrict__ tb,
+                                             const float* __restrict__ ctab, float rs, float sc, uint32_t (&W)[B],
+                                             float& g2)
+{
+#pragma unroll
+    for (int w = 0; w < B; ++w) W[w] = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        uint64_t gg = 0;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float Z = y[t][r];  // -Y
+            const float yy = -Z * rs;
+            int k = 0;
+#pragma unroll
+            for (int step = 1 << (B - 1); step >= 1; step >>= 1) k += tb[k + step - 1] < yy ? step : 0;
+            gg |= (uint64_t)k << (B * t);
+            if constexpr (QJL) {
+                const float rn = fmaf(Z, sc, ctab[k]);  // negated residual
+                g2 = fmaf(rn, rn, g2);
+                y[t][r] = rn;
+            }
+        }
+        constexpr int FB = 8 * B;  // bits per group
+        const int o = FB * r, ow = o >> 5, ob = o & 31;
+        W[ow] |= (uint32_t)(gg << ob);
+        if (ob + FB > 32) W[ow + 1] |= (uint32_t)(gg >> (32 - ob));
+        if (ob + FB > 64) W[ow + 2] |= (uint32_t)(gg >> (64 - ob));
+    }
+}
+
 // Shift the sign bits of the four projections t[3], .., t[0] into w from
 // below. The projections are negated (t = -(S r)), so the sign bit of t is
 // the stored bit [S r >= 0] everywhere except at S r = 0 exactly.
@@ -259,11 +297,12 @@ __device__ __forceinline__ void rotate_batch(const uint4 (&xin)[4], const RotCon
 // arithmetic), the centroid table and the lookup grid in LDS.
 template <int B>
 struct CodeConsts {
-    static constexpr int L = 1 << B, K = L / 2 - 1;
+    static constexpr int L = 1 << B, K = B <= 4 ? L / 2 - 1 : 0;
     float Mth[K > 0 ? K : 1];
     float Cq[K + 1];
     const float* ctab;
     const uint2* lut;
+    const float* tb;  // widths 5..8: boundaries, padded with +inf to 2^B entries
     bool use_lut;
 };
 
@@ -272,16 +311,18 @@ struct CodeConsts {
 // codebook. Ends with a barrier.
 template <int B>
 __device__ void build_tables(CodeConsts<B>& cc, const float* __restrict__ cent, const float* __restrict__ bnd,
-                             float unit, float* ctab, uint2* lut, int* lut_bad)
+                             float unit, float* ctab, uint2* lut, int* lut_bad, float* tb)
 {
-    constexpr int L = 1 << B, K = L / 2 - 1;
-    constexpr bool LUT = B >= 3;
+    constexpr int L = 1 << B, K = CodeConsts<B>::K;
+    constexpr bool LUT = B >= 3 && B <= 4;
 #pragma unroll
     for (int j = 1; j <= K; ++j) cc.Mth[j - 1] = bnd[L / 2 - 1 + j];
 #pragma unroll
     for (int m = 0; m <= K; ++m) cc.Cq[m] = cent[L / 2 + m] * unit;
     if (threadIdx.x == 0) *lut_bad = 0;
-    if (threadIdx.x < L) ctab[threadIdx.x] = cent[threadIdx.x] * unit;
+    for (int l = threadIdx.x; l < L; l += blockDim.x) ctab[l] = cent[l] * unit;
+    if constexpr (B > 4)
+        for (int l = threadIdx.x; l < L; l += blockDim.x) tb[l] = l < L - 1 ? bnd[l] : INFINITY;
     __syncthreads();
     if constexpr (LUT) {
         for (int c = threadIdx.x; c < kLutEntries; c += blockDim.x) {
@@ -303,6 +344,7 @@ __device__ void build_tables(CodeConsts<B>& cc, const float* __restrict__ cent, 
     __syncthreads();
     cc.ctab = ctab;
     cc.lut = lut;
+    cc.tb = tb;
     cc.use_lut = LUT && !*lut_bad;
 }
 
@@ -315,7 +357,7 @@ __device__ __forceinline__ void code_batch(const float4_t (&acc)[2][4], float ss
                                            uint32_t (&W)[B], float& nrm, float& gam, half8_t (&ahi)[4],
                                            half8_t (&alo)[4], Pre&& pre = [](int) {})
 {
-    constexpr int K = (1 << B) / 2 - 1;
+    constexpr int K = CodeConsts<B>::K;
     constexpr float sqrt_d = 11.313708498984761f;  // sqrt(128)
     auto none = [](int) {};
     // y[t][r]: coordinate 4 q + r + 16 t, t = 2 a + tau
@@ -338,7 +380,8 @@ __device__ __forceinline__ void code_batch(const float4_t (&acc)[2][4], float ss
     for (int j = 0; j < K; ++j) Ms[j] = cc.Mth[j] * s;
 
     float g2 = 0.f;
-    if (cc.use_lut) codes_lut<B, QJL>(y, cc.lut, cc.ctab, s, (float)kLutCells / s, sc, W, g2, pre, none);
+    if constexpr (B > 4) codes_search<B, QJL>(y, cc.tb, cc.ctab, __builtin_amdgcn_rcpf(s), sc, W, g2);
+    else if (cc.use_lut) codes_lut<B, QJL>(y, cc.lut, cc.ctab, s, (float)kLutCells / s, sc, W, g2, pre, none);
     else codes_compare<B, QJL>(y, Ms, cc.Cq, cc.ctab, sc, W, g2, pre, none);
     gam = 0.f;
     if constexpr (QJL) {
@@ -415,8 +458,9 @@ __global__ __launch_bounds__(256) void k_quantize_values_m128(const uint16_t* __
                                                               uint32_t* __restrict__ codes,
                                                               uint16_t* __restrict__ norm)
 {
-    __shared__ uint2 lut[B >= 3 ? kLutEntries : 1];
+    __shared__ uint2 lut[B >= 3 && B <= 4 ? kLutEntries : 1];
     __shared__ float ctab[1 << B];
+    __shared__ float tbl[B > 4 ? 1 << B : 1];
     __shared__ int lut_bad;
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -424,7 +468,7 @@ __global__ __launch_bounds__(256) void k_quantize_values_m128(const uint16_t* __
     RotConsts rc;
     rot_consts(rc, diag, v, q);
     CodeConsts<B> cc;
-    build_tables<B>(cc, cent, bnd, 1.0f, ctab, lut, &lut_bad);
+    build_tables<B>(cc, cent, bnd, 1.0f, ctab, lut, &lut_bad, tbl);
 
     const int64_t step = (int64_t)gridDim.x * 64;  // vectors between a wave's batches
     int64_t base = ((int64_t)blockIdx.x * 4 + wid) * 16;
@@ -463,15 +507,16 @@ __global__ __launch_bounds__(256) void k_quantize_keys_m128(const uint16_t* __re
 {
     constexpr int NT = 8, KS = 4;  // projection m-tiles (m = 128) and k-steps
     __shared__ __align__(16) half8_t sfrag[KS * NT * 64];  // 32 KiB
-    __shared__ uint2 lut[B >= 3 ? kLutEntries : 1];
+    __shared__ uint2 lut[B >= 3 && B <= 4 ? kLutEntries : 1];
     __shared__ float ctab[1 << B];
+    __shared__ float tbl[B > 4 ? 1 << B : 1];
     __shared__ int lut_bad;
 
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int v = lane & 15, q = lane >> 4;
     CodeConsts<B> cc;
-    build_tables<B>(cc, cent, bnd, kResUnit, ctab, lut, &lut_bad);
+    build_tables<B>(cc, cent, bnd, kResUnit, ctab, lut, &lut_bad, tbl);
     // A fragments: lane (row c, k-block kb) of fragment (ks, nu), element e
     // holds S[proj_row(nu, c)][4 kb + ks + 16 e]
     for (int e = threadIdx.x; e < KS * NT * 64; e += 256) {
@@ -561,7 +606,11 @@ void launch_quantize_m128(const tq_quantizer* q, const void* x, int64_t n, const
         case 1: launch_b<1>(q, xh, n, out, s); break;
         case 2: launch_b<2>(q, xh, n, out, s); break;
         case 3: launch_b<3>(q, xh, n, out, s); break;
-        default: launch_b<4>(q, xh, n, out, s); break;
+        case 4: launch_b<4>(q, xh, n, out, s); break;
+        case 5: launch_b<5>(q, xh, n, out, s); break;
+        case 6: launch_b<6>(q, xh, n, out, s); break;
+        case 7: launch_b<7>(q, xh, n, out, s); break;
+        default: launch_b<8>(q, xh, n, out, s); break;
     }
 }
 
