@@ -289,9 +289,12 @@ __global__ __launch_bounds__(256) void k_decode_wide(const uint32_t* __restrict_
     constexpr int KROW = 8 * W + 1;          // staged key row stride (words)
     constexpr int TPC = 256 / D;             // phase C threads per coordinate
     constexpr int HPT = (kMaxG + TPC - 1) / TPC;  // heads per phase C thread (at most)
-    __shared__ __align__(16) float sq[kMaxG][D];
-    __shared__ __align__(16) float sp[QJL ? kMaxG : 1][D];
-    __shared__ float z[kMaxG][kTC];          // scores, then weights times value norms
+    // dynamic LDS, sized for the call's G: queries q' [G][D], projections p
+    // [G][D] (QJL), scores then weights times value norms z [G][kTC]
+    extern __shared__ __align__(16) float dsm[];
+    float(*sq)[D] = reinterpret_cast<float(*)[D]>(dsm);
+    float(*sp)[D] = reinterpret_cast<float(*)[D]>(dsm + G * D);
+    float(*z)[kTC] = reinterpret_cast<float(*)[kTC]>(dsm + (QJL ? 2 : 1) * G * D);
     __shared__ uint32_t ks[kTC * KROW];      // key code rows (phase A), value code rows (phase C)
     __shared__ float kc[kMaxL], vc[kMaxL];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -321,6 +324,7 @@ __global__ __launch_bounds__(256) void k_decode_wide(const uint32_t* __restrict_
         uint32_t sw[W];
 #pragma unroll
         for (int w = 0; w < W; ++w) sw[w] = QJL ? ksigns[v * W + w] : 0u;
+#pragma unroll 2
         for (int i0 = 0; i0 < D; i0 += 4) {
             float c[4], sg[4];
 #pragma unroll
@@ -384,6 +388,7 @@ __global__ __launch_bounds__(256) void k_decode_wide(const uint32_t* __restrict_
         float acc[HPT];
 #pragma unroll
         for (int k = 0; k < HPT; ++k) acc[k] = 0.f;
+#pragma unroll 4
         for (int tt = 0; tt < nt; ++tt) {
             const uint32_t* row = ks + tt * KROW;
             uint32_t cw = row[w] >> off;
@@ -497,12 +502,13 @@ void decode_wide_d(const tq_quantizer* qk, const tq_quantizer* qv, const tq_pack
                    float zscale, float* parts, int n_chunks, hipStream_t s)
 {
     const dim3 grid((unsigned)n_chunks, (unsigned)n_streams), block(256);
+    const size_t lds = ((size_t)(qk->qjl_m ? 2 : 1) * G * D + (size_t)G * kTC) * sizeof(float);
     if (qk->qjl_m)
-        hipLaunchKernelGGL((k_decode_wide<D, true>), grid, block, 0, s, k->codes, k->signs, k->norm, k->rnorm,
+        hipLaunchKernelGGL((k_decode_wide<D, true>), grid, block, lds, s, k->codes, k->signs, k->norm, k->rnorm,
                            qk->mse_bits, v->codes, v->norm, qv->mse_bits, T, stride, G, qr, p, qk->centroids,
                            qv->centroids, zscale, parts, n_chunks);
     else
-        hipLaunchKernelGGL((k_decode_wide<D, false>), grid, block, 0, s, k->codes, k->signs, k->norm, k->rnorm,
+        hipLaunchKernelGGL((k_decode_wide<D, false>), grid, block, lds, s, k->codes, k->signs, k->norm, k->rnorm,
                            qk->mse_bits, v->codes, v->norm, qv->mse_bits, T, stride, G, qr, p, qk->centroids,
                            qv->centroids, zscale, parts, n_chunks);
 }
