@@ -345,10 +345,9 @@ def decode_step(tq, qk, qv, units, T, G, d, attn_us, tok_bytes, dev, passes=3):
 
 
 def wide_widths(tq, qv, u, T, G, d, diag_k, S, diag_v, dev, passes=3):
-    """Code widths above 4 bits (the wide-code kernels) on the first batch: 8-bit
-    keys (7-bit codes + the 1-bit sketch) beside the workload's values, and
-    8-bit values; quantize and decode times per launch with their algorithmic
-    GB/s."""
+    """Code widths above 4 bits on the first batch: 8-bit keys (7-bit codes + the
+    1-bit sketch) beside the workload's values, and 8-bit values; quantize and
+    decode times per launch with their algorithmic GB/s."""
     import torch
     ns = u["ns"]
     nvec = ns * T
@@ -385,7 +384,8 @@ def wide_widths(tq, qv, u, T, G, d, diag_k, S, diag_v, dev, passes=3):
         us = timed(fn)
         res[name] = {"us_per_launch": round(us, 2), "GB_per_s": round(alg / (us * 1e-6) / 1e9, 1),
                      "frac_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-    res["note"] = "plain wide-code kernels (binary-search codes, scalar scores and decode)"
+    res["note"] = ("MFMA quantizer with binary-search codes; MFMA decode with single-code tables "
+                   "(values of 4 or 8 bits)")
     return res
 
 

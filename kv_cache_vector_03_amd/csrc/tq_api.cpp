@@ -43,13 +43,11 @@ int tq_scores(const tq_quantizer* q, const tq_packed* keys, int64_t n_keys,
     if (!ws || ws_bytes < need)
         return fail(TQ_ERR_WORKSPACE, "tq_scores: workspace %zu bytes < %zu", ws_bytes, need);
     if ((uintptr_t)ws % 256) return fail(TQ_ERR_INVALID, "tq_scores: workspace must be 256-byte aligned");
-    if (q->d == 128 && q->mse_bits <= 4)
-        return launch_scores_mfma(q, keys, n_keys, queries, q_dtype, n_q, scores, ws, (hipStream_t)stream);
+    if (q->d == 128) return launch_scores_mfma(q, keys, n_keys, queries, q_dtype, n_q, scores, ws, (hipStream_t)stream);
     float* qr = (float*)ws;
     float* p = (float*)((char*)ws + up256((size_t)n_q * q->d * 4));
     if ((rc = launch_qprep(q, queries, q_dtype, n_q, qr, p, (hipStream_t)stream)) != TQ_OK) return rc;
-    if (q->mse_bits > 4) return launch_scores_wide(q, keys, n_keys, qr, p, n_q, scores, (hipStream_t)stream);
-    return launch_scores(q, keys, n_keys, qr, p, n_q, scores, (hipStream_t)stream);
+    return launch_scores_wide(q, keys, n_keys, qr, p, n_q, scores, (hipStream_t)stream);
 }
 
 int tq_dequantize(const tq_quantizer* q, const tq_packed* in, int64_t n, int include_qjl,
@@ -94,7 +92,7 @@ int tq_decode_attn(const tq_quantizer* qk, const tq_quantizer* qv,
     if ((rc = check_packed(qv, v, "tq_decode_attn", "v")) != TQ_OK) return rc;
     if ((rc = check_dense(q, q_dtype, "tq_decode_attn", "q")) != TQ_OK) return rc;
     if ((rc = check_dense(out, TQ_F32, "tq_decode_attn", "out")) != TQ_OK) return rc;
-    const DecodePlan plan = decode_plan(qk, n_streams, T, G, qk->mse_bits > 4 || qv->mse_bits > 4);
+    const DecodePlan plan = decode_plan(qk, n_streams, T, G, !mfma_decode_widths(qk->mse_bits, qv->mse_bits));
     if (!ws || ws_bytes < plan.total)
         return fail(TQ_ERR_WORKSPACE, "tq_decode_attn: workspace %zu bytes < %zu", ws_bytes, plan.total);
     if ((uintptr_t)ws % 256) return fail(TQ_ERR_INVALID, "tq_decode_attn: workspace must be 256-byte aligned");
@@ -130,7 +128,7 @@ int tq_decode_step(const tq_quantizer* qk, const tq_quantizer* qv,
     if ((rc = check_dense(v_new, new_dtype, "tq_decode_step", "v_new")) != TQ_OK) return rc;
     if ((rc = check_dense(q, q_dtype, "tq_decode_step", "q")) != TQ_OK) return rc;
     if ((rc = check_dense(out, TQ_F32, "tq_decode_step", "out")) != TQ_OK) return rc;
-    const DecodePlan plan = decode_plan(qk, n_streams, T + 1, G, qk->mse_bits > 4 || qv->mse_bits > 4);
+    const DecodePlan plan = decode_plan(qk, n_streams, T + 1, G, !mfma_decode_widths(qk->mse_bits, qv->mse_bits));
     if (!ws || ws_bytes < plan.total)
         return fail(TQ_ERR_WORKSPACE, "tq_decode_step: workspace %zu bytes < %zu", ws_bytes, plan.total);
     if ((uintptr_t)ws % 256) return fail(TQ_ERR_INVALID, "tq_decode_step: workspace must be 256-byte aligned");

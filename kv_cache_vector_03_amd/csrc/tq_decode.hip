@@ -140,22 +140,33 @@ __global__ __launch_bounds__(256) void k_qprep_frag(const void* __restrict__ q, 
     }
 }
 
+// Entries of a block's key code table: a byte of four codes (widths 1, 2), a
+// field of two codes (3, 4), or one code (5..8, where a two-code table would
+// reach 256 KiB).
+__host__ __device__ constexpr int key_lut_entries(int bk)
+{
+    return bk <= 2 ? 1 << (4 * bk) : (bk <= 4 ? 1 << (2 * bk) : 1 << bk);
+}
+
 // Key lookup tables of a block: for up to 2-bit codes one entry maps a byte of
-// four codes to four fp16 centroids (klut4), else a field of two codes to two
-// (klut2); slut maps a byte of sign bits to eight fp16 +-1 values.
+// four codes to four fp16 centroids (klut4), for 3 and 4 bits a field of two
+// codes to two (klut2), above 4 bits one code to its fp16 centroid in both
+// halves (klut2); slut maps a byte of sign bits to eight fp16 +-1 values.
 template <int BK, bool QJL>
 __device__ void fill_key_luts(uint2* klut4, uint32_t* klut2, uint4* slut, const float* __restrict__ kcent)
 {
     constexpr bool K4 = BK <= 2;
-    constexpr int KLUT = K4 ? (1 << (4 * BK)) : (1 << (2 * BK));
+    constexpr int KLUT = key_lut_entries(BK);
     for (int i = threadIdx.x; i < KLUT; i += blockDim.x) {
         if constexpr (K4) {
             uint32_t h[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) h[j] = f2h(kcent[(i >> (BK * j)) & ((1 << BK) - 1)]);
             klut4[i] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-        } else {
+        } else if constexpr (BK <= 4) {
             klut2[i] = (uint32_t)f2h(kcent[i & ((1 << BK) - 1)]) | ((uint32_t)f2h(kcent[i >> BK]) << 16);
+        } else {
+            klut2[i] = (uint32_t)f2h(kcent[i]) * 0x10001u;
         }
     }
     if constexpr (QJL)
@@ -177,6 +188,20 @@ __device__ __forceinline__ half8_t key_codes_a(const uint32_t (&kf)[BK], int t, 
     constexpr bool K4 = BK <= 2;
     constexpr int FB = 8 * BK;
     const int bit = FB * t;
+    if constexpr (BK > 4) {
+        // a 40..64-bit field over two or three words; eight single-code lookups
+        const int lo = bit >> 5, sh = bit & 31;
+        uint64_t f = (((uint64_t)kf[lo + 1] << 32) | kf[lo]) >> sh;
+        if (sh + FB > 64) f |= (uint64_t)kf[lo + 2] << (64 - sh);
+        uint32_t wds[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t a = klut2[(uint32_t)(f >> (BK * 2 * j)) & ((1u << BK) - 1u)];
+            const uint32_t b = klut2[(uint32_t)(f >> (BK * (2 * j + 1))) & ((1u << BK) - 1u)];
+            wds[j] = __builtin_amdgcn_perm(b, a, 0x05040100u);  // low half of a, then low half of b
+        }
+        return __builtin_bit_cast(half8_t, wds);
+    }
     uint32_t field;
     if constexpr (BK == 4) field = kf[t];
     else {
@@ -202,7 +227,7 @@ template <int BK, int BV>
 struct Step {
     uint32_t kf[2][BK];   // key code words of this lane's 4 groups, tiles 0 and 1
     uint32_t sf[2];       // key sign bytes of this lane's 4 groups
-    uint32_t x0[8], x1[8];// value field words (x1: second word, 3-bit codes only)
+    uint32_t x0[8], x1[8];// value field words (x1: second word, 3- and 8-bit codes only)
     uint16_t nk[2], ng[2], nv[2];  // norms of token tb + 16 u + 4 g + (col & 3), u = 0, 1
 };
 
@@ -236,7 +261,7 @@ __device__ __forceinline__ void load_step(Step<BK, BV>& st, int64_t tb, int64_t 
         const uint32_t* rec = vcodes + t * VW;
         st.x0[e] = rec[w];
         // 3-bit fields may straddle two words; the last field of a token does not
-        if constexpr (BV == 3) st.x1[e] = rec[w + 1 < VW ? w + 1 : w];
+        if constexpr (BV == 3 || BV == 8) st.x1[e] = rec[w + 1 < VW ? w + 1 : w];
         else st.x1[e] = 0u;
     }
 #pragma unroll
@@ -293,7 +318,7 @@ __device__ __forceinline__ void load_full(Step<BK, BV>& st, int64_t t0, const La
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         st.x0[e] = vc[lo.v + (16 * (e >> 2) + (e & 3)) * VW];
-        if constexpr (BV == 3) st.x1[e] = vc[lo.v1 + (16 * (e >> 2) + (e & 3)) * VW];
+        if constexpr (BV == 3 || BV == 8) st.x1[e] = vc[lo.v1 + (16 * (e >> 2) + (e & 3)) * VW];
         else st.x1[e] = 0u;
     }
 #pragma unroll
@@ -321,9 +346,9 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
     constexpr int KS = D / 32;                 // 4 code groups per lane per token
     constexpr int KSTEPS = KS * (QJL ? 2 : 1);
     constexpr int CT = D / 16;                 // value coordinate tiles
-    constexpr bool K4 = BK <= 2;               // one key table entry = 4 codes (else 2)
-    constexpr int KLUT = K4 ? (1 << (4 * BK)) : (1 << (2 * BK));
-    constexpr int VLUT = 1 << (2 * BV);
+    constexpr bool K4 = BK <= 2;               // one key table entry = 4 codes (else 2, or 1 above 4 bits)
+    constexpr int KLUT = key_lut_entries(BK);
+    constexpr int VLUT = BV <= 4 ? 1 << (2 * BV) : 1 << BV;  // code pairs, or single codes above 4 bits
     constexpr float kappa = 1.2533141373155003f / D;  // sqrt(pi/2) / m
 
     __shared__ uint2 klut4[K4 ? KLUT : 1];
@@ -342,7 +367,10 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
     fill_key_luts<BK, QJL>(klut4, klut2, slut, kcent);
     for (int i = tid; i < VLUT * 32; i += 256) {
         const int e = i >> 5;
-        vlut[e][i & 31] = (uint32_t)f2h(vcent[e & ((1 << BV) - 1)]) | ((uint32_t)f2h(vcent[e >> BV]) << 16);
+        if constexpr (BV <= 4)
+            vlut[e][i & 31] = (uint32_t)f2h(vcent[e & ((1 << BV) - 1)]) | ((uint32_t)f2h(vcent[e >> BV]) << 16);
+        else
+            vlut[e][i & 31] = (uint32_t)f2h(vcent[e]) * 0x10001u;  // one code, its centroid in both halves
     }
     __syncthreads();
 
@@ -468,10 +496,27 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 if constexpr (BV == 3) X[e] = __builtin_amdgcn_alignbit(st.x1[e], st.x0[e], (24 * col) & 31) & 0xFFFFFFu;
-                else if constexpr (BV == 4) X[e] = st.x0[e];
+                else if constexpr (BV == 4 || BV == 8) X[e] = st.x0[e];
                 else X[e] = (st.x0[e] >> ((8 * BV * col) & 31)) & ((1u << (8 * BV)) - 1u);
             }
-            if constexpr (BV == 3) {
+            if constexpr (BV == 8) {
+                // one byte per code: member c of the group is byte c of (x1:x0); single-code
+                // table entries carry the centroid in both halves, so a bit-field insert
+                // pairs two tokens
+#pragma unroll
+                for (int c = 0; c < CT; ++c) {
+                    uint32_t bw[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t wa = c < 4 ? X[2 * j] : st.x1[2 * j];
+                        const uint32_t wb = c < 4 ? X[2 * j + 1] : st.x1[2 * j + 1];
+                        const uint32_t a = vlut[(wa >> (8 * (c & 3))) & 0xFFu][lane & 31];
+                        const uint32_t b = vlut[(wb >> (8 * (c & 3))) & 0xFFu][lane & 31];
+                        bw[j] = (a & 0xFFFFu) | (b & 0xFFFF0000u);
+                    }
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, bw), acc[c], 0, 0, 0);
+                }
+            } else if constexpr (BV == 3) {
 #pragma unroll
                 for (int c = 0; c < CT; ++c) {
                     uint32_t bw[4];
@@ -590,11 +635,13 @@ void launch_bv(int bv, const tq_packed* k, const tq_packed* v, int64_t ns, int64
                const tq_quantizer* qk, const tq_quantizer* qv, float zs, float* parts, int nc, int tc,
                hipStream_t s)
 {
+    // value widths 1..4 with keys of 1..4 bits, 4 and 8 with any key width
     switch (bv) {
-        case 1: launch_mfma<D, BK, QJL, 1>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
-        case 2: launch_mfma<D, BK, QJL, 2>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
-        case 3: launch_mfma<D, BK, QJL, 3>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
-        default: launch_mfma<D, BK, QJL, 4>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
+        case 1: if constexpr (BK <= 4) launch_mfma<D, BK, QJL, 1>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
+        case 2: if constexpr (BK <= 4) launch_mfma<D, BK, QJL, 2>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
+        case 3: if constexpr (BK <= 4) launch_mfma<D, BK, QJL, 3>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
+        case 4: launch_mfma<D, BK, QJL, 4>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
+        default: launch_mfma<D, BK, QJL, 8>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
     }
 }
 
@@ -641,7 +688,7 @@ __global__ __launch_bounds__(256, 2) void k_scores_mfma(const uint32_t* __restri
     constexpr int KS = D / 32, KSTEPS = KS * (QJL ? 2 : 1);
     constexpr int KW = BK * D / 32, SWN = D / 32;
     constexpr bool K4 = BK <= 2;
-    constexpr int KLUT = K4 ? (1 << (4 * BK)) : (1 << (2 * BK));
+    constexpr int KLUT = key_lut_entries(BK);
     constexpr float kappa = 1.2533141373155003f / D;  // sqrt(pi/2) / m
     __shared__ uint2 klut4[K4 ? KLUT : 1];
     __shared__ uint32_t klut2[K4 ? 1 : KLUT];
@@ -772,8 +819,16 @@ int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_
                     : launch_bv<D, 2, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
         case 3: qjl ? launch_bv<D, 3, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
                     : launch_bv<D, 3, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
-        default: qjl ? launch_bv<D, 4, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
-                     : launch_bv<D, 4, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
+        case 4: qjl ? launch_bv<D, 4, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
+                    : launch_bv<D, 4, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
+        case 5: qjl ? launch_bv<D, 5, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
+                    : launch_bv<D, 5, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
+        case 6: qjl ? launch_bv<D, 6, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
+                    : launch_bv<D, 6, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
+        case 7: qjl ? launch_bv<D, 7, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
+                    : launch_bv<D, 7, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
+        default: qjl ? launch_bv<D, 8, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
+                     : launch_bv<D, 8, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "tq_decode_attn: %s", hipGetErrorString(e));
@@ -792,7 +847,11 @@ int launch_scores_mfma(const tq_quantizer* q, const tq_packed* k, int64_t n_keys
         case 1: qjl ? launch_scores_k<D, 1, true>(k, n_keys, fr, n_q, q, scores, s) : launch_scores_k<D, 1, false>(k, n_keys, fr, n_q, q, scores, s); break;
         case 2: qjl ? launch_scores_k<D, 2, true>(k, n_keys, fr, n_q, q, scores, s) : launch_scores_k<D, 2, false>(k, n_keys, fr, n_q, q, scores, s); break;
         case 3: qjl ? launch_scores_k<D, 3, true>(k, n_keys, fr, n_q, q, scores, s) : launch_scores_k<D, 3, false>(k, n_keys, fr, n_q, q, scores, s); break;
-        default: qjl ? launch_scores_k<D, 4, true>(k, n_keys, fr, n_q, q, scores, s) : launch_scores_k<D, 4, false>(k, n_keys, fr, n_q, q, scores, s); break;
+        case 4: qjl ? launch_scores_k<D, 4, true>(k, n_keys, fr, n_q, q, scores, s) : launch_scores_k<D, 4, false>(k, n_keys, fr, n_q, q, scores, s); break;
+        case 5: qjl ? launch_scores_k<D, 5, true>(k, n_keys, fr, n_q, q, scores, s) : launch_scores_k<D, 5, false>(k, n_keys, fr, n_q, q, scores, s); break;
+        case 6: qjl ? launch_scores_k<D, 6, true>(k, n_keys, fr, n_q, q, scores, s) : launch_scores_k<D, 6, false>(k, n_keys, fr, n_q, q, scores, s); break;
+        case 7: qjl ? launch_scores_k<D, 7, true>(k, n_keys, fr, n_q, q, scores, s) : launch_scores_k<D, 7, false>(k, n_keys, fr, n_q, q, scores, s); break;
+        default: qjl ? launch_scores_k<D, 8, true>(k, n_keys, fr, n_q, q, scores, s) : launch_scores_k<D, 8, false>(k, n_keys, fr, n_q, q, scores, s); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "tq_scores: %s", hipGetErrorString(e));

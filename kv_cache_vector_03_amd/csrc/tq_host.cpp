@@ -346,9 +346,9 @@ size_t scores_frag_bytes(const tq_quantizer* q, int64_t n_q)
 
 size_t scores_ws(const tq_quantizer* q, int64_t n_q)
 {
-    // d = 128 with codes of at most 4 bits: MFMA query fragments; else
-    // prepared queries: fp32 q' [n_q][d] and p = S q' [n_q][m]
-    if (q->d == 128 && q->mse_bits <= 4) return scores_frag_bytes(q, n_q);
+    // d = 128: MFMA query fragments; else prepared queries: fp32 q' [n_q][d]
+    // and p = S q' [n_q][m]
+    if (q->d == 128) return scores_frag_bytes(q, n_q);
     return up256((size_t)n_q * q->d * 4) + up256((size_t)n_q * (q->qjl_m ? q->qjl_m : 1) * 4);
 }
 

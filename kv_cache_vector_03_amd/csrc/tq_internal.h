@@ -34,12 +34,16 @@ constexpr int kPartAcc = 4;
 constexpr int kDecodeSlots = 512;
 
 struct DecodePlan {
-    bool mfma;          // MFMA kernel (d = 128, G <= 8, widths <= 4); else a scalar kernel
+    bool mfma;          // MFMA kernel (d = 128, G <= 8, mfma_decode_widths); else a scalar kernel
     int64_t tc;         // tokens per block
     int n_chunks;       // blocks per stream
     size_t off_qr, off_p, off_frag, off_parts, total;
 };
-// wide: a key or value code width above 4 bits (the scalar wide-code kernel)
+// Key and value code widths the MFMA decode kernel takes (d = 128, G <= 8):
+// values of 1..4 bits with keys of 1..4 bits, values of 4 or 8 bits with any
+// key width. Other pairs run on the scalar kernels.
+inline bool mfma_decode_widths(int bk, int bv) { return bv == 4 || bv == 8 || (bk <= 4 && bv <= 4); }
+// wide: a width pair the MFMA kernel does not take (mfma_decode_widths false)
 DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G, bool wide);
 
 // compute units of the current device (cached per device)
@@ -52,8 +56,6 @@ int launch_quantize(const tq_quantizer* q, const void* x, int dtype, int64_t n,
                     const tq_packed* out, hipStream_t s);
 int launch_qprep(const tq_quantizer* q, const void* queries, int dtype, int64_t nq,
                  float* qr, float* p, hipStream_t s);
-int launch_scores(const tq_quantizer* q, const tq_packed* k, int64_t n_keys, const float* qr,
-                  const float* p, int64_t n_q, float* scores, hipStream_t s);
 int launch_dequantize(const tq_quantizer* q, const tq_packed* in, int64_t n, int include_qjl,
                       void* out, int dtype, hipStream_t s);
 // The decode step's append: the new token of stream s (row s of k_new and
@@ -79,8 +81,10 @@ int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_
                        int q_dtype, float zscale, void* frags, float* parts, int n_chunks, int tc,
                        const AppendArgs* app, hipStream_t s);
 
-// code widths 5..8 (tq_wide.hip); scores and decode take prepared queries
-// (launch_qprep) like the scalar narrow kernels
+// scalar kernels with run-time code widths 1..8 (tq_wide.hip): quantize and
+// dequantize for widths 5..8 (and shapes the tuned kernels do not take), scores
+// for d != 128, decode for shapes and width pairs the MFMA kernel does not
+// take; scores and decode use prepared queries (launch_qprep)
 int launch_quantize_wide(const tq_quantizer* q, const void* x, int dtype, int64_t n, const tq_packed* out,
                          hipStream_t s);
 int launch_dequantize_wide(const tq_quantizer* q, const tq_packed* in, int64_t n, int include_qjl, void* out,

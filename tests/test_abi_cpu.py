@@ -136,8 +136,8 @@ def test_scores_and_decode_argument_errors():
                                 A + 0x8000, tq.TQ_F16, C.c_float(scale), A + 0x9000, ws, wsb, None)
 
     # tq_workspace_size covers either kernel family (the value width is not
-    # an argument); the wide-code plan (8-bit values here) needs all of it
-    assert dec(qvv=qstruct(bits=8, m=0, S=False), wsb=wsd - 1) == tq.TQ_ERR_WORKSPACE
+    # an argument); the scalar wide-code plan (6-bit values here) needs all of it
+    assert dec(qvv=qstruct(bits=6, m=0, S=False), wsb=wsd - 1) == tq.TQ_ERR_WORKSPACE
     assert dec(wsb=4096) == tq.TQ_ERR_WORKSPACE
     assert dec(G=0) == tq.TQ_ERR_UNSUPPORTED
     assert dec(G=17) == tq.TQ_ERR_UNSUPPORTED

@@ -97,9 +97,15 @@ def test_wide_dequantize_parity(d, bits, m, include_qjl, out_dtype):
 
 DCASES = [
     # d, key mse bits, key QJL, value bits, streams, tokens, G
+    # MFMA kernel (d = 128, G <= 8, values of 4 or 8 bits with any keys)
     (128, 7, True, 4, 2, 700, 8),     # 8-bit keys (7 + QJL), 4-bit values
     (128, 2, True, 8, 2, 300, 8),     # narrow keys, 8-bit values
-    (128, 8, False, 8, 1, 513, 16),   # 8-bit codes-only keys and values
+    (128, 8, True, 8, 2, 2100, 8),    # 8-bit codes + QJL keys, 8-bit values, several steps per wave
+    (128, 5, False, 4, 3, 257, 3),
+    (128, 6, True, 8, 1, 4100, 8),
+    # scalar wide kernel (other widths, G > 8, other d)
+    (128, 6, True, 6, 2, 300, 8),
+    (128, 8, False, 8, 1, 513, 16),   # 8-bit codes-only keys and values, G = 16
     (64, 5, True, 6, 3, 257, 4),
     (256, 6, True, 3, 2, 256, 5),
 ]
