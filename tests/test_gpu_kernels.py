@@ -270,3 +270,69 @@ def test_quantize_crowded_codebook(m):
         n = 700
         x = synth.to_f16(synth.normals(23, synth.ROLE_DATA_K, np.arange(n * d)).reshape(n, d) * 2.0)
         check_quantize(qo, x.astype(np.float64), gpu_quantize(qg, x).to_host())
+
+
+# ---- the sweep workload at full size: 2^20 unit-norm fp32 vectors per (d, width)
+
+SWEEP_PAGE_DIST = {(128, 3): 0.000270, (256, 3): 0.000135}   # the pages' Lloyd-Max table
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("qjl", [False, True])
+def test_sweep_full_size(d, bits, qjl):
+    """2^20 random unit vectors (normalised N(0, I), fp32) quantized in one call
+    at total width `bits` (with QJL: bits - 1 code bits + the sketch). Checks:
+    2000 sampled vectors against the oracle (codes, signs, scalars); the
+    whole set's distortion per coordinate (from the codes-only reconstruction)
+    against the distortion the oracle measures on the sample and, where the
+    pages print it, against their value; and 1024 x 1024 scores on both
+    packings."""
+    tq = tqmod()
+    from synth import gpu as sgpu
+    n = 1 << 20
+    mse = bits - 1 if qjl else bits
+    qg, qo = quantizers(d, mse, d if qjl else 0)
+    g = torch.empty((n, d), dtype=torch.float32, device=DEV)
+    sgpu.fill_f32(g, 61, synth.ROLE_DATA_K)
+    x = g / torch.linalg.vector_norm(g, dim=1, keepdim=True)
+    del g
+    p = tq.Packed.empty(qg, n, DEV)
+    tq.tq_quantize(qg, x, p)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(d * 10 + bits).choice(n, 2000, replace=False))
+    rt = torch.from_numpy(rows).to(DEV)
+    xs = x[rt].cpu().numpy().astype(np.float64)
+    sub = tuple(None if a is None else a[rt].cpu().numpy().view(np.uint32 if a.dtype == torch.int32 else np.uint16)
+                for a in (p.codes, p.signs, p.norm, p.rnorm))
+    _, _, ref = check_quantize(qo, xs, sub)
+    # distortion per coordinate over all 2^20 vectors: ||x - x_hat||^2 / d with
+    # the codes-only reconstruction (unit norms, orthogonal rotation)
+    xh = torch.empty_like(x)
+    tq.tq_dequantize(qg, p, n, False, xh)
+    torch.cuda.synchronize()
+    dist_gpu = float(((x - xh) ** 2).sum(dim=1).mean().item()) / d
+    del xh
+    y = oracle.quantize(qo, xs, want_y=True)[1]
+    idx = oracle.unpack_codes(qo, ref.codes)
+    dist_sample = float(np.mean((y - qo.cent.astype(np.float64)[idx]) ** 2))
+    assert abs(dist_gpu - dist_sample) <= 0.05 * dist_sample, (dist_gpu, dist_sample)
+    if not qjl and (d, bits) in SWEEP_PAGE_DIST:
+        assert abs(dist_gpu - SWEEP_PAGE_DIST[(d, bits)]) <= 0.03 * SWEEP_PAGE_DIST[(d, bits)], dist_gpu
+    # scores of 1024 unit queries against the first 1024 keys, both packings
+    nk = nq = 1024
+    qh = torch.empty((nq, d), dtype=torch.float32, device=DEV)
+    sgpu.fill_f32(qh, 61, synth.ROLE_QUERY)
+    qh = qh / torch.linalg.vector_norm(qh, dim=1, keepdim=True)
+    keys = tq.Packed(p.codes[:nk], p.signs[:nk] if qjl else None, p.norm[:nk], p.rnorm[:nk] if qjl else None)
+    sc = torch.empty((nq, nk), dtype=torch.float32, device=DEV)
+    tq.tq_scores(qg, keys, nk, qh, sc)
+    torch.cuda.synchronize()
+    qn = qh.cpu().numpy().astype(np.float64)
+    check_close(sc.cpu().numpy(), oracle.scores(qo, to_oracle_packed(qo, keys.to_host()), qn),
+                what="sweep scores on GPU-packed keys")
+    rk = oracle.quantize(qo, x[:nk].cpu().numpy().astype(np.float64))
+    po = tq.Packed.from_host(rk.codes, rk.signs if qjl else None, rk.norm, rk.rnorm if qjl else None, DEV)
+    tq.tq_scores(qg, po, nk, qh, sc)
+    torch.cuda.synchronize()
+    check_close(sc.cpu().numpy(), oracle.scores(qo, rk, qn), what="sweep scores on oracle-packed keys")
