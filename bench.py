@@ -234,6 +234,8 @@ def main():
         result["small_keyset"] = small_keyset(tq, qk, dev)
         result["wide_widths"] = wide_widths(tq, qv, units[0], T, G, d, diag_k, S, diag_v, dev)
         if args.workload == "128k":
+            result["sweep_quantize"] = sweep_quantize(tq, dev)
+        if args.workload == "128k":
             result["prefill_scores"] = prefill_scores(tq, qk, units[0]["PK"], T, dev)
 
     if not args.no_cpu_baseline:
@@ -386,6 +388,46 @@ def wide_widths(tq, qv, u, T, G, d, diag_k, S, diag_v, dev, passes=3):
                      "frac_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     res["note"] = ("MFMA quantizer with binary-search codes; MFMA decode with single-code tables "
                    "(values of 4 or 8 bits)")
+    return res
+
+
+def sweep_quantize(tq, dev, n=1 << 20, passes=3):
+    """Quantize throughput of the sweep workload: 2^20 unit-norm fp32 vectors
+    (normalised N(0, I)) for d in {64, 128, 256} and total widths 2..4, with
+    the QJL sketch (width - 1 code bits) and without; us per launch and
+    algorithmic GB/s (fp32 input read, packed output written)."""
+    import torch
+    import synth
+    from synth import gpu as sgpu
+    from synth import workloads as W
+    stream = torch.cuda.current_stream()
+    res = {}
+    for d in (64, 128, 256):
+        diag_k, S, diag_v = W.quantizer_inputs(d)
+        g = torch.empty((n, d), dtype=torch.float32, device=dev)
+        sgpu.fill_f32(g, 61, synth.ROLE_DATA_K)
+        x = g / torch.linalg.vector_norm(g, dim=1, keepdim=True)
+        del g
+        for bits in (2, 3, 4):
+            for qjl in (False, True):
+                mse = bits - 1 if qjl else bits
+                q = tq.Quantizer(d, mse, d if qjl else 0, diag_k if qjl else diag_v, S if qjl else None, dev)
+                p = tq.Packed.empty(q, n, dev)
+                tq.tq_quantize(q, x, p)
+                ev = []
+                for _ in range(passes):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    tq.tq_quantize(q, x, p)
+                    b.record(stream)
+                    ev.append((a, b))
+                torch.cuda.synchronize()
+                us = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e3
+                alg = n * (4 * d + packed_bytes_per_vector(d, mse, qjl))
+                res[f"d{d}_b{bits}_{'qjl' if qjl else 'mse'}"] = {
+                    "us_per_launch": round(us, 2), "GB_per_s": round(alg / (us * 1e-6) / 1e9, 1),
+                    "frac_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del x
     return res
 
 

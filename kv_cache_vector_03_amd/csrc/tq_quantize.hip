@@ -22,8 +22,8 @@
 // matrix S; row order of S is permuted so that each ballot of the MFMA output
 // is two ready bytes of the group-major sign stream.
 //
-// d = 256: wave kernel (one wave per vector, coordinate 64 r + lane), packing
-// through LDS.
+// d = 256: one wave per vector at a time (coordinate 64 r + lane), 16 vectors
+// per block pass, the residual projection on MFMA with S held in registers.
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -336,23 +336,45 @@ __global__ __launch_bounds__(256) void k_quantize_quad(const void* __restrict__ 
     }
 }
 
-// ---------------------------------------------------------------- wave kernel (d = 256)
+// ---------------------------------------------------------------- d = 256 kernel
 
-template <int D, int B, bool QJL, bool F16>
-__global__ __launch_bounds__(256) void k_quantize_wave(const void* __restrict__ x, int64_t n,
-                                                       const float* __restrict__ cent,
-                                                       const float* __restrict__ bnd,
-                                                       const uint32_t* __restrict__ diag,
-                                                       const uint16_t* __restrict__ S,
-                                                       uint32_t* __restrict__ codes,
-                                                       uint32_t* __restrict__ signs,
-                                                       uint16_t* __restrict__ norm,
-                                                       uint16_t* __restrict__ rnorm)
+// d = 256. A wave takes two vectors per pass, one at a time, with coordinate
+// 64 r + lane in slot r (the rotation is fwht_wave); a 512-thread block takes
+// 16 vectors per pass, and each vector of the next pass is loaded as soon as
+// its slot is free. In that layout lane l holds members t = 2 r + [l >= 32] of
+// group l % 32, so one exchange with lane l ^ 32 completes every group and
+// lanes 0..31 store them. For keys each vector's residual goes to LDS as fp16
+// hi + lo parts (in units of 2^-10, so both stay normal fp16 numbers and their
+// sum carries about 22 bits) and the block projects its 16 residuals on MFMA:
+// the A operand is S (wave w keeps rows 32 w .. 32 w + 31 in registers for the
+// whole kernel), the B operand's columns are the vectors. Output register i
+// of m-tile mt in lane (v, q) = (lane % 16, lane / 16) is projection
+// j = 32 w + 16 mt + 4 q + i of vector v: bit w of sign byte 16 mt + 4 q + i.
+constexpr int kD256Waves = 8, kD256Pass = 16;
+// The launch bound asks for four waves per SIMD, i.e. two blocks per compute
+// unit, so one block's barriers overlap the other's work; the keys variant
+// then spills a few registers, and still runs 10-20% faster than with one block.
+
+template <int B, bool QJL, bool F16>
+__global__ __launch_bounds__(64 * kD256Waves, 4) void k_quantize_d256(const void* __restrict__ x, int64_t n,
+                                                                   const float* __restrict__ cent,
+                                                                   const float* __restrict__ bnd,
+                                                                   const uint32_t* __restrict__ diag,
+                                                                   const uint16_t* __restrict__ S,
+                                                                   uint32_t* __restrict__ codes,
+                                                                   uint32_t* __restrict__ signs,
+                                                                   uint16_t* __restrict__ norm,
+                                                                   uint16_t* __restrict__ rnorm)
 {
-    constexpr int R = D / 64, L = 1 << B, G = D / 8;
-    __shared__ float res[kWavesPerBlock][D];
-    __shared__ unsigned char cidx[kWavesPerBlock][D];
+    constexpr int D = 256, R = 4, L = 1 << B, VW = kD256Pass / kD256Waves;
+    constexpr int RS = D + 8;  // fp16 elements per LDS residual row (16-byte pad)
+    constexpr int NB = QJL ? kD256Pass : 1;
+    __shared__ __align__(16) uint16_t rh[NB][RS];
+    __shared__ __align__(16) uint16_t rl[NB][RS];
+    // wave w's bit (bit w) of the 32 sign bytes of each vector
+    __shared__ __align__(16) uint32_t part[QJL ? kD256Waves : 1][NB][8];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int hi32 = lane >> 5;
     float t[L - 1], c[L];
 #pragma unroll
     for (int l = 0; l < L - 1; ++l) t[l] = bnd[l];
@@ -361,71 +383,121 @@ __global__ __launch_bounds__(256) void k_quantize_wave(const void* __restrict__ 
     uint32_t dm[R];
     load_diag<R>(diag, lane, dm);
 
-    for (int64_t base = (int64_t)blockIdx.x * kWavesPerBlock; base < n;
-         base += (int64_t)gridDim.x * kWavesPerBlock) {
-        const int64_t v = base + wid;
-        const bool active = v < n;
-        float y[R];
-        float ss = 0.f;
+    half8_t sf[QJL ? 2 : 1][QJL ? 8 : 1];
+    if constexpr (QJL) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            y[r] = active ? load_elem<F16>(x, v * D + 64 * r + lane) : 0.f;
-            ss += y[r] * y[r];
-        }
-        const float nrm = sqrtf(wave_sum(ss));
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < R; ++r) y[r] = flip(y[r], dm[r]);
-        fwht_wave<R>(y, lane);
-        const float sc = nrm > 0.f ? 1.0f / (sqrtf((float)D) * nrm) : 0.f;
-        float g2 = 0.f;
+            for (int ks = 0; ks < 8; ++ks) {
+                const int row = 32 * wid + 16 * mt + (lane & 15);
+                const uint4 w = *reinterpret_cast<const uint4*>(S + row * D + 32 * ks + 8 * (lane >> 4));
+                sf[mt][ks] = __builtin_bit_cast(half8_t, w);
+            }
+    }
+
+    const int64_t step = (int64_t)gridDim.x * kD256Pass;
+    float xn[VW][R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            y[r] *= sc;
-            int k = 0;
+    for (int i = 0; i < VW; ++i) {
+        const int64_t v = (int64_t)blockIdx.x * kD256Pass + VW * wid + i;
 #pragma unroll
-            for (int l = 0; l < L - 1; ++l) k += (t[l] < y[r]) ? 1 : 0;
-            cidx[wid][64 * r + lane] = (unsigned char)k;
-            if (QJL) {
-                const float rr = y[r] - pick<L>(c, k);
-                g2 += rr * rr;
-                res[wid][64 * r + lane] = rr;
+        for (int r = 0; r < R; ++r) xn[i][r] = v < n ? load_elem<F16>(x, v * D + 64 * r + lane) : 0.f;
+    }
+    for (int64_t base = (int64_t)blockIdx.x * kD256Pass; base < n; base += step) {
+#pragma unroll
+        for (int i = 0; i < VW; ++i) {
+            float y[R];
+            const int64_t v = base + VW * wid + i, vn = v + step;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                y[r] = xn[i][r];
+                xn[i][r] = vn < n ? load_elem<F16>(x, vn * D + 64 * r + lane) : 0.f;  // next pass
+            }
+            float ss = 0.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) ss += y[r] * y[r];
+            const float nrm = sqrtf(wave_sum(ss));
+#pragma unroll
+            for (int r = 0; r < R; ++r) y[r] = flip(y[r], dm[r]);
+            fwht_wave<R>(y, lane);
+            const float sc = nrm > 0.f ? 1.0f / (16.0f * nrm) : 0.f;
+            uint32_t own = 0;
+            float g2 = 0.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float yy = y[r] * sc;
+                // boundaries ascend, so the compares that pass are a prefix
+                // and the last one names the centroid c[k]
+                int k = 0;
+                float ck = c[0];
+#pragma unroll
+                for (int l = 0; l < L - 1; ++l) {
+                    const bool above = t[l] < yy;
+                    k += above ? 1 : 0;
+                    if constexpr (QJL) ck = above ? c[l + 1] : ck;
+                }
+                own |= (uint32_t)k << (B * (2 * r + hi32));
+                if constexpr (QJL) {
+                    const float rr = yy - ck;
+                    g2 += rr * rr;
+                    const float s = rr * 1024.0f;
+                    const _Float16 h = (_Float16)s;
+                    const _Float16 lo = (_Float16)(s - (float)h);
+                    rh[VW * wid + i][64 * r + lane] = __builtin_bit_cast(uint16_t, h);
+                    rl[VW * wid + i][64 * r + lane] = __builtin_bit_cast(uint16_t, lo);
+                }
+            }
+            // lane l and lane l ^ 32 together hold group l % 32
+            const uint32_t fg = own | (uint32_t)__shfl_xor((int)own, 32);
+            if constexpr (QJL) g2 = wave_sum(g2);
+            if (v < n) {
+                if (lane < 32) {
+                    unsigned char* dst = reinterpret_cast<unsigned char*>(codes + v * (B * D / 32)) + B * lane;
+                    if constexpr (B == 4) *reinterpret_cast<uint32_t*>(dst) = fg;
+                    else if constexpr (B == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)fg;
+                    else
+#pragma unroll
+                        for (int b = 0; b < B; ++b) dst[b] = (unsigned char)(fg >> (8 * b));
+                }
+                if (lane == 0) {
+                    norm[v] = f2h(nrm);
+                    if constexpr (QJL) rnorm[v] = f2h(sqrtf(g2));
+                }
             }
         }
-        __syncthreads();
-        // one lane per group packs its 8 codes (8 B bits) into the byte stream
-        if (active && lane < G) {
-            uint32_t f = 0;
-#pragma unroll
-            for (int tt = 0; tt < 8; ++tt) f |= (uint32_t)cidx[wid][lane + G * tt] << (B * tt);
-            unsigned char* dst = reinterpret_cast<unsigned char*>(codes + v * (B * D / 32)) + B * lane;
-#pragma unroll
-            for (int b = 0; b < B; ++b) dst[b] = (unsigned char)(f >> (8 * b));
-        }
-        if (active && lane == 0) norm[v] = f2h(nrm);
         if constexpr (QJL) {
-            g2 = wave_sum(g2);
-            uint32_t sb[R];
+            __syncthreads();
+            float4_t acc[2];
 #pragma unroll
-            for (int k = 0; k < R; ++k) {
-                const int j = 64 * k + lane;
-                const uint16_t* Sj = S + (int64_t)j * D;
-                float u = 0.f;
-                for (int i = 0; i < D; ++i) u += h2f(Sj[i]) * res[wid][i];
-                sb[k] = u >= 0.f ? 1u : 0u;
+            for (int mt = 0; mt < 2; ++mt) acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+            const int vc = lane & 15, q = lane >> 4;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const half8_t bh = *reinterpret_cast<const half8_t*>(&rh[vc][32 * ks + 8 * q]);
+                const half8_t bl = *reinterpret_cast<const half8_t*>(&rl[vc][32 * ks + 8 * q]);
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sf[mt][ks], bh, acc[mt], 0, 0, 0);
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sf[mt][ks], bl, acc[mt], 0, 0, 0);
+                }
+            }
+            // bytes 16 mt + 4 q .. + 3 of vector vc, each holding this wave's bit
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                uint32_t wv = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wv |= (acc[mt][i] >= 0.f ? 1u : 0u) << (8 * i);
+                part[wid][vc][4 * mt + q] = wv;
             }
             __syncthreads();
+            // thread (vector tid / 32, sign byte tid % 32)
+            const int v = threadIdx.x >> 5, cb = threadIdx.x & 31;
+            uint32_t sbyte = 0;
 #pragma unroll
-            for (int k = 0; k < R; ++k) cidx[wid][64 * k + lane] = (unsigned char)sb[k];
-            __syncthreads();
-            if (active && lane < G) {
-                uint32_t f = 0;
-#pragma unroll
-                for (int tt = 0; tt < 8; ++tt) f |= (uint32_t)cidx[wid][lane + G * tt] << tt;
-                reinterpret_cast<unsigned char*>(signs + v * (D / 32))[lane] = (unsigned char)f;
-            }
-            if (active && lane == 0) rnorm[v] = f2h(sqrtf(g2));
+            for (int w = 0; w < kD256Waves; ++w)
+                sbyte |= (uint32_t)reinterpret_cast<const unsigned char*>(&part[w][v][0])[cb] << w;
+            if (base + v < n) reinterpret_cast<unsigned char*>(signs + (base + v) * (D / 32))[cb] = (unsigned char)sbyte;
         }
-        __syncthreads();
     }
 }
 
@@ -573,13 +645,16 @@ void quantize_d_b(const tq_quantizer* q, const void* x, int dtype, int64_t n, co
                                o->rnorm);
         }
     } else {
-        dim3 grid(grid_for(n, kWavesPerBlock));
-        if (dtype == TQ_F16)
-            hipLaunchKernelGGL((k_quantize_wave<D, B, QJL, true>), grid, block, 0, s, x, n, q->centroids,
+        static_assert(D == 256, "d = 256 kernel");
+        if (dtype == TQ_F16) {
+            auto kern = k_quantize_d256<B, QJL, true>;
+            hipLaunchKernelGGL(kern, dim3(resident_grid(kern, kD256Pass, n, 64 * kD256Waves)), dim3(64 * kD256Waves), 0, s, x, n, q->centroids,
                                q->boundaries, q->diag_signs, q->S, o->codes, o->signs, o->norm, o->rnorm);
-        else
-            hipLaunchKernelGGL((k_quantize_wave<D, B, QJL, false>), grid, block, 0, s, x, n, q->centroids,
+        } else {
+            auto kern = k_quantize_d256<B, QJL, false>;
+            hipLaunchKernelGGL(kern, dim3(resident_grid(kern, kD256Pass, n, 64 * kD256Waves)), dim3(64 * kD256Waves), 0, s, x, n, q->centroids,
                                q->boundaries, q->diag_signs, q->S, o->codes, o->signs, o->norm, o->rnorm);
+        }
     }
 }
 

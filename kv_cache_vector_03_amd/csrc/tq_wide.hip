@@ -74,7 +74,8 @@ __global__ __launch_bounds__(64 * kWaves) void k_quantize_wide(const void* __res
         cb[l] = cent[l];
         tb[l] = l < L - 1 ? bnd[l] : INFINITY;
     }
-    if constexpr (QJL)
+    constexpr bool ST = QJL && D <= 128;  // S^T in LDS (d = 256: 128 KiB, too much; rows read from S)
+    if constexpr (ST)
         for (int e = threadIdx.x; e < D * D; e += blockDim.x) st[(e % D) * D + e / D] = S[e];
     __syncthreads();
     uint32_t dm[R];
@@ -125,10 +126,25 @@ __global__ __launch_bounds__(64 * kWaves) void k_quantize_wide(const void* __res
             float u[R];
 #pragma unroll
             for (int k = 0; k < R; ++k) u[k] = 0.f;
-            for (int i = 0; i < D; ++i) {
-                const float ri = res[wid][i];
+            if constexpr (ST) {
+                for (int i = 0; i < D; ++i) {
+                    const float ri = res[wid][i];
 #pragma unroll
-                for (int k = 0; k < R; ++k) u[k] = fmaf(h2f(st[i * D + 64 * k + lane]), ri, u[k]);
+                    for (int k = 0; k < R; ++k) u[k] = fmaf(h2f(st[i * D + 64 * k + lane]), ri, u[k]);
+                }
+            } else {
+                // each lane walks its own rows of S, 16 bytes (8 entries) per load
+#pragma unroll
+                for (int k = 0; k < R; ++k) {
+                    const uint4* Sj = reinterpret_cast<const uint4*>(S + (int64_t)(64 * k + lane) * D);
+                    for (int i8 = 0; i8 < D / 8; ++i8) {
+                        const uint4 w = Sj[i8];
+                        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            u[k] = fmaf(h2f((uint16_t)(ww[e >> 1] >> (16 * (e & 1)))), res[wid][8 * i8 + e], u[k]);
+                    }
+                }
             }
 #pragma unroll
             for (int k = 0; k < R; ++k) sb[k] = u[k] >= 0.f ? 1u : 0u;
@@ -446,7 +462,7 @@ void quantize_wide_d(const tq_quantizer* q, const void* x, int dtype, int64_t n,
     const dim3 grid(wide_grid(n, kWaves)), block(64 * kWaves);
     const int b = q->mse_bits;
     if (q->qjl_m) {
-        constexpr size_t lds = (size_t)D * D * 2;
+        constexpr size_t lds = D <= 128 ? (size_t)D * D * 2 : 0;  // S^T for d <= 128
         if (dtype == TQ_F16) launch_wide_q(k_quantize_wide<D, true, true>, lds, n, x, b, q, o, s);
         else launch_wide_q(k_quantize_wide<D, true, false>, lds, n, x, b, q, o, s);
     } else {
