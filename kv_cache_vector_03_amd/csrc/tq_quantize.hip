@@ -339,17 +339,107 @@ __global__ __launch_bounds__(256) void k_quantize_quad(const void* __restrict__ 
 // ---------------------------------------------------------------- d = 256 kernel
 
 // d = 256. A wave takes two vectors per pass, one at a time, with coordinate
-// 64 r + lane in slot r (the rotation is fwht_wave); a 512-thread block takes
+// 64 r + lane in slot r (the rotation is fwht256); a 512-thread block takes
 // 16 vectors per pass, and each vector of the next pass is loaded as soon as
 // its slot is free. In that layout lane l holds members t = 2 r + [l >= 32] of
-// group l % 32, so one exchange with lane l ^ 32 completes every group and
-// lanes 0..31 store them. For keys each vector's residual goes to LDS as fp16
+// group l % 32, so one exchange with lane l ^ 32 (a permlane swap) completes
+// every group and lanes 0..31 store them. For keys each vector's residual goes to LDS as fp16
 // hi + lo parts (in units of 2^-10, so both stay normal fp16 numbers and their
 // sum carries about 22 bits) and the block projects its 16 residuals on MFMA:
 // the A operand is S (wave w keeps rows 32 w .. 32 w + 31 in registers for the
 // whole kernel), the B operand's columns are the vectors. Output register i
 // of m-tile mt in lane (v, q) = (lane % 16, lane / 16) is projection
 // j = 32 w + 16 mt + 4 q + i of vector v: bit w of sign byte 16 mt + 4 q + i.
+// Value held by lane l ^ M (M = 1, 2, 4, 8) by DPP moves within 16-lane rows:
+// quad permutations for 1 and 2, quad reversal (l ^ 3) then half-row mirror
+// (l ^ 7) for 4, a rotation by 8 within the row for 8.
+template <int M>
+__device__ __forceinline__ float dpp_xor(float v)
+{
+    const int i = __float_as_int(v);
+    if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, false));
+    else if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, false));
+    else if constexpr (M == 4)
+        return __int_as_float(
+            __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(i, 0x1B, 0xF, 0xF, false), 0x141, 0xF, 0xF, false));
+    else return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0x128, 0xF, 0xF, false));
+}
+
+// (own value, value of lane l ^ M) for M = 16, 32: a permlane swap of a
+// register with itself returns (row pair's even row, odd row) in every lane
+template <int M>
+__device__ __forceinline__ void row_pair(float v, float& even, float& odd)
+{
+    const uint32_t u = __float_as_uint(v);
+    if constexpr (M == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        even = __uint_as_float(p[0]);
+        odd = __uint_as_float(p[1]);
+    } else {
+        const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        even = __uint_as_float(p[0]);
+        odd = __uint_as_float(p[1]);
+    }
+}
+
+// Butterfly on lane bit M: a + b where the lane's bit is clear, a - b where it
+// is set, a being the value of the lane with the bit clear -- the same
+// operands and roundings as fwht_wave. sm = sign bit where the lane bit is set.
+template <int M>
+__device__ __forceinline__ float lane_bfly(float v, uint32_t sm)
+{
+    if constexpr (M <= 8) {
+        return dpp_xor<M>(v) + flip(v, sm);  // p + v, or p - v with p the bit-clear lane's value
+    } else {
+        float e, o;
+        row_pair<M>(v, e, o);
+        return e + flip(o, sm);
+    }
+}
+
+// Sum over the wave in the order of wave_sum (lane bits 5, 4, .., 0), so the
+// result is the same to the bit.
+__device__ __forceinline__ float wave_sum_dpp(float v)
+{
+    float e, o;
+    row_pair<32>(v, e, o);
+    v = e + o;
+    row_pair<16>(v, e, o);
+    v = e + o;
+    v += dpp_xor<8>(v);
+    v += dpp_xor<4>(v);
+    v += dpp_xor<2>(v);
+    v += dpp_xor<1>(v);
+    return v;
+}
+
+// fwht_wave for d = 256 (lane l, slot r = coordinate 64 r + l) with the lane
+// stages on DPP and permlane swaps instead of LDS exchanges; same stage order.
+__device__ __forceinline__ void fwht256(float (&v)[4], const uint32_t (&sm)[6])
+{
+#pragma unroll
+    for (int h = 1; h < 4; h <<= 1)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (!(r & h)) {
+                const float a = v[r], b = v[r + h];
+                v[r] = a + b;
+                v[r + h] = a - b;
+            }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = lane_bfly<1>(v[r], sm[0]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = lane_bfly<2>(v[r], sm[1]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = lane_bfly<4>(v[r], sm[2]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = lane_bfly<8>(v[r], sm[3]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = lane_bfly<16>(v[r], sm[4]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = lane_bfly<32>(v[r], sm[5]);
+}
+
 constexpr int kD256Waves = 8, kD256Pass = 16;
 // The launch bound asks for four waves per SIMD, i.e. two blocks per compute
 // unit, so one block's barriers overlap the other's work; the keys variant
@@ -382,6 +472,9 @@ __global__ __launch_bounds__(64 * kD256Waves, 4) void k_quantize_d256(const void
     for (int l = 0; l < L; ++l) c[l] = cent[l];
     uint32_t dm[R];
     load_diag<R>(diag, lane, dm);
+    uint32_t sm[6];
+#pragma unroll
+    for (int b = 0; b < 6; ++b) sm[b] = ((uint32_t)(lane >> b) & 1u) << 31;
 
     half8_t sf[QJL ? 2 : 1][QJL ? 8 : 1];
     if constexpr (QJL) {
@@ -396,31 +489,35 @@ __global__ __launch_bounds__(64 * kD256Waves, 4) void k_quantize_d256(const void
     }
 
     const int64_t step = (int64_t)gridDim.x * kD256Pass;
+    // vector v's coordinates, or zeros past the end (read from the last vector
+    // and discarded, so the loads need no branch; n >= 1 at every launch)
+    auto fetch = [&](int64_t v, float (&o)[R]) {
+        const int64_t vr = v < n ? v : n - 1;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float e = load_elem<F16>(x, vr * D + 64 * r + lane);
+            o[r] = v < n ? e : 0.f;
+        }
+    };
     float xn[VW][R];
 #pragma unroll
-    for (int i = 0; i < VW; ++i) {
-        const int64_t v = (int64_t)blockIdx.x * kD256Pass + VW * wid + i;
-#pragma unroll
-        for (int r = 0; r < R; ++r) xn[i][r] = v < n ? load_elem<F16>(x, v * D + 64 * r + lane) : 0.f;
-    }
+    for (int i = 0; i < VW; ++i) fetch((int64_t)blockIdx.x * kD256Pass + VW * wid + i, xn[i]);
     for (int64_t base = (int64_t)blockIdx.x * kD256Pass; base < n; base += step) {
 #pragma unroll
         for (int i = 0; i < VW; ++i) {
             float y[R];
-            const int64_t v = base + VW * wid + i, vn = v + step;
+            const int64_t v = base + VW * wid + i;
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                y[r] = xn[i][r];
-                xn[i][r] = vn < n ? load_elem<F16>(x, vn * D + 64 * r + lane) : 0.f;  // next pass
-            }
+            for (int r = 0; r < R; ++r) y[r] = xn[i][r];
+            fetch(v + step, xn[i]);  // next pass
             float ss = 0.f;
 #pragma unroll
             for (int r = 0; r < R; ++r) ss += y[r] * y[r];
-            const float nrm = sqrtf(wave_sum(ss));
+            const float nrm = sqrtf(wave_sum_dpp(ss));
 #pragma unroll
             for (int r = 0; r < R; ++r) y[r] = flip(y[r], dm[r]);
-            fwht_wave<R>(y, lane);
-            const float sc = nrm > 0.f ? 1.0f / (16.0f * nrm) : 0.f;
+            fwht256(y, sm);
+            const float sc = nrm > 0.f ? __builtin_amdgcn_rcpf(16.0f * nrm) : 0.f;
             uint32_t own = 0;
             float g2 = 0.f;
 #pragma unroll
@@ -448,8 +545,10 @@ __global__ __launch_bounds__(64 * kD256Waves, 4) void k_quantize_d256(const void
                 }
             }
             // lane l and lane l ^ 32 together hold group l % 32
-            const uint32_t fg = own | (uint32_t)__shfl_xor((int)own, 32);
-            if constexpr (QJL) g2 = wave_sum(g2);
+            float fe, fo;
+            row_pair<32>(__uint_as_float(own), fe, fo);
+            const uint32_t fg = __float_as_uint(fe) | __float_as_uint(fo);
+            if constexpr (QJL) g2 = wave_sum_dpp(g2);
             if (v < n) {
                 if (lane < 32) {
                     unsigned char* dst = reinterpret_cast<unsigned char*>(codes + v * (B * D / 32)) + B * lane;
