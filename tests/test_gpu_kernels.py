@@ -63,18 +63,18 @@ def test_quantize_parity(d, bits, m, dtype):
     check_quantize(qo, x.astype(np.float64), p.to_host())
 
 
-@pytest.mark.parametrize("n", [1, 3, 4, 5, 65, 257])
-def test_quantize_ragged_counts(n):
-    qg, qo = quantizers(128, 2, 128)
-    x = synth.to_f16(synth.normals(19, synth.ROLE_DATA_K, np.arange(n * 128)).reshape(n, 128))
+@pytest.mark.parametrize("d,bits,m", [(128, 2, 128), (256, 3, 256), (256, 2, 0)])
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 17, 65, 257])
+def test_quantize_ragged_counts(d, bits, m, n):
+    qg, qo = quantizers(d, bits, m)
+    x = synth.to_f16(synth.normals(19, synth.ROLE_DATA_K, np.arange(n * d)).reshape(n, d))
     check_quantize(qo, x.astype(np.float64), gpu_quantize(qg, x).to_host())
 
 
-@pytest.mark.parametrize("bits,m", [(2, 128), (3, 128), (4, 0)])
-def test_quantize_many_rounds_full(bits, m):
+@pytest.mark.parametrize("d,bits,m", [(128, 2, 128), (128, 3, 128), (128, 4, 0), (256, 3, 256), (256, 4, 0)])
+def test_quantize_many_rounds_full(d, bits, m):
     """Enough fp16 vectors that every resident block loops over several rounds
     of batches (and a ragged last round); every output is checked."""
-    d = 128
     qg, qo = quantizers(d, bits, m)
     n = 3 * 256 * 64 + 4 * 64 + 37
     x = synth.to_f16(synth.normals(23, synth.ROLE_DATA_K, np.arange(n * d)).reshape(n, d) * 2.0)
