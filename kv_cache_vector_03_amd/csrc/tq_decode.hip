@@ -85,14 +85,17 @@ __global__ __launch_bounds__(256) void k_qprep_frag(const void* __restrict__ q, 
                         s * app.stride + app.pos, &qs[0][0]);
         return;
     }
-    // thread (h, i) projects row j = tt + (d/32) i of S onto head h; its row is
-    // fetched first so the load overlaps the rotation
+    // thread (h, i) projects row j = tt + (d/32) i of S onto head h; the block's
+    // 32 rows are copied to LDS first (coalesced, each row once), so the copy
+    // overlaps the rotation
     const int ph = tid >> 5, pi = tid & 31;
-    uint4 srow[QJL ? D / 8 : 1];
+    __shared__ uint4 srs[QJL ? 32 : 1][D / 8 + 1];
     if constexpr (QJL) {
-        const uint4* row = reinterpret_cast<const uint4*>(S + (int64_t)(tt + KS * pi) * D);
 #pragma unroll
-        for (int c = 0; c < D / 8; ++c) srow[c] = row[c];
+        for (int k = 0; k < 2; ++k) {
+            const int e = tid + 256 * k, row = e >> 4, c = e & 15;
+            srs[row][c] = reinterpret_cast<const uint4*>(S + (int64_t)(tt + KS * row) * D)[c];
+        }
     }
     uint32_t dm[R];
     load_diag<R>(diag, lane, dm);
@@ -111,7 +114,8 @@ __global__ __launch_bounds__(256) void k_qprep_frag(const void* __restrict__ q, 
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < D / 8; ++c) {
-            const uint32_t w4[4] = {srow[c].x, srow[c].y, srow[c].z, srow[c].w};
+            const uint4 sw = srs[pi][c];
+            const uint32_t w4[4] = {sw.x, sw.y, sw.z, sw.w};
             const float4 qa = *reinterpret_cast<const float4*>(&qs[ph][8 * c]);
             const float4 qb = *reinterpret_cast<const float4*>(&qs[ph][8 * c + 4]);
             const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
