@@ -72,7 +72,8 @@ KERNEL_SOURCES = {
     "quantize_k": ["kv_cache_vector_03_amd/csrc/tq_quantize_m128.hip", "kv_cache_vector_03_amd/csrc/tq_device.h"],
     "quantize_v": ["kv_cache_vector_03_amd/csrc/tq_quantize_m128.hip", "kv_cache_vector_03_amd/csrc/tq_device.h"],
     "decode_attn": ["kv_cache_vector_03_amd/csrc/tq_decode.hip", "kv_cache_vector_03_amd/csrc/tq_attn.hip",
-                    "kv_cache_vector_03_amd/csrc/tq_device.h", "kv_cache_vector_03_amd/csrc/tq_host.cpp"],
+                    "kv_cache_vector_03_amd/csrc/tq_append.h", "kv_cache_vector_03_amd/csrc/tq_device.h",
+                    "kv_cache_vector_03_amd/csrc/tq_host.cpp"],
 }
 
 
