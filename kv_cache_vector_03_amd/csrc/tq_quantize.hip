@@ -709,6 +709,139 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint32_t* __restrict__
     }
 }
 
+// d = 128 dequantize; for keys the sketch term runs on MFMA. A wave takes 16
+// vectors per pass; the term u_i = sum_j S[j][i] s_j (s_j = +-1) is a 16-vector x 128 x
+// 128 product. The A operand is vector (lane % 16)'s sign byte c = 4 ks + q
+// (rows c + 16 e of the group-major sign stream, e = 0..7), expanded to +-1
+// through an LDS table; the B operand holds the same rows of S for coordinate
+// 16 nt + lane % 16 (fragments built once per block in LDS). Output register
+// r of n-tile nt in lane (i, q) = (lane % 16, lane / 16) is coordinate
+// 16 nt + i of vector 4 q + r. In the group-major code layout the codes of
+// coordinates i + 16 t are group i's field, so one B-byte load per vector
+// gives the lane all its codes; the inverse rotation runs over nt in registers
+// (coordinate bits 4..6) and over i by DPP (bits 0..3).
+template <int B, bool QJL, bool F16OUT>
+__global__ __launch_bounds__(256, 4) void k_dequantize128(const uint32_t* __restrict__ codes,
+                                                            const uint32_t* __restrict__ signs,
+                                                            const uint16_t* __restrict__ norm,
+                                                            const uint16_t* __restrict__ rnorm, int64_t n,
+                                                            const float* __restrict__ cent,
+                                                            const uint32_t* __restrict__ diag,
+                                                            const uint16_t* __restrict__ S,
+                                                            void* __restrict__ out)
+{
+    constexpr int D = 128, L = 1 << B, NT = 8, KS = 4, NV = 16;
+    __shared__ half8_t sfr[QJL ? KS * NT * 64 : 1];
+    __shared__ uint4 slut[QJL ? 256 : 1];
+    __shared__ float ctab[L];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int i = lane & 15, q = lane >> 4;
+    for (int e = tid; e < (QJL ? KS * NT * 64 : 0); e += 256) {
+        const int ks = e / (NT * 64), nt = (e / 64) % NT, ln = e & 63;
+        const int col = 16 * nt + (ln & 15), c = 4 * ks + (ln >> 4);
+        half8_t f;
+#pragma unroll
+        for (int ee = 0; ee < 8; ++ee) f[ee] = __builtin_bit_cast(_Float16, S[(c + 16 * ee) * D + col]);
+        sfr[e] = f;
+    }
+    if constexpr (QJL) {
+        // sign byte tid -> eight fp16 values, element t = +1 where bit t is set, else -1
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            w[j] = (((tid >> (2 * j)) & 1) ? 0x3C00u : 0xBC00u) |
+                   ((((tid >> (2 * j + 1)) & 1) ? 0x3C00u : 0xBC00u) << 16);
+        slut[tid] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    if (tid < L) ctab[tid] = cent[tid];
+    // diagonal flips of this lane's coordinates 16 nt + i (bit nt), and the
+    // sign masks of the DPP butterflies (lane bit b of i)
+    uint32_t dmask = 0;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int cc = 16 * nt + i;
+        dmask |= ((diag[cc >> 5] >> (cc & 31)) & 1u) << nt;
+    }
+    uint32_t sm[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) sm[b] = ((uint32_t)(i >> b) & 1u) << 31;
+    const float kap = kSqrtHalfPi / (float)D;
+    const float isd = 1.0f / sqrtf((float)D);
+    __syncthreads();
+
+    for (int64_t base = (int64_t)blockIdx.x * (kWavesPerBlock * NV); base < n;
+         base += (int64_t)gridDim.x * (kWavesPerBlock * NV)) {
+        const int64_t vb = base + (int64_t)wid * NV;
+        if (vb >= n) continue;  // whole waves; no block synchronisation below
+        // A fragments: sign bytes 4 ks + q (byte q of sign word ks) of vector vb + i
+        const int64_t va = vb + i < n ? vb + i : n - 1;
+        uint32_t swa[4] = {0u, 0u, 0u, 0u};
+        if constexpr (QJL) {
+            const uint4 sw = *reinterpret_cast<const uint4*>(signs + va * (D / 32));
+            swa[0] = sw.x;
+            swa[1] = sw.y;
+            swa[2] = sw.z;
+            swa[3] = sw.w;
+        }
+        float4_t acc[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < (QJL ? KS : 0); ++ks) {
+            const half8_t a = __builtin_bit_cast(half8_t, slut[(swa[ks] >> (8 * q)) & 0xFFu]);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, sfr[(ks * NT + nt) * 64 + lane], acc[nt], 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t v = vb + 4 * q + r;
+            const bool ok = v < n;
+            const int64_t vr = ok ? v : n - 1;
+            // group i's field: bytes B i .. B i + B - 1 of the vector's code stream
+            const unsigned char* cb = reinterpret_cast<const unsigned char*>(codes + vr * (B * D / 32)) + B * i;
+            uint32_t f;
+            if constexpr (B == 4) f = *reinterpret_cast<const uint32_t*>(cb);
+            else if constexpr (B == 2) f = *reinterpret_cast<const uint16_t*>(cb);
+            else if constexpr (B == 3) f = (uint32_t)cb[0] | ((uint32_t)cb[1] << 8) | ((uint32_t)cb[2] << 16);
+            else f = cb[0];
+            const float g = QJL ? h2f(rnorm[vr]) * kap : 0.f;
+            float a[NT];
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                a[nt] = ctab[(f >> (B * nt)) & (L - 1)];
+                if constexpr (QJL) a[nt] += g * acc[nt][r];
+            }
+#pragma unroll
+            for (int h = 1; h < NT; h <<= 1)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    if (!(nt & h)) {
+                        const float x0 = a[nt], x1 = a[nt + h];
+                        a[nt] = x0 + x1;
+                        a[nt + h] = x0 - x1;
+                    }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                a[nt] = lane_bfly<1>(a[nt], sm[0]);
+                a[nt] = lane_bfly<2>(a[nt], sm[1]);
+                a[nt] = lane_bfly<4>(a[nt], sm[2]);
+                a[nt] = lane_bfly<8>(a[nt], sm[3]);
+            }
+            const float sc = h2f(norm[vr]) * isd;
+            if (ok) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const float o = flip(a[nt], ((dmask >> nt) & 1u) << 31) * sc;
+                    const int64_t e = v * D + 16 * nt + i;
+                    if constexpr (F16OUT) static_cast<uint16_t*>(out)[e] = f2h(o);
+                    else static_cast<float*>(out)[e] = o;
+                }
+            }
+        }
+    }
+}
+
 int grid_for(int64_t units, int per_block, int cap = 65536)
 {
     int64_t b = (units + per_block - 1) / per_block;
@@ -789,6 +922,18 @@ template <int D, int B, bool QJL>
 void dequant_d_b(const tq_quantizer* q, const tq_packed* in, int64_t n, void* out, int dtype, hipStream_t s)
 {
     dim3 grid(grid_for(n, kWavesPerBlock)), block(256);
+    if constexpr (D == 128) {
+        if (dtype == TQ_F16) {
+            auto kern = k_dequantize128<B, QJL, true>;
+            hipLaunchKernelGGL(kern, dim3(resident_grid(kern, kWavesPerBlock * 16, n)), block, 0, s, in->codes,
+                               in->signs, in->norm, in->rnorm, n, q->centroids, q->diag_signs, q->S, out);
+        } else {
+            auto kern = k_dequantize128<B, QJL, false>;
+            hipLaunchKernelGGL(kern, dim3(resident_grid(kern, kWavesPerBlock * 16, n)), block, 0, s, in->codes,
+                               in->signs, in->norm, in->rnorm, n, q->centroids, q->diag_signs, q->S, out);
+        }
+        return;
+    }
     if (dtype == TQ_F16)
         hipLaunchKernelGGL((k_dequantize<D, B, QJL, true>), grid, block, 0, s, in->codes, in->signs,
                            in->norm, in->rnorm, n, q->centroids, q->diag_signs, q->S, out);

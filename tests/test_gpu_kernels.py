@@ -209,7 +209,8 @@ def test_scores_prefill_scale_sampled():
     del sc
 
 
-@pytest.mark.parametrize("d,bits,m", [(64, 2, 64), (128, 2, 128), (128, 4, 0), (256, 3, 256)])
+@pytest.mark.parametrize("d,bits,m", [(64, 2, 64), (128, 1, 128), (128, 2, 128), (128, 3, 128), (128, 4, 128),
+                                      (128, 4, 0), (256, 3, 256)])
 @pytest.mark.parametrize("include_qjl", [True, False])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.float16])
 def test_dequantize_parity(d, bits, m, include_qjl, out_dtype):
@@ -224,6 +225,21 @@ def test_dequantize_parity(d, bits, m, include_qjl, out_dtype):
     ref = oracle.dequantize(qo, to_oracle_packed(qo, p.to_host()), include_qjl=include_qjl)
     tol = TOL if out_dtype == torch.float32 else 2.0 ** -11 * np.abs(ref).max() + TOL
     check_close(out.float().cpu().numpy(), ref, tol=tol, what="dequantize")
+
+
+def test_dequantize_keys_many_rounds():
+    """d = 128 keys with the sketch term: enough vectors that every resident
+    block loops over several rounds (ragged last round); every output checked."""
+    tq = tqmod()
+    qg, qo = quantizers(128, 2, 128)
+    n = 70001
+    x = synth.normals(31, synth.ROLE_DATA_K, np.arange(n * 128)).reshape(n, 128).astype(np.float32)
+    p = gpu_quantize(qg, x)
+    out = torch.empty((n, 128), dtype=torch.float32, device=DEV)
+    tq.tq_dequantize(qg, p, n, True, out)
+    torch.cuda.synchronize()
+    ref = oracle.dequantize(qo, to_oracle_packed(qo, p.to_host()), include_qjl=True)
+    check_close(out.cpu().numpy(), ref, what="dequantize")
 
 
 def test_synth_gpu_twin_matches_host():
