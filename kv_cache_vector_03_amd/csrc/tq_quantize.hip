@@ -24,6 +24,9 @@
 //
 // d = 256: one wave per vector at a time (coordinate 64 r + lane), 16 vectors
 // per block pass, the residual projection on MFMA with S held in registers.
+//
+// Dequantize: d = 128 takes 16 vectors per wave pass with the sketch term
+// S^T s on MFMA; d = 64 and 256 take one wave per vector.
 #include "tq_device.h"
 #include "tq_internal.h"
 
