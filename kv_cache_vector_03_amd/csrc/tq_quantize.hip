@@ -19,8 +19,8 @@
 // complemented for y <= 0; thresholds are scaled by sqrt(d) ||x|| instead of
 // normalising every coordinate. For keys the residual is split into fp16
 // hi + lo parts (both exact operands) and projected on MFMA against the fp16
-// matrix S; row order of S is permuted so that each ballot of the MFMA output
-// is two ready bytes of the group-major sign stream.
+// matrix S (the A operand, rows permuted) so that each lane receives the sign
+// bits of one word (d = 128) or half-word (d = 64) of its own vector's stream.
 //
 // d = 256: one wave per vector at a time (coordinate 64 r + lane), 16 vectors
 // per block pass, the residual projection on MFMA with S held in registers.
@@ -58,10 +58,17 @@ struct QuadShape {
     {
         return g | (((t >> 1) & 1) << Y1) | (((t >> 2) & 1) << Y2) | ((t & 1) << (LOG - 3));
     }
-    // S row feeding column n of n-tile nu (sign stream bits 16 nu .. 16 nu + 15)
+    // S row feeding row n = 4 q + r4 of m-tile nu. The projection lands in lane
+    // (v, q), register r4, of vector v; the rows are chosen so that lane q's
+    // 4 x NT projections are exactly sign word q (d = 128) or the 16-bit half q
+    // of the sign stream (d = 64), at bit sign_pos(nu, r4).
     __host__ __device__ static constexpr int proj_row(int nu, int n)
     {
-        return 2 * nu + n / 8 + (D / 8) * (n % 8);
+        return D == 128 ? n + 16 * nu : 2 * (n >> 2) + (n & 1) + 8 * (2 * nu + ((n & 3) >> 1));
+    }
+    __host__ __device__ static constexpr int sign_pos(int nu, int r4)
+    {
+        return D == 128 ? 8 * r4 + nu : 8 * (r4 & 1) + 2 * nu + (r4 >> 1);
     }
 };
 
@@ -299,39 +306,25 @@ __global__ __launch_bounds__(256) void k_quantize_quad(const void* __restrict__ 
                     ahi[t][e2] = hi;
                     alo[t][e2] = (_Float16)(rs - (float)hi);
                 }
-            uint32_t SW[SWN];
+            // S as the A operand (rows = projections), the residual as the B operand
+            // (columns = vectors): lane (v, q) receives its own sign bits
+            uint32_t sw = 0;
 #pragma unroll
-            for (int w = 0; w < SWN; ++w) SW[w] = 0;
+            for (int nu = 0; nu < NT; ++nu) {
+                float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int nu = 0; nu < NT; nu += 2) {
-                uint64_t mk[2][4];
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    float4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int t = 0; t < KS; ++t) {
-                        const half8_t bf = bfrag[(t * NT + nu + hh) * 64 + lane];
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[t], bf, acc, 0, 0, 0);
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[t], bf, acc, 0, 0, 0);
-                    }
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) mk[hh][r4] = __ballot(acc[r4] >= 0.f);
+                for (int t = 0; t < KS; ++t) {
+                    const half8_t bf = bfrag[(t * NT + nu) * 64 + lane];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf, ahi[t], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(bf, alo[t], acc, 0, 0, 0);
                 }
-                // output row 4 g + r4 is vector 4 g + r4 of the pass; its 16 bits in each
-                // ballot are bits 16 g .. 16 g + 15
-                uint32_t sw = SW[nu >> 1];
-                static_for<0, 16>([&](auto k) {
-                    constexpr int g = decltype(k)::value / 4, r4 = decltype(k)::value % 4;
-                    const uint32_t lo = (uint32_t)(mk[0][r4] >> (16 * g)) & 0xFFFFu;
-                    const uint32_t hi = (uint32_t)(mk[1][r4] >> (16 * g)) & 0xFFFFu;
-                    sw = write_lane<4 * g + r4>(sw, lo | (hi << 16));
-                });
-                SW[nu >> 1] = sw;
-            }
-            if (live && q == 0) {
 #pragma unroll
-                for (int w = 0; w < SWN; ++w) signs[vec * SWN + w] = SW[w];
-                rnorm[vec] = f2h(sqrtf(g2) / s);
+                for (int r4 = 0; r4 < 4; ++r4) sw |= (acc[r4] >= 0.f ? 1u : 0u) << Sh::sign_pos(nu, r4);
+            }
+            if (live) {
+                if constexpr (D == 128) signs[vec * SWN + q] = sw;
+                else reinterpret_cast<uint16_t*>(signs + vec * SWN)[q] = (uint16_t)sw;
+                if (q == 0) rnorm[vec] = f2h(sqrtf(g2) / s);
             }
         }
         if (live && q == 0) norm[vec] = f2h(nrm);
