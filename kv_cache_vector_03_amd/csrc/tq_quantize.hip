@@ -148,18 +148,31 @@ __global__ __launch_bounds__(256) void k_quantize_quad(const void* __restrict__ 
     const unsigned char* xb = static_cast<const unsigned char*>(x);
     unsigned char* st = stage[wid];
 
-    for (int64_t base = (int64_t)blockIdx.x * (kWavesPerBlock * NV); base < n;
-         base += (int64_t)gridDim.x * (kWavesPerBlock * NV)) {
+    // coalesced loads of a pass's NV vectors per wave (16 bytes per lane per
+    // chunk); the next pass's chunks are in flight while a pass is processed
+    const int64_t pstep = (int64_t)gridDim.x * (kWavesPerBlock * NV);
+    uint4 pre[CH];
+    auto fetch = [&](int64_t b0) {
+        const int64_t vb0 = b0 + (int64_t)wid * NV;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int off = (c * 64 + lane) * 16;
+            const int vec = off / (D * ES);
+            pre[c] = vb0 + vec < n ? *reinterpret_cast<const uint4*>(xb + (vb0 * D) * ES + off)
+                                   : make_uint4(0, 0, 0, 0);
+        }
+    };
+    fetch((int64_t)blockIdx.x * (kWavesPerBlock * NV));
+    for (int64_t base = (int64_t)blockIdx.x * (kWavesPerBlock * NV); base < n; base += pstep) {
         const int64_t vb = base + (int64_t)wid * NV;
-        // coalesced load of NV vectors into this wave's staging rows
+        // this pass's chunks into the wave's staging rows
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int off = (c * 64 + lane) * 16;
             const int vec = off / (D * ES), in = off % (D * ES);
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (vb + vec < n) val = *reinterpret_cast<const uint4*>(xb + (vb * D) * ES + off);
-            *reinterpret_cast<uint4*>(st + vec * ROW + in) = val;
+            *reinterpret_cast<uint4*>(st + vec * ROW + in) = pre[c];
         }
+        fetch(base + pstep);
         __syncthreads();
 
         // this lane's quarter, with the diagonal flips and the first butterfly
