@@ -778,20 +778,46 @@ __global__ __launch_bounds__(256, 4) void k_dequantize128(const uint32_t* __rest
     const float isd = 1.0f / sqrtf((float)D);
     __syncthreads();
 
-    for (int64_t base = (int64_t)blockIdx.x * (kWavesPerBlock * NV); base < n;
-         base += (int64_t)gridDim.x * (kWavesPerBlock * NV)) {
+    // one pass's packed inputs for this lane: sign words of vector vb + i, and
+    // group i's code field and the norms of vectors vb + 4 q + r (rows past the
+    // end read the last vector and are not stored); the next pass's are loaded
+    // while a pass is processed
+    struct In {
+        uint32_t sw[4], f[4];
+        uint16_t nv[4], rn[4];
+    };
+    auto fetch = [&](int64_t vb, In& t) {
+        if constexpr (QJL) {
+            const int64_t va = vb + i < n ? vb + i : n - 1;
+            const uint4 w = *reinterpret_cast<const uint4*>(signs + va * (D / 32));
+            t.sw[0] = w.x;
+            t.sw[1] = w.y;
+            t.sw[2] = w.z;
+            t.sw[3] = w.w;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t v = vb + 4 * q + r;
+            const int64_t vr = v < n ? v : n - 1;
+            const unsigned char* cb = reinterpret_cast<const unsigned char*>(codes + vr * (B * D / 32)) + B * i;
+            if constexpr (B == 4) t.f[r] = *reinterpret_cast<const uint32_t*>(cb);
+            else if constexpr (B == 2) t.f[r] = *reinterpret_cast<const uint16_t*>(cb);
+            else if constexpr (B == 3) t.f[r] = (uint32_t)cb[0] | ((uint32_t)cb[1] << 8) | ((uint32_t)cb[2] << 16);
+            else t.f[r] = cb[0];
+            t.nv[r] = norm[vr];
+            t.rn[r] = QJL ? rnorm[vr] : (uint16_t)0;
+        }
+    };
+    const int64_t pstep = (int64_t)gridDim.x * (kWavesPerBlock * NV);
+    In cur;
+    if ((int64_t)blockIdx.x * (kWavesPerBlock * NV) + (int64_t)wid * NV < n)
+        fetch((int64_t)blockIdx.x * (kWavesPerBlock * NV) + (int64_t)wid * NV, cur);
+    for (int64_t base = (int64_t)blockIdx.x * (kWavesPerBlock * NV); base < n; base += pstep) {
         const int64_t vb = base + (int64_t)wid * NV;
         if (vb >= n) continue;  // whole waves; no block synchronisation below
-        // A fragments: sign bytes 4 ks + q (byte q of sign word ks) of vector vb + i
-        const int64_t va = vb + i < n ? vb + i : n - 1;
-        uint32_t swa[4] = {0u, 0u, 0u, 0u};
-        if constexpr (QJL) {
-            const uint4 sw = *reinterpret_cast<const uint4*>(signs + va * (D / 32));
-            swa[0] = sw.x;
-            swa[1] = sw.y;
-            swa[2] = sw.z;
-            swa[3] = sw.w;
-        }
+        In nxt = cur;
+        if (vb + pstep < n) fetch(vb + pstep, nxt);
+        const uint32_t swa[4] = {cur.sw[0], cur.sw[1], cur.sw[2], cur.sw[3]};
         float4_t acc[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -806,15 +832,8 @@ __global__ __launch_bounds__(256, 4) void k_dequantize128(const uint32_t* __rest
         for (int r = 0; r < 4; ++r) {
             const int64_t v = vb + 4 * q + r;
             const bool ok = v < n;
-            const int64_t vr = ok ? v : n - 1;
-            // group i's field: bytes B i .. B i + B - 1 of the vector's code stream
-            const unsigned char* cb = reinterpret_cast<const unsigned char*>(codes + vr * (B * D / 32)) + B * i;
-            uint32_t f;
-            if constexpr (B == 4) f = *reinterpret_cast<const uint32_t*>(cb);
-            else if constexpr (B == 2) f = *reinterpret_cast<const uint16_t*>(cb);
-            else if constexpr (B == 3) f = (uint32_t)cb[0] | ((uint32_t)cb[1] << 8) | ((uint32_t)cb[2] << 16);
-            else f = cb[0];
-            const float g = QJL ? h2f(rnorm[vr]) * kap : 0.f;
+            const uint32_t f = cur.f[r];  // group i's codes, code t at bit B t
+            const float g = QJL ? h2f(cur.rn[r]) * kap : 0.f;
             float a[NT];
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
@@ -837,7 +856,7 @@ __global__ __launch_bounds__(256, 4) void k_dequantize128(const uint32_t* __rest
                 a[nt] = lane_bfly<4>(a[nt], sm[2]);
                 a[nt] = lane_bfly<8>(a[nt], sm[3]);
             }
-            const float sc = h2f(norm[vr]) * isd;
+            const float sc = h2f(cur.nv[r]) * isd;
             if (ok) {
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
@@ -848,6 +867,7 @@ __global__ __launch_bounds__(256, 4) void k_dequantize128(const uint32_t* __rest
                 }
             }
         }
+        cur = nxt;
     }
 }
 
