@@ -130,6 +130,14 @@ __device__ __forceinline__ void codes_compare(float (&y)[8][4], const float (&Ms
 constexpr int kLutCells = 256;
 constexpr int kLutEntries = 2 * kLutCells + 2;
 constexpr uint32_t kMagicBits = 0x4B000000u;  // bit pattern of 2^23
+// Widths 5..8: a finer grid over y in [-1/2, 1/2] (cells of 2^-11; the
+// boundaries of these codebooks lie well inside, and the build checks that
+// none is within two cells of the edge).
+constexpr int kLutCellsW = 1024;                    // cells per half-span
+constexpr float kLutPerUnitW = 2.0f * kLutCellsW;    // cells per unit of y
+constexpr int kLutEntriesW = 2 * kLutCellsW + 2;
+template <int B>
+constexpr int lut_entries() { return B >= 3 && B <= 4 ? kLutEntries : (B > 4 ? kLutEntriesW : 1); }
 
 template <int B, bool QJL, typename Pre, typename Post>
 __device__ __forceinline__ void codes_lut(float (&y)[8][4], const uint2* __restrict__ lut,
@@ -176,16 +184,20 @@ __device__ __forceinline__ void codes_lut(float (&y)[8][4], const uint2* __restr
 }
 
 // Codes of the 32 coordinates a lane holds for widths 5..8: y = -Z / s, its
-// code the number of boundaries strictly below y, found by a branch-free
-// binary search over the boundaries in LDS (tb, padded to 2^B entries).
+// code the number of boundaries strictly below y, read from the fine lookup
+// grid (LUT: one LDS read and one comparison, as in codes_lut) or found by a
+// branch-free binary search over the boundaries in LDS (tb, padded to 2^B
+// entries) when the grid does not resolve the codebook.
 // Group r's eight codes form a 64-bit field (code t at bit B t) placed at
 // bit 8 B r of the lane's B code words. For keys, y is replaced by the
 // negated scaled residual and its square accumulates in g2, as in codes_lut.
-template <int B, bool QJL>
+template <int B, bool QJL, bool LUT>
 __device__ __forceinline__ void codes_search(float (&y)[8][4], const float* __restrict__ tb,
-                                             const float* __restrict__ ctab, float rs, float sc, uint32_t (&W)[B],
-                                             float& g2)
+                                             const uint2* __restrict__ lut, const float* __restrict__ ctab,
+                                             float s, float rs, float sc, uint32_t (&W)[B], float& g2)
 {
+    constexpr float magic = 8388608.0f + kLutCellsW;  // 2^23 + NC: rounds to an integer index
+    const float rs_cells = kLutPerUnitW * rs;
 #pragma unroll
     for (int w = 0; w < B; ++w) W[w] = 0;
 #pragma unroll
@@ -194,10 +206,18 @@ __device__ __forceinline__ void codes_search(float (&y)[8][4], const float* __re
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const float Z = y[t][r];  // -Y
-            const float yy = -Z * rs;
             int k = 0;
+            if constexpr (LUT) {
+                uint32_t bits = __float_as_uint(fmaf(Z, -rs_cells, magic));
+                bits = min(max(bits, kMagicBits), kMagicBits + (uint32_t)(kLutEntriesW - 1));
+                const uint2 ent = lut[bits - kMagicBits];
+                const float e = fmaf(__uint_as_float(ent.x), s, Z);  // < 0 iff Y > next boundary
+                k = (int)(ent.y - (uint32_t)((int32_t)__float_as_uint(e) >> 31));
+            } else {
+                const float yy = -Z * rs;
 #pragma unroll
-            for (int step = 1 << (B - 1); step >= 1; step >>= 1) k += tb[k + step - 1] < yy ? step : 0;
+                for (int step = 1 << (B - 1); step >= 1; step >>= 1) k += tb[k + step - 1] < yy ? step : 0;
+            }
             gg |= (uint64_t)k << (B * t);
             if constexpr (QJL) {
                 const float rn = fmaf(Z, sc, ctab[k]);  // negated residual
@@ -314,7 +334,10 @@ __device__ void build_tables(CodeConsts<B>& cc, const float* __restrict__ cent, 
                              float unit, float* ctab, uint2* lut, int* lut_bad, float* tb)
 {
     constexpr int L = 1 << B, K = CodeConsts<B>::K;
-    constexpr bool LUT = B >= 3 && B <= 4;
+    constexpr bool LUT = B >= 3;
+    constexpr bool WIDE = B > 4;
+    constexpr int NCB = WIDE ? kLutCellsW : kLutCells, NE = lut_entries<B>();
+    constexpr float PER = WIDE ? kLutPerUnitW : (float)kLutCells;  // cells per unit of y
 #pragma unroll
     for (int j = 1; j <= K; ++j) cc.Mth[j - 1] = bnd[L / 2 - 1 + j];
 #pragma unroll
@@ -325,20 +348,37 @@ __device__ void build_tables(CodeConsts<B>& cc, const float* __restrict__ cent, 
         for (int l = threadIdx.x; l < L; l += blockDim.x) tb[l] = l < L - 1 ? bnd[l] : INFINITY;
     __syncthreads();
     if constexpr (LUT) {
-        for (int c = threadIdx.x; c < kLutEntries; c += blockDim.x) {
-            const float lo = ((float)(c - kLutCells) - 0.5f) / kLutCells;  // exact
-            const float win = lo + 2.0f / kLutCells;
+        for (int c = threadIdx.x; c < NE; c += blockDim.x) {
+            const float lo = ((float)(c - NCB) - 0.5f) / PER;  // exact
+            const float win = lo + 2.0f / PER;
             uint32_t base = 0;
-            int inwin = 0;
             float next = INFINITY;
-            for (int j = 0; j < L - 1; ++j) {
-                const float b = bnd[j];
-                base += b < lo ? 1u : 0u;
-                if (b >= lo && b < next) next = b;
-                inwin += (b >= lo && b < win) ? 1 : 0;
+            if constexpr (WIDE) {
+                // boundaries sorted in tb (padded with +inf): base = #{b < lo} by
+                // binary search, next = tb[base]; a second boundary in the
+                // two-cell window makes the grid unusable
+                int k = 0;
+#pragma unroll
+                for (int step = 1 << (B - 1); step >= 1; step >>= 1) k += tb[k + step - 1] < lo ? step : 0;
+                base = (uint32_t)k;
+                next = tb[k];
+                if (k + 1 < L - 1 && tb[k + 1] < win) *lut_bad = 1;
+            } else {
+                int inwin = 0;
+                for (int j = 0; j < L - 1; ++j) {
+                    const float b = bnd[j];
+                    base += b < lo ? 1u : 0u;
+                    if (b >= lo && b < next) next = b;
+                    inwin += (b >= lo && b < win) ? 1 : 0;
+                }
+                if (inwin > 1) *lut_bad = 1;
             }
-            if (inwin > 1) *lut_bad = 1;
             lut[c] = make_uint2(__float_as_uint(next), base);
+        }
+        if constexpr (WIDE) {
+            // the clamped end cells are exact only if every boundary lies inside the span
+            const float edge = ((float)NCB - 2.5f) / PER;
+            if (threadIdx.x == 0 && !(fabsf(bnd[0]) < edge && fabsf(bnd[L - 2]) < edge)) *lut_bad = 1;
         }
     }
     __syncthreads();
@@ -380,7 +420,10 @@ __device__ __forceinline__ void code_batch(const float4_t (&acc)[2][4], float ss
     for (int j = 0; j < K; ++j) Ms[j] = cc.Mth[j] * s;
 
     float g2 = 0.f;
-    if constexpr (B > 4) codes_search<B, QJL>(y, cc.tb, cc.ctab, __builtin_amdgcn_rcpf(s), sc, W, g2);
+    if constexpr (B > 4) {
+        if (cc.use_lut) codes_search<B, QJL, true>(y, cc.tb, cc.lut, cc.ctab, s, __builtin_amdgcn_rcpf(s), sc, W, g2);
+        else codes_search<B, QJL, false>(y, cc.tb, cc.lut, cc.ctab, s, __builtin_amdgcn_rcpf(s), sc, W, g2);
+    }
     else if (cc.use_lut) codes_lut<B, QJL>(y, cc.lut, cc.ctab, s, (float)kLutCells / s, sc, W, g2, pre, none);
     else codes_compare<B, QJL>(y, Ms, cc.Cq, cc.ctab, sc, W, g2, pre, none);
     gam = 0.f;
@@ -458,7 +501,7 @@ __global__ __launch_bounds__(256) void k_quantize_values_m128(const uint16_t* __
                                                               uint32_t* __restrict__ codes,
                                                               uint16_t* __restrict__ norm)
 {
-    __shared__ uint2 lut[B >= 3 && B <= 4 ? kLutEntries : 1];
+    __shared__ uint2 lut[lut_entries<B>()];
     __shared__ float ctab[1 << B];
     __shared__ float tbl[B > 4 ? 1 << B : 1];
     __shared__ int lut_bad;
@@ -507,7 +550,7 @@ __global__ __launch_bounds__(256) void k_quantize_keys_m128(const uint16_t* __re
 {
     constexpr int NT = 8, KS = 4;  // projection m-tiles (m = 128) and k-steps
     __shared__ __align__(16) half8_t sfrag[KS * NT * 64];  // 32 KiB
-    __shared__ uint2 lut[B >= 3 && B <= 4 ? kLutEntries : 1];
+    __shared__ uint2 lut[lut_entries<B>()];
     __shared__ float ctab[1 << B];
     __shared__ float tbl[B > 4 ? 1 << B : 1];
     __shared__ int lut_bad;
