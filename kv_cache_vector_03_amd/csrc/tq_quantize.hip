@@ -479,6 +479,36 @@ __global__ __launch_bounds__(64 * kD256Waves, 4) void k_quantize_d256(const void
     for (int l = 0; l < L - 1; ++l) t[l] = bnd[l];
 #pragma unroll
     for (int l = 0; l < L; ++l) c[l] = cent[l];
+    // 3 and 4 bits: a lookup grid over y in [-1, 1] (cells of 1/256; entry:
+    // boundaries below the cell start, first boundary at or above it), used
+    // if no window of two cells holds two boundaries; else the compare chain
+    constexpr bool GRID = B >= 3;
+    constexpr int NC = 256, NE = GRID ? 2 * NC + 2 : 1;
+    __shared__ uint2 lut[NE];
+    __shared__ float ctab[L];
+    __shared__ int lut_bad;
+    if (threadIdx.x == 0) lut_bad = 0;
+    if (threadIdx.x < L) ctab[threadIdx.x] = cent[threadIdx.x];
+    __syncthreads();
+    if constexpr (GRID) {
+        for (int e = threadIdx.x; e < NE; e += blockDim.x) {
+            const float lo = ((float)(e - NC) - 0.5f) / NC;  // exact
+            const float win = lo + 2.0f / NC;
+            uint32_t base = 0;
+            int inwin = 0;
+            float next = INFINITY;
+#pragma unroll
+            for (int l = 0; l < L - 1; ++l) {
+                base += t[l] < lo ? 1u : 0u;
+                if (t[l] >= lo && t[l] < next) next = t[l];
+                inwin += (t[l] >= lo && t[l] < win) ? 1 : 0;
+            }
+            if (inwin > 1) lut_bad = 1;
+            lut[e] = make_uint2(__float_as_uint(next), base);
+        }
+    }
+    __syncthreads();
+    const bool use_grid = GRID && !lut_bad;
     uint32_t dm[R];
     load_diag<R>(diag, lane, dm);
     uint32_t sm[6];
@@ -532,15 +562,24 @@ __global__ __launch_bounds__(64 * kD256Waves, 4) void k_quantize_d256(const void
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const float yy = y[r] * sc;
-                // boundaries ascend, so the compares that pass are a prefix
-                // and the last one names the centroid c[k]
                 int k = 0;
                 float ck = c[0];
+                if (use_grid) {
+                    // cell index round(256 y) + 256 by the 2^23 rounding trick, clamped
+                    uint32_t bits = __float_as_uint(fmaf(yy, (float)NC, 8388608.0f + NC));
+                    bits = min(max(bits, 0x4B000000u), 0x4B000000u + (uint32_t)(NE - 1));
+                    const uint2 ent = lut[bits - 0x4B000000u];
+                    k = (int)ent.y + (yy > __uint_as_float(ent.x) ? 1 : 0);
+                    if constexpr (QJL) ck = ctab[k];
+                } else {
+                    // boundaries ascend, so the compares that pass are a prefix
+                    // and the last one names the centroid c[k]
 #pragma unroll
-                for (int l = 0; l < L - 1; ++l) {
-                    const bool above = t[l] < yy;
-                    k += above ? 1 : 0;
-                    if constexpr (QJL) ck = above ? c[l + 1] : ck;
+                    for (int l = 0; l < L - 1; ++l) {
+                        const bool above = t[l] < yy;
+                        k += above ? 1 : 0;
+                        if constexpr (QJL) ck = above ? c[l + 1] : ck;
+                    }
                 }
                 own |= (uint32_t)k << (B * (2 * r + hi32));
                 if constexpr (QJL) {
