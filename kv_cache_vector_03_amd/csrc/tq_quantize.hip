@@ -106,6 +106,39 @@ __global__ __launch_bounds__(256) void k_quantize_quad(const void* __restrict__ 
     for (int j = 1; j <= K; ++j) Mth[j - 1] = bnd[L / 2 - 1 + j];
 #pragma unroll
     for (int m = 0; m <= K; ++m) Cm[m] = cent[L / 2 + m];
+    // 3 and 4 bits without the sketch: a lookup grid over y in [-1, 1] (cells
+    // of 1/256; entry: boundaries below the cell start, first boundary at or
+    // above it), used if no window of two cells holds two boundaries (the cell
+    // index of the scaled coordinate may be off by one at a cell edge); else,
+    // and for keys (where the second code path costs occupancy), sign-bit
+    // arithmetic
+    constexpr bool GRID = B >= 3 && !QJL;
+    constexpr int NC = 256, NE = GRID ? 2 * NC + 2 : 1;
+    __shared__ uint2 glut[NE];
+    __shared__ float gcent[L];
+    __shared__ int glut_bad;
+    if (threadIdx.x == 0) glut_bad = 0;
+    if (threadIdx.x < L) gcent[threadIdx.x] = cent[threadIdx.x];
+    __syncthreads();
+    if constexpr (GRID) {
+        for (int e = threadIdx.x; e < NE; e += 256) {
+            const float lo = ((float)(e - NC) - 0.5f) / NC;  // exact
+            const float win = lo + 2.0f / NC;
+            uint32_t base = 0;
+            int inwin = 0;
+            float next = INFINITY;
+            for (int l = 0; l < L - 1; ++l) {
+                const float bl = bnd[l];
+                base += bl < lo ? 1u : 0u;
+                if (bl >= lo && bl < next) next = bl;
+                inwin += (bl >= lo && bl < win) ? 1 : 0;
+            }
+            if (inwin > 1) glut_bad = 1;
+            glut[e] = make_uint2(__float_as_uint(next), base);
+        }
+    }
+    __syncthreads();
+    const bool use_grid = GRID && !glut_bad;
 
     // sign flips of this lane's initial coordinates q*Q4 + k
     uint32_t fl[F16 ? Q4 / 2 : Q4];
@@ -253,6 +286,31 @@ __global__ __launch_bounds__(256) void k_quantize_quad(const void* __restrict__ 
 #pragma unroll
         for (int w = 0; w < LW; ++w) W[w] = 0;
         float g2 = 0.f;
+        if (use_grid) {
+            const float rs_cells = (float)NC * __builtin_amdgcn_rcpf(s);
+#pragma unroll
+            for (int gp = GL - 1; gp >= 0; --gp)
+#pragma unroll
+                for (int t = 7; t >= 0; --t) {
+                    const int r = Sh::reg(gp, t);
+                    const float Y = y[r];
+                    uint32_t bits = __float_as_uint(fmaf(Y, rs_cells, 8388608.0f + NC));
+                    bits = min(max(bits, 0x4B000000u), 0x4B000000u + (uint32_t)(NE - 1));
+                    const uint2 ent = glut[bits - 0x4B000000u];
+                    const float e = fmaf(-__uint_as_float(ent.x), s, Y);  // > 0 iff Y > next boundary
+                    const uint32_t k = ent.y + (e > 0.f ? 1u : 0u);
+#pragma unroll
+                    for (int p = B - 1; p >= 0; --p) {
+                        const int P = 8 * B * gp + B * t + p;
+                        W[P >> 5] = __builtin_amdgcn_alignbit(W[P >> 5], k << (31 - p), 31);
+                    }
+                    if constexpr (QJL) {
+                        const float rr = fmaf(-gcent[k], s, Y);
+                        g2 += rr * rr;
+                        y[r] = rr;
+                    }
+                }
+        } else
 #pragma unroll
         for (int gp = GL - 1; gp >= 0; --gp)
 #pragma unroll
