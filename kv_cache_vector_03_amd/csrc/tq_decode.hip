@@ -639,11 +639,11 @@ void launch_bv(int bv, const tq_packed* k, const tq_packed* v, int64_t ns, int64
                const tq_quantizer* qk, const tq_quantizer* qv, float zs, float* parts, int nc, int tc,
                hipStream_t s)
 {
-    // value widths 1..4 with keys of 1..4 bits, 4 and 8 with any key width
+    // value widths 1..4 with keys of 1..4 bits, 3, 4 and 8 with any key width
     switch (bv) {
         case 1: if constexpr (BK <= 4) launch_mfma<D, BK, QJL, 1>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
         case 2: if constexpr (BK <= 4) launch_mfma<D, BK, QJL, 2>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
-        case 3: if constexpr (BK <= 4) launch_mfma<D, BK, QJL, 3>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
+        case 3: launch_mfma<D, BK, QJL, 3>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
         case 4: launch_mfma<D, BK, QJL, 4>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
         default: launch_mfma<D, BK, QJL, 8>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
     }

@@ -40,9 +40,9 @@ struct DecodePlan {
     size_t off_qr, off_p, off_frag, off_parts, total;
 };
 // Key and value code widths the MFMA decode kernel takes (d = 128, G <= 8):
-// values of 1..4 bits with keys of 1..4 bits, values of 4 or 8 bits with any
-// key width. Other pairs run on the scalar kernels.
-inline bool mfma_decode_widths(int bk, int bv) { return bv == 4 || bv == 8 || (bk <= 4 && bv <= 4); }
+// values of 1..4 bits with keys of 1..4 bits, values of 3, 4 or 8 bits with
+// any key width. Other pairs run on the scalar kernels.
+inline bool mfma_decode_widths(int bk, int bv) { return bv == 3 || bv == 4 || bv == 8 || (bk <= 4 && bv <= 4); }
 // wide: a width pair the MFMA kernel does not take (mfma_decode_widths false)
 DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G, bool wide);
 

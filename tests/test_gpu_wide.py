@@ -97,8 +97,10 @@ def test_wide_dequantize_parity(d, bits, m, include_qjl, out_dtype):
 
 DCASES = [
     # d, key mse bits, key QJL, value bits, streams, tokens, G
-    # MFMA kernel (d = 128, G <= 8, values of 4 or 8 bits with any keys)
+    # MFMA kernel (d = 128, G <= 8, values of 3, 4 or 8 bits with any keys)
     (128, 7, True, 4, 2, 700, 8),     # 8-bit keys (7 + QJL), 4-bit values
+    (128, 7, True, 3, 3, 1300, 8),    # 8-bit keys (7 + QJL), 3-bit values
+    (128, 5, False, 3, 2, 333, 4),
     (128, 2, True, 8, 2, 300, 8),     # narrow keys, 8-bit values
     (128, 8, True, 8, 2, 2100, 8),    # 8-bit codes + QJL keys, 8-bit values, several steps per wave
     (128, 5, False, 4, 3, 257, 3),
