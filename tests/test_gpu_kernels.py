@@ -262,29 +262,41 @@ def test_synth_gpu_twin_matches_host():
     assert np.array_equal(u.cpu().numpy(), synth.unit_vectors_f32(5, synth.ROLE_DATA_K, 50, 64, first=1000))
 
 
-@pytest.mark.parametrize("m", [0, 128])
-def test_quantize_crowded_codebook(m):
-    """A symmetric 3-bit codebook with two boundaries 0.0075 apart near zero
-    (closer than the lookup grid of the d = 128 fp16 kernel resolves), and one
-    with well-spread levels: both must give the codebook's codes exactly. The
-    crowded one exercises the comparison path that the grid check falls back to."""
+@pytest.mark.parametrize("m", [0, 1])
+@pytest.mark.parametrize("d,bits,dtype", [(128, 3, np.float16), (64, 3, np.float16), (128, 3, np.float32),
+                                          (256, 3, np.float16), (128, 5, np.float16)])
+def test_quantize_crowded_codebook(d, bits, dtype, m):
+    """Codebooks with two boundaries closer than a kernel's lookup grid resolves
+    (3 bits: 0.0075 apart near zero against cells of 1/256; 5 bits: 0.0006 apart
+    against cells of 2^-11), and well-spread ones: both must give the codebook's
+    codes exactly. The crowded ones exercise the paths the grid check falls back
+    to (d = 128 fp16: the MFMA kernel; d = 64 and fp32: the quad kernel; d = 256)."""
     import dataclasses
     tq = tqmod()
-    d = 128
+    m = d if m else 0
     diag = synth.diag_signs(7, synth.ROLE_DIAG_K, d)
     S = synth.proj_matrix_f16(7, synth.ROLE_PROJ_K, d, d) if m else None
-    for cent in ([-0.3, -0.2, -0.01, -0.005, 0.005, 0.01, 0.2, 0.3],
-                 [-0.25, -0.15, -0.08, -0.02, 0.02, 0.08, 0.15, 0.25]):
+    base = oracle.codebook(d, bits)
+    if bits == 3:
+        books = ([-0.3, -0.2, -0.01, -0.005, 0.005, 0.01, 0.2, 0.3],
+                 [-0.25, -0.15, -0.08, -0.02, 0.02, 0.08, 0.15, 0.25])
+    else:
+        crowded = base.centroids.astype(np.float64).copy()
+        crowded[14:18] = [-0.0009, -0.0003, 0.0003, 0.0009]
+        books = (crowded, base.centroids.astype(np.float64))
+    L = 1 << bits
+    for cent in books:
         cent = np.asarray(cent, np.float32)
+        assert np.all(np.diff(cent) > 0)
         bnd = ((cent[1:].astype(np.float64) + cent[:-1]) / 2).astype(np.float32)
-        base = oracle.codebook(d, 3)
         cb = dataclasses.replace(base, c_exact=cent.astype(np.float64), centroids=cent, boundaries=bnd)
-        qo = oracle.Quantizer(d, 3, m, diag, S, cb=cb)
-        qg = tq.Quantizer(d, 3, m, diag, S, DEV)
+        qo = oracle.Quantizer(d, bits, m, diag, S, cb=cb)
+        qg = tq.Quantizer(d, bits, m, diag, S, DEV)
         qg.centroids.copy_(torch.from_numpy(cent))
-        qg.boundaries[:7].copy_(torch.from_numpy(bnd))
+        qg.boundaries[:L - 1].copy_(torch.from_numpy(bnd))
         n = 700
-        x = synth.to_f16(synth.normals(23, synth.ROLE_DATA_K, np.arange(n * d)).reshape(n, d) * 2.0)
+        x = synth.normals(23, synth.ROLE_DATA_K, np.arange(n * d)).reshape(n, d) * 2.0
+        x = synth.to_f16(x) if dtype == np.float16 else x.astype(np.float32)
         check_quantize(qo, x.astype(np.float64), gpu_quantize(qg, x).to_host())
 
 
