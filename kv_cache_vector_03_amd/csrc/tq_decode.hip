@@ -100,14 +100,31 @@ __global__ __launch_bounds__(256) void k_qprep_frag(const void* __restrict__ q, 
     uint32_t dm[R];
     load_diag<R>(diag, lane, dm);
     const float inv_sqrt_d = 0.08838834764831845f;  // 1 / sqrt(128)
-    for (int h = wid; h < 8; h += 4) {
-        float y[R];
+    // heads wid and wid + 4 of this wave, loaded together and rotated as two
+    // independent chains (one transform over both slots' pairs)
+    {
+        float y[2 * R];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-            y[r] = h < G && s * G + h < total ? flip(load_elem<F16>(q, (s * G + h) * D + 64 * r + lane), dm[r]) : 0.f;
-        fwht_wave<R>(y, lane);
+        for (int hh = 0; hh < 2; ++hh) {
+            const int h = wid + 4 * hh;
 #pragma unroll
-        for (int r = 0; r < R; ++r) qs[h][64 * r + lane] = y[r] * inv_sqrt_d;
+            for (int r = 0; r < R; ++r)
+                y[R * hh + r] =
+                    h < G && s * G + h < total ? flip(load_elem<F16>(q, (s * G + h) * D + 64 * r + lane), dm[r]) : 0.f;
+        }
+        float ya[R], yb[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            ya[r] = y[r];
+            yb[r] = y[R + r];
+        }
+        fwht_wave<R>(ya, lane);
+        fwht_wave<R>(yb, lane);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            qs[wid][64 * r + lane] = ya[r] * inv_sqrt_d;
+            qs[wid + 4][64 * r + lane] = yb[r] * inv_sqrt_d;
+        }
     }
     __syncthreads();
     if constexpr (QJL) {
