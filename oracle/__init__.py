@@ -49,18 +49,14 @@ def lib():
         dp, fp = C.POINTER(C.c_double), C.POINTER(C.c_float)
         u32p, u16p = C.POINTER(C.c_uint32), C.POINTER(C.c_uint16)
         qp = C.POINTER(_Quantizer)
-        L.tqref_codebook.argtypes = [C.c_int, C.c_int, dp, fp, fp, dp, dp]
-        L.tqref_codebook.restype = C.c_int
         L.tqref_codebook_law.argtypes = [C.c_int, C.c_int, C.c_int, dp, fp, fp, dp, dp]
         L.tqref_codebook_law.restype = C.c_int
         L.tqref_sphere_moments.argtypes = [C.c_int, C.c_double, C.c_double, dp]
         L.tqref_sphere_moments.restype = None
-        L.tqref_lloyd_discrete.argtypes = [dp, dp, C.c_int, C.c_int, dp, dp]
-        L.tqref_lloyd_discrete.restype = C.c_int
-        L.tqref_gauss_distortion.argtypes = [C.c_int, C.c_int, dp, dp]
-        L.tqref_gauss_distortion.restype = C.c_double
         L.tqref_quantize.argtypes = [qp, dp, C.c_int64, u32p, u32p, u16p, u16p, dp, dp]
         L.tqref_quantize.restype = None
+        L.tqref_sketch.argtypes = [qp, dp, u32p, C.c_int64, u32p, u16p, dp]
+        L.tqref_sketch.restype = None
         L.tqref_scores.argtypes = [qp, u32p, u32p, u16p, u16p, C.c_int64, dp, C.c_int64, dp]
         L.tqref_scores.restype = None
         L.tqref_dequantize.argtypes = [qp, u32p, u32p, u16p, u16p, C.c_int64, C.c_int, dp]
@@ -128,22 +124,6 @@ def sphere_moments(d: int, a: float, b: float) -> np.ndarray:
     m = np.zeros(3, np.float64)
     lib().tqref_sphere_moments(d, a, b, _p(m, C.c_double))
     return m
-
-
-def lloyd_discrete(x: np.ndarray, w: np.ndarray, levels: int):
-    x = np.ascontiguousarray(x, np.float64)
-    w = np.ascontiguousarray(w, np.float64)
-    c = np.zeros(levels, np.float64)
-    D = C.c_double()
-    it = lib().tqref_lloyd_discrete(_p(x, C.c_double), _p(w, C.c_double), len(x), levels,
-                                    _p(c, C.c_double), C.byref(D))
-    return c, D.value, it
-
-
-def gauss_distortion(d: int, c: np.ndarray, t: np.ndarray) -> float:
-    c = np.ascontiguousarray(c, np.float64)
-    t = np.ascontiguousarray(t, np.float64)
-    return lib().tqref_gauss_distortion(d, len(c), _p(c, C.c_double), _p(t, C.c_double))
 
 
 def half_to_double(h: int) -> float:
@@ -226,6 +206,24 @@ def quantize(Q: Quantizer, x: np.ndarray, want_y: bool = False, want_u: bool = F
     if want_u:
         out.append(u)
     return out[0] if len(out) == 1 else tuple(out)
+
+
+def sketch(Q: Quantizer, y: np.ndarray, codes: np.ndarray, want_u: bool = False):
+    """The QJL stage on given codes: (signs uint32 [n, m/32], rnorm fp16 bits [n]
+    and, with want_u, u = S r [n, m]) for rotated unit vectors y [n, d] whose
+    packed codes are ``codes`` -- what ``quantize`` writes when those are its
+    own codes. Keys only (m > 0)."""
+    assert Q.m > 0
+    y = np.ascontiguousarray(np.asarray(y, np.float64).reshape(-1, Q.d))
+    n = y.shape[0]
+    codes = np.ascontiguousarray(np.asarray(codes, np.uint32).reshape(n, Q.bits * Q.words))
+    signs = np.zeros((n, Q.sign_words), np.uint32)
+    rnorm = np.zeros(n, np.uint16)
+    u = np.zeros((n, Q.m), np.float64) if want_u else None
+    lib().tqref_sketch(C.byref(Q._s), _p(y, C.c_double), _p(codes, C.c_uint32), n,
+                       _p(signs, C.c_uint32), _p(rnorm, C.c_uint16),
+                       _p(u, C.c_double) if u is not None else None)
+    return (signs, rnorm, u) if want_u else (signs, rnorm)
 
 
 def _packed_args(Q: Quantizer, P: Packed):

@@ -7,6 +7,8 @@ bit width; the pages give neither the pair count nor the exact statistic, so
 both the signed mean and the multiplicative shrinkage are provided.
 [P2] section "Needle-in-Haystack（Synthetic）": argmax of the estimated scores
 must hit the planted key.
+[P2] section "Lloyd-Max Codebook": distortion per coordinate, measured here as
+the mean squared difference between rotated coordinates and their centroids.
 """
 from __future__ import annotations
 

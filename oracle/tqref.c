@@ -98,11 +98,8 @@ static int had(int i, int j) { return (__builtin_popcount((unsigned)(i & j)) & 1
 /* ------------------------------------------------------------ laws */
 
 typedef struct {
-    int kind;              /* 0 = N(0, sigma^2); 1 = exact coordinate law in dimension dim; 2 = discrete points */
-    double sigma;
-    const double* x;       /* discrete: sorted points */
-    const double* w;       /* discrete: weights */
-    int n;
+    int kind;              /* 0 = N(0, sigma^2); 1 = exact coordinate law in dimension dim */
+    double sigma;          /* 1 / sqrt(d): the scale of both laws */
     int dim;               /* kind 1 */
 } law_t;
 
@@ -204,23 +201,7 @@ static void law_moments(const law_t* L, double a, double b, double* m0, double* 
         *m0 = sphere_mass(d, lo, hi);
         *m1 = K / (d - 1) * (pow(1.0 - lo * lo, e) - pow(1.0 - hi * hi, e));
         *m2 = *m0 - (double)(d - 1) / d * sphere_mass(d + 2, lo, hi);
-    } else {
-        double s0 = 0, s1 = 0, s2 = 0;
-        for (int i = 0; i < L->n; ++i) {
-            double v = L->x[i];
-            if (v > a && v <= b) { s0 += L->w[i]; s1 += L->w[i] * v; s2 += L->w[i] * v * v; }
-        }
-        *m0 = s0; *m1 = s1; *m2 = s2;
     }
-}
-
-static double law_sigma(const law_t* L)
-{
-    if (L->kind == 0 || L->kind == 1) return L->sigma;
-    double s0 = 0, s1 = 0, s2 = 0;
-    for (int i = 0; i < L->n; ++i) { s0 += L->w[i]; s1 += L->w[i] * L->x[i]; s2 += L->w[i] * L->x[i] * L->x[i]; }
-    double mu = s1 / s0;
-    return sqrt(s2 / s0 - mu * mu);
 }
 
 /* Lloyd-Max fixed point: boundaries are midpoints of neighbouring centroids,
@@ -228,7 +209,7 @@ static double law_sigma(const law_t* L)
  * or -1 without convergence. */
 static int lloyd(const law_t* L, int nl, double* c, double tol, int maxit, int symmetric)
 {
-    double sg = law_sigma(L);
+    double sg = L->sigma;
     /* start spread over +-2.5 sigma (inside the support for the bounded law) */
     double r = 2.5 * sg;
     if (L->kind == 1 && r > 1.0 - 1.0 / nl) r = 1.0 - 1.0 / nl;
@@ -266,11 +247,6 @@ static double law_distortion(const law_t* L, int nl, const double* c, const doub
         law_moments(L, a, b, &m0, &m1, &m2);
         D += m2 - 2.0 * c[l] * m1 + c[l] * c[l] * m0;
     }
-    if (L->kind == 2) {
-        double s0 = 0;
-        for (int i = 0; i < L->n; ++i) s0 += L->w[i];
-        D /= s0;
-    }
     return D;
 }
 
@@ -289,7 +265,7 @@ int tqref_codebook_law(int d, int bits, int law, double* c_exact, float* c_store
     if (d < 1 || bits < 1 || bits > 8 || law < 0 || law > 1) return -2;
     if (law == 1 && d < 2) return -2;
     int nl = 1 << bits;
-    law_t L = {law, 1.0 / sqrt((double)d), NULL, NULL, 0, d};
+    law_t L = {law, 1.0 / sqrt((double)d), d};
     double c[TQREF_MAXL];
     /* 1e-15 sigma for the widths the cache uses (<= 4 bits); wider codebooks
      * have cells of tiny mass whose conditional means carry more rounding
@@ -315,38 +291,11 @@ int tqref_codebook_law(int d, int bits, int law, double* c_exact, float* c_store
     return it;
 }
 
-int tqref_codebook(int d, int bits, double* c_exact, float* c_stored, float* t_stored,
-                   double* dist_exact, double* dist_stored)
-{
-    return tqref_codebook_law(d, bits, 0, c_exact, c_stored, t_stored, dist_exact, dist_stored);
-}
-
 /* moments (m0, m1, m2) of the coordinate law in dimension d over (a, b] */
 void tqref_sphere_moments(int d, double a, double b, double* m)
 {
-    law_t L = {1, 1.0 / sqrt((double)d), NULL, NULL, 0, d};
+    law_t L = {1, 1.0 / sqrt((double)d), d};
     law_moments(&L, a, b, &m[0], &m[1], &m[2]);
-}
-
-/* The same Lloyd iteration on a discrete law (sorted points x, weights w);
- * used by the brute-force optimality test. Returns iterations or -1. */
-int tqref_lloyd_discrete(const double* x, const double* w, int n, int nl, double* c_out,
-                         double* dist)
-{
-    law_t L = {2, 0, x, w, n, 0};
-    double c[TQREF_MAXL], t[TQREF_MAXL];
-    int it = lloyd(&L, nl, c, 1e-15, 100000, 0);
-    for (int l = 0; l < nl; ++l) c_out[l] = c[l];
-    for (int l = 0; l + 1 < nl; ++l) t[l] = 0.5 * (c[l] + c[l + 1]);
-    *dist = law_distortion(&L, nl, c, t);
-    return it;
-}
-
-/* analytic distortion of an arbitrary codebook under N(0, 1/d) */
-double tqref_gauss_distortion(int d, int nl, const double* c, const double* t)
-{
-    law_t L = {0, 1.0 / sqrt((double)d), NULL, NULL, 0, 0};
-    return law_distortion(&L, nl, c, t);
 }
 
 /* ------------------------------------------------------------ quantizer */
@@ -408,6 +357,35 @@ static void rotate(const tqref_quantizer* Q, const double* HD, const double* x, 
 }
 
 /*
+ * The QJL stage of one vector ([P2] "TurboQuant 是什麼：30 秒懶人包", step two):
+ * residual r = y - c[idx] of the rotated unit vector y against its chosen
+ * centroids, gamma = ||r||, u = S r, sign bit j = [u_j >= 0]. Writes the sign
+ * words sv (m bits, grouped as the codes), returns gamma; u_out (nullable)
+ * receives u.
+ */
+static double qjl_stage(const tqref_quantizer* Q, const double* Sd, const double* y, const int* idx,
+                        double* r, uint32_t* sv, double* u_out)
+{
+    int d = Q->d, m = Q->m;
+    double g2 = 0;
+    for (int i = 0; i < d; ++i) {
+        r[i] = y[i] - (double)Q->cent[idx[i]];
+        g2 += r[i] * r[i];
+    }
+    memset(sv, 0, sizeof(uint32_t) * words_of(m));
+    for (int j = 0; j < m; ++j) {
+        double u = 0;
+        for (int i = 0; i < d; ++i) u += Sd[(int64_t)j * d + i] * r[i];
+        if (u_out) u_out[j] = u;
+        if (u >= 0) {
+            int64_t b = sign_bit(m, j);
+            sv[b >> 5] |= 1u << (b & 31);
+        }
+    }
+    return sqrt(g2);
+}
+
+/*
  * Quantize n vectors x[n][d] (values given exactly as doubles).
  * Writes packed codes, signs (if m > 0), fp16 norms and fp16 residual norms.
  * Optional y_out[n][d] receives the rotated unit vector, u_out[n][m] the
@@ -440,8 +418,6 @@ void tqref_quantize(const tqref_quantizer* Q, const double* x, int64_t n,
             }
             uint32_t* cv = codes + v * (int64_t)Q->bits * W;
             memset(cv, 0, sizeof(uint32_t) * Q->bits * W);
-            (void)W;
-            double g2 = 0;
             for (int i = 0; i < d; ++i) {
                 int k = 0;
                 for (int l = 0; l + 1 < nl; ++l) if ((double)Q->bnd[l] < y[i]) k++;
@@ -451,29 +427,47 @@ void tqref_quantize(const tqref_quantizer* Q, const double* x, int64_t n,
                         int64_t b = code_bit(d, Q->bits, i, p);
                         cv[b >> 5] |= 1u << (b & 31);
                     }
-                r[i] = y[i] - (double)Q->cent[k];
-                g2 += r[i] * r[i];
             }
             if (y_out) memcpy(y_out + v * d, y, sizeof(double) * d);
             norm16[v] = tqref_double_to_half(nrm);
-            if (m > 0) {
-                uint32_t* sv = signs + v * WS;
-                memset(sv, 0, sizeof(uint32_t) * WS);
-                for (int j = 0; j < m; ++j) {
-                    double u = 0;
-                    for (int i = 0; i < d; ++i) u += Sd[(int64_t)j * d + i] * r[i];
-                    if (u_out) u_out[v * m + j] = u;
-                    if (u >= 0) {
-                        int64_t b = sign_bit(m, j);
-                        sv[b >> 5] |= 1u << (b & 31);
-                    }
-                }
-                rnorm16[v] = tqref_double_to_half(sqrt(g2));
-            }
+            if (m > 0)
+                rnorm16[v] = tqref_double_to_half(qjl_stage(Q, Sd, y, idx, r, signs + v * WS,
+                                                            u_out ? u_out + v * m : NULL));
         }
         free(y); free(r); free(z); free(idx);
     }
     free(Sd); free(HD);
+}
+
+static int code_at(const uint32_t* cv, int d, int bits, int i);
+
+/*
+ * The QJL stage alone, for n rotated unit vectors y[n][d] whose codes are
+ * given (packed codes[n][bits*d/32]) rather than chosen here: signs, fp16
+ * gamma and (nullable) u[n][m] exactly as tqref_quantize computes them from
+ * its own codes. Tests use it to check a sketch built on codes that differ
+ * from the oracle's by one level inside the boundary window. m must be > 0.
+ */
+void tqref_sketch(const tqref_quantizer* Q, const double* y, const uint32_t* codes, int64_t n,
+                  uint32_t* signs, uint16_t* rnorm16, double* u_out)
+{
+    int d = Q->d, m = Q->m, W = words_of(d), WS = words_of(m);
+    if (m <= 0) return;
+    double* Sd = widen_S(Q);
+#pragma omp parallel
+    {
+        double* r = malloc(sizeof(double) * d);
+        int* idx = malloc(sizeof(int) * d);
+#pragma omp for schedule(static)
+        for (int64_t v = 0; v < n; ++v) {
+            const uint32_t* cv = codes + v * (int64_t)Q->bits * W;
+            for (int i = 0; i < d; ++i) idx[i] = code_at(cv, d, Q->bits, i);
+            rnorm16[v] = tqref_double_to_half(qjl_stage(Q, Sd, y + v * d, idx, r, signs + v * WS,
+                                                        u_out ? u_out + v * m : NULL));
+        }
+        free(r); free(idx);
+    }
+    free(Sd);
 }
 
 /* code index of coordinate i of packed vector cv */

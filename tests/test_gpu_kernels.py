@@ -10,6 +10,7 @@ import torch
 
 import oracle
 import synth
+from oracle import stats
 from synth import workloads as W
 
 from parity import TOL, check_close, check_quantize
@@ -343,7 +344,7 @@ def test_sweep_full_size(d, bits, qjl):
     del xh
     y = oracle.quantize(qo, xs, want_y=True)[1]
     idx = oracle.unpack_codes(qo, ref.codes)
-    dist_sample = float(np.mean((y - qo.cent.astype(np.float64)[idx]) ** 2))
+    dist_sample = stats.distortion_per_coord(y, qo.cent.astype(np.float64)[idx])
     assert abs(dist_gpu - dist_sample) <= 0.05 * dist_sample, (dist_gpu, dist_sample)
     if not qjl and (d, bits) in SWEEP_PAGE_DIST:
         assert abs(dist_gpu - SWEEP_PAGE_DIST[(d, bits)]) <= 0.03 * SWEEP_PAGE_DIST[(d, bits)], dist_gpu

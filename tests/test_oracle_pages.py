@@ -12,8 +12,9 @@ the statistics they describe.
   QJL it is zero within noise. The printed signed values are single random
   draws (pair count not given) and stay parity-unpinned; we check only that
   our signed means are noise-level.
-* Measured distortion per coordinate on random unit vectors equals the
-  quadrature value under the exact (Beta) coordinate law.
+* Measured distortion per coordinate on random unit vectors
+  (``stats.distortion_per_coord``) equals the quadrature value under the exact
+  (Beta) coordinate law.
 """
 import json
 import math
@@ -100,7 +101,7 @@ def test_measured_distortion_matches_exact_coordinate_law():
     P, y = oracle.quantize(Q, x, want_y=True)
     c = Q.cent.astype(np.float64)[oracle.unpack_codes(Q, P.codes)]
     per_vec = np.mean((y - c) ** 2, axis=1)
-    mc = per_vec.mean()
+    mc = stats.distortion_per_coord(y, c)
     se = per_vec.std(ddof=1) / np.sqrt(n)
     ref = beta_distortion(d, Q.cb)
     assert abs(mc - ref) < 4 * se

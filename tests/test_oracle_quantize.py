@@ -186,3 +186,46 @@ def test_zero_vector():
         L = 1 << bits
         assert np.all(oracle.unpack_codes(Q, P.codes) == L // 2 - 1)
         assert P.norm[0] == 0
+
+
+@pytest.mark.parametrize("d,bits", [(64, 2), (128, 1), (128, 2), (256, 3)])
+def test_sketch_on_own_codes_reproduces_quantize(d, bits):
+    """The QJL stage run on the oracle's own codes gives back exactly the
+    signs, residual norms and projections ``quantize`` wrote."""
+    Q = make_q(d, bits, d)
+    x = synth.normals(13, synth.ROLE_DATA_K, np.arange(300 * d)).reshape(300, d)
+    P, y, u = oracle.quantize(Q, x, want_y=True, want_u=True)
+    s2, r2, u2 = oracle.sketch(Q, y, P.codes, want_u=True)
+    assert np.array_equal(s2, P.signs) and np.array_equal(r2, P.rnorm)
+    assert np.array_equal(u2, u)
+
+
+def test_sketch_on_shifted_code_is_linear_in_the_change():
+    """Moving coordinate i of a vector one level up changes the residual by
+    -(c[k+1] - c[k]) e_i, so u = S r moves by -(c[k+1] - c[k]) S[:, i] and
+    gamma^2 by -2 r_i dc + dc^2 (checked with numpy's S and the oracle's y);
+    the packed code change is made by hand on the group-major layout."""
+    d, bits = 128, 2
+    Q = make_q(d, bits, d)
+    x = synth.normals(29, synth.ROLE_DATA_K, np.arange(40 * d)).reshape(40, d)
+    P, y, u = oracle.quantize(Q, x, want_y=True, want_u=True)
+    idx = oracle.unpack_codes(Q, P.codes)
+    S = Q.S_f64()
+    cent = Q.cent.astype(np.float64)
+    G = d // 8
+    for v, i in [(0, 0), (3, 17), (11, 64), (39, 127)]:
+        k = idx[v, i]
+        k2 = k + 1 if k + 1 < (1 << bits) else k - 1
+        codes = P.codes.copy()
+        base = 8 * bits * (i % G) + bits * (i // G)
+        for p in range(bits):
+            w, b = (base + p) // 32, (base + p) % 32
+            codes[v, w] = (codes[v, w] & ~np.uint32(1 << b)) | np.uint32(((k2 >> p) & 1) << b)
+        s2, r2, u2 = oracle.sketch(Q, y[v:v + 1], codes[v:v + 1], want_u=True)
+        dc = cent[k2] - cent[k]
+        np.testing.assert_allclose(u2[0], u[v] - dc * S[:, i], rtol=0, atol=1e-13)
+        r_i = y[v, i] - cent[k]
+        g2 = np.sum((y[v] - cent[idx[v]]) ** 2) - 2 * r_i * dc + dc * dc
+        assert abs(r2[0].view(np.float16).astype(np.float64) - np.sqrt(g2)) <= np.spacing(np.float16(np.sqrt(g2)))
+        expect = (u2[0] >= 0).astype(np.int64)
+        assert np.array_equal(oracle.unpack_signs(Q, s2)[0], expect)
