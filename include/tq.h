@@ -13,12 +13,16 @@
  *    (same section; "MSE-Only vs QJL：bias 差異確認");
  *  - reconstruction of vectors (the "dequantize back to BF16" path of the
  *    vLLM summary page, section "延遲：dequantization 是隱藏成本");
- *  - a fused decode-attention step over compressed K and V.
+ *  - a fused decode-attention step over compressed K and V: the logits are
+ *    computed on the compressed form instead of dequantizing the cache to
+ *    BF16 first, which the vLLM summary page names as the hidden cost
+ *    ("延遲：dequantization 是隱藏成本"), and the GB10 page attributes its slow
+ *    estimated inner products to the missing fused kernel ("GB10 速度").
  *
  * Conventions shared by every entry point:
  *  - Ownership: the caller owns every buffer. The library never allocates
  *    device memory and keeps no state between calls except the thread-local
- *    error message.
+ *    error message and the fixed scratch array of tq_decode_attn_noalloc.
  *  - Device pointers are plain HIP device addresses on the current device;
  *    "stream" is a hipStream_t (NULL = the default stream). GPU work is
  *    enqueued asynchronously on that stream; nothing synchronises.
@@ -153,7 +157,10 @@ int tq_dequantize(const tq_quantizer* q, const tq_packed* in, int64_t n, int inc
                   void* out, int out_dtype, void* stream);
 
 /*
- * tq_decode_attn -- one decode step of attention over compressed K/V.
+ * tq_decode_attn -- one decode step of attention over compressed K/V, the
+ * scores taken directly from the packed keys (the estimator of tq_scores)
+ * rather than from a dequantized copy ("延遲：dequantization 是隱藏成本" on the
+ * vLLM benchmark summary; "GB10 速度" on the GX10 page).
  * n_streams streams (one stream = one (layer, KV head) token sequence) of T
  * tokens each; stream s, token t is packed vector s*T + t of k and of v.
  * q: [n_streams][G][d] (TQ_F32 or TQ_F16), G query heads per KV head.
@@ -170,6 +177,27 @@ int tq_decode_attn(const tq_quantizer* qk, const tq_quantizer* qv,
                    int64_t n_streams, int64_t T, int G,
                    const void* q, int q_dtype, float scale, float* out,
                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * tq_decode_attn_noalloc -- tq_decode_attn without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops that forbid allocation). Same arguments, semantics, kernels
+ * and results as tq_decode_attn, minus ws and ws_bytes: the workspace is a
+ * fixed scratch array of TQ_NOALLOC_SCRATCH_BYTES in the library, one per
+ * device, held until the process ends (its address is looked up on the first
+ * call on each device). The call allocates nothing. A call whose workspace
+ * (tq_workspace_size(TQ_OP_DECODE_ATTN, ...)) would exceed the scratch returns
+ * TQ_ERR_WORKSPACE before any launch. Every call on one device shares that
+ * device's scratch: calls that overlap in time on one device (other streams,
+ * other threads) race and must be serialised by the caller; calls on one
+ * stream are ordered and safe. Asynchronous on stream.
+ */
+#define TQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+int tq_decode_attn_noalloc(const tq_quantizer* qk, const tq_quantizer* qv,
+                           const tq_packed* k, const tq_packed* v,
+                           int64_t n_streams, int64_t T, int G,
+                           const void* q, int q_dtype, float scale, float* out,
+                           void* stream);
 
 /*
  * tq_decode_step -- append one token to every stream's compressed cache, then

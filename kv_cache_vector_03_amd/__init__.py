@@ -45,7 +45,8 @@ class tq_packed(C.Structure):
 
 
 EXPORTS = ("tq_codebook", "tq_quantize", "tq_scores", "tq_dequantize", "tq_decode_attn",
-           "tq_decode_step", "tq_workspace_size", "tq_last_error")
+           "tq_decode_attn_noalloc", "tq_decode_step", "tq_workspace_size", "tq_last_error")
+TQ_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
 
@@ -70,6 +71,9 @@ def lib() -> C.CDLL:
         L.tq_decode_attn.argtypes = [qp, qp, pp, pp, C.c_int64, C.c_int64, C.c_int, vp, C.c_int,
                                      C.c_float, vp, vp, C.c_size_t, vp]
         L.tq_decode_attn.restype = C.c_int
+        L.tq_decode_attn_noalloc.argtypes = [qp, qp, pp, pp, C.c_int64, C.c_int64, C.c_int, vp, C.c_int,
+                                             C.c_float, vp, vp]
+        L.tq_decode_attn_noalloc.restype = C.c_int
         L.tq_decode_step.argtypes = [qp, qp, pp, pp, C.c_int64, C.c_int64, C.c_int64, C.c_int, vp, vp,
                                      C.c_int, vp, C.c_int, C.c_float, vp, vp, C.c_size_t, vp]
         L.tq_decode_step.restype = C.c_int
@@ -233,6 +237,15 @@ def tq_decode_attn(qk: Quantizer, qv: Quantizer, k: Packed, v: Packed, n_streams
     _check(lib().tq_decode_attn(C.byref(qk.struct), C.byref(qv.struct), C.byref(k.struct),
                                 C.byref(v.struct), n_streams, T, G, _ptr(q), _dtype_code(q),
                                 float(scale), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def tq_decode_attn_noalloc(qk: Quantizer, qv: Quantizer, k: Packed, v: Packed, n_streams: int, T: int,
+                           G: int, q: torch.Tensor, out: torch.Tensor, scale: float = 0.0, stream=None) -> None:
+    """tq_decode_attn with the library's fixed per-device scratch as its
+    workspace: the call allocates nothing (calls that overlap on one device race)."""
+    _check(lib().tq_decode_attn_noalloc(C.byref(qk.struct), C.byref(qv.struct), C.byref(k.struct),
+                                        C.byref(v.struct), n_streams, T, G, _ptr(q), _dtype_code(q),
+                                        float(scale), _ptr(out), _stream(stream)))
 
 
 def tq_decode_step(qk: Quantizer, qv: Quantizer, k: Packed, v: Packed, n_streams: int, T: int, cap: int,

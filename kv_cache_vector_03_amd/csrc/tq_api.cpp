@@ -10,6 +10,30 @@ namespace {
 
 size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// Argument checks shared by the decode-attention entry points; on success
+// fills the work split (plan) for a non-empty call.
+int check_decode_args(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k, const tq_packed* v,
+                      int64_t n_streams, int64_t T, int G, const void* q, int q_dtype, float scale,
+                      const float* out, const char* who, DecodePlan* plan)
+{
+    int rc;
+    if ((rc = check_quantizer(qk, who, "key")) != TQ_OK) return rc;
+    if ((rc = check_quantizer(qv, who, "value")) != TQ_OK) return rc;
+    if (qv->d != qk->d) return fail(TQ_ERR_UNSUPPORTED, "%s: key d=%d != value d=%d", who, qk->d, qv->d);
+    if (qv->qjl_m != 0) return fail(TQ_ERR_UNSUPPORTED, "%s: value quantizer must be codes-only (qjl_m=0)", who);
+    if (n_streams < 0) return fail(TQ_ERR_INVALID, "%s: n_streams < 0", who);
+    if (G < 1 || G > 16) return fail(TQ_ERR_UNSUPPORTED, "%s: G=%d not in 1..16", who, G);
+    if (n_streams == 0) return TQ_OK;
+    if (T < 1) return fail(TQ_ERR_INVALID, "%s: T=%lld < 1", who, (long long)T);
+    if (!std::isfinite(scale) || scale < 0) return fail(TQ_ERR_INVALID, "%s: bad scale", who);
+    if ((rc = check_packed(qk, k, who, "k")) != TQ_OK) return rc;
+    if ((rc = check_packed(qv, v, who, "v")) != TQ_OK) return rc;
+    if ((rc = check_dense(q, q_dtype, who, "q")) != TQ_OK) return rc;
+    if ((rc = check_dense(out, TQ_F32, who, "out")) != TQ_OK) return rc;
+    *plan = decode_plan(qk, n_streams, T, G, !mfma_decode_widths(qk->mse_bits, qv->mse_bits));
+    return TQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -77,25 +101,32 @@ int tq_decode_attn(const tq_quantizer* qk, const tq_quantizer* qv,
                    void* ws, size_t ws_bytes, void* stream)
 {
     clear_error();
-    int rc;
-    if ((rc = check_quantizer(qk, "tq_decode_attn", "key")) != TQ_OK) return rc;
-    if ((rc = check_quantizer(qv, "tq_decode_attn", "value")) != TQ_OK) return rc;
-    if (qv->d != qk->d) return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attn: key d=%d != value d=%d", qk->d, qv->d);
-    if (qv->qjl_m != 0)
-        return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attn: value quantizer must be codes-only (qjl_m=0)");
-    if (n_streams < 0) return fail(TQ_ERR_INVALID, "tq_decode_attn: n_streams < 0");
-    if (G < 1 || G > 16) return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attn: G=%d not in 1..16", G);
-    if (n_streams == 0) return TQ_OK;
-    if (T < 1) return fail(TQ_ERR_INVALID, "tq_decode_attn: T=%lld < 1", (long long)T);
-    if (!std::isfinite(scale) || scale < 0) return fail(TQ_ERR_INVALID, "tq_decode_attn: bad scale");
-    if ((rc = check_packed(qk, k, "tq_decode_attn", "k")) != TQ_OK) return rc;
-    if ((rc = check_packed(qv, v, "tq_decode_attn", "v")) != TQ_OK) return rc;
-    if ((rc = check_dense(q, q_dtype, "tq_decode_attn", "q")) != TQ_OK) return rc;
-    if ((rc = check_dense(out, TQ_F32, "tq_decode_attn", "out")) != TQ_OK) return rc;
-    const DecodePlan plan = decode_plan(qk, n_streams, T, G, !mfma_decode_widths(qk->mse_bits, qv->mse_bits));
+    DecodePlan plan;
+    int rc = check_decode_args(qk, qv, k, v, n_streams, T, G, q, q_dtype, scale, out, "tq_decode_attn", &plan);
+    if (rc != TQ_OK || n_streams == 0) return rc;
     if (!ws || ws_bytes < plan.total)
         return fail(TQ_ERR_WORKSPACE, "tq_decode_attn: workspace %zu bytes < %zu", ws_bytes, plan.total);
     if ((uintptr_t)ws % 256) return fail(TQ_ERR_INVALID, "tq_decode_attn: workspace must be 256-byte aligned");
+    if (scale == 0.0f) scale = 1.0f / std::sqrt((float)qk->d);
+    return launch_decode(qk, qv, k, v, n_streams, T, T, G, q, q_dtype, plan, ws, scale, out, nullptr,
+                         (hipStream_t)stream);
+}
+
+int tq_decode_attn_noalloc(const tq_quantizer* qk, const tq_quantizer* qv,
+                           const tq_packed* k, const tq_packed* v,
+                           int64_t n_streams, int64_t T, int G,
+                           const void* q, int q_dtype, float scale, float* out, void* stream)
+{
+    clear_error();
+    DecodePlan plan;
+    int rc = check_decode_args(qk, qv, k, v, n_streams, T, G, q, q_dtype, scale, out, "tq_decode_attn_noalloc",
+                               &plan);
+    if (rc != TQ_OK || n_streams == 0) return rc;
+    if (plan.total > kNoallocScratchBytes)
+        return fail(TQ_ERR_WORKSPACE, "tq_decode_attn_noalloc: the call needs %zu bytes of scratch, more than the "
+                    "library's fixed %zu", plan.total, kNoallocScratchBytes);
+    void* ws = nullptr;
+    if ((rc = noalloc_scratch(&ws)) != TQ_OK) return rc;
     if (scale == 0.0f) scale = 1.0f / std::sqrt((float)qk->d);
     return launch_decode(qk, qv, k, v, n_streams, T, T, G, q, q_dtype, plan, ws, scale, out, nullptr,
                          (hipStream_t)stream);

@@ -13,6 +13,8 @@
 // stream and applies the inverse value rotation D_v H / sqrt(d) once per head.
 #include <float.h>
 
+#include <mutex>
+
 #include "tq_append.h"
 #include "tq_device.h"
 #include "tq_internal.h"
@@ -106,6 +108,35 @@ __global__ __launch_bounds__(256) void k_append(tq_quantizer qk, tq_quantizer qv
     const bool val = blockIdx.y == 1;
     quantize_one<D>(val ? qv : qk, val ? v : k, val ? v_new : k_new, dtype, s, s * stride + pos, sm);
 }
+
+}  // namespace
+
+// The fixed scratch of tq_decode_attn_noalloc, one copy per device (zero at
+// load, kept until the process ends). Host code never uses the array's name
+// as an address: noalloc_scratch looks up the device address once per device
+// with hipGetSymbolAddress and every launch takes that address.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+int noalloc_scratch(void** ptr)
+{
+    static std::mutex mu;
+    static void* addr[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return fail(TQ_ERR_DEVICE, "tq_decode_attn_noalloc: no current device");
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(TQ_ERR_DEVICE, "tq_decode_attn_noalloc: scratch address: %s", hipGetErrorString(e));
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return TQ_OK;
+}
+
+namespace {
 
 int device_status(const char* who)
 {

@@ -370,9 +370,10 @@ DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int
     p.n_chunks = (int)((T + p.tc - 1) / p.tc);
     const size_t nq = (size_t)n_streams * G;
     const int ksteps = (qk->d / 32) * (qk->qjl_m ? 2 : 1);
+    // prepared queries (scalar kernels) or query fragments (MFMA kernel)
     p.off_qr = 0;
-    p.off_p = up256(nq * qk->d * 4);
-    p.off_frag = p.off_p + up256(nq * (qk->qjl_m ? qk->qjl_m : 1) * 4);
+    p.off_p = p.mfma ? 0 : up256(nq * qk->d * 4);
+    p.off_frag = p.off_p + (p.mfma ? 0 : up256(nq * (qk->qjl_m ? qk->qjl_m : 1) * 4));
     p.off_parts = p.off_frag + (p.mfma ? up256((size_t)n_streams * ksteps * 64 * 16) : 0);
     p.total = p.off_parts + up256((size_t)n_streams * p.n_chunks * G * part_stride(qk->d) * 4);
     return p;

@@ -46,6 +46,13 @@ inline bool mfma_decode_widths(int bk, int bv) { return bv == 3 || bv == 4 || bv
 // wide: a width pair the MFMA kernel does not take (mfma_decode_widths false)
 DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G, bool wide);
 
+// Fixed scratch of tq_decode_attn_noalloc: a static device array of this many
+// bytes per device, in place of a caller workspace.
+constexpr size_t kNoallocScratchBytes = TQ_NOALLOC_SCRATCH_BYTES;
+// Device address of the current device's scratch array (looked up once per
+// device); TQ_ERR_DEVICE if the lookup fails.
+int noalloc_scratch(void** ptr);
+
 // compute units of the current device (cached per device)
 int device_cus();
 

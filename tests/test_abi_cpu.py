@@ -153,6 +153,31 @@ def test_scores_and_decode_argument_errors():
     assert L.tq_workspace_size(tq.TQ_OP_DECODE_ATTN, C.byref(qstruct(d=100)), 1, 1, 8) == 0
 
 
+def test_decode_noalloc_argument_errors():
+    """The no-allocation decode entry point: the same checks as tq_decode_attn,
+    and calls whose workspace would exceed the fixed scratch are refused on the
+    host (nothing is launched for any of these)."""
+    L = tq.lib()
+    q = qstruct()
+    qv = qstruct(bits=3, m=0, S=False)
+    p, pv = pstruct(), pstruct(signs=False)
+
+    def dec(qk=q, qvv=qv, ns=72, T=8192, G=8, scale=0.0):
+        return L.tq_decode_attn_noalloc(C.byref(qk), C.byref(qvv), C.byref(p), C.byref(pv), ns, T, G,
+                                        A + 0x8000, tq.TQ_F16, C.c_float(scale), A + 0x9000, None)
+
+    assert dec(G=17) == tq.TQ_ERR_UNSUPPORTED
+    assert dec(T=0) == tq.TQ_ERR_INVALID
+    assert dec(scale=-1.0) == tq.TQ_ERR_INVALID
+    assert dec(qvv=qstruct(bits=3, m=128)) == tq.TQ_ERR_UNSUPPORTED
+    assert dec(ns=0) == tq.TQ_OK
+    # 4096 streams of 2^20 tokens on the scalar kernels: far more than the scratch
+    big = L.tq_workspace_size(tq.TQ_OP_DECODE_ATTN, C.byref(q), 4096, 1 << 20, 8)
+    assert big > tq.TQ_NOALLOC_SCRATCH_BYTES
+    assert dec(qvv=qstruct(bits=6, m=0, S=False), ns=4096, T=1 << 20) == tq.TQ_ERR_WORKSPACE
+    assert "scratch" in tq.tq_last_error()
+
+
 def test_dequantize_argument_errors():
     L = tq.lib()
     q = qstruct()
