@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ parts
 #pragma unroll
         for (int q = 0; q < CL; ++q) v[r] += fq[q] * omf[q * D + 64 * r + lane];
     }
-    fwht_wave<R>(v, lane);
+    fwht_wave_dpp<R>(v, lane);
     uint32_t dm[R];
     load_diag<R>(vdiag, lane, dm);
     const float sc = 1.0f / (sqrtf((float)D) * L);

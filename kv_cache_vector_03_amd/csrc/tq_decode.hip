@@ -118,8 +118,8 @@ __global__ __launch_bounds__(256) void k_qprep_frag(const void* __restrict__ q, 
             ya[r] = y[r];
             yb[r] = y[R + r];
         }
-        fwht_wave<R>(ya, lane);
-        fwht_wave<R>(yb, lane);
+        fwht_wave_dpp<R>(ya, lane);
+        fwht_wave_dpp<R>(yb, lane);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             qs[wid][64 * r + lane] = ya[r] * inv_sqrt_d;
@@ -200,6 +200,34 @@ __device__ void fill_key_luts(uint2* klut4, uint32_t* klut2, uint4* slut, const 
         }
 }
 
+// fill_key_luts from fp16 centroids already in LDS (kc16[code]).
+template <int BK, bool QJL>
+__device__ void fill_key_luts_lds(uint2* klut4, uint32_t* klut2, uint4* slut, const uint16_t* kc16)
+{
+    constexpr bool K4 = BK <= 2;
+    constexpr int KLUT = key_lut_entries(BK);
+    for (int i = threadIdx.x; i < KLUT; i += blockDim.x) {
+        if constexpr (K4) {
+            uint32_t h[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) h[j] = kc16[(i >> (BK * j)) & ((1 << BK) - 1)];
+            klut4[i] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+        } else if constexpr (BK <= 4) {
+            klut2[i] = (uint32_t)kc16[i & ((1 << BK) - 1)] | ((uint32_t)kc16[i >> BK] << 16);
+        } else {
+            klut2[i] = (uint32_t)kc16[i] * 0x10001u;
+        }
+    }
+    if constexpr (QJL)
+        for (int i = threadIdx.x; i < 256; i += blockDim.x) {
+            uint32_t w[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                w[j] = (((i >> (2 * j)) & 1) ? 0x3C00u : 0xBC00u) | ((((i >> (2 * j + 1)) & 1) ? 0x3C00u : 0xBC00u) << 16);
+            slut[i] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+}
+
 // A operand of code group t of a key (8 codes, 8 BK bits at bit 8 BK t of
 // the lane's BK code words) as fp16 centroids.
 template <int BK>
@@ -241,6 +269,14 @@ __device__ __forceinline__ half8_t key_codes_a(const uint32_t (&kf)[BK], int t, 
         for (int j = 0; j < 4; ++j) wds[j] = klut2[(field >> (2 * BK * j)) & ((1u << (2 * BK)) - 1u)];
         return __builtin_bit_cast(half8_t, wds);
     }
+}
+
+// max of three floats without NaN canonicalization (scores are never NaN)
+__device__ __forceinline__ float max3f(float a, float b, float c)
+{
+    float d;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
 }
 
 // One 32-token step's packed inputs for one lane (prefetched a step ahead).
@@ -376,56 +412,88 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
     __shared__ uint32_t klut2[K4 ? 1 : KLUT];
     __shared__ uint4 slut[QJL ? 256 : 1];
     __shared__ uint32_t vlut[VLUT][32];  // one copy per bank: lane l reads copy l % 32
-    __shared__ float mrg_m[4][8], mrg_l[4][8];
-    __shared__ float mrg_o[4][8][D];
+    __shared__ float mrg_m[4][8], mrg_l[4][8], mrg_f[4][8], mrg_x[8];
+    __shared__ __align__(16) float mrg_o[4][8][D];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int col = lane & 15, g = lane >> 4;
     const LaneOff loff = lane_offsets<D, BK, BV>(lane);
 
-    // ---- lookup tables: codes -> fp16 centroids, sign bytes -> +-1 (built once per block)
-    fill_key_luts<BK, QJL>(klut4, klut2, slut, kcent);
-    for (int i = tid; i < VLUT * 32; i += 256) {
-        const int e = i >> 5;
-        if constexpr (BV <= 4)
-            vlut[e][i & 31] = (uint32_t)f2h(vcent[e & ((1 << BV) - 1)]) | ((uint32_t)f2h(vcent[e >> BV]) << 16);
-        else
-            vlut[e][i & 31] = (uint32_t)f2h(vcent[e]) * 0x10001u;  // one code, its centroid in both halves
-    }
-    __syncthreads();
+    // the two codebooks (one global load per thread) are the first loads in
+    // flight, so they can be waited for while the first item's loads are not
+    __shared__ uint16_t cb16[2][256];
+    const float kc_v = kcent[min(tid, (1 << BK) - 1)];  // clamped: no branch around the loads
+    const float vc_v = vcent[min(tid, (1 << BV) - 1)];
 
-    for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int64_t s = item / n_chunks;
-        const int chunk = (int)(item % n_chunks);
-        const int64_t base = s * stride;
+    int64_t item = blockIdx.x;
+    if (item >= n_items) return;  // the whole block (the grid never exceeds the items)
+
+    // the current item's geometry and first loads: the first 512 value norms of
+    // each wave's range (indices clamped into it), then the first two full steps
+    // and the query fragments. Loads complete in order, so the norms, needed
+    // first, are issued first.
+    int64_t s, base, w0, w1, nfull;
+    int chunk;
+    uint16_t hv[8];
+    Step<BK, BV> sa, sb;
+    half8_t bq[KSTEPS];
+    auto begin_item = [&]() {
+        // items number fewer than 2^31 (streams times chunks): 32-bit division
+        const uint32_t it = (uint32_t)item, nc = (uint32_t)n_chunks;
+        s = it / nc;
+        chunk = (int)(it - (uint32_t)s * nc);
+        base = s * stride;
         const int64_t c0 = (int64_t)chunk * tc;
         const int64_t c1 = c0 + tc < T ? c0 + tc : T;
-        const int64_t w0 = c0 + (int64_t)wid * (tc / 4);
-        const int64_t w1 = w0 + tc / 4 < c1 ? w0 + tc / 4 : c1;
-
-        // the first full step's loads go out first, so that they are in flight
-        // while the query fragments and the norms of the range arrive
-        const int64_t nfull = w1 > w0 ? (w1 - w0) >> 5 : 0;  // a wave past the chunk's end has none
-        Step<BK, BV> sa, sb;
-        if (nfull > 0) load_full<D, BK, QJL, BV>(sa, base + w0, loff, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
-
-        half8_t bq[KSTEPS];
+        w0 = c0 + (int64_t)wid * (tc / 4);
+        w1 = w0 + tc / 4 < c1 ? w0 + tc / 4 : c1;
+        nfull = w1 > w0 ? (w1 - w0) >> 5 : 0;  // a wave past the chunk's end has none
+        // no branches around these loads, so that waiting for the codebooks does not
+        // wait for them: indices are clamped to the range's last token, or to the
+        // chunk's last one for a wave past its end
+        const int64_t lim = w1 > w0 ? w1 : c1;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) hv[k] = vnorm[base + min(w0 + lane + 64 * k, lim - 1)];
+        load_step<D, BK, QJL, BV>(sa, w0, lim, base, lane, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
+        load_step<D, BK, QJL, BV>(sb, w0 + 32, lim, base, lane, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
 #pragma unroll
         for (int k = 0; k < KSTEPS; ++k) bq[k] = frags[(s * KSTEPS + k) * 64 + lane];
+    };
+    begin_item();
+
+    // ---- lookup tables, built while the first item's loads are in flight:
+    // codes -> fp16 centroids, sign bytes -> +-1 (LDS-only barriers)
+    if (tid < (1 << BK)) cb16[0][tid] = f2h(kc_v);
+    if (tid < (1 << BV)) cb16[1][tid] = f2h(vc_v);
+    lds_barrier();
+    fill_key_luts_lds<BK, QJL>(klut4, klut2, slut, cb16[0]);
+    // value table: entry e (a code pair, or one code above 4 bits) in all 32
+    // copies; a wave writes 8 entries' 128-byte rows per instruction
+    for (int i = tid; i < VLUT * 8; i += 256) {
+        const int e = i >> 3;
+        uint32_t v;
+        if constexpr (BV <= 4) v = (uint32_t)cb16[1][e & ((1 << BV) - 1)] | ((uint32_t)cb16[1][e >> BV] << 16);
+        else v = (uint32_t)cb16[1][e] * 0x10001u;  // one code, its centroid in both halves
+        reinterpret_cast<uint4*>(&vlut[e][0])[i & 7] = make_uint4(v, v, v, v);
+    }
+    lds_barrier();
+
+    for (;;) {
 
         // fixed weight scale for this wave: max weight * norm stays below 2^15 in fp16.
-        // The norms of the wave's range are read 512 at a time with all loads in
-        // flight together (indices clamped into the range, as for the steps).
+        // The norms of the wave's range, 512 at a time (the first 512 loaded above).
         float nmax = 0.f;
-        for (int64_t t0 = w0; t0 < w1; t0 += 512) {
-            uint16_t hv[8];
+        if (w1 > w0)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) nmax = fmaxf(nmax, h2f(hv[k]));
+        for (int64_t t0 = w0 + 512; t0 < w1; t0 += 512) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) hv[k] = vnorm[base + min(t0 + lane + 64 * k, w1 - 1)];
 #pragma unroll
             for (int k = 0; k < 8; ++k) nmax = fmaxf(nmax, h2f(hv[k]));
         }
-        nmax = wave_max(nmax);
+        nmax = wave_max_dpp(nmax);
         int ex = 0;
         (void)frexpf(nmax, &ex);
         const float wscale = nmax > 0.f ? ldexpf(1.0f, 7 - ex) : 1.0f;
@@ -435,49 +503,51 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
 #pragma unroll
         for (int c = 0; c < CT; ++c) acc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-        // one 32-token step from tb; MASK: the step runs past the wave's range
-        auto compute = [&](const Step<BK, BV>& st, int64_t tb, auto MASK) {
-            // per-token factors of this lane's quad: row 16 u + 4 g + r sits in quad lane r
-            float fk[2], fq[2], fv[2];
+        // Score MFMAs of one 32-token step (two 16-token tiles): code part am and
+        // sign part aq per tile, raw (hi and lo columns not yet added).
+        struct Raw {
+            float4_t am[2], aq[2];
+        };
+        auto issue_scores = [&](const Step<BK, BV>& st, Raw& rw) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                fk[u] = h2f(st.nk[u]) * zscale;
-                fq[u] = fk[u] * (h2f(st.ng[u]) * kappa);
-                fv[u] = h2f(st.nv[u]) * wscale;
-            }
-
-            // ---- scores for two 16-token tiles
-            float zz[8];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                float4_t am = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+                rw.am[u] = float4_t{0.f, 0.f, 0.f, 0.f};
+                rw.aq[u] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int t = 0; t < KS; ++t) {
                     const half8_t a = key_codes_a<BK>(st.kf[u], t, klut4, klut2);
-                    am = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[t], am, 0, 0, 0);
+                    rw.am[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[t], rw.am[u], 0, 0, 0);
                     if constexpr (QJL) {
                         const uint4 sv = slut[(st.sf[u] >> (8 * t)) & 0xFFu];
-                        aq = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, sv), bq[KS + t], aq,
-                                                                    0, 0, 0);
+                        rw.aq[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, sv), bq[KS + t],
+                                                                          rw.aq[u], 0, 0, 0);
                     }
                 }
+            }
+        };
+        // scores in log2 units: zz[4 u + r] is token tb + 16 u + 4 g + r for head
+        // column col & 7 (hi + lo columns added); MASK: -inf past the range
+        auto finish_scores = [&](const Step<BK, BV>& st, const Raw& rw, int64_t tb, float (&zz)[8], auto MASK) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                // per-token factors of this lane's quad: row 16 u + 4 g + r sits in quad lane r
+                const float fk = h2f(st.nk[u]) * zscale;
+                const float fq = fk * (h2f(st.ng[u]) * kappa);
                 static_for<0, 4>([&](auto rr) {
                     constexpr int r = decltype(rr)::value;
                     const int row = 16 * u + 4 * g + r;
-                    const float zm = am[r] + xor8(am[r]);
-                    float z = quad_bcast<r>(fk[u]) * zm;
-                    if constexpr (QJL) z = fmaf(quad_bcast<r>(fq[u]), aq[r] + xor8(aq[r]), z);
+                    float z = quad_bcast<r>(fk) * (rw.am[u][r] + xor8(rw.am[u][r]));
+                    if constexpr (QJL) z = fmaf(quad_bcast<r>(fq), rw.aq[u][r] + xor8(rw.aq[u][r]), z);
                     if constexpr (decltype(MASK)::value) zz[4 * u + r] = (tb + row < w1) ? z : -INFINITY;
                     else zz[4 * u + r] = z;
                 });
             }
-
-            // ---- block max per head column; rescale only when it beats the running max by 2^8
-            float bm = zz[0];
-#pragma unroll
-            for (int e = 1; e < 8; ++e) bm = fmaxf(bm, zz[e]);
-            bm = fmaxf(bm, __shfl_xor(bm, 16));
-            bm = fmaxf(bm, __shfl_xor(bm, 32));
+        };
+        // the block max per head column (permlane swaps across the row groups);
+        // rescale the running sums only when it beats the running max by 2^8
+        auto softmax_check = [&](const float (&zz)[8]) {
+            float bm = max3f(max3f(zz[0], zz[1], zz[2]), max3f(zz[3], zz[4], zz[5]), fmaxf(zz[6], zz[7]));
+            bm = rows_max(bm);
             if (__ballot(bm > M + 8.0f)) {
                 const float nM = fmaxf(M, bm);
                 const float f = __builtin_amdgcn_exp2f(M - nM);
@@ -490,8 +560,14 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                 }
                 M = nM;
             }
-
-            // ---- weights as the A operand (row = head column, K slot = token)
+        };
+        // weights of one step (A operand: row = head column, K slot = token) times
+        // its value centroids, accumulated in the rotated value domain
+        const float negsel = col >= 8 ? -1.0f : 0.0f;
+        auto accumulate = [&](const Step<BK, BV>& st, const float (&zz)[8]) {
+            float fv[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) fv[u] = h2f(st.nv[u]) * wscale;
             uint32_t awd[4];
             static_for<0, 4>([&](auto jj) {
                 constexpr int j = decltype(jj)::value;
@@ -502,13 +578,14 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                     lsum += w;
                     W[decltype(hh)::value] = w * quad_bcast<e & 3>(fv[e >> 2]);
                 });
-                // fp16(W) for head rows, fp16(W - fp16(W)) for remainder rows
-                const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)W[0]);
-                const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)W[1]);
-                uint32_t lw = 0;
-                asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "+v"(lw) : "v"(h0), "v"(W[0]));
-                asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "+v"(lw) : "v"(h1), "v"(W[1]));
-                awd[j] = col < 8 ? (h0 | (h1 << 16)) : lw;
+                // head rows take fp16(W), remainder rows fp16(W - fp16(W)): both are
+                // fp16(W + negsel fp16(W)), negsel = 0 or -1 by lane
+                uint32_t hw = 0, ow = 0;
+                asm("v_fma_mixlo_f16 %0, %1, 1.0, 0" : "+v"(hw) : "v"(W[0]));
+                asm("v_fma_mixhi_f16 %0, %1, 1.0, 0" : "+v"(hw) : "v"(W[1]));
+                asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "+v"(ow) : "v"(hw), "v"(negsel), "v"(W[0]));
+                asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(ow) : "v"(hw), "v"(negsel), "v"(W[1]));
+                awd[j] = ow;
             });
             const half8_t aw = __builtin_bit_cast(half8_t, awd);
 
@@ -571,69 +648,126 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                 }
             }
         };
-        // full steps (no masking, uniform-base loads, next step in flight),
-        // then at most one partial step with clamped loads and masked scores
         using Full = std::integral_constant<bool, false>;
         using Tail = std::integral_constant<bool, true>;
+
+        // Full steps, software-pipelined: the next step's key lookups and score
+        // MFMAs are issued before the current step's softmax check (whose rare
+        // rescale is a branch), so they run under the current step's weight and
+        // value work; loads run a step ahead of the scores. sa / sb alternate.
+        float za[8], zb[8];
+        Raw rw;
         int64_t i = 0;
-        for (; i + 2 <= nfull; i += 2) {
-            const int64_t tb = w0 + 32 * i;
-            load_full<D, BK, QJL, BV>(sb, base + tb + 32, loff, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
-            compute(sa, tb, Full{});
-            if (i + 2 < nfull)
+        if (nfull > 0) {
+            issue_scores(sa, rw);
+            finish_scores(sa, rw, w0, za, Full{});
+            // steady state: steps i (sa, za) and i + 1 (sb); steps i + 2 and i + 3 exist
+            for (; i + 3 < nfull; i += 2) {
+                const int64_t tb = w0 + 32 * i;
+                issue_scores(sb, rw);
+                softmax_check(za);
+                accumulate(sa, za);
+                finish_scores(sb, rw, tb + 32, zb, Full{});
                 load_full<D, BK, QJL, BV>(sa, base + tb + 64, loff, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
-            compute(sb, tb + 32, Full{});
+                issue_scores(sa, rw);
+                softmax_check(zb);
+                accumulate(sb, zb);
+                finish_scores(sa, rw, tb + 64, za, Full{});
+                load_full<D, BK, QJL, BV>(sb, base + tb + 96, loff, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
+            }
+            // the last one to three full steps: i (sa, za), i + 1 (sb), i + 2 (into sa)
+            const int64_t rem = nfull - i, tb = w0 + 32 * i;
+            if (rem >= 2) issue_scores(sb, rw);
+            softmax_check(za);
+            accumulate(sa, za);
+            if (rem >= 2) {
+                finish_scores(sb, rw, tb + 32, zb, Full{});
+                if (rem >= 3) {
+                    load_full<D, BK, QJL, BV>(sa, base + tb + 64, loff, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
+                    issue_scores(sa, rw);
+                }
+                softmax_check(zb);
+                accumulate(sb, zb);
+                if (rem >= 3) {
+                    finish_scores(sa, rw, tb + 64, za, Full{});
+                    softmax_check(za);
+                    accumulate(sa, za);
+                }
+            }
         }
-        if (i < nfull) compute(sa, w0 + 32 * i, Full{});
+        // at most one partial step: clamped loads, masked scores
         const int64_t tt = w0 + 32 * nfull;
         if (tt < w1) {
             load_step<D, BK, QJL, BV>(sa, tt, w1, base, lane, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
-            compute(sa, tt, Tail{});
+            issue_scores(sa, rw);
+            finish_scores(sa, rw, tt, za, Tail{});
+            softmax_check(za);
+            accumulate(sa, za);
         }
 
-        // ---- per-wave results: sum over row groups, hi rows + lo rows
-        lsum += __shfl_xor(lsum, 16);
-        lsum += __shfl_xor(lsum, 32);
+        // ---- per-wave results: sum over row groups, hi rows + lo rows (permlane swaps)
+        {
+            float e_, o_;
+            row_pair<16>(lsum, e_, o_);
+            lsum = e_ + o_;
+            row_pair<32>(lsum, e_, o_);
+            lsum = e_ + o_;
+        }
         const float inv = 1.0f / wscale;
 #pragma unroll
         for (int c = 0; c < CT; ++c)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float o = acc[c][r] + __shfl_xor(acc[c][r], 32);
+                float e_, o_;
+                row_pair<32>(acc[c][r], e_, o_);  // rows 4 g + r of the upper half are the lo rows
                 const int h = 4 * g + r;
-                if (g < 2 && h < G) mrg_o[wid][h][col + 16 * c] = o * inv;
+                if (g < 2 && h < G) mrg_o[wid][h][col + 16 * c] = (e_ + o_) * inv;
             }
         if (lane < 8) {
             mrg_m[wid][lane] = M;
             mrg_l[wid][lane] = lsum;
         }
-        __syncthreads();
+        // the next item's first loads go out under the merge
+        float* part0 = parts + ((s * n_chunks + chunk) * G) * part_stride(D);
+        item += gridDim.x;
+        const bool more = item < n_items;
+        if (more) begin_item();
+        lds_barrier();
 
-        // ---- merge the four waves into one partial per head
+        // ---- merge the four waves into one partial per head: the 32 factors
+        // exp2(m_w - max) once, then float4 rows
         constexpr int PS = part_stride(D);
-        float* part0 = parts + ((s * n_chunks + chunk) * G) * PS;
-        for (int e = tid; e < G * D; e += 256) {
-            const int h = e / D, i = e % D;
+        if (tid < 32) {
+            const int w = tid >> 3, h = tid & 7;
             float mx = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) mx = fmaxf(mx, mrg_m[w][h]);
-            float o = 0.f;
-            if (mx != -INFINITY)
+            for (int v = 0; v < 4; ++v) mx = fmaxf(mx, mrg_m[v][h]);
+            mrg_f[w][h] = (mx == -INFINITY || mrg_m[w][h] == -INFINITY) ? 0.f : exp2f(mrg_m[w][h] - mx);
+            if (w == 0) mrg_x[h] = mx;
+        }
+        lds_barrier();
+        for (int e = tid; e < G * (D / 4); e += 256) {
+            const int h = e / (D / 4), i4 = e % (D / 4);
+            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    if (mrg_m[w][h] != -INFINITY) o += exp2f(mrg_m[w][h] - mx) * mrg_o[w][h][i];
-            part0[h * PS + kPartAcc + i] = o;
-            if (i == 0) {
+            for (int w = 0; w < 4; ++w) {
+                const float f = mrg_f[w][h];
+                const float4 v = *reinterpret_cast<const float4*>(&mrg_o[w][h][4 * i4]);
+                o.x += f * v.x;
+                o.y += f * v.y;
+                o.z += f * v.z;
+                o.w += f * v.w;
+            }
+            *reinterpret_cast<float4*>(part0 + h * PS + kPartAcc + 4 * i4) = o;
+            if (i4 == 0) {
                 float l = 0.f;
-                if (mx != -INFINITY)
 #pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        if (mrg_m[w][h] != -INFINITY) l += exp2f(mrg_m[w][h] - mx) * mrg_l[w][h];
-                part0[h * PS] = mx;
-                part0[h * PS + 1] = l;
+                for (int w = 0; w < 4; ++w) l += mrg_f[w][h] * mrg_l[w][h];
+                *reinterpret_cast<float2*>(part0 + h * PS) = make_float2(mrg_x[h], l);
             }
         }
-        __syncthreads();
+        if (!more) break;
+        lds_barrier();  // the merge buffers are rewritten by the next item
     }
 }
 
@@ -829,6 +963,9 @@ int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_
 {
     constexpr int D = 128;
     const bool qjl = qk->qjl_m != 0;
+    if (n_streams * n_chunks >= (int64_t)1 << 31)
+        return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attn: %lld streams x %d chunks is more work items than 2^31",
+                    (long long)n_streams, n_chunks);
     AppendDev ad{};
     if (app) ad = AppendDev{*qk, *qv, *k, *v, app->k_new, app->v_new, app->dtype, stride, app->pos};
     launch_qprep_frag(qk, q, q_dtype, n_streams, G, n_streams * G, (half8_t*)frags, app ? &ad : nullptr, s);

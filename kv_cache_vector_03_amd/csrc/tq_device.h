@@ -13,6 +13,26 @@ namespace tq {
 
 constexpr int kWave = 64;
 
+template <int V>
+struct ic {
+    static constexpr int value = V;
+};
+
+// compile-time loop: f(ic<I>{}) for I in [B, E)
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    if constexpr (B < E) {
+        f(ic<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Block barrier for LDS traffic only: waits for this wave's LDS operations and
+// meets the other waves, leaving global loads in flight (a __syncthreads fence
+// would also wait for those).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ float h2f(uint16_t h) { return __half2float(__ushort_as_half(h)); }
 __device__ __forceinline__ uint16_t f2h(float f) { return __half_as_ushort(__float2half_rn(f)); }
 
@@ -77,6 +97,118 @@ __device__ __forceinline__ void load_diag(const uint32_t* diag, int lane, uint32
 
 __device__ __forceinline__ float flip(float x, uint32_t m) { return __uint_as_float(__float_as_uint(x) ^ m); }
 
+// (own value, value of lane l ^ M) for M = 16, 32: a permlane swap of a
+// register with itself returns (row pair's even row, odd row) in every lane
+template <int M>
+__device__ __forceinline__ void row_pair(float v, float& even, float& odd)
+{
+    const uint32_t u = __float_as_uint(v);
+    if constexpr (M == 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        even = __uint_as_float(p[0]);
+        odd = __uint_as_float(p[1]);
+    } else {
+        const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        even = __uint_as_float(p[0]);
+        odd = __uint_as_float(p[1]);
+    }
+}
+
+// max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four rows of 16 lanes), on
+// permlane swaps instead of LDS round trips
+__device__ __forceinline__ float rows_max(float v)
+{
+    float e, o;
+    row_pair<16>(v, e, o);
+    v = fmaxf(e, o);
+    row_pair<32>(v, e, o);
+    return fmaxf(e, o);
+}
+
+// Value held by lane l ^ M (M = 1, 2, 4, 8) by DPP moves within 16-lane rows:
+// quad permutations for 1 and 2, quad reversal (l ^ 3) then half-row mirror
+// (l ^ 7) for 4, a rotation by 8 within the row for 8.
+template <int M>
+__device__ __forceinline__ float dpp_xor(float v)
+{
+    const int i = __float_as_int(v);
+    if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, false));
+    else if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, false));
+    else if constexpr (M == 4)
+        return __int_as_float(
+            __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(i, 0x1B, 0xF, 0xF, false), 0x141, 0xF, 0xF, false));
+    else return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0x128, 0xF, 0xF, false));
+}
+
+// Butterfly on lane bit M: a + b where the lane's bit is clear, a - b where it
+// is set, a being the value of the lane with the bit clear -- the same
+// operands and roundings as fwht_wave. sm = sign bit where the lane bit is set.
+template <int M>
+__device__ __forceinline__ float lane_bfly(float v, uint32_t sm)
+{
+    if constexpr (M <= 8) {
+        return dpp_xor<M>(v) + flip(v, sm);  // p + v, or p - v with p the bit-clear lane's value
+    } else {
+        float e, o;
+        row_pair<M>(v, e, o);
+        return e + flip(o, sm);
+    }
+}
+
+// Sum over the wave in the order of wave_sum (lane bits 5, 4, .., 0), so the
+// result is the same to the bit.
+__device__ __forceinline__ float wave_sum_dpp(float v)
+{
+    float e, o;
+    row_pair<32>(v, e, o);
+    v = e + o;
+    row_pair<16>(v, e, o);
+    v = e + o;
+    v += dpp_xor<8>(v);
+    v += dpp_xor<4>(v);
+    v += dpp_xor<2>(v);
+    v += dpp_xor<1>(v);
+    return v;
+}
+
+// Wave max in the lane-bit order 5, 4, .., 0 on permlane swaps and DPP.
+__device__ __forceinline__ float wave_max_dpp(float v)
+{
+    float e, o;
+    row_pair<32>(v, e, o);
+    v = fmaxf(e, o);
+    row_pair<16>(v, e, o);
+    v = fmaxf(e, o);
+    v = fmaxf(v, dpp_xor<8>(v));
+    v = fmaxf(v, dpp_xor<4>(v));
+    v = fmaxf(v, dpp_xor<2>(v));
+    return fmaxf(v, dpp_xor<1>(v));
+}
+
+// fwht_wave with the lane stages on DPP and permlane swaps instead of LDS
+// exchanges: the same butterflies, operands and roundings, in the same order
+// (register stages, then lane bits 0 .. 5).
+template <int R>
+__device__ __forceinline__ void fwht_wave_dpp(float (&v)[R], int lane)
+{
+#pragma unroll
+    for (int h = 1; h < R; h <<= 1)
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (!(r & h)) {
+                const float a = v[r], b = v[r + h];
+                v[r] = a + b;
+                v[r + h] = a - b;
+            }
+    static_for<0, 6>([&](auto bb) {
+        constexpr int M = 1 << decltype(bb)::value;
+        const uint32_t sm = (lane & M) ? 0x80000000u : 0u;
+#pragma unroll
+        for (int r = 0; r < R; ++r) v[r] = lane_bfly<M>(v[r], sm);
+    });
+}
+
+
 // c[k] for a small register table without dynamic register indexing
 template <int L>
 __device__ __forceinline__ float pick(const float (&c)[L], int k)
@@ -110,21 +242,6 @@ __device__ __forceinline__ uint32_t write_lane(uint32_t dst, uint32_t val)
 {
     asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(dst) : "s"(val), "n"(LN));
     return dst;
-}
-
-template <int V>
-struct ic {
-    static constexpr int value = V;
-};
-
-// compile-time loop: f(ic<I>{}) for I in [B, E)
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f)
-{
-    if constexpr (B < E) {
-        f(ic<B>{});
-        static_for<B + 1, E>(f);
-    }
 }
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));

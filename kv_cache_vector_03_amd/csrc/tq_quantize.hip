@@ -417,69 +417,6 @@ __global__ __launch_bounds__(256) void k_quantize_quad(const void* __restrict__ 
 // whole kernel), the B operand's columns are the vectors. Output register i
 // of m-tile mt in lane (v, q) = (lane % 16, lane / 16) is projection
 // j = 32 w + 16 mt + 4 q + i of vector v: bit w of sign byte 16 mt + 4 q + i.
-// Value held by lane l ^ M (M = 1, 2, 4, 8) by DPP moves within 16-lane rows:
-// quad permutations for 1 and 2, quad reversal (l ^ 3) then half-row mirror
-// (l ^ 7) for 4, a rotation by 8 within the row for 8.
-template <int M>
-__device__ __forceinline__ float dpp_xor(float v)
-{
-    const int i = __float_as_int(v);
-    if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, false));
-    else if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, false));
-    else if constexpr (M == 4)
-        return __int_as_float(
-            __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(i, 0x1B, 0xF, 0xF, false), 0x141, 0xF, 0xF, false));
-    else return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0x128, 0xF, 0xF, false));
-}
-
-// (own value, value of lane l ^ M) for M = 16, 32: a permlane swap of a
-// register with itself returns (row pair's even row, odd row) in every lane
-template <int M>
-__device__ __forceinline__ void row_pair(float v, float& even, float& odd)
-{
-    const uint32_t u = __float_as_uint(v);
-    if constexpr (M == 16) {
-        const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-        even = __uint_as_float(p[0]);
-        odd = __uint_as_float(p[1]);
-    } else {
-        const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-        even = __uint_as_float(p[0]);
-        odd = __uint_as_float(p[1]);
-    }
-}
-
-// Butterfly on lane bit M: a + b where the lane's bit is clear, a - b where it
-// is set, a being the value of the lane with the bit clear -- the same
-// operands and roundings as fwht_wave. sm = sign bit where the lane bit is set.
-template <int M>
-__device__ __forceinline__ float lane_bfly(float v, uint32_t sm)
-{
-    if constexpr (M <= 8) {
-        return dpp_xor<M>(v) + flip(v, sm);  // p + v, or p - v with p the bit-clear lane's value
-    } else {
-        float e, o;
-        row_pair<M>(v, e, o);
-        return e + flip(o, sm);
-    }
-}
-
-// Sum over the wave in the order of wave_sum (lane bits 5, 4, .., 0), so the
-// result is the same to the bit.
-__device__ __forceinline__ float wave_sum_dpp(float v)
-{
-    float e, o;
-    row_pair<32>(v, e, o);
-    v = e + o;
-    row_pair<16>(v, e, o);
-    v = e + o;
-    v += dpp_xor<8>(v);
-    v += dpp_xor<4>(v);
-    v += dpp_xor<2>(v);
-    v += dpp_xor<1>(v);
-    return v;
-}
-
 // fwht_wave for d = 256 (lane l, slot r = coordinate 64 r + l) with the lane
 // stages on DPP and permlane swaps instead of LDS exchanges; same stage order.
 __device__ __forceinline__ void fwht256(float (&v)[4], const uint32_t (&sm)[6])

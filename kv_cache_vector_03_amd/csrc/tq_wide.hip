@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256) void k_decode_wide(const uint32_t* __restrict_
                                                      const float* __restrict__ p,
                                                      const float* __restrict__ kcent,
                                                      const float* __restrict__ vcent, float scale,
-                                                     float* __restrict__ parts, int n_chunks)
+                                                     float* __restrict__ parts, int n_chunks, int64_t s0)
 {
     constexpr int W = D / 32;
     constexpr int KROW = 8 * W + 1;          // staged key row stride (words)
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(256) void k_decode_wide(const uint32_t* __restrict_
     __shared__ uint32_t ks[kTC * KROW];      // key code rows (phase A), value code rows (phase C)
     __shared__ float kc[kMaxL], vc[kMaxL];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int64_t s = blockIdx.y;
+    const int64_t s = s0 + blockIdx.y;  // launches cover at most 65535 streams each
     const int chunk = blockIdx.x;
     const int64_t t0 = (int64_t)chunk * kTC;
     const int64_t row0 = s * stride + t0;     // first vector of the chunk
@@ -517,16 +517,20 @@ void decode_wide_d(const tq_quantizer* qk, const tq_quantizer* qv, const tq_pack
                    int64_t n_streams, int64_t T, int64_t stride, int G, const float* qr, const float* p,
                    float zscale, float* parts, int n_chunks, hipStream_t s)
 {
-    const dim3 grid((unsigned)n_chunks, (unsigned)n_streams), block(256);
     const size_t lds = ((size_t)(qk->qjl_m ? 2 : 1) * G * D + (size_t)G * kTC) * sizeof(float);
-    if (qk->qjl_m)
-        hipLaunchKernelGGL((k_decode_wide<D, true>), grid, block, lds, s, k->codes, k->signs, k->norm, k->rnorm,
-                           qk->mse_bits, v->codes, v->norm, qv->mse_bits, T, stride, G, qr, p, qk->centroids,
-                           qv->centroids, zscale, parts, n_chunks);
-    else
-        hipLaunchKernelGGL((k_decode_wide<D, false>), grid, block, lds, s, k->codes, k->signs, k->norm, k->rnorm,
-                           qk->mse_bits, v->codes, v->norm, qv->mse_bits, T, stride, G, qr, p, qk->centroids,
-                           qv->centroids, zscale, parts, n_chunks);
+    // grid.y is limited to 65535: streams go in launches of at most that many
+    for (int64_t s0 = 0; s0 < n_streams; s0 += 65535) {
+        const int64_t ns = n_streams - s0 < 65535 ? n_streams - s0 : 65535;
+        const dim3 grid((unsigned)n_chunks, (unsigned)ns), block(256);
+        if (qk->qjl_m)
+            hipLaunchKernelGGL((k_decode_wide<D, true>), grid, block, lds, s, k->codes, k->signs, k->norm,
+                               k->rnorm, qk->mse_bits, v->codes, v->norm, qv->mse_bits, T, stride, G, qr, p,
+                               qk->centroids, qv->centroids, zscale, parts, n_chunks, s0);
+        else
+            hipLaunchKernelGGL((k_decode_wide<D, false>), grid, block, lds, s, k->codes, k->signs, k->norm,
+                               k->rnorm, qk->mse_bits, v->codes, v->norm, qv->mse_bits, T, stride, G, qr, p,
+                               qk->centroids, qv->centroids, zscale, parts, n_chunks, s0);
+    }
 }
 
 }  // namespace
