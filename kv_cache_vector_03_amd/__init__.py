@@ -18,7 +18,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtq.so")
+# TQ_SANITIZE=1 loads the host-sanitizer build (build.py --sanitize) instead
+LIB_PATH = (os.path.join(os.path.dirname(_HERE), "_build", "san", "libtq_san.so")
+            if os.environ.get("TQ_SANITIZE") == "1" else os.path.join(_HERE, "libtq.so"))
 
 TQ_OK, TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_DEVICE, TQ_ERR_NOCONV = range(6)
 TQ_F32, TQ_F16 = 0, 1
@@ -168,6 +170,12 @@ class Packed:
     @property
     def n(self) -> int:
         return self.codes.shape[0]
+
+    def slice(self, a: int, b: int) -> "Packed":
+        """Vectors a..b-1 as views of the same device buffers."""
+        def v(t):
+            return t[a:b] if t is not None else None
+        return Packed(v(self.codes), v(self.signs), v(self.norm), v(self.rnorm))
 
     def to_host(self):
         """numpy copies (codes/signs as uint32, norms as uint16 fp16 bits)."""

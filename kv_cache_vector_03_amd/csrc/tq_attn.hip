@@ -156,21 +156,23 @@ int launch_decode(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packe
     float* p = (float*)((char*)ws + plan.off_p);
     float* parts = (float*)((char*)ws + plan.off_parts);
     const float zscale = scale * 1.4426950408889634f;  // scores in log2 units
+    // the decode step's append first (one block per stream and tensor)
+    if (app) {
+        const dim3 ag((unsigned)n_streams, 2u);
+        switch (qk->d) {
+            case 64: hipLaunchKernelGGL((k_append<64>), ag, dim3(256), 0, s, *qk, *qv, *k, *v, app->k_new, app->v_new, app->dtype, stride, app->pos); break;
+            case 128: hipLaunchKernelGGL((k_append<128>), ag, dim3(256), 0, s, *qk, *qv, *k, *v, app->k_new, app->v_new, app->dtype, stride, app->pos); break;
+            default: hipLaunchKernelGGL((k_append<256>), ag, dim3(256), 0, s, *qk, *qv, *k, *v, app->k_new, app->v_new, app->dtype, stride, app->pos); break;
+        }
+    }
     if (plan.mfma) {
-        int rc = launch_decode_mfma(qk, qv, k, v, n_streams, T, stride, G, q, q_dtype, zscale,
-                                    (char*)ws + plan.off_frag, parts, plan.n_chunks, (int)plan.tc, app, s);
+        // the MFMA kernel prepares its stream's queries itself
+        int rc = launch_decode_mfma(qk, qv, k, v, n_streams, T, stride, G, q, q_dtype, zscale, parts, plan.n_chunks,
+                                    (int)plan.tc, s);
         if (rc != TQ_OK) return rc;
     } else {
-        // every other shape and width pair: the scalar kernel with run-time
-        // widths, after the decode step's append (one block per stream and tensor)
-        if (app) {
-            const dim3 ag((unsigned)n_streams, 2u);
-            switch (qk->d) {
-                case 64: hipLaunchKernelGGL((k_append<64>), ag, dim3(256), 0, s, *qk, *qv, *k, *v, app->k_new, app->v_new, app->dtype, stride, app->pos); break;
-                case 128: hipLaunchKernelGGL((k_append<128>), ag, dim3(256), 0, s, *qk, *qv, *k, *v, app->k_new, app->v_new, app->dtype, stride, app->pos); break;
-                default: hipLaunchKernelGGL((k_append<256>), ag, dim3(256), 0, s, *qk, *qv, *k, *v, app->k_new, app->v_new, app->dtype, stride, app->pos); break;
-            }
-        }
+        // every other shape and width pair: prepared queries and the scalar
+        // kernel with run-time widths
         int rc = launch_qprep(qk, q, q_dtype, n_streams * G, qr, p, s);
         if (rc != TQ_OK) return rc;
         rc = launch_decode_wide(qk, qv, k, v, n_streams, T, stride, G, qr, p, zscale, parts, plan.n_chunks, s);

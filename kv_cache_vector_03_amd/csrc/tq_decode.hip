@@ -22,7 +22,6 @@
 // The four waves merge in LDS; one partial (max, sum, rotated-domain
 // accumulator) per block goes to the workspace, and the combine kernel merges
 // the partials of a stream and undoes the value rotation.
-#include "tq_append.h"
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -33,6 +32,15 @@ __device__ __forceinline__ float xor8(float x)
 {
     // lane i <-> lane i ^ 8 inside each row of 16 lanes (DPP row rotate by 8)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
+// Lanes of the upper half of each 16-lane row (bank_mask 0xC) or of the lower
+// half (0x3) take the value of lane i ^ 8; the others keep their own.
+template <int BANKS>
+__device__ __forceinline__ float take_xor8(float x)
+{
+    const int i = __float_as_int(x);
+    return __int_as_float(__builtin_amdgcn_update_dpp(i, i, 0x128, 0xF, BANKS, false));
 }
 
 // Value of lane (lane & ~3) + R within each quad of lanes (DPP quad_perm).
@@ -52,39 +60,20 @@ __device__ __forceinline__ float quad_bcast(float x)
 // k-step t maps to coordinate (or projection row) (4 g + t) + (d/8) e, the
 // group-major order the key codes arrive in. Arithmetic is fp32: its relative
 // error (~1e-7) is far below what the hi/lo operands carry into the scores.
-//
-// With the decode step's append, grid.y has two more blocks per stream: they
-// quantize the stream's new key (y = d/32) and value (y = d/32 + 1) into the
-// caches, beside the fragment blocks and in the same launch.
-struct AppendDev {
-    tq_quantizer qk, qv;
-    tq_packed k, v;
-    const void* k_new;
-    const void* v_new;
-    int dtype;
-    int64_t stride, pos;
-};
-
+// (The decode kernel prepares its queries itself, in the same layout.)
 template <int D, bool QJL, bool F16>
 __global__ __launch_bounds__(256) void k_qprep_frag(const void* __restrict__ q, int G, int64_t total,
                                                     const uint32_t* __restrict__ diag,
                                                     const uint16_t* __restrict__ S,
-                                                    half8_t* __restrict__ frags, AppendDev app)
+                                                    half8_t* __restrict__ frags)
 {
     static_assert(D == 128, "fragment layout is laid out for d = 128");
-    static_assert(8 * D >= append_smem_floats(D), "append scratch reuses the query buffer");
     constexpr int R = D / 64, KS = D / 32, KSTEPS = KS * (QJL ? 2 : 1);
     __shared__ float qs[8][D];
     __shared__ float ps[QJL ? 8 : 1][32];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int64_t s = blockIdx.x;
     const int tt = blockIdx.y;
-    if (tt >= KS) {
-        const bool val = tt == KS + 1;
-        quantize_one<D>(val ? app.qv : app.qk, val ? app.v : app.k, val ? app.v_new : app.k_new, app.dtype, s,
-                        s * app.stride + app.pos, &qs[0][0]);
-        return;
-    }
     // thread (h, i) projects row j = tt + (d/32) i of S onto head h; the block's
     // 32 rows are copied to LDS first (coalesced, each row once), so the copy
     // overlaps the rotation
@@ -202,11 +191,11 @@ __device__ void fill_key_luts(uint2* klut4, uint32_t* klut2, uint4* slut, const 
 
 // fill_key_luts from fp16 centroids already in LDS (kc16[code]).
 template <int BK, bool QJL>
-__device__ void fill_key_luts_lds(uint2* klut4, uint32_t* klut2, uint4* slut, const uint16_t* kc16)
+__device__ void fill_key_luts_lds(uint2* klut4, uint32_t* klut2, uint4* slut, const uint16_t* kc16, bool codes)
 {
     constexpr bool K4 = BK <= 2;
     constexpr int KLUT = key_lut_entries(BK);
-    for (int i = threadIdx.x; i < KLUT; i += blockDim.x) {
+    for (int i = threadIdx.x; codes && i < KLUT; i += blockDim.x) {
         if constexpr (K4) {
             uint32_t h[4];
 #pragma unroll
@@ -269,6 +258,14 @@ __device__ __forceinline__ half8_t key_codes_a(const uint32_t (&kf)[BK], int t, 
         for (int j = 0; j < 4; ++j) wds[j] = klut2[(field >> (2 * BK * j)) & ((1u << (2 * BK)) - 1u)];
         return __builtin_bit_cast(half8_t, wds);
     }
+}
+
+// Table address (index byte k of y) * 256 + copy byte: one v_perm that puts
+// byte k of y in bits 8..15 next to the low byte of `copy`.
+template <int K>
+__device__ __forceinline__ uint32_t row_addr(uint32_t y, uint32_t copy)
+{
+    return __builtin_amdgcn_perm(y, copy, 0x0C0C0000u | ((4u + K) << 8));
 }
 
 // max of three floats without NaN canonicalization (scores are never NaN)
@@ -393,11 +390,12 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                                                      const uint16_t* __restrict__ krnorm,
                                                      const uint32_t* __restrict__ vcodes,
                                                      const uint16_t* __restrict__ vnorm, int64_t T,
-                                                     int64_t stride, int G, const half8_t* __restrict__ frags,
+                                                     int64_t stride, int G, const void* __restrict__ q,
+                                                     int q_f16, const uint32_t* __restrict__ kdiag,
+                                                     const uint16_t* __restrict__ S,
                                                      const float* __restrict__ kcent,
                                                      const float* __restrict__ vcent, float zscale,
-                                                     float* __restrict__ parts, int n_chunks, int tc,
-                                                     int64_t n_items)
+                                                     float* __restrict__ parts, int n_chunks, int tc)
 {
     static_assert(D == 128, "MFMA decode is laid out for d = 128");
     constexpr int KS = D / 32;                 // 4 code groups per lane per token
@@ -408,17 +406,33 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
     constexpr int VLUT = BV <= 4 ? 1 << (2 * BV) : 1 << BV;  // code pairs, or single codes above 4 bits
     constexpr float kappa = 1.2533141373155003f / D;  // sqrt(pi/2) / m
 
-    __shared__ uint2 klut4[K4 ? KLUT : 1];
+    // 2-bit keys and 4-bit values: tables in 256-byte rows, entry e's 32 value
+    // copies (4 bytes, lane l reads copy l % 32) in bytes 0..127 and its 16 key
+    // copies (8 bytes, copy l % 16) in 128..255. The index is a byte of the
+    // packed codes, so an address is that byte next to the lane's copy byte (one
+    // v_perm). The rows also hold the value table of other widths (first half),
+    // and, after the scan, the merge buffers (rebuilt for a further item).
+    constexpr bool PV = BV == 4, PK = BK == 2, ROWS = PV || PK;
+    __shared__ __align__(16) uint32_t rows[ROWS ? 256 : 1][64];
+    __shared__ uint2 klut4[K4 && !PK ? KLUT : 1];
     __shared__ uint32_t klut2[K4 ? 1 : KLUT];
     __shared__ uint4 slut[QJL ? 256 : 1];
-    __shared__ uint32_t vlut[VLUT][32];  // one copy per bank: lane l reads copy l % 32
+    __shared__ uint32_t vlut[ROWS ? 1 : VLUT][32];  // one copy per bank: lane l reads copy l % 32
     __shared__ float mrg_m[4][8], mrg_l[4][8], mrg_f[4][8], mrg_x[8];
-    __shared__ __align__(16) float mrg_o[4][8][D];
+    __shared__ __align__(16) float mrg_own[ROWS ? 1 : 4][8][D];
+    float(*const mrg_o)[8][D] = ROWS ? reinterpret_cast<float(*)[8][D]>(&rows[0][0]) : mrg_own;
+    const char* const rowsb = reinterpret_cast<const char*>(&rows[0][0]);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int col = lane & 15, g = lane >> 4;
     const LaneOff loff = lane_offsets<D, BK, BV>(lane);
+    const uint32_t vcopy = (lane & 31) * 4, kcopy = 128 + (lane & 15) * 8;  // copy bytes in a row
+    // value table entry e, copy of this lane
+    auto vl = [&](uint32_t e) -> uint32_t {
+        if constexpr (ROWS) return rows[e][lane & 31];
+        else return vlut[e][lane & 31];
+    };
 
     // the two codebooks (one global load per thread) are the first loads in
     // flight, so they can be waited for while the first item's loads are not
@@ -426,8 +440,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
     const float kc_v = kcent[min(tid, (1 << BK) - 1)];  // clamped: no branch around the loads
     const float vc_v = vcent[min(tid, (1 << BV) - 1)];
 
-    int64_t item = blockIdx.x;
-    if (item >= n_items) return;  // the whole block (the grid never exceeds the items)
+    const int64_t item = blockIdx.x;  // one work item (stream, chunk) per block
 
     // the current item's geometry and first loads: the first 512 value norms of
     // each wave's range (indices clamped into it), then the first two full steps
@@ -438,6 +451,15 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
     uint16_t hv[8];
     Step<BK, BV> sa, sb;
     half8_t bq[KSTEPS];
+    // query preparation inputs of the item's stream: heads wid and wid + 4 (two
+    // coordinates per lane each; heads past G read as zero) and this wave's two
+    // 16-row tiles of S for the projection (MFMA A operands, 8 per lane)
+    __shared__ __align__(16) float qs[8][D];      // q' = H D q / sqrt(d), per head
+    __shared__ __align__(16) float ps[QJL ? 8 : 1][D];  // p = S q', per head
+    uint32_t qw[2][2];  // raw query words (fp32 bits, or the 32-bit word holding the fp16 value)
+    uint4 sA[QJL ? 2 : 1][4];
+    uint32_t dm[2];
+    load_diag<2>(kdiag, lane, dm);
     auto begin_item = [&]() {
         // items number fewer than 2^31 (streams times chunks): 32-bit division
         const uint32_t it = (uint32_t)item, nc = (uint32_t)n_chunks;
@@ -453,34 +475,156 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
         // wait for them: indices are clamped to the range's last token, or to the
         // chunk's last one for a wave past its end
         const int64_t lim = w1 > w0 ? w1 : c1;
+        // the query (clamped head index, zeroed past G) and S first: they are needed first
+        // (32-bit word loads for both dtypes, no branch: the fp16 pair's word)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int64_t row = (s * G + min(wid + 4 * hh, G - 1)) * D + lane;
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+                qw[hh][r] = static_cast<const uint32_t*>(q)[q_f16 ? (row + 64 * r) >> 1 : row + 64 * r];
+        }
+        if constexpr (QJL) {
+            // A operand of tile 2 wid + u, k-step k: row j = 16 (2 wid + u) + col,
+            // coordinates 32 k + 8 g .. + 7
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    sA[u][k] = *reinterpret_cast<const uint4*>(S + (16 * (2 * wid + u) + col) * D + 32 * k + 8 * g);
+        }
 #pragma unroll
         for (int k = 0; k < 8; ++k) hv[k] = vnorm[base + min(w0 + lane + 64 * k, lim - 1)];
         load_step<D, BK, QJL, BV>(sa, w0, lim, base, lane, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
         load_step<D, BK, QJL, BV>(sb, w0 + 32, lim, base, lane, kcodes, ksigns, knorm, krnorm, vcodes, vnorm);
-#pragma unroll
-        for (int k = 0; k < KSTEPS; ++k) bq[k] = frags[(s * KSTEPS + k) * 64 + lane];
     };
     begin_item();
 
-    // ---- lookup tables, built while the first item's loads are in flight:
-    // codes -> fp16 centroids, sign bytes -> +-1 (LDS-only barriers)
-    if (tid < (1 << BK)) cb16[0][tid] = f2h(kc_v);
-    if (tid < (1 << BV)) cb16[1][tid] = f2h(vc_v);
-    lds_barrier();
-    fill_key_luts_lds<BK, QJL>(klut4, klut2, slut, cb16[0]);
-    // value table: entry e (a code pair, or one code above 4 bits) in all 32
-    // copies; a wave writes 8 entries' 128-byte rows per instruction
-    for (int i = tid; i < VLUT * 8; i += 256) {
-        const int e = i >> 3;
-        uint32_t v;
-        if constexpr (BV <= 4) v = (uint32_t)cb16[1][e & ((1 << BV) - 1)] | ((uint32_t)cb16[1][e >> BV] << 16);
-        else v = (uint32_t)cb16[1][e] * 0x10001u;  // one code, its centroid in both halves
-        reinterpret_cast<uint4*>(&vlut[e][0])[i & 7] = make_uint4(v, v, v, v);
+    // fp16 parts of a pair of fp32 values for this lane's column half: fp16(x) for
+    // col < 8, fp16(x - fp16(x)) for col >= 8; both are fp16(x + negsel fp16(x))
+    const float negsel = col >= 8 ? -1.0f : 0.0f;
+    auto split2 = [&](float x0, float x1) -> uint32_t {
+        uint32_t hw = 0, ow = 0;
+        asm("v_fma_mixlo_f16 %0, %1, 1.0, 0" : "+v"(hw) : "v"(x0));
+        asm("v_fma_mixhi_f16 %0, %1, 1.0, 0" : "+v"(hw) : "v"(x1));
+        asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "+v"(ow) : "v"(hw), "v"(negsel), "v"(x0));
+        asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(ow) : "v"(hw), "v"(negsel), "v"(x1));
+        return ow;
+    };
+    const int head = col & 7;
+
+    // ---- prologue, while the first steps' loads are in flight: lookup tables
+    // (codes -> fp16 centroids, sign bytes -> +-1) and the query preparation
+    // (q' by the rotation, p = S q' on MFMA, then the score B fragments bq). Lane
+    // (g, col) element e of k-step t holds coordinate (or projection row)
+    // 4 g + t + 16 e of head col & 7, split as split2 does, in the group-major
+    // order the key codes arrive in. Arithmetic is fp32 (the products of fp16 S
+    // and the fp16 parts of q' are exact). LDS-only barriers.
+
+    // (1) the codebooks and q' = H D q / sqrt(d) to LDS. Every thread writes a
+    // codebook slot (slots past the codebook repeat its last centroid and are
+    // never read): no branch for the compiler to sink the loads into.
+    cb16[0][tid] = f2h(kc_v);
+    cb16[1][tid] = f2h(vc_v);
+    {
+        constexpr float inv_sqrt_d = 0.08838834764831845f;  // 1 / sqrt(128)
+        float qv[2][2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const float v = q_f16 ? h2f((uint16_t)(qw[hh][r] >> (16 * (lane & 1)))) : __uint_as_float(qw[hh][r]);
+                qv[hh][r] = wid + 4 * hh < G ? v : 0.f;  // heads past G are zero
+            }
+        float ya[2] = {flip(qv[0][0], dm[0]), flip(qv[0][1], dm[1])};
+        float yb[2] = {flip(qv[1][0], dm[0]), flip(qv[1][1], dm[1])};
+        fwht_wave_dpp<2>(ya, lane);
+        fwht_wave_dpp<2>(yb, lane);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            qs[wid][64 * r + lane] = ya[r] * inv_sqrt_d;
+            qs[wid + 4][64 * r + lane] = yb[r] * inv_sqrt_d;
+        }
     }
     lds_barrier();
 
-    for (;;) {
+    // (2) the tables from the codebooks, and p = S q' to LDS
+    // value table entry e: a code pair, or one code above 4 bits in both halves
+    auto ventry = [&](int e) -> uint32_t {
+        if constexpr (BV <= 4) return (uint32_t)cb16[1][e & ((1 << BV) - 1)] | ((uint32_t)cb16[1][e >> BV] << 16);
+        else return (uint32_t)cb16[1][e] * 0x10001u;
+    };
+    if constexpr (ROWS) {
+        // the row tables: 16 uint4 per row, 8 of value copies and 8 of key copies
+        for (int i = tid; i < 256 * 16; i += 256) {
+            const int e = i >> 4, qq = i & 15;
+            if (qq < 8) {
+                if (e < VLUT) {
+                    const uint32_t v = ventry(e);
+                    reinterpret_cast<uint4*>(&rows[e][0])[qq] = make_uint4(v, v, v, v);
+                }
+            } else if constexpr (PK) {
+                uint32_t h[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) h[j] = cb16[0][(e >> (2 * j)) & 3];
+                const uint32_t x = h[0] | (h[1] << 16), y = h[2] | (h[3] << 16);
+                reinterpret_cast<uint4*>(&rows[e][0])[qq] = make_uint4(x, y, x, y);
+            }
+        }
+        fill_key_luts_lds<BK, QJL>(klut4, klut2, slut, cb16[0], !PK);
+    } else {
+        fill_key_luts_lds<BK, QJL>(klut4, klut2, slut, cb16[0], true);
+        // value table: entry e in all 32 copies; a wave writes 8 entries' 128-byte
+        // rows per instruction
+        for (int i = tid; i < VLUT * 8; i += 256) {
+            const uint32_t v = ventry(i >> 3);
+            reinterpret_cast<uint4*>(&vlut[i >> 3][0])[i & 7] = make_uint4(v, v, v, v);
+        }
+    }
+    if constexpr (QJL) {
+        // tiles 2 wid, 2 wid + 1 of p: rows j, columns = head col & 7's hi / lo parts
+        float4_t pa[2] = {float4_t{0.f, 0.f, 0.f, 0.f}, float4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float4 x0 = *reinterpret_cast<const float4*>(&qs[head][32 * k + 8 * g]);
+            const float4 x1 = *reinterpret_cast<const float4*>(&qs[head][32 * k + 8 * g + 4]);
+            const uint32_t bw[4] = {split2(x0.x, x0.y), split2(x0.z, x0.w), split2(x1.x, x1.y), split2(x1.z, x1.w)};
+            const half8_t b = __builtin_bit_cast(half8_t, bw);
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                pa[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, sA[u][k]), b, pa[u], 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float pv = pa[u][r] + xor8(pa[u][r]);  // hi + lo columns
+                if (col < 8) ps[head][16 * (2 * wid + u) + 4 * g + r] = pv;
+            }
+    }
+    lds_barrier();
 
+    // (3) the score B fragments: element e of k-steps t = 0..3 is one float4 of
+    // four consecutive coordinates
+#pragma unroll
+    for (int part = 0; part < (QJL ? 2 : 1); ++part) {
+        const float* src = part ? &ps[QJL ? head : 0][4 * g] : &qs[head][4 * g];
+        float4 x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = *reinterpret_cast<const float4*>(src + 16 * e);
+        uint32_t w[4][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            w[0][j] = split2(x[2 * j].x, x[2 * j + 1].x);
+            w[1][j] = split2(x[2 * j].y, x[2 * j + 1].y);
+            w[2][j] = split2(x[2 * j].z, x[2 * j + 1].z);
+            w[3][j] = split2(x[2 * j].w, x[2 * j + 1].w);
+        }
+#pragma unroll
+        for (int t = 0; t < KS; ++t) bq[KS * part + t] = __builtin_bit_cast(half8_t, w[t]);
+    }
+
+    {
         // fixed weight scale for this wave: max weight * norm stays below 2^15 in fp16.
         // The norms of the wave's range, 512 at a time (the first 512 loaded above).
         float nmax = 0.f;
@@ -515,7 +659,19 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                 rw.aq[u] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int t = 0; t < KS; ++t) {
-                    const half8_t a = key_codes_a<BK>(st.kf[u], t, klut4, klut2);
+                    half8_t a;
+                    if constexpr (PK) {
+                        // group t: bytes 2 (t & 1) and 2 (t & 1) + 1 of word t >> 1 index two entries
+                        const uint32_t w = st.kf[u][t >> 1];
+                        const uint2 e0 = *reinterpret_cast<const uint2*>(
+                            rowsb + (t & 1 ? row_addr<2>(w, kcopy) : row_addr<0>(w, kcopy)));
+                        const uint2 e1 = *reinterpret_cast<const uint2*>(
+                            rowsb + (t & 1 ? row_addr<3>(w, kcopy) : row_addr<1>(w, kcopy)));
+                        const uint32_t wds[4] = {e0.x, e0.y, e1.x, e1.y};
+                        a = __builtin_bit_cast(half8_t, wds);
+                    } else {
+                        a = key_codes_a<BK>(st.kf[u], t, klut4, klut2);
+                    }
                     rw.am[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq[t], rw.am[u], 0, 0, 0);
                     if constexpr (QJL) {
                         const uint4 sv = slut[(st.sf[u] >> (8 * t)) & 0xFFu];
@@ -525,31 +681,39 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                 }
             }
         };
-        // scores in log2 units: zz[4 u + r] is token tb + 16 u + 4 g + r for head
-        // column col & 7 (hi + lo columns added); MASK: -inf past the range
-        auto finish_scores = [&](const Step<BK, BV>& st, const Raw& rw, int64_t tb, float (&zz)[8], auto MASK) {
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                // per-token factors of this lane's quad: row 16 u + 4 g + r sits in quad lane r
-                const float fk = h2f(st.nk[u]) * zscale;
-                const float fq = fk * (h2f(st.ng[u]) * kappa);
-                static_for<0, 4>([&](auto rr) {
-                    constexpr int r = decltype(rr)::value;
-                    const int row = 16 * u + 4 * g + r;
-                    float z = quad_bcast<r>(fk) * (rw.am[u][r] + xor8(rw.am[u][r]));
-                    if constexpr (QJL) z = fmaf(quad_bcast<r>(fq), rw.aq[u][r] + xor8(rw.aq[u][r]), z);
-                    if constexpr (decltype(MASK)::value) zz[4 * u + r] = (tb + row < w1) ? z : -INFINITY;
-                    else zz[4 * u + r] = z;
-                });
-            }
+        // The score MFMAs give head col & 7's hi (col < 8) and lo (col >= 8) column
+        // parts for both 16-token tiles. Each lane finishes the scores of one tile:
+        // the lower half of a 16-lane row tile 0, the upper half tile 1 (own tile
+        // `up`), so the softmax and weight work is done once per token and head.
+        const bool up = col >= 8;
+        // scores in log2 units: zz[r] is token tb + 16 up + 4 g + r for head
+        // col & 7 (hi + lo columns added); MASK: -inf past the range
+        auto finish_scores = [&](const Step<BK, BV>& st, const Raw& rw, int64_t tb, float (&zz)[4], auto MASK) {
+            // per-token factors of the lane's quad (all four lanes of a quad lie in
+            // one half): row 16 up + 4 g + r sits in quad lane r
+            const float fk = h2f(up ? st.nk[1] : st.nk[0]) * zscale;
+            const float fq = fk * (h2f(up ? st.ng[1] : st.ng[0]) * kappa);
+            static_for<0, 4>([&](auto rr) {
+                constexpr int r = decltype(rr)::value;
+                const float a0 = rw.am[0][r] + xor8(rw.am[0][r]), a1 = rw.am[1][r] + xor8(rw.am[1][r]);
+                float z = quad_bcast<r>(fk) * (up ? a1 : a0);
+                if constexpr (QJL) {
+                    const float q0 = rw.aq[0][r] + xor8(rw.aq[0][r]), q1 = rw.aq[1][r] + xor8(rw.aq[1][r]);
+                    z = fmaf(quad_bcast<r>(fq), up ? q1 : q0, z);
+                }
+                if constexpr (decltype(MASK)::value) zz[r] = (tb + (up ? 16 : 0) + 4 * g + r < w1) ? z : -INFINITY;
+                else zz[r] = z;
+            });
         };
-        // the block max per head column (permlane swaps across the row groups);
-        // rescale the running sums only when it beats the running max by 2^8
-        auto softmax_check = [&](const float (&zz)[8]) {
-            float bm = max3f(max3f(zz[0], zz[1], zz[2]), max3f(zz[3], zz[4], zz[5]), fmaxf(zz[6], zz[7]));
+        // the block max per head column (the other tile's lane, then permlane swaps
+        // across the row groups); rescale the running sums only when it beats the
+        // running max by 2^8
+        auto softmax_check = [&](const float (&zz)[4]) {
+            float bm = max3f(zz[0], zz[1], max2nn(zz[2], zz[3]));
+            bm = max2nn(bm, xor8(bm));
             bm = rows_max(bm);
-            if (__ballot(bm > M + 8.0f)) {
-                const float nM = fmaxf(M, bm);
+            if (__builtin_expect(__ballot(bm > M + 8.0f) != 0, 0)) {
+                const float nM = max2nn(M, bm);
                 const float f = __builtin_amdgcn_exp2f(M - nM);
                 lsum *= f;
 #pragma unroll
@@ -563,30 +727,31 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
         };
         // weights of one step (A operand: row = head column, K slot = token) times
         // its value centroids, accumulated in the rotated value domain
-        const float negsel = col >= 8 ? -1.0f : 0.0f;
-        auto accumulate = [&](const Step<BK, BV>& st, const float (&zz)[8]) {
-            float fv[2];
+        auto accumulate = [&](const Step<BK, BV>& st, const float (&zz)[4]) {
+            const float fv = h2f(up ? st.nv[1] : st.nv[0]) * wscale;
+            float Wo[4];  // own tile's weights times value norms
 #pragma unroll
-            for (int u = 0; u < 2; ++u) fv[u] = h2f(st.nv[u]) * wscale;
+            for (int r = 0; r < 4; ++r) {
+                const float w = __builtin_amdgcn_exp2f(zz[r] - M);
+                lsum += w;
+                Wo[r] = w;
+            }
+            Wo[0] *= quad_bcast<0>(fv);
+            Wo[1] *= quad_bcast<1>(fv);
+            Wo[2] *= quad_bcast<2>(fv);
+            Wo[3] *= quad_bcast<3>(fv);
+            // K slot 4 u + r is token 16 u + 4 g + r: tile 0's weights from the lower
+            // lane of the pair, tile 1's from the upper one
+            float W8[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                W8[r] = take_xor8<0xC>(Wo[r]);
+                W8[4 + r] = take_xor8<0x3>(Wo[r]);
+            }
+            // head rows take fp16(W), remainder rows fp16(W - fp16(W))
             uint32_t awd[4];
-            static_for<0, 4>([&](auto jj) {
-                constexpr int j = decltype(jj)::value;
-                float W[2];
-                static_for<0, 2>([&](auto hh) {
-                    constexpr int e = 2 * j + decltype(hh)::value;
-                    const float w = __builtin_amdgcn_exp2f(zz[e] - M);
-                    lsum += w;
-                    W[decltype(hh)::value] = w * quad_bcast<e & 3>(fv[e >> 2]);
-                });
-                // head rows take fp16(W), remainder rows fp16(W - fp16(W)): both are
-                // fp16(W + negsel fp16(W)), negsel = 0 or -1 by lane
-                uint32_t hw = 0, ow = 0;
-                asm("v_fma_mixlo_f16 %0, %1, 1.0, 0" : "+v"(hw) : "v"(W[0]));
-                asm("v_fma_mixhi_f16 %0, %1, 1.0, 0" : "+v"(hw) : "v"(W[1]));
-                asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "+v"(ow) : "v"(hw), "v"(negsel), "v"(W[0]));
-                asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(ow) : "v"(hw), "v"(negsel), "v"(W[1]));
-                awd[j] = ow;
-            });
+#pragma unroll
+            for (int j = 0; j < 4; ++j) awd[j] = split2(W8[2 * j], W8[2 * j + 1]);
             const half8_t aw = __builtin_bit_cast(half8_t, awd);
 
             // ---- value codes: lane column = code group, slot e = token 4g+e (tile 0) / 16+4g+e-4 (tile 1)
@@ -608,8 +773,8 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                     for (int j = 0; j < 4; ++j) {
                         const uint32_t wa = c < 4 ? X[2 * j] : st.x1[2 * j];
                         const uint32_t wb = c < 4 ? X[2 * j + 1] : st.x1[2 * j + 1];
-                        const uint32_t a = vlut[(wa >> (8 * (c & 3))) & 0xFFu][lane & 31];
-                        const uint32_t b = vlut[(wb >> (8 * (c & 3))) & 0xFFu][lane & 31];
+                        const uint32_t a = vl((wa >> (8 * (c & 3))) & 0xFFu);
+                        const uint32_t b = vl((wb >> (8 * (c & 3))) & 0xFFu);
                         bw[j] = (a & 0xFFFFu) | (b & 0xFFFF0000u);
                     }
                     acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, bw), acc[c], 0, 0, 0);
@@ -621,7 +786,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const uint32_t ia = (X[2 * j] >> (3 * c)) & 7u, ib = (X[2 * j + 1] >> (3 * c)) & 7u;
-                        bw[j] = vlut[ia | (ib << 3)][lane & 31];
+                        bw[j] = vl(ia | (ib << 3));
                     }
                     acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, bw), acc[c], 0, 0, 0);
                 }
@@ -642,7 +807,19 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const uint32_t y = (c & 1) ? y1[j] : y0[j];
-                        bw[j] = vlut[(y >> (2 * BV * (c >> 1))) & ((1u << (2 * BV)) - 1u)][lane & 31];
+                        if constexpr (PV) {
+                            // 4-bit codes: the index of tile c is byte c >> 1 of y
+                            uint32_t ad;
+                            switch (c >> 1) {
+                                case 0: ad = row_addr<0>(y, vcopy); break;
+                                case 1: ad = row_addr<1>(y, vcopy); break;
+                                case 2: ad = row_addr<2>(y, vcopy); break;
+                                default: ad = row_addr<3>(y, vcopy); break;
+                            }
+                            bw[j] = *reinterpret_cast<const uint32_t*>(rowsb + ad);
+                        } else {
+                            bw[j] = vl((y >> (2 * BV * (c >> 1))) & ((1u << (2 * BV)) - 1u));
+                        }
                     }
                     acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, bw), acc[c], 0, 0, 0);
                 }
@@ -655,7 +832,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
         // MFMAs are issued before the current step's softmax check (whose rare
         // rescale is a branch), so they run under the current step's weight and
         // value work; loads run a step ahead of the scores. sa / sb alternate.
-        float za[8], zb[8];
+        float za[4], zb[4];
         Raw rw;
         int64_t i = 0;
         if (nfull > 0) {
@@ -705,7 +882,10 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
             accumulate(sa, za);
         }
 
-        // ---- per-wave results: sum over row groups, hi rows + lo rows (permlane swaps)
+        // ---- per-wave results: sum over the tile pair and the row groups, hi rows +
+        // lo rows (permlane swaps)
+        lsum += xor8(lsum);
+        if constexpr (ROWS) lds_barrier();  // every wave is done with the tables the merge rows overwrite
         {
             float e_, o_;
             row_pair<16>(lsum, e_, o_);
@@ -727,11 +907,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
             mrg_m[wid][lane] = M;
             mrg_l[wid][lane] = lsum;
         }
-        // the next item's first loads go out under the merge
         float* part0 = parts + ((s * n_chunks + chunk) * G) * part_stride(D);
-        item += gridDim.x;
-        const bool more = item < n_items;
-        if (more) begin_item();
         lds_barrier();
 
         // ---- merge the four waves into one partial per head: the 32 factors
@@ -766,27 +942,29 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                 *reinterpret_cast<float2*>(part0 + h * PS) = make_float2(mrg_x[h], l);
             }
         }
-        if (!more) break;
-        lds_barrier();  // the merge buffers are rewritten by the next item
     }
 }
 
+// Query rows as the kernel takes them: pointer and fp16 flag.
+struct QueryIn {
+    const void* q;
+    int f16;
+};
+
 template <int D, int BK, bool QJL, int BV>
 void launch_mfma(const tq_packed* k, const tq_packed* v, int64_t n_streams, int64_t T, int64_t stride, int G,
-                 const half8_t* frags, const tq_quantizer* qk, const tq_quantizer* qv, float zscale,
+                 QueryIn fr, const tq_quantizer* qk, const tq_quantizer* qv, float zscale,
                  float* parts, int n_chunks, int tc, hipStream_t s)
 {
     const int64_t n_items = n_streams * n_chunks;
-    const int64_t cap = (int64_t)device_cus() * 2;
-    const unsigned grid = (unsigned)(n_items < cap ? n_items : cap);
-    hipLaunchKernelGGL((k_decode_mfma<D, BK, QJL, BV>), dim3(grid), dim3(256), 0, s, k->codes, k->signs, k->norm,
-                       k->rnorm, v->codes, v->norm, T, stride, G, frags, qk->centroids, qv->centroids, zscale, parts,
-                       n_chunks, tc, n_items);
+    hipLaunchKernelGGL((k_decode_mfma<D, BK, QJL, BV>), dim3((unsigned)n_items), dim3(256), 0, s, k->codes, k->signs, k->norm,
+                       k->rnorm, v->codes, v->norm, T, stride, G, fr.q, fr.f16, qk->diag_signs, qk->S,
+                       qk->centroids, qv->centroids, zscale, parts, n_chunks, tc);
 }
 
 template <int D, int BK, bool QJL>
 void launch_bv(int bv, const tq_packed* k, const tq_packed* v, int64_t ns, int64_t T, int64_t stride, int G,
-               const half8_t* fr,
+               QueryIn fr,
                const tq_quantizer* qk, const tq_quantizer* qv, float zs, float* parts, int nc, int tc,
                hipStream_t s)
 {
@@ -801,21 +979,19 @@ void launch_bv(int bv, const tq_packed* k, const tq_packed* v, int64_t ns, int64
 }
 
 // Score fragments of `tiles` groups of G query rows (rows at or past `total`
-// count as zero); with app (one tile per stream), also the append blocks.
+// count as zero).
 void launch_qprep_frag(const tq_quantizer* qk, const void* q, int q_dtype, int64_t tiles, int G, int64_t total,
-                       half8_t* frags, const AppendDev* app, hipStream_t s)
+                       half8_t* frags, hipStream_t s)
 {
     constexpr int D = 128;
     const bool qjl = qk->qjl_m != 0;
-    AppendDev a{};
-    if (app) a = *app;
-    const dim3 pg((unsigned)tiles, (unsigned)(D / 32 + (app ? 2 : 0))), pb(256);
+    const dim3 pg((unsigned)tiles, (unsigned)(D / 32)), pb(256);
     if (q_dtype == TQ_F16) {
-        if (qjl) hipLaunchKernelGGL((k_qprep_frag<D, true, true>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags, a);
-        else hipLaunchKernelGGL((k_qprep_frag<D, false, true>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags, a);
+        if (qjl) hipLaunchKernelGGL((k_qprep_frag<D, true, true>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags);
+        else hipLaunchKernelGGL((k_qprep_frag<D, false, true>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags);
     } else {
-        if (qjl) hipLaunchKernelGGL((k_qprep_frag<D, true, false>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags, a);
-        else hipLaunchKernelGGL((k_qprep_frag<D, false, false>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags, a);
+        if (qjl) hipLaunchKernelGGL((k_qprep_frag<D, true, false>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags);
+        else hipLaunchKernelGGL((k_qprep_frag<D, false, false>), pg, pb, 0, s, q, G, total, qk->diag_signs, qk->S, frags);
     }
 }
 
@@ -958,18 +1134,14 @@ void launch_scores_k(const tq_packed* k, int64_t n_keys, const half8_t* fr, int6
 
 int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
                        const tq_packed* v, int64_t n_streams, int64_t T, int64_t stride, int G, const void* q,
-                       int q_dtype, float zscale, void* frags, float* parts, int n_chunks, int tc,
-                       const AppendArgs* app, hipStream_t s)
+                       int q_dtype, float zscale, float* parts, int n_chunks, int tc, hipStream_t s)
 {
     constexpr int D = 128;
     const bool qjl = qk->qjl_m != 0;
     if (n_streams * n_chunks >= (int64_t)1 << 31)
         return fail(TQ_ERR_UNSUPPORTED, "tq_decode_attn: %lld streams x %d chunks is more work items than 2^31",
                     (long long)n_streams, n_chunks);
-    AppendDev ad{};
-    if (app) ad = AppendDev{*qk, *qv, *k, *v, app->k_new, app->v_new, app->dtype, stride, app->pos};
-    launch_qprep_frag(qk, q, q_dtype, n_streams, G, n_streams * G, (half8_t*)frags, app ? &ad : nullptr, s);
-    const half8_t* fr = (const half8_t*)frags;
+    const QueryIn fr{q, q_dtype == TQ_F16 ? 1 : 0};
     switch (qk->mse_bits) {
         case 1: qjl ? launch_bv<D, 1, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
                     : launch_bv<D, 1, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
@@ -998,7 +1170,7 @@ int launch_scores_mfma(const tq_quantizer* q, const tq_packed* k, int64_t n_keys
 {
     constexpr int D = 128;
     const int64_t n_qt = (n_q + 7) / 8;
-    launch_qprep_frag(q, queries, q_dtype, n_qt, 8, n_q, (half8_t*)frags, nullptr, s);
+    launch_qprep_frag(q, queries, q_dtype, n_qt, 8, n_q, (half8_t*)frags, s);
     const half8_t* fr = (const half8_t*)frags;
     const bool qjl = q->qjl_m != 0;
     switch (q->mse_bits) {

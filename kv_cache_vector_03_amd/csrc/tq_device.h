@@ -114,15 +114,24 @@ __device__ __forceinline__ void row_pair(float v, float& even, float& odd)
     }
 }
 
+// max of two floats that are never NaN, without the compiler's NaN quieting
+// of each operand (two extra instructions per fmaxf on cross-lane values)
+__device__ __forceinline__ float max2nn(float a, float b)
+{
+    float d;
+    asm("v_max_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+}
+
 // max over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four rows of 16 lanes), on
-// permlane swaps instead of LDS round trips
+// permlane swaps instead of LDS round trips; never-NaN values
 __device__ __forceinline__ float rows_max(float v)
 {
     float e, o;
     row_pair<16>(v, e, o);
-    v = fmaxf(e, o);
+    v = max2nn(e, o);
     row_pair<32>(v, e, o);
-    return fmaxf(e, o);
+    return max2nn(e, o);
 }
 
 // Value held by lane l ^ M (M = 1, 2, 4, 8) by DPP moves within 16-lane rows:

@@ -358,9 +358,22 @@ DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int
     p.mfma = qk->d == 128 && G <= 8 && !wide;
     if (p.mfma) {
         // spread the n_streams * T tokens over at most kDecodeSlots equal chunks
-        // (multiples of 128 tokens: four waves of 32-token steps)
+        // (multiples of 128 tokens: four waves of 32-token steps). With more
+        // streams than slots, the chunks per stream (up to 8) that fill whole
+        // rounds of slots best: 640 streams take 4 (2560 blocks, 5 full rounds)
+        // rather than 1 (640 blocks, the second round a quarter full).
         int64_t per = kDecodeSlots / n_streams;
-        if (per < 1) per = 1;
+        if (per < 1) {
+            double best = 0;
+            for (int64_t c = 1; c <= 8; ++c) {
+                const int64_t rounds = (n_streams * c + kDecodeSlots - 1) / kDecodeSlots;
+                const double cost = (double)rounds / (double)c;
+                if (c == 1 || cost < best - 1e-9) {
+                    best = cost;
+                    per = c;
+                }
+            }
+        }
         int64_t tc = (T + per - 1) / per;
         tc = (tc + 127) / 128 * 128;
         p.tc = tc;
@@ -369,12 +382,10 @@ DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int
     }
     p.n_chunks = (int)((T + p.tc - 1) / p.tc);
     const size_t nq = (size_t)n_streams * G;
-    const int ksteps = (qk->d / 32) * (qk->qjl_m ? 2 : 1);
-    // prepared queries (scalar kernels) or query fragments (MFMA kernel)
+    // prepared queries (scalar kernels; the MFMA kernel prepares its own), then partials
     p.off_qr = 0;
     p.off_p = p.mfma ? 0 : up256(nq * qk->d * 4);
-    p.off_frag = p.off_p + (p.mfma ? 0 : up256(nq * (qk->qjl_m ? qk->qjl_m : 1) * 4));
-    p.off_parts = p.off_frag + (p.mfma ? up256((size_t)n_streams * ksteps * 64 * 16) : 0);
+    p.off_parts = p.off_p + (p.mfma ? 0 : up256(nq * (qk->qjl_m ? qk->qjl_m : 1) * 4));
     p.total = p.off_parts + up256((size_t)n_streams * p.n_chunks * G * part_stride(qk->d) * 4);
     return p;
 }

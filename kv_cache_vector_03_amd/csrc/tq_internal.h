@@ -37,7 +37,7 @@ struct DecodePlan {
     bool mfma;          // MFMA kernel (d = 128, G <= 8, mfma_decode_widths); else a scalar kernel
     int64_t tc;         // tokens per block
     int n_chunks;       // blocks per stream
-    size_t off_qr, off_p, off_frag, off_parts, total;
+    size_t off_qr, off_p, off_parts, total;
 };
 // Key and value code widths the MFMA decode kernel takes (d = 128, G <= 8):
 // values of 1..4 bits with keys of 1..4 bits, values of 3, 4 or 8 bits with
@@ -85,8 +85,7 @@ int launch_scores_mfma(const tq_quantizer* q, const tq_packed* k, int64_t n_keys
                        int q_dtype, int64_t n_q, float* scores, void* frags, hipStream_t s);
 int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
                        const tq_packed* v, int64_t n_streams, int64_t T, int64_t stride, int G, const void* q,
-                       int q_dtype, float zscale, void* frags, float* parts, int n_chunks, int tc,
-                       const AppendArgs* app, hipStream_t s);
+                       int q_dtype, float zscale, float* parts, int n_chunks, int tc, hipStream_t s);
 
 // scalar kernels with run-time code widths 1..8 (tq_wide.hip): quantize and
 // dequantize for widths 5..8 (and shapes the tuned kernels do not take), scores
