@@ -68,6 +68,38 @@ def build_product(jobs: int = 8) -> str:
     return LIB
 
 
+# Host-only sanitizer build: the C++ host code (argument validation, plans,
+# codebook solver) with AddressSanitizer and UBSan, linked with the ordinary
+# kernel objects of build_product; the kernels themselves are not instrumented.
+SAN_LIB = os.path.join(BUILD, "san", "libtq_san.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-g"]
+HOST_SOURCES = [s for s in SOURCES if s.endswith(".cpp")]
+
+
+def build_sanitized() -> str:
+    """_build/san/libtq_san.so: host objects with SAN_FLAGS (g++), kernel
+    objects as built by build_product (run that first). Loaded instead of
+    libtq.so when TQ_SANITIZE=1; see tests/sanitize_cpu_suite.sh."""
+    sdir = os.path.join(BUILD, "san")
+    os.makedirs(sdir, exist_ok=True)
+    objs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(sdir, src + ".o")
+        _run(["g++", *HOST_FLAGS, *SAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    for src in SOURCES:
+        if src.endswith(".hip"):
+            obj = os.path.join(BUILD, src + ".o")
+            if not os.path.exists(obj):
+                raise RuntimeError(f"{obj} is missing: run build_product first")
+            objs.append(obj)
+    tmp = SAN_LIB + ".tmp"
+    _run(["g++", "-shared", *SAN_FLAGS, *objs, "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib",
+          "-o", tmp])
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 def build_synth() -> str:
     src = os.path.join(ROOT, "synth", "gen.hip")
     tmp = SYNTH_LIB + ".tmp"
@@ -87,6 +119,11 @@ def build_all() -> None:
 
 
 if __name__ == "__main__":
-    build_all()
-    print(LIB)
-    print(SYNTH_LIB)
+    if "--sanitize" in sys.argv[1:]:
+        if not os.path.exists(LIB):
+            build_product()
+        print(build_sanitized())
+    else:
+        build_all()
+        print(LIB)
+        print(SYNTH_LIB)

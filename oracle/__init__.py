@@ -19,16 +19,21 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "tqref.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# TQ_SANITIZE=1: a separate build with AddressSanitizer and UBSan
+_SAN = os.environ.get("TQ_SANITIZE") == "1"
+_LIB = (os.path.join(os.path.dirname(_HERE), "_build", "san", "liboracle_san.so") if _SAN
+        else os.path.join(_HERE, "liboracle.so"))
 _lib = None
 
 CFLAGS = ["-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
-          "-std=gnu11", "-Wall"]
+          "-std=gnu11", "-Wall"] + (["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-g"]
+                                    if _SAN else [])
 
 
 def build(force: bool = False) -> str:
     """Compile ``tqref.c`` into ``liboracle.so`` (gcc, no fast-math)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        os.makedirs(os.path.dirname(_LIB), exist_ok=True)
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
