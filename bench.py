@@ -127,6 +127,11 @@ def main():
         for r in range(args.replicas):
             units.append(dict(layers=list(range(layers)), ns=layers * H))
     t_gen = time.time()
+    # one packed buffer pair for the whole step (batches are slices of it), so that
+    # every layer's cache can also be attended in a single call
+    n_all = sum(u["ns"] for u in units) * T
+    PK_all, PV_all = tq.Packed.empty(qk, n_all, dev), tq.Packed.empty(qv, n_all, dev)
+    off = 0
     for u in units:
         nvec = u["ns"] * T
         u["K"] = torch.empty((nvec, d), dtype=torch.float16, device=dev)
@@ -138,8 +143,8 @@ def main():
                 W.kv_layer_device(cfg, l, role, buf[li * per:(li + 1) * per], sc)
         q = np.stack([W.kv_queries_host(cfg, l) for l in u["layers"]]).reshape(u["ns"], G, d)
         u["Q"] = torch.from_numpy(np.ascontiguousarray(q)).to(dev)
-        u["PK"] = tq.Packed.empty(qk, nvec, dev)
-        u["PV"] = tq.Packed.empty(qv, nvec, dev)
+        u["PK"], u["PV"] = PK_all.slice(off, off + nvec), PV_all.slice(off, off + nvec)
+        off += nvec
         u["out"] = torch.empty((u["ns"], G, d), dtype=torch.float32, device=dev)
     max_ns = max(u["ns"] for u in units)
     ws = tq.workspace(tq.tq_workspace_size(tq.TQ_OP_DECODE_ATTN, qk, max_ns, T, G), dev)
@@ -238,6 +243,9 @@ def main():
             result["sweep_quantize"] = sweep_quantize(tq, dev)
         if args.workload == "128k":
             result["prefill_scores"] = prefill_scores(tq, qk, units[0]["PK"], T, dev)
+            result["decode_all_layers_one_call"] = decode_one_call(
+                tq, qk, qv, PK_all, PV_all, units, T, G, d, kern["decode_attn"]["us_per_launch"], kb + vb, dev)
+            result["workload_8k"] = workload_8k(tq, dev, steps=max(3, args.steps // 2), warmup=2)
 
     if not args.no_cpu_baseline:
         nb = args.cpu_batches or (5 if args.workload == "128k" else 8)
@@ -273,10 +281,143 @@ def cpu_baseline(cfg, diag_k, S, diag_v, kb, vb, units, n_batches):
         alg += n * (2 * d + kb) + n * (2 * d + vb) + n * (kb + vb) + ns * G * d * 6
         toks += n
         del K, V, pk, pv
-    return {"value": round(alg / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(),
+    cores = oracle.max_threads()
+    # the same on one core: the first stream of the first batch
+    u = units[0]
+    K = u["K"][:T].cpu().numpy().astype("float64")
+    V = u["V"][:T].cpu().numpy().astype("float64")
+    Q = u["Q"][:1].cpu().numpy().astype("float64")
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        pk = oracle.quantize(qko, K)
+        pv = oracle.quantize(qvo, V)
+        oracle.decode_attn(qko, qvo, pk, pv, 1, T, G, Q)
+        dt1 = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(cores)
+    alg1 = T * (2 * d + kb) + T * (2 * d + vb) + T * (kb + vb) + G * d * 6
+    return {"value": round(alg / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{n_batches} batches of the step ({toks} tokens in all): quantize K and V, decode "
-                      f"with {G} query heads per stream; {dt:.1f} s of oracle time"}
+                      f"with {G} query heads per stream; {dt:.1f} s of oracle time",
+            "value_1core": round(alg1 / dt1 / 1e9, 5),
+            "sample_1core": f"one stream ({T} tokens) of the first batch, the same three steps, on one "
+                            f"thread; {dt1:.1f} s"}
+
+
+def timed_us(fn, passes, stream):
+    """Mean microseconds per call of fn over `passes` calls (after one untimed call)."""
+    import torch
+    fn()
+    ev = []
+    for _ in range(passes):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e3
+
+
+def decode_one_call(tq, qk, qv, PK_all, PV_all, units, T, G, d, layer_us, tok_bytes, dev, passes=3):
+    """Every layer's cache attended in one call (all layers x KV heads streams
+    over the step's single packed buffer pair), beside the per-layer calls."""
+    import torch
+    ns = sum(u["ns"] for u in units)
+    Q = torch.cat([u["Q"] for u in units])
+    out = torch.empty((ns, G, d), dtype=torch.float32, device=dev)
+    ws = tq.workspace(tq.tq_workspace_size(tq.TQ_OP_DECODE_ATTN, qk, ns, T, G), dev)
+    us = timed_us(lambda: tq.tq_decode_attn(qk, qv, PK_all, PV_all, ns, T, G, Q, out, ws=ws), passes,
+                  torch.cuda.current_stream())
+    alg = ns * T * tok_bytes + ns * G * d * 6
+    return {"streams": ns, "us_per_launch": round(us, 1), "GB_per_s": round(alg / (us * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "per_layer_calls_us": round(layer_us * len(units), 1)}
+
+
+def workload_8k(tq, dev, steps=10, warmup=2, replicas=5):
+    """The Qwen2.5-3B-shaped 8K workload (36 layers x 2 KV heads x 8192 tokens,
+    K 2+1 QJL, V 3-bit): quantize K and V of the whole model per call, decode
+    all 72 streams in one call (the model's KV for one decode step), and decode
+    one layer per call (2 streams, 36 calls); `replicas` copies of the cache
+    rotate so consecutive calls do not hit in cache. us per launch, GB/s of
+    algorithmic bytes, fraction of 8 TB/s, and counter traffic when profiles/
+    holds it for the current sources."""
+    import numpy as np
+    import torch
+    import synth
+    from synth import gpu as sgpu
+    from synth import workloads as W
+    cfg = W.CONFIG3
+    d, T, G, H, L = cfg.d, cfg.tokens, cfg.G, cfg.kv_heads, cfg.layers
+    diag_k, S, diag_v = W.quantizer_inputs(d)
+    qk = tq.Quantizer(d, cfg.k_mse_bits, d, diag_k, S, dev)
+    qv = tq.Quantizer(d, cfg.v_bits, 0, diag_v, None, dev)
+    ns, per = L * H, H * T
+    n = ns * T
+    reps = []
+    for r in range(replicas):
+        u = {"K": torch.empty((n, d), dtype=torch.float16, device=dev),
+             "V": torch.empty((n, d), dtype=torch.float16, device=dev)}
+        for l in range(L):
+            for role, buf in ((synth.ROLE_DATA_K, u["K"]), (synth.ROLE_DATA_V, u["V"])):
+                sc = sgpu.scales_to_device(W.kv_seed_scales(cfg, l, role), dev)
+                W.kv_layer_device(cfg, l, role, buf[l * per:(l + 1) * per], sc)
+        q = np.stack([W.kv_queries_host(cfg, l) for l in range(L)]).reshape(ns, G, d)
+        u["Q"] = torch.from_numpy(np.ascontiguousarray(q)).to(dev)
+        u["PK"], u["PV"] = tq.Packed.empty(qk, n, dev), tq.Packed.empty(qv, n, dev)
+        u["out"] = torch.empty((ns, G, d), dtype=torch.float32, device=dev)
+        reps.append(u)
+    ws = tq.workspace(tq.tq_workspace_size(tq.TQ_OP_DECODE_ATTN, qk, ns, T, G), dev)
+    stream = torch.cuda.current_stream()
+    kb = packed_bytes_per_vector(d, cfg.k_mse_bits, True)
+    vb = packed_bytes_per_vector(d, cfg.v_bits, False)
+    ops = {
+        "quantize_k": (lambda u: tq.tq_quantize(qk, u["K"], u["PK"]), n * (2 * d + kb)),
+        "quantize_v": (lambda u: tq.tq_quantize(qv, u["V"], u["PV"]), n * (2 * d + vb)),
+        "decode_attn": (lambda u: tq.tq_decode_attn(qk, qv, u["PK"], u["PV"], ns, T, G, u["Q"], u["out"], ws=ws),
+                        n * (kb + vb) + ns * G * d * 6),
+    }
+    for u in reps:
+        for o in ops:
+            ops[o][0](u)
+    torch.cuda.synchronize()
+    res = {"workload": cfg.name, "layers": L, "kv_heads": H, "tokens": T, "G": G,
+           "k_bits": f"{cfg.k_mse_bits}+1qjl", "v_bits": cfg.v_bits, "replicas": replicas}
+    for o, (fn, alg) in ops.items():
+        ev = []
+        for i in range(warmup + steps * replicas):
+            u = reps[i % replicas]
+            if i < warmup:
+                fn(u)
+                continue
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn(u)
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        us = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e3
+        gbs = alg / (us * 1e-6) / 1e9
+        res[o] = {"us_per_launch": round(us, 2), "alg_bytes_per_launch": alg, "GB_per_s": round(gbs, 1),
+                  "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(o, alg, "8k")}
+    # one layer per call: streams 2 l, 2 l + 1 of a replica's buffers
+    outs = torch.empty((H, G, d), dtype=torch.float32, device=dev)
+
+    def layer_calls(u):
+        for l in range(L):
+            tq.tq_decode_attn(qk, qv, u["PK"].slice(l * per, (l + 1) * per), u["PV"].slice(l * per, (l + 1) * per),
+                              H, T, G, u["Q"][l * H:(l + 1) * H], outs, ws=ws)
+    us = timed_us(lambda: layer_calls(reps[0]), max(3, steps), stream) / L
+    alg = per * (kb + vb) + H * G * d * 6
+    res["decode_attn_per_layer"] = {"calls_per_step": L, "us_per_launch": round(us, 2),
+                                    "GB_per_s": round(alg / (us * 1e-6) / 1e9, 1),
+                                    "frac_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del reps
+    torch.cuda.empty_cache()
+    return res
 
 
 def small_keyset(tq, qk, dev, reps=50):
@@ -392,11 +533,18 @@ def wide_widths(tq, qv, u, T, G, d, diag_k, S, diag_v, dev, passes=3):
     return res
 
 
-def sweep_quantize(tq, dev, n=1 << 20, passes=3):
+def sweep_quantize(tq, dev, n=1 << 20, passes=3, n_pairs=4096):
     """Quantize throughput of the sweep workload: 2^20 unit-norm fp32 vectors
     (normalised N(0, I)) for d in {64, 128, 256} and total widths 2..4, with
     the QJL sketch (width - 1 code bits) and without; us per launch and
-    algorithmic GB/s (fp32 input read, packed output written)."""
+    algorithmic GB/s (fp32 input read, packed output written). From the same
+    GPU-packed vectors: the distortion per coordinate of the code stage
+    (mean (x - x_hat)^2 over all coordinates, x_hat dequantized without the
+    sketch term), and the score bias over n_pairs (key, query) pairs of unit
+    vectors, est = tq_scores: signed mean(est - exact) and the shrinkage
+    1 - sum(est exact) / sum(exact^2) with its delta-method standard error
+    ("MSE-Only vs QJL" section of the benchmark page; its printed distortion
+    is 0.000270 at d = 128, b = 3 and 0.000135 at d = 256)."""
     import torch
     import synth
     from synth import gpu as sgpu
@@ -408,7 +556,12 @@ def sweep_quantize(tq, dev, n=1 << 20, passes=3):
         g = torch.empty((n, d), dtype=torch.float32, device=dev)
         sgpu.fill_f32(g, 61, synth.ROLE_DATA_K)
         x = g / torch.linalg.vector_norm(g, dim=1, keepdim=True)
+        sgpu.fill_f32(g[:n_pairs], 62, synth.ROLE_PAIR_Q)
+        qp = (g[:n_pairs] / torch.linalg.vector_norm(g[:n_pairs], dim=1, keepdim=True)).contiguous()
         del g
+        exact = (x[:n_pairs].double() * qp.double()).sum(dim=1)
+        xhat = torch.empty((n, d), dtype=torch.float32, device=dev)
+        sc = torch.empty((n_pairs, n_pairs), dtype=torch.float32, device=dev)
         for bits in (2, 3, 4):
             for qjl in (False, True):
                 mse = bits - 1 if qjl else bits
@@ -425,10 +578,21 @@ def sweep_quantize(tq, dev, n=1 << 20, passes=3):
                 torch.cuda.synchronize()
                 us = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e3
                 alg = n * (4 * d + packed_bytes_per_vector(d, mse, qjl))
+                tq.tq_dequantize(q, p, n, False, xhat)
+                dist = float(((x - xhat).double() ** 2).mean())
+                tq.tq_scores(q, p, n_pairs, qp, sc)
+                est = torch.diagonal(sc).double()
+                s2 = float((exact * exact).sum())
+                b = float((est * exact).sum()) / s2
+                resid = exact * (est - b * exact)
                 res[f"d{d}_b{bits}_{'qjl' if qjl else 'mse'}"] = {
                     "us_per_launch": round(us, 2), "GB_per_s": round(alg / (us * 1e-6) / 1e9, 1),
-                    "frac_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        del x
+                    "frac_hbm_peak": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "code_bits": mse, "distortion_per_coord": float(f"{dist:.4g}"),
+                    "bias_signed": float(f"{float((est - exact).mean()):.3g}"),
+                    "bias_mult": round(1.0 - b, 5),
+                    "bias_mult_se": float(f"{float(torch.sqrt((resid * resid).sum())) / s2:.2g}")}
+        del x, xhat, sc
     return res
 
 
@@ -481,10 +645,26 @@ def unfused_baseline(tq, qk, qv, units, T, G, d, fused_us, dev, passes=3, n_unit
     tq.tq_decode_attn(qk, qv, u["PK"], u["PV"], ns, T, G, u["Q"], fused)
     torch.cuda.synchronize()
     diff = float((ref - fused).abs().max())
+    # the unfused design's floor at the rate a plain device copy reaches here:
+    # packed K and V read, fp16 K and V written, then read by the attention
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    copy_us = timed_us(lambda: dst.copy_(src), 5, stream)
+    del src, dst
+    copy_gbs = 2 * nbytes / (copy_us * 1e-6) / 1e9
+    kb = packed_bytes_per_vector(d, qk.mse_bits, qk.qjl_m > 0)
+    vb = packed_bytes_per_vector(d, qv.mse_bits, False)
+    unfused_bytes = n * (kb + vb) + 2 * (2 * n * d * 2)
+    floor_us = unfused_bytes / (copy_gbs * 1e9) * 1e6
     return {"us_per_launch": round(dq + at, 2), "dequantize_us": round(dq, 2), "dense_attention_us": round(at, 2),
             "fused_decode_attn_us": fused_us, "fused_speedup": round((dq + at) / fused_us, 2),
+            "unfused_floor_us": round(floor_us, 1), "copy_GB_per_s": round(copy_gbs, 1),
+            "fused_speedup_vs_floor": round(floor_us / fused_us, 2),
             "max_abs_diff_vs_fused": round(diff, 5),
-            "note": "dequantize to fp16 + torch fp16 attention on the same packed caches"}
+            "note": ("dequantize to fp16 + torch fp16 attention on the same packed caches; the floor is "
+                     "that design's bytes (packed read, fp16 K and V written and read back) at the "
+                     "measured device-copy rate")}
 
 
 def prefill_scores(tq, qk, pk, T, dev, n_q=2048, reps=5):
