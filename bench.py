@@ -485,7 +485,7 @@ def decode_step(tq, qk, qv, units, T, G, d, attn_us, tok_bytes, dev, passes=3):
     alg = ns * T * tok_bytes + ns * G * d * 6 + ns * 2 * d * 2
     return {"us_per_launch": round(us, 2), "decode_attn_us_per_launch": attn_us,
             "append_overhead_us": round(us - attn_us, 2), "GB_per_s": round(alg / (us * 1e-6) / 1e9, 1),
-            "note": "append of one new token per stream fused into the decode launch"}
+            "note": "append of one new token per stream (its own launch), then the decode launches"}
 
 
 def wide_widths(tq, qv, u, T, G, d, diag_k, S, diag_v, dev, passes=3):
