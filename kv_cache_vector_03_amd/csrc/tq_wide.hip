@@ -518,6 +518,19 @@ void decode_wide_d(const tq_quantizer* qk, const tq_quantizer* qv, const tq_pack
                    float zscale, float* parts, int n_chunks, hipStream_t s)
 {
     const size_t lds = ((size_t)(qk->qjl_m ? 2 : 1) * G * D + (size_t)G * kTC) * sizeof(float);
+    // allow each instance the dynamic LDS of the largest G (d = 256 with the sketch and
+    // G = 16 needs 48 KiB beside 65 KiB of static LDS)
+    static bool sized[2] = {false, false};
+    if (!sized[qk->qjl_m ? 1 : 0]) {
+        const int most = (int)(((qk->qjl_m ? 2 : 1) * kMaxG * D + kMaxG * kTC) * sizeof(float));
+        if (qk->qjl_m)
+            (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_decode_wide<D, true>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, most);
+        else
+            (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_decode_wide<D, false>),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, most);
+        sized[qk->qjl_m ? 1 : 0] = true;
+    }
     // grid.y is limited to 65535: streams go in launches of at most that many
     for (int64_t s0 = 0; s0 < n_streams; s0 += 65535) {
         const int64_t ns = n_streams - s0 < 65535 ? n_streams - s0 : 65535;

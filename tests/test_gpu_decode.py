@@ -62,8 +62,12 @@ SMALL = [
     (64, 2, 3, 3, 600, 8, True),
     (256, 2, 4, 2, 300, 5, True),
     (256, 1, 1, 1, 260, 2, True),
-    # more (stream, chunk) items than resident blocks: blocks loop over items
+    # the scalar kernel's largest LDS footprint: d = 256, sketch keys, G = 16
+    (256, 2, 4, 2, 300, 16, True),
+    # more streams than the 512 block slots: several chunks per stream chosen to fill
+    # whole rounds of blocks
     (128, 2, 4, 600, 130, 8, True),
+    (128, 2, 4, 640, 600, 8, True),
     # one long stream split into many chunks
     (128, 2, 3, 1, 70000, 8, True),
 ]
