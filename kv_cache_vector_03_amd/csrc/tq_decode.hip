@@ -12,8 +12,10 @@
 // halves of the 16 output columns (query side) or rows (weight side), so the
 // products are exact and only the fp32 accumulation rounds.
 //
-// Work split: a block owns a chunk of one stream's tokens, each of its four
-// waves a contiguous quarter, processed 32 tokens at a time:
+// Work split: a block owns a chunk of one stream's tokens (one block per
+// chunk), each of its four waves a contiguous quarter, processed 32 tokens at
+// a time, after the block has prepared its stream's queries (rotation, S q'
+// on MFMA, score fragments) and its lookup tables:
 //   scores  16 tokens x 16 columns (8 heads x hi/lo) per MFMA tile, K = 256
 //           (128 code slots + 128 sign slots, in group-major order);
 //   softmax exact max per 32-token block; the running max moves (and the
