@@ -414,15 +414,21 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
     // packed codes, so an address is that byte next to the lane's copy byte (one
     // v_perm). The rows also hold the value table of other widths (first half),
     // and, after the scan, the merge buffers (rebuilt for a further item).
-    constexpr bool PV = BV == 4, PK = BK == 2, ROWS = PV || PK;
+    // 3-bit values (V12): one table of 4096 entries indexed by two codes of each
+    // of a token pair (6 bits each), giving the B-operand words of two value
+    // tiles per lookup; the key table is then the plain one.
+    constexpr bool V12 = BV == 3;
+    constexpr bool PV = BV == 4, PK = BK == 2 && !V12, ROWS = PV || PK;
     __shared__ __align__(16) uint32_t rows[ROWS ? 256 : 1][64];
     __shared__ uint2 klut4[K4 && !PK ? KLUT : 1];
     __shared__ uint32_t klut2[K4 ? 1 : KLUT];
     __shared__ uint4 slut[QJL ? 256 : 1];
-    __shared__ uint32_t vlut[ROWS ? 1 : VLUT][32];  // one copy per bank: lane l reads copy l % 32
+    __shared__ uint32_t vlut[ROWS || V12 ? 1 : VLUT][32];  // one copy per bank: lane l reads copy l % 32
+    __shared__ __align__(16) uint2 vlut12[V12 ? 4096 : 1];
     __shared__ float mrg_m[4][8], mrg_l[4][8], mrg_f[4][8], mrg_x[8];
-    __shared__ __align__(16) float mrg_own[ROWS ? 1 : 4][8][D];
-    float(*const mrg_o)[8][D] = ROWS ? reinterpret_cast<float(*)[8][D]>(&rows[0][0]) : mrg_own;
+    __shared__ __align__(16) float mrg_own[ROWS || V12 ? 1 : 4][8][D];
+    float(*const mrg_o)[8][D] = ROWS ? reinterpret_cast<float(*)[8][D]>(&rows[0][0])
+                                     : (V12 ? reinterpret_cast<float(*)[8][D]>(&vlut12[0]) : mrg_own);
     const char* const rowsb = reinterpret_cast<const char*>(&rows[0][0]);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -576,11 +582,20 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
         fill_key_luts_lds<BK, QJL>(klut4, klut2, slut, cb16[0], !PK);
     } else {
         fill_key_luts_lds<BK, QJL>(klut4, klut2, slut, cb16[0], true);
-        // value table: entry e in all 32 copies; a wave writes 8 entries' 128-byte
-        // rows per instruction
-        for (int i = tid; i < VLUT * 8; i += 256) {
-            const uint32_t v = ventry(i >> 3);
-            reinterpret_cast<uint4*>(&vlut[i >> 3][0])[i & 7] = make_uint4(v, v, v, v);
+        if constexpr (V12) {
+            // entry aa | bb << 6: (codes aa & 7, bb & 7) for the even tile, (aa >> 3, bb >> 3) for the odd one
+            for (int i = tid; i < 4096; i += 256) {
+                const int aa = i & 63, bb = i >> 6;
+                vlut12[i] = make_uint2((uint32_t)cb16[1][aa & 7] | ((uint32_t)cb16[1][bb & 7] << 16),
+                                       (uint32_t)cb16[1][aa >> 3] | ((uint32_t)cb16[1][bb >> 3] << 16));
+            }
+        } else {
+            // value table: entry e in all 32 copies; a wave writes 8 entries' 128-byte
+            // rows per instruction
+            for (int i = tid; i < VLUT * 8; i += 256) {
+                const uint32_t v = ventry(i >> 3);
+                reinterpret_cast<uint4*>(&vlut[i >> 3][0])[i & 7] = make_uint4(v, v, v, v);
+            }
         }
     }
     if constexpr (QJL) {
@@ -782,15 +797,21 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                     acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, bw), acc[c], 0, 0, 0);
                 }
             } else if constexpr (BV == 3) {
+                // tiles 2 cp and 2 cp + 1 from one lookup: codes 2 cp, 2 cp + 1 of each token
+                // of pair j are bits 6 cp .. 6 cp + 5 of its field
 #pragma unroll
-                for (int c = 0; c < CT; ++c) {
-                    uint32_t bw[4];
+                for (int cp = 0; cp < CT / 2; ++cp) {
+                    uint32_t be[4], bo[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const uint32_t ia = (X[2 * j] >> (3 * c)) & 7u, ib = (X[2 * j + 1] >> (3 * c)) & 7u;
-                        bw[j] = vl(ia | (ib << 3));
+                        const uint32_t aa = (X[2 * j] >> (6 * cp)) & 63u, bb = (X[2 * j + 1] >> (6 * cp)) & 63u;
+                        const uint2 e = vlut12[aa | (bb << 6)];
+                        be[j] = e.x;
+                        bo[j] = e.y;
                     }
-                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, bw), acc[c], 0, 0, 0);
+                    acc[2 * cp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, be), acc[2 * cp], 0, 0, 0);
+                    acc[2 * cp + 1] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, bo), acc[2 * cp + 1], 0, 0, 0);
                 }
             } else {
                 // interleave the two tokens' fields: slot k of y0 (2*BV bits) is the index for
@@ -887,7 +908,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
         // ---- per-wave results: sum over the tile pair and the row groups, hi rows +
         // lo rows (permlane swaps)
         lsum += xor8(lsum);
-        if constexpr (ROWS) lds_barrier();  // every wave is done with the tables the merge rows overwrite
+        if constexpr (ROWS || V12) lds_barrier();  // every wave is done with the tables the merge buffers overwrite
         {
             float e_, o_;
             row_pair<16>(lsum, e_, o_);
