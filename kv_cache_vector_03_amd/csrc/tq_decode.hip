@@ -424,11 +424,15 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
     __shared__ uint32_t klut2[K4 ? 1 : KLUT];
     __shared__ uint4 slut[QJL ? 256 : 1];
     __shared__ uint32_t vlut[ROWS || V12 ? 1 : VLUT][32];  // one copy per bank: lane l reads copy l % 32
-    __shared__ __align__(16) uint2 vlut12[V12 ? 4096 : 1];
+    // even-tile words at [i], odd-tile words at [kV12Odd + i]: 16388 bytes apart, a
+    // distance no paired LDS read spans, so each lands in its operand's register
+    constexpr int kV12Odd = 4097;
+    __shared__ __align__(16) uint32_t vlut12[V12 ? 2 * kV12Odd : 1];
     __shared__ float mrg_m[4][8], mrg_l[4][8], mrg_f[4][8], mrg_x[8];
     __shared__ __align__(16) float mrg_own[ROWS || V12 ? 1 : 4][8][D];
     float(*const mrg_o)[8][D] = ROWS ? reinterpret_cast<float(*)[8][D]>(&rows[0][0])
                                      : (V12 ? reinterpret_cast<float(*)[8][D]>(&vlut12[0]) : mrg_own);
+    static_assert(!V12 || 2 * kV12Odd * 4 >= 4 * 8 * D * 4, "the merge buffers fit in the 3-bit value table");
     const char* const rowsb = reinterpret_cast<const char*>(&rows[0][0]);
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -511,11 +515,13 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
     // fp16 parts of a pair of fp32 values for this lane's column half: fp16(x) for
     // col < 8, fp16(x - fp16(x)) for col >= 8; both are fp16(x + negsel fp16(x))
     const float negsel = col >= 8 ? -1.0f : 0.0f;
+    // (each mixlo leaves its high half to the mixhi that follows, so it is an
+    // output-only operand and needs no initial value)
     auto split2 = [&](float x0, float x1) -> uint32_t {
-        uint32_t hw = 0, ow = 0;
-        asm("v_fma_mixlo_f16 %0, %1, 1.0, 0" : "+v"(hw) : "v"(x0));
+        uint32_t hw, ow;
+        asm("v_fma_mixlo_f16 %0, %1, 1.0, 0" : "=v"(hw) : "v"(x0));
         asm("v_fma_mixhi_f16 %0, %1, 1.0, 0" : "+v"(hw) : "v"(x1));
-        asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "+v"(ow) : "v"(hw), "v"(negsel), "v"(x0));
+        asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(ow) : "v"(hw), "v"(negsel), "v"(x0));
         asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(ow) : "v"(hw), "v"(negsel), "v"(x1));
         return ow;
     };
@@ -586,8 +592,8 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
             // entry aa | bb << 6: (codes aa & 7, bb & 7) for the even tile, (aa >> 3, bb >> 3) for the odd one
             for (int i = tid; i < 4096; i += 256) {
                 const int aa = i & 63, bb = i >> 6;
-                vlut12[i] = make_uint2((uint32_t)cb16[1][aa & 7] | ((uint32_t)cb16[1][bb & 7] << 16),
-                                       (uint32_t)cb16[1][aa >> 3] | ((uint32_t)cb16[1][bb >> 3] << 16));
+                vlut12[i] = (uint32_t)cb16[1][aa & 7] | ((uint32_t)cb16[1][bb & 7] << 16);
+                vlut12[kV12Odd + i] = (uint32_t)cb16[1][aa >> 3] | ((uint32_t)cb16[1][bb >> 3] << 16);
             }
         } else {
             // value table: entry e in all 32 copies; a wave writes 8 entries' 128-byte
@@ -805,9 +811,9 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const uint32_t aa = (X[2 * j] >> (6 * cp)) & 63u, bb = (X[2 * j + 1] >> (6 * cp)) & 63u;
-                        const uint2 e = vlut12[aa | (bb << 6)];
-                        be[j] = e.x;
-                        bo[j] = e.y;
+                        const uint32_t ix = aa | (bb << 6);
+                        be[j] = vlut12[ix];
+                        bo[j] = vlut12[kV12Odd + ix];
                     }
                     acc[2 * cp] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, __builtin_bit_cast(half8_t, be), acc[2 * cp], 0, 0, 0);
                     acc[2 * cp + 1] =

@@ -441,8 +441,8 @@ __device__ __forceinline__ void code_batch(const float4_t (&acc)[2][4], float ss
             for (int j = 0; j < 4; ++j) {
                 const float r0 = y[2 * j][r], r1 = y[2 * j + 1][r];
                 hw[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
-                uint32_t l = 0;
-                asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "+v"(l) : "v"(hw[j]), "v"(r0));
+                uint32_t l;  // the mixhi below writes the high half
+                asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(l) : "v"(hw[j]), "v"(r0));
                 asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
                     : "+v"(l) : "v"(hw[j]), "v"(r1));
                 lw[j] = l;
