@@ -156,21 +156,24 @@ def main():
     events = {o: [] for o in ops}
 
     def step(record):
-        def timed(op, fn):
+        # each op's launches of the step back to back between two events (one pair
+        # per op and step, so the events add nothing between launches): every
+        # layer's K, then every layer's V, then one decode call per batch
+        def group(op, fn):
             if record:
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
-                fn()
+                for u in units:
+                    fn(u)
                 b.record(stream)
                 events[op].append((a, b))
             else:
-                fn()
-        for u in units:
-            timed("quantize_k", lambda: tq.tq_quantize(qk, u["K"], u["PK"]))
-            timed("quantize_v", lambda: tq.tq_quantize(qv, u["V"], u["PV"]))
-        for u in units:
-            timed("decode_attn", lambda: tq.tq_decode_attn(qk, qv, u["PK"], u["PV"], u["ns"], T, G, u["Q"],
-                                                          u["out"], ws=ws))
+                for u in units:
+                    fn(u)
+        group("quantize_k", lambda u: tq.tq_quantize(qk, u["K"], u["PK"]))
+        group("quantize_v", lambda u: tq.tq_quantize(qv, u["V"], u["PV"]))
+        group("decode_attn", lambda u: tq.tq_decode_attn(qk, qv, u["PK"], u["PV"], u["ns"], T, G, u["Q"],
+                                                        u["out"], ws=ws))
 
     for _ in range(args.warmup):
         step(False)
@@ -193,10 +196,10 @@ def main():
         per_launch["decode_attn"] = nvec * (kb + vb) + u["ns"] * G * d * (2 + 4)
     units_per_launch = {"quantize_k": units[0]["ns"] * T, "quantize_v": units[0]["ns"] * T,
                         "decode_attn": units[0]["ns"] * T}
-    launches = {o: len(events[o]) for o in ops}
+    launches = {o: len(events[o]) * len(units) for o in ops}
     kern = {}
     for o in ops:
-        ms = [a.elapsed_time(b) for a, b in events[o]]
+        ms = [a.elapsed_time(b) / len(units) for a, b in events[o]]
         avg_s = float(np.mean(ms)) * 1e-3
         gbs = per_launch[o] / avg_s / 1e9
         kern[o] = {"us_per_launch": round(avg_s * 1e6, 2), "alg_bytes_per_launch": per_launch[o],
@@ -387,19 +390,19 @@ def workload_8k(tq, dev, steps=10, warmup=2, replicas=5):
     res = {"workload": cfg.name, "layers": L, "kv_heads": H, "tokens": T, "G": G,
            "k_bits": f"{cfg.k_mse_bits}+1qjl", "v_bits": cfg.v_bits, "replicas": replicas}
     for o, (fn, alg) in ops.items():
+        for i in range(warmup):
+            fn(reps[i % replicas])
+        # one event pair per pass over the replicas
         ev = []
-        for i in range(warmup + steps * replicas):
-            u = reps[i % replicas]
-            if i < warmup:
-                fn(u)
-                continue
+        for _ in range(steps):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            fn(u)
+            for u in reps:
+                fn(u)
             b.record(stream)
             ev.append((a, b))
         torch.cuda.synchronize()
-        us = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e3
+        us = sum(a.elapsed_time(b) for a, b in ev) / (len(ev) * replicas) * 1e3
         gbs = alg / (us * 1e-6) / 1e9
         res[o] = {"us_per_launch": round(us, 2), "alg_bytes_per_launch": alg, "GB_per_s": round(gbs, 1),
                   "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic_for(o, alg, "8k")}
