@@ -134,6 +134,17 @@ __device__ __forceinline__ float rows_max(float v)
     return max2nn(e, o);
 }
 
+// sum over lanes l, l ^ 16, l ^ 32, l ^ 48, on permlane swaps; every lane adds
+// the same two values in the same order, so all four get the same sum
+__device__ __forceinline__ float rows_sum(float v)
+{
+    float e, o;
+    row_pair<16>(v, e, o);
+    v = e + o;
+    row_pair<32>(v, e, o);
+    return e + o;
+}
+
 // Value held by lane l ^ M (M = 1, 2, 4, 8) by DPP moves within 16-lane rows:
 // quad permutations for 1 and 2, quad reversal (l ^ 3) then half-row mirror
 // (l ^ 7) for 4, a rotation by 8 within the row for 8.

@@ -37,6 +37,10 @@ namespace tq {
 namespace {
 
 constexpr int kD = 128;
+// keys below this count take the short-input kernel: the two-group kernel
+// needs a few rounds per block (256 vectors each, one block per compute unit)
+// before its alternating phases pay off
+constexpr int64_t kKeysShort = 131072;
 constexpr float kResUnit = 1024.0f;  // residual scale for the projection operands
 
 // S row feeding row c of m-tile nu. The projection lands in lane (v, c / 4),
@@ -408,8 +412,7 @@ __device__ __forceinline__ void code_batch(const float4_t (&acc)[2][4], float ss
         for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[2 * a + tau][r] = acc[tau][a][r];
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
+    ss = rows_sum(ss);
     // hardware square root (within an ulp of fp32); the stored value is fp16
     nrm = __builtin_amdgcn_sqrtf(ss);
     const float sr = nrm * sqrt_d;  // sqrt(d) ||x||
@@ -428,8 +431,7 @@ __device__ __forceinline__ void code_batch(const float4_t (&acc)[2][4], float ss
     else codes_compare<B, QJL>(y, Ms, cc.Cq, cc.ctab, sc, W, g2, pre, none);
     gam = 0.f;
     if constexpr (QJL) {
-        g2 += __shfl_xor(g2, 16);
-        g2 += __shfl_xor(g2, 32);
+        g2 = rows_sum(g2);
         gam = __builtin_amdgcn_sqrtf(g2) * (1.0f / kResUnit);
         // hi rounds toward zero; lo is the remainder r - hi (exact in fp32, hi
         // taken straight from its fp16 half) rounded once to fp16, written
@@ -533,12 +535,182 @@ __global__ __launch_bounds__(256) void k_quantize_values_m128(const uint16_t* __
     }
 }
 
-// Keys (codes + QJL sketch). A wave codes two 16-vector batches, then projects
-// both residuals against S in one pass in which each S fragment read from LDS
-// (A-fragment order) feeds four MFMAs (both batches, hi and lo). The next pair
-// of batches is fetched while the current pair is processed.
+// Phase boundary of the keys kernel: a block barrier that the compiler may not
+// move any instruction across, so each phase's work stays between its barriers.
+__device__ __forceinline__ void phase_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Keys (codes + QJL sketch). A wave works through pairs of 16-vector batches
+// in two alternating phases: coding (vector ALU only: norms, codes, residual
+// norm and the residual's fp16 hi + lo operands) and matrix (the rotation of
+// its next pair and the projection of the coded pair against S, each S
+// fragment read from LDS feeding four MFMAs: both batches, hi and lo). A
+// 512-thread block places waves w and w + 4 on one SIMD; waves 4..7 run one
+// phase behind waves 0..3 and a block barrier closes every phase, so the two
+// waves of a SIMD are always in opposite phases and one's vector work issues
+// while the other's matrix products run. Round k of block b covers vectors
+// 256 (k G + b) .. + 255 (G blocks), wave w the 32 from 32 (8 (k G + b) + w);
+// every wave of a block runs the same number of rounds (rows past the end are
+// computed from clamped loads and not stored), so the barriers pair up.
 template <int B>
-__global__ __launch_bounds__(256) void k_quantize_keys_m128(const uint16_t* __restrict__ x, int64_t n,
+__global__ __launch_bounds__(512) void k_quantize_keys_m128(const uint16_t* __restrict__ x, int64_t n,
+                                                            const float* __restrict__ cent,
+                                                            const float* __restrict__ bnd,
+                                                            const uint32_t* __restrict__ diag,
+                                                            const uint16_t* __restrict__ S,
+                                                            uint32_t* __restrict__ codes,
+                                                            uint32_t* __restrict__ signs,
+                                                            uint16_t* __restrict__ norm,
+                                                            uint16_t* __restrict__ rnorm)
+{
+    constexpr int NT = 8, KS = 4;  // projection m-tiles (m = 128) and k-steps
+    __shared__ __align__(16) half8_t sfrag[KS * NT * 64];  // 32 KiB
+    __shared__ uint2 lut[lut_entries<B>()];
+    __shared__ float ctab[1 << B];
+    __shared__ float tbl[B > 4 ? 1 << B : 1];
+    __shared__ int lut_bad;
+    // the rotation's constants (RotConsts) per lane, read from LDS where the
+    // rotation runs instead of held in registers through the loop
+    __shared__ __align__(16) half8_t rot_a[4][64];
+    __shared__ __align__(16) uint4 rot_m[4][4];
+
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+    const bool late = wid >= 4;
+    const int v = lane & 15, q = lane >> 4;
+    CodeConsts<B> cc;
+    build_tables<B>(cc, cent, bnd, kResUnit, ctab, lut, &lut_bad, tbl);
+    // A fragments: lane (row c, k-block kb) of fragment (ks, nu), element e
+    // holds S[proj_row(nu, c)][4 kb + ks + 16 e]
+    for (int e = threadIdx.x; e < KS * NT * 64; e += blockDim.x) {
+        const int ks = e / (NT * 64), nu = (e / 64) % NT, ln = e & 63;
+        const int kb = ln >> 4, c = ln & 15;
+        const uint16_t* row = S + (int64_t)m128_proj_row(nu, c) * kD;
+        half8_t f;
+#pragma unroll
+        for (int ee = 0; ee < 8; ++ee) f[ee] = __builtin_bit_cast(_Float16, row[4 * kb + ks + 16 * ee]);
+        sfrag[(ks * NT + nu) * 64 + ln] = f;
+    }
+    if (wid == 0) {
+        RotConsts rc;
+        rot_consts(rc, diag, v, q);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) rot_a[t][lane] = rc.hA[t >> 1][t & 1];
+        if (v == 0)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) rot_m[q][a] = make_uint4(rc.dm[a][0], rc.dm[a][1], rc.dm[a][2], rc.dm[a][3]);
+    }
+    __syncthreads();
+    auto rotate_pair = [&](const uint4(&ia)[4], const uint4(&ib)[4], float4_t(&aa)[2][4], float4_t(&ab)[2][4],
+                           float& sa, float& sb) {
+        RotConsts rc;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) rc.hA[t >> 1][t & 1] = rot_a[t][lane];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const uint4 m = rot_m[q][a];
+            rc.dm[a][0] = m.x;
+            rc.dm[a][1] = m.y;
+            rc.dm[a][2] = m.z;
+            rc.dm[a][3] = m.w;
+        }
+        rotate_batch(ia, rc, aa, sa);
+        rotate_batch(ib, rc, ab, sb);
+    };
+
+    const int64_t G = gridDim.x;
+    const int64_t first = (int64_t)blockIdx.x * 256;
+    if (first >= n) return;  // the whole block: no barrier is left waiting
+    const int64_t rounds = (n - first + G * 256 - 1) / (G * 256);
+    auto pair_base = [&](int64_t k) { return ((k * G + blockIdx.x) * 8 + wid) * 32; };
+
+    uint4 inA[4], inB[4];
+    float4_t accA[2][4], accB[2][4];
+    float ssA, ssB;
+    load_clamped(inA, x, pair_base(0) + v, n, q);
+    load_clamped(inB, x, pair_base(0) + 16 + v, n, q);
+    rotate_pair(inA, inB, accA, accB, ssA, ssB);
+    if (rounds > 1) {
+        load_clamped(inA, x, pair_base(1) + v, n, q);
+        load_clamped(inB, x, pair_base(1) + 16 + v, n, q);
+    }
+    if (late) phase_barrier();
+    for (int64_t k = 0; k < rounds; ++k) {
+        const int64_t base = pair_base(k), baseB = base + 16;
+        // coding phase
+        half8_t hiA[KS], loA[KS], hiB[KS], loB[KS];
+        {
+            float nrm, gam;
+            uint32_t W[B];
+            code_batch<B, true>(accA, ssA, cc, W, nrm, gam, hiA, loA);
+            store_coded<B, true>(W, nrm, gam, base + v, n, q, codes, norm, rnorm);
+            code_batch<B, true>(accB, ssB, cc, W, nrm, gam, hiB, loB);
+            store_coded<B, true>(W, nrm, gam, baseB + v, n, q, codes, norm, rnorm);
+        }
+        phase_barrier();
+        // matrix phase: project this pair, then rotate the next and fetch the
+        // one after (the operands of one step are dead before the next's live)
+        // m-tiles from the top so the sign bits enter the words from bit 31 down.
+        // Step i = 4 (3 - pt) + ks multiplies the fragments of m-tiles 2 pt and
+        // 2 pt + 1 at k-step ks; each step's fragments are read from LDS two
+        // steps ahead of their products.
+        uint32_t swA = 0, swB = 0;
+        constexpr int NS = KS * NT / 2;
+        half8_t fr[NS][2];
+        auto fetch = [&](int i) {
+            const int pt = NT / 2 - 1 - i / KS, ks = i % KS;
+            fr[i][0] = sfrag[(ks * NT + 2 * pt) * 64 + lane];
+            fr[i][1] = sfrag[(ks * NT + 2 * pt + 1) * 64 + lane];
+        };
+        fetch(0);
+        fetch(1);
+        float4_t pA0, pA1, pB0, pB1;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            if (i + 2 < NS) fetch(i + 2);
+            __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+            const int ks = i % KS;
+            if (ks == 0) pA0 = pA1 = pB0 = pB1 = float4_t{0.f, 0.f, 0.f, 0.f};
+            const half8_t s0 = fr[i][0], s1 = fr[i][1];
+            pA0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(s0, hiA[ks], pA0, 0, 0, 0);
+            pA1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(s1, hiA[ks], pA1, 0, 0, 0);
+            pB0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(s0, hiB[ks], pB0, 0, 0, 0);
+            pB1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(s1, hiB[ks], pB1, 0, 0, 0);
+            pA0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(s0, loA[ks], pA0, 0, 0, 0);
+            pA1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(s1, loA[ks], pA1, 0, 0, 0);
+            pB0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(s0, loB[ks], pB0, 0, 0, 0);
+            pB1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(s1, loB[ks], pB1, 0, 0, 0);
+            if (ks == KS - 1) {
+                swA = shift_signs(shift_signs(swA, pA1), pA0);
+                swB = shift_signs(shift_signs(swB, pB1), pB0);
+                asm volatile("" : "+v"(swA), "+v"(swB));  // take the sign bits now, freeing the products
+            }
+        }
+        if (base + v < n) __builtin_nontemporal_store(swA, signs + (base + v) * 4 + q);
+        if (baseB + v < n) __builtin_nontemporal_store(swB, signs + (baseB + v) * 4 + q);
+        if (k + 1 < rounds) {
+            rotate_pair(inA, inB, accA, accB, ssA, ssB);
+            if (k + 2 < rounds) {
+                load_clamped(inA, x, pair_base(k + 2) + v, n, q);
+                load_clamped(inB, x, pair_base(k + 2) + 16 + v, n, q);
+            }
+        }
+        phase_barrier();
+    }
+    if (!late) phase_barrier();
+}
+
+// Keys for inputs too short to give every block of the kernel above several
+// rounds: 256-thread blocks, each wave coding two 16-vector batches, then
+// projecting both residuals against S in one pass in which each S fragment
+// read from LDS feeds four MFMAs (both batches, hi and lo). The next pair of
+// batches is fetched while the current pair is processed.
+template <int B>
+__global__ __launch_bounds__(256) void k_quantize_keys_m128_short(const uint16_t* __restrict__ x, int64_t n,
                                                             const float* __restrict__ cent,
                                                             const float* __restrict__ bnd,
                                                             const uint32_t* __restrict__ diag,
@@ -627,10 +799,15 @@ __global__ __launch_bounds__(256) void k_quantize_keys_m128(const uint16_t* __re
 template <int B>
 void launch_b(const tq_quantizer* q, const uint16_t* x, int64_t n, const tq_packed* o, hipStream_t s)
 {
-    if (q->qjl_m != 0) {
-        auto kern = k_quantize_keys_m128<B>;
+    if (q->qjl_m != 0 && n < kKeysShort) {
+        auto kern = k_quantize_keys_m128_short<B>;
         const int grid = resident_grid(kern, 64, n);
         hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, x, n, q->centroids, q->boundaries, q->diag_signs,
+                           q->S, o->codes, o->signs, o->norm, o->rnorm);
+    } else if (q->qjl_m != 0) {
+        auto kern = k_quantize_keys_m128<B>;
+        const int grid = resident_grid(kern, 256, n, 512);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(512), 0, s, x, n, q->centroids, q->boundaries, q->diag_signs,
                            q->S, o->codes, o->signs, o->norm, o->rnorm);
     } else {
         auto kern = k_quantize_values_m128<B>;
