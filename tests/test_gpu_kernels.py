@@ -75,12 +75,15 @@ def test_quantize_ragged_counts(d, bits, m, n):
 @pytest.mark.parametrize("d,bits,m,n", [(128, 2, 128, 3 * 256 * 64 + 4 * 64 + 37), (128, 3, 128, 3 * 256 * 64 + 4 * 64 + 37),
                                          (128, 4, 0, 3 * 256 * 64 + 4 * 64 + 37), (256, 3, 256, 3 * 256 * 64 + 4 * 64 + 37),
                                          (256, 4, 0, 3 * 256 * 64 + 4 * 64 + 37),
-                                         (128, 2, 128, 3 * 256 * 256 + 4 * 64 + 37), (128, 3, 128, 3 * 256 * 256 + 4 * 64 + 37)])
+                                         (128, 2, 128, 3 * 256 * 256 + 4 * 64 + 37), (128, 3, 128, 3 * 256 * 256 + 4 * 64 + 37),
+                                         (128, 5, 128, 3 * 256 * 256 + 4 * 64 + 37), (128, 8, 128, 2 * 256 * 256 + 37)])
 def test_quantize_many_rounds_full(d, bits, m, n):
     """Enough fp16 vectors that every resident block loops over several rounds
     of batches (and a ragged last round); every output is checked. The second
     size is past the short-input limit of the d = 128 keys kernels (131072),
-    so the two-group keys kernel runs four rounds per block."""
+    so the two-group keys kernel runs three or four rounds per block, with
+    sign-bit codes (2 bits), the lookup grid (3 bits) and the fine grid (5 and
+    8 bits)."""
     qg, qo = quantizers(d, bits, m)
     x = synth.to_f16(synth.normals(23, synth.ROLE_DATA_K, np.arange(n * d)).reshape(n, d) * 2.0)
     check_quantize(qo, x.astype(np.float64), gpu_quantize(qg, x).to_host())
