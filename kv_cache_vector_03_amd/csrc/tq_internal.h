@@ -59,6 +59,9 @@ int device_cus();
 // kernel launchers (tq_*.hip); each returns TQ_OK or TQ_ERR_DEVICE
 void launch_quantize_m128(const tq_quantizer* q, const void* x, int64_t n, const tq_packed* out,
                           hipStream_t s);
+// d = 256 values (MSE codes, widths 1..4, fp16 or fp32 input) on MFMA
+void launch_quantize_values_d256(const tq_quantizer* q, const void* x, int dtype, int64_t n,
+                                 const tq_packed* out, hipStream_t s);
 int launch_quantize(const tq_quantizer* q, const void* x, int dtype, int64_t n,
                     const tq_packed* out, hipStream_t s);
 int launch_qprep(const tq_quantizer* q, const void* queries, int dtype, int64_t nq,

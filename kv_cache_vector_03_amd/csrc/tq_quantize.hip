@@ -22,8 +22,10 @@
 // matrix S (the A operand, rows permuted) so that each lane receives the sign
 // bits of one word (d = 128) or half-word (d = 64) of its own vector's stream.
 //
-// d = 256: one wave per vector at a time (coordinate 64 r + lane), 16 vectors
-// per block pass, the residual projection on MFMA with S held in registers.
+// d = 256 keys: one wave per vector at a time (coordinate 64 r + lane), 16
+// vectors per block pass, the residual projection on MFMA with S held in
+// registers. d = 256 values (codes only) take the MFMA rotation kernel in
+// tq_quantize_m128.hip.
 //
 // Dequantize: d = 128 takes 16 vectors per wave pass with the sketch term
 // S^T s on MFMA; d = 64 and 256 take one wave per vector.
@@ -405,7 +407,7 @@ __global__ __launch_bounds__(256) void k_quantize_quad(const void* __restrict__ 
 
 // ---------------------------------------------------------------- d = 256 kernel
 
-// d = 256. A wave takes two vectors per pass, one at a time, with coordinate
+// d = 256 keys. A wave takes two vectors per pass, one at a time, with coordinate
 // 64 r + lane in slot r (the rotation is fwht256); a 512-thread block takes
 // 16 vectors per pass, and each vector of the next pass is loaded as soon as
 // its slot is free. In that layout lane l holds members t = 2 r + [l >= 32] of
@@ -941,7 +943,9 @@ void quantize_d_b(const tq_quantizer* q, const void* x, int dtype, int64_t n, co
         }
     } else {
         static_assert(D == 256, "d = 256 kernel");
-        if (dtype == TQ_F16) {
+        if constexpr (!QJL) {
+            launch_quantize_values_d256(q, x, dtype, n, o, s);
+        } else if (dtype == TQ_F16) {
             auto kern = k_quantize_d256<B, QJL, true>;
             hipLaunchKernelGGL(kern, dim3(resident_grid(kern, kD256Pass, n, 64 * kD256Waves)), dim3(64 * kD256Waves), 0, s, x, n, q->centroids,
                                q->boundaries, q->diag_signs, q->S, o->codes, o->signs, o->norm, o->rnorm);

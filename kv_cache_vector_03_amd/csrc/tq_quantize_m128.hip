@@ -796,6 +796,172 @@ __global__ __launch_bounds__(256) void k_quantize_keys_m128_short(const uint16_t
     }
 }
 
+// Values (MSE codes only) for d = 256 on MFMA, fp16 or fp32 input.
+// H_256 = H_8 (x) H_32 over the coordinate bits (i = 32 a + rho): a wave takes
+// 16 vectors at a time, lane (v, q) holding coordinates 32 a' + 8 q .. + 7 of
+// vector v for each input chunk a' = 0..7 (the B operand of a 16x16x32 MFMA).
+// The A operand of chunk a' and slab tau is the negated H_32 slab (rows
+// 16 tau + rho) with the random diagonal's signs of chunk a' folded into its
+// columns, read from LDS, so acc[tau][a'] register r holds
+// -(H_32 D x)[16 tau + 4 q + r] of chunk a'. H_8 across a' then runs as
+// butterflies in registers: output chunk a gives coordinate
+// 32 a + 16 tau + 4 q + r, i.e. group n = 16 tau + 4 q + r and member a of the
+// group-major layout (groups of stride 32), so lane (v, q) holds groups
+// 4 q .. 4 q + 3 (tau = 0) and 16 + 4 q .. (tau = 1) complete and codes them as
+// the d = 128 kernels do (Z = -Y, s = sqrt(d) ||x||). fp32 input is scaled by
+// a power of two that brings the norm into [1/2, 1) and split into fp16 hi and
+// lo operands (two passes; the remainder left over is below 2^-22 of the
+// norm); fp16 input is exact as it is.
+template <int B, bool F16>
+__global__ __launch_bounds__(256) void k_quantize_values_d256(const void* __restrict__ x, int64_t n,
+                                                              const float* __restrict__ cent,
+                                                              const float* __restrict__ bnd,
+                                                              const uint32_t* __restrict__ diag,
+                                                              uint32_t* __restrict__ codes,
+                                                              uint16_t* __restrict__ norm)
+{
+    constexpr int D = 256, NA = 8, CW = B * D / 32;  // input chunks, code words per vector
+    __shared__ uint2 lut[lut_entries<B>()];
+    __shared__ float ctab[1 << B];
+    __shared__ float tbl[1];
+    __shared__ int lut_bad;
+    __shared__ __align__(16) half8_t slab[2][NA][64];  // A operands [tau][a'][lane]
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int v = lane & 15, q = lane >> 4;
+    CodeConsts<B> cc;
+    build_tables<B>(cc, cent, bnd, 1.0f, ctab, lut, &lut_bad, tbl);
+    // lane (row rho, k-block kb) of slab (tau, a'), element e: column c = 8 kb + e,
+    // -H_32[16 tau + rho][c] times the diagonal sign of coordinate 32 a' + c
+    for (int i = threadIdx.x; i < 2 * NA * 64; i += blockDim.x) {
+        const int tau = i / (NA * 64), ap = (i / 64) % NA, ln = i & 63;
+        const int rho = ln & 15, kb = ln >> 4;
+        const uint32_t dw = diag[ap];
+        half8_t h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = 8 * kb + e;
+            const bool neg = ((__builtin_popcount((16 * tau + rho) & c) & 1) != 0) != (((dw >> c) & 1u) != 0);
+            h[e] = neg ? (_Float16)1.0f : (_Float16)-1.0f;
+        }
+        slab[tau][ap][ln] = h;
+    }
+    __syncthreads();
+
+    constexpr float sqrt_d = 16.0f;
+    const int64_t step = (int64_t)gridDim.x * 64;  // vectors between a wave's batches
+    int64_t base = ((int64_t)blockIdx.x * 4 + wid) * 16;
+    if (base >= n) return;
+    // one batch's input for lane (v, q): chunk a' holds coordinates 32 a' + 8 q .. + 7;
+    // rows past the end repeat the last row (not stored)
+    typedef float f8_t __attribute__((ext_vector_type(8)));
+    uint4 in16[F16 ? NA : 1];
+    f8_t in32[F16 ? 1 : NA];
+    auto load = [&](int64_t b0) {
+        const int64_t vec = b0 + v < n ? b0 + v : n - 1;
+#pragma unroll
+        for (int ap = 0; ap < NA; ++ap) {
+            if constexpr (F16) in16[ap] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + vec * D + 32 * ap + 8 * q);
+            else in32[ap] = *reinterpret_cast<const f8_t*>(static_cast<const float*>(x) + vec * D + 32 * ap + 8 * q);
+        }
+    };
+    load(base);
+    for (; base < n; base += step) {
+        // norm (the lane's 64 coordinates, then the four lanes of the vector)
+        float ss = 0.f;
+#pragma unroll
+        for (int ap = 0; ap < NA; ++ap) {
+            if constexpr (F16) {
+                const uint32_t w4[4] = {in16[ap].x, in16[ap].y, in16[ap].z, in16[ap].w};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const auto h2 = __builtin_bit_cast(__attribute__((ext_vector_type(2))) _Float16, w4[w]);
+                    ss = __builtin_amdgcn_fdot2(h2, h2, ss, false);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss = fmaf(in32[ap][e], in32[ap][e], ss);
+            }
+        }
+        ss = rows_sum(ss);
+        const float nrm = __builtin_amdgcn_sqrtf(ss);
+        // fp32: scale 2^-ex with nrm = m 2^ex, m in [1/2, 1) (1 for a zero vector)
+        int ex = 0;
+        if constexpr (!F16) (void)frexpf(nrm, &ex);
+        const float sc = F16 ? 1.0f : ldexpf(1.0f, -ex);
+        // H_32 of each chunk on MFMA
+        float4_t acc[2][NA];
+#pragma unroll
+        for (int ap = 0; ap < NA; ++ap) {
+            half8_t bh, bl;
+            if constexpr (F16) {
+                bh = __builtin_bit_cast(half8_t, in16[ap]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float xs = in32[ap][e] * sc;  // exact: a power of two
+                    const _Float16 h = (_Float16)xs;
+                    bh[e] = h;
+                    bl[e] = (_Float16)(xs - (float)h);  // the remainder is exact in fp32
+                }
+            }
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+                const half8_t a = slab[tau][ap][lane];
+                acc[tau][ap] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                if constexpr (!F16) acc[tau][ap] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, acc[tau][ap], 0, 0, 0);
+            }
+        }
+        load(base + step);  // the next batch, into the registers just read
+        // H_8 across the chunks: butterflies (u, w) -> (u + w, u - w) on chunk bit h
+#pragma unroll
+        for (int h = 1; h < NA; h <<= 1)
+#pragma unroll
+            for (int ap = 0; ap < NA; ++ap)
+                if (!(ap & h))
+#pragma unroll
+                    for (int tau = 0; tau < 2; ++tau) {
+                        const float4_t u = acc[tau][ap], w = acc[tau][ap + h];
+                        acc[tau][ap] = u + w;
+                        acc[tau][ap + h] = u - w;
+                    }
+        // codes of the two group sets (tau); Z and s carry the same scale
+        const float sr = nrm * sc * sqrt_d;
+        const float s_ = sr > 0.f ? sr : 1.0f;
+        float Ms[CodeConsts<B>::K > 0 ? CodeConsts<B>::K : 1];
+#pragma unroll
+        for (int j = 0; j < CodeConsts<B>::K; ++j) Ms[j] = cc.Mth[j] * s_;
+        const int64_t vec = base + v;
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            float y[8][4];
+#pragma unroll
+            for (int a = 0; a < NA; ++a)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) y[a][r] = acc[tau][a][r];
+            uint32_t W[B];
+            float g2 = 0.f;
+            auto none = [](int) {};
+            if (cc.use_lut) codes_lut<B, false>(y, cc.lut, cc.ctab, s_, (float)kLutCells / s_, 0.f, W, g2, none, none);
+            else codes_compare<B, false>(y, Ms, cc.Cq, cc.ctab, 0.f, W, g2, none, none);
+            if (vec < n) {
+                uint32_t* dst = codes + vec * CW + B * (4 * tau + q);
+                typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+                typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+                if constexpr (B == 2) {
+                    __builtin_nontemporal_store(u2v{W[0], W[1]}, reinterpret_cast<u2v*>(dst));
+                } else if constexpr (B == 4) {
+                    __builtin_nontemporal_store(u4v{W[0], W[1], W[2], W[3]}, reinterpret_cast<u4v*>(dst));
+                } else {
+#pragma unroll
+                    for (int w = 0; w < B; ++w) __builtin_nontemporal_store(W[w], dst + w);
+                }
+            }
+        }
+        if (vec < n && q == 0) __builtin_nontemporal_store(f2h(nrm), norm + vec);
+    }
+}
+
 template <int B>
 void launch_b(const tq_quantizer* q, const uint16_t* x, int64_t n, const tq_packed* o, hipStream_t s)
 {
@@ -818,6 +984,23 @@ void launch_b(const tq_quantizer* q, const uint16_t* x, int64_t n, const tq_pack
 }
 
 }  // namespace
+
+void launch_quantize_values_d256(const tq_quantizer* q, const void* x, int dtype, int64_t n, const tq_packed* out,
+                                 hipStream_t s)
+{
+    auto go = [&](auto kern) {
+        const int grid = resident_grid(kern, 64, n);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, x, n, q->centroids, q->boundaries, q->diag_signs,
+                           out->codes, out->norm);
+    };
+    const bool f16 = dtype == TQ_F16;
+    switch (q->mse_bits) {
+        case 1: f16 ? go(k_quantize_values_d256<1, true>) : go(k_quantize_values_d256<1, false>); break;
+        case 2: f16 ? go(k_quantize_values_d256<2, true>) : go(k_quantize_values_d256<2, false>); break;
+        case 3: f16 ? go(k_quantize_values_d256<3, true>) : go(k_quantize_values_d256<3, false>); break;
+        default: f16 ? go(k_quantize_values_d256<4, true>) : go(k_quantize_values_d256<4, false>); break;
+    }
+}
 
 void launch_quantize_m128(const tq_quantizer* q, const void* x, int64_t n, const tq_packed* out, hipStream_t s)
 {

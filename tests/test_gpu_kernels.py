@@ -102,6 +102,28 @@ def test_quantize_zero_and_one_hot_vectors():
     assert host[2][0] == 0   # zero vector: norm 0
 
 
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+@pytest.mark.parametrize("dtype", [np.float32, np.float16])
+def test_quantize_d256_values_norm_range(bits, dtype):
+    """d = 256 values (MSE codes): vectors whose norms span 1e-3 .. 1e4 (fp32;
+    1e-1 .. 1e3 for fp16), a zero vector and one-hot vectors, in several rounds
+    of 16-vector batches with a ragged tail. The fp32 path scales each vector
+    by a power of two before splitting it into fp16 operands."""
+    d = 256
+    qg, qo = quantizers(d, bits, 0)
+    n = 4 * 64 * 3 + 29
+    x = synth.normals(41, synth.ROLE_DATA_K, np.arange(n * d)).reshape(n, d)
+    lo, hi = (-3.0, 4.0) if dtype == np.float32 else (-1.0, 3.0)
+    x = x / np.linalg.norm(x, axis=1, keepdims=True) * (10.0 ** np.linspace(lo, hi, n))[:, None]
+    x[0] = 0.0
+    x[1] = 0.0
+    x[1, 5] = 1.0
+    x[2] = 0.0
+    x[2, 200] = -3.5
+    x = x.astype(np.float32).astype(dtype)
+    check_quantize(qo, x.astype(np.float64), gpu_quantize(qg, x).to_host())
+
+
 def test_quantize_output_untouched_beyond_n():
     tq = tqmod()
     qg, _ = quantizers(128, 2, 128)
@@ -272,7 +294,7 @@ def test_synth_gpu_twin_matches_host():
 
 @pytest.mark.parametrize("m", [0, 1])
 @pytest.mark.parametrize("d,bits,dtype", [(128, 3, np.float16), (64, 3, np.float16), (128, 3, np.float32),
-                                          (256, 3, np.float16), (128, 5, np.float16)])
+                                          (256, 3, np.float16), (256, 3, np.float32), (128, 5, np.float16)])
 def test_quantize_crowded_codebook(d, bits, dtype, m):
     """Codebooks with two boundaries closer than a kernel's lookup grid resolves
     (3 bits: 0.0075 apart near zero against cells of 1/256; 5 bits: 0.0006 apart
