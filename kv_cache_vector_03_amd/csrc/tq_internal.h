@@ -62,6 +62,9 @@ void launch_quantize_m128(const tq_quantizer* q, const void* x, int64_t n, const
 // d = 256 values (MSE codes, widths 1..4, fp16 or fp32 input) on MFMA
 void launch_quantize_values_d256(const tq_quantizer* q, const void* x, int dtype, int64_t n,
                                  const tq_packed* out, hipStream_t s);
+// d = 256 keys (MSE codes widths 1..4 plus the m = 256 sketch) on MFMA
+void launch_quantize_keys_d256(const tq_quantizer* q, const void* x, int dtype, int64_t n,
+                               const tq_packed* out, hipStream_t s);
 int launch_quantize(const tq_quantizer* q, const void* x, int dtype, int64_t n,
                     const tq_packed* out, hipStream_t s);
 int launch_qprep(const tq_quantizer* q, const void* queries, int dtype, int64_t nq,

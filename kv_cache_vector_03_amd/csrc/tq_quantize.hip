@@ -22,10 +22,8 @@
 // matrix S (the A operand, rows permuted) so that each lane receives the sign
 // bits of one word (d = 128) or half-word (d = 64) of its own vector's stream.
 //
-// d = 256 keys: one wave per vector at a time (coordinate 64 r + lane), 16
-// vectors per block pass, the residual projection on MFMA with S held in
-// registers. d = 256 values (codes only) take the MFMA rotation kernel in
-// tq_quantize_m128.hip.
+// d = 256: the MFMA rotation kernels in tq_quantize_m128.hip (values, and
+// keys with the m = 256 projection).
 //
 // Dequantize: d = 128 takes 16 vectors per wave pass with the sketch term
 // S^T s on MFMA; d = 64 and 256 take one wave per vector.
@@ -405,246 +403,6 @@ __global__ __launch_bounds__(256) void k_quantize_quad(const void* __restrict__ 
     }
 }
 
-// ---------------------------------------------------------------- d = 256 kernel
-
-// d = 256 keys. A wave takes two vectors per pass, one at a time, with coordinate
-// 64 r + lane in slot r (the rotation is fwht256); a 512-thread block takes
-// 16 vectors per pass, and each vector of the next pass is loaded as soon as
-// its slot is free. In that layout lane l holds members t = 2 r + [l >= 32] of
-// group l % 32, so one exchange with lane l ^ 32 (a permlane swap) completes
-// every group and lanes 0..31 store them. For keys each vector's residual goes to LDS as fp16
-// hi + lo parts (in units of 2^-10, so both stay normal fp16 numbers and their
-// sum carries about 22 bits) and the block projects its 16 residuals on MFMA:
-// the A operand is S (wave w keeps rows 32 w .. 32 w + 31 in registers for the
-// whole kernel), the B operand's columns are the vectors. Output register i
-// of m-tile mt in lane (v, q) = (lane % 16, lane / 16) is projection
-// j = 32 w + 16 mt + 4 q + i of vector v: bit w of sign byte 16 mt + 4 q + i.
-// fwht_wave for d = 256 (lane l, slot r = coordinate 64 r + l) with the lane
-// stages on DPP and permlane swaps instead of LDS exchanges; same stage order.
-__device__ __forceinline__ void fwht256(float (&v)[4], const uint32_t (&sm)[6])
-{
-#pragma unroll
-    for (int h = 1; h < 4; h <<= 1)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (!(r & h)) {
-                const float a = v[r], b = v[r + h];
-                v[r] = a + b;
-                v[r + h] = a - b;
-            }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = lane_bfly<1>(v[r], sm[0]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = lane_bfly<2>(v[r], sm[1]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = lane_bfly<4>(v[r], sm[2]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = lane_bfly<8>(v[r], sm[3]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = lane_bfly<16>(v[r], sm[4]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) v[r] = lane_bfly<32>(v[r], sm[5]);
-}
-
-constexpr int kD256Waves = 8, kD256Pass = 16;
-// The launch bound asks for four waves per SIMD, i.e. two blocks per compute
-// unit, so one block's barriers overlap the other's work; the keys variant
-// then spills a few registers, and still runs 10-20% faster than with one block.
-
-template <int B, bool QJL, bool F16>
-__global__ __launch_bounds__(64 * kD256Waves, 4) void k_quantize_d256(const void* __restrict__ x, int64_t n,
-                                                                   const float* __restrict__ cent,
-                                                                   const float* __restrict__ bnd,
-                                                                   const uint32_t* __restrict__ diag,
-                                                                   const uint16_t* __restrict__ S,
-                                                                   uint32_t* __restrict__ codes,
-                                                                   uint32_t* __restrict__ signs,
-                                                                   uint16_t* __restrict__ norm,
-                                                                   uint16_t* __restrict__ rnorm)
-{
-    constexpr int D = 256, R = 4, L = 1 << B, VW = kD256Pass / kD256Waves;
-    constexpr int RS = D + 8;  // fp16 elements per LDS residual row (16-byte pad)
-    constexpr int NB = QJL ? kD256Pass : 1;
-    __shared__ __align__(16) uint16_t rh[NB][RS];
-    __shared__ __align__(16) uint16_t rl[NB][RS];
-    // wave w's bit (bit w) of the 32 sign bytes of each vector
-    __shared__ __align__(16) uint32_t part[QJL ? kD256Waves : 1][NB][8];
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int hi32 = lane >> 5;
-    float t[L - 1], c[L];
-#pragma unroll
-    for (int l = 0; l < L - 1; ++l) t[l] = bnd[l];
-#pragma unroll
-    for (int l = 0; l < L; ++l) c[l] = cent[l];
-    // 3 and 4 bits: a lookup grid over y in [-1, 1] (cells of 1/256; entry:
-    // boundaries below the cell start, first boundary at or above it), used
-    // if no window of two cells holds two boundaries; else the compare chain
-    constexpr bool GRID = B >= 3;
-    constexpr int NC = 256, NE = GRID ? 2 * NC + 2 : 1;
-    __shared__ uint2 lut[NE];
-    __shared__ float ctab[L];
-    __shared__ int lut_bad;
-    if (threadIdx.x == 0) lut_bad = 0;
-    if (threadIdx.x < L) ctab[threadIdx.x] = cent[threadIdx.x];
-    __syncthreads();
-    if constexpr (GRID) {
-        for (int e = threadIdx.x; e < NE; e += blockDim.x) {
-            const float lo = ((float)(e - NC) - 0.5f) / NC;  // exact
-            const float win = lo + 2.0f / NC;
-            uint32_t base = 0;
-            int inwin = 0;
-            float next = INFINITY;
-#pragma unroll
-            for (int l = 0; l < L - 1; ++l) {
-                base += t[l] < lo ? 1u : 0u;
-                if (t[l] >= lo && t[l] < next) next = t[l];
-                inwin += (t[l] >= lo && t[l] < win) ? 1 : 0;
-            }
-            if (inwin > 1) lut_bad = 1;
-            lut[e] = make_uint2(__float_as_uint(next), base);
-        }
-    }
-    __syncthreads();
-    const bool use_grid = GRID && !lut_bad;
-    uint32_t dm[R];
-    load_diag<R>(diag, lane, dm);
-    uint32_t sm[6];
-#pragma unroll
-    for (int b = 0; b < 6; ++b) sm[b] = ((uint32_t)(lane >> b) & 1u) << 31;
-
-    half8_t sf[QJL ? 2 : 1][QJL ? 8 : 1];
-    if constexpr (QJL) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const int row = 32 * wid + 16 * mt + (lane & 15);
-                const uint4 w = *reinterpret_cast<const uint4*>(S + row * D + 32 * ks + 8 * (lane >> 4));
-                sf[mt][ks] = __builtin_bit_cast(half8_t, w);
-            }
-    }
-
-    const int64_t step = (int64_t)gridDim.x * kD256Pass;
-    // vector v's coordinates, or zeros past the end (read from the last vector
-    // and discarded, so the loads need no branch; n >= 1 at every launch)
-    auto fetch = [&](int64_t v, float (&o)[R]) {
-        const int64_t vr = v < n ? v : n - 1;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const float e = load_elem<F16>(x, vr * D + 64 * r + lane);
-            o[r] = v < n ? e : 0.f;
-        }
-    };
-    float xn[VW][R];
-#pragma unroll
-    for (int i = 0; i < VW; ++i) fetch((int64_t)blockIdx.x * kD256Pass + VW * wid + i, xn[i]);
-    for (int64_t base = (int64_t)blockIdx.x * kD256Pass; base < n; base += step) {
-#pragma unroll
-        for (int i = 0; i < VW; ++i) {
-            float y[R];
-            const int64_t v = base + VW * wid + i;
-#pragma unroll
-            for (int r = 0; r < R; ++r) y[r] = xn[i][r];
-            fetch(v + step, xn[i]);  // next pass
-            float ss = 0.f;
-#pragma unroll
-            for (int r = 0; r < R; ++r) ss += y[r] * y[r];
-            const float nrm = sqrtf(wave_sum_dpp(ss));
-#pragma unroll
-            for (int r = 0; r < R; ++r) y[r] = flip(y[r], dm[r]);
-            fwht256(y, sm);
-            const float sc = nrm > 0.f ? __builtin_amdgcn_rcpf(16.0f * nrm) : 0.f;
-            uint32_t own = 0;
-            float g2 = 0.f;
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float yy = y[r] * sc;
-                int k = 0;
-                float ck = c[0];
-                if (use_grid) {
-                    // cell index round(256 y) + 256 by the 2^23 rounding trick, clamped
-                    uint32_t bits = __float_as_uint(fmaf(yy, (float)NC, 8388608.0f + NC));
-                    bits = min(max(bits, 0x4B000000u), 0x4B000000u + (uint32_t)(NE - 1));
-                    const uint2 ent = lut[bits - 0x4B000000u];
-                    k = (int)ent.y + (yy > __uint_as_float(ent.x) ? 1 : 0);
-                    if constexpr (QJL) ck = ctab[k];
-                } else {
-                    // boundaries ascend, so the compares that pass are a prefix
-                    // and the last one names the centroid c[k]
-#pragma unroll
-                    for (int l = 0; l < L - 1; ++l) {
-                        const bool above = t[l] < yy;
-                        k += above ? 1 : 0;
-                        if constexpr (QJL) ck = above ? c[l + 1] : ck;
-                    }
-                }
-                own |= (uint32_t)k << (B * (2 * r + hi32));
-                if constexpr (QJL) {
-                    const float rr = yy - ck;
-                    g2 += rr * rr;
-                    const float s = rr * 1024.0f;
-                    const _Float16 h = (_Float16)s;
-                    const _Float16 lo = (_Float16)(s - (float)h);
-                    rh[VW * wid + i][64 * r + lane] = __builtin_bit_cast(uint16_t, h);
-                    rl[VW * wid + i][64 * r + lane] = __builtin_bit_cast(uint16_t, lo);
-                }
-            }
-            // lane l and lane l ^ 32 together hold group l % 32
-            float fe, fo;
-            row_pair<32>(__uint_as_float(own), fe, fo);
-            const uint32_t fg = __float_as_uint(fe) | __float_as_uint(fo);
-            if constexpr (QJL) g2 = wave_sum_dpp(g2);
-            if (v < n) {
-                if (lane < 32) {
-                    unsigned char* dst = reinterpret_cast<unsigned char*>(codes + v * (B * D / 32)) + B * lane;
-                    if constexpr (B == 4) *reinterpret_cast<uint32_t*>(dst) = fg;
-                    else if constexpr (B == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)fg;
-                    else
-#pragma unroll
-                        for (int b = 0; b < B; ++b) dst[b] = (unsigned char)(fg >> (8 * b));
-                }
-                if (lane == 0) {
-                    norm[v] = f2h(nrm);
-                    if constexpr (QJL) rnorm[v] = f2h(sqrtf(g2));
-                }
-            }
-        }
-        if constexpr (QJL) {
-            __syncthreads();
-            float4_t acc[2];
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
-            const int vc = lane & 15, q = lane >> 4;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const half8_t bh = *reinterpret_cast<const half8_t*>(&rh[vc][32 * ks + 8 * q]);
-                const half8_t bl = *reinterpret_cast<const half8_t*>(&rl[vc][32 * ks + 8 * q]);
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sf[mt][ks], bh, acc[mt], 0, 0, 0);
-                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sf[mt][ks], bl, acc[mt], 0, 0, 0);
-                }
-            }
-            // bytes 16 mt + 4 q .. + 3 of vector vc, each holding this wave's bit
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                uint32_t wv = 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) wv |= (acc[mt][i] >= 0.f ? 1u : 0u) << (8 * i);
-                part[wid][vc][4 * mt + q] = wv;
-            }
-            __syncthreads();
-            // thread (vector tid / 32, sign byte tid % 32)
-            const int v = threadIdx.x >> 5, cb = threadIdx.x & 31;
-            uint32_t sbyte = 0;
-#pragma unroll
-            for (int w = 0; w < kD256Waves; ++w)
-                sbyte |= (uint32_t)reinterpret_cast<const unsigned char*>(&part[w][v][0])[cb] << w;
-            if (base + v < n) reinterpret_cast<unsigned char*>(signs + (base + v) * (D / 32))[cb] = (unsigned char)sbyte;
-        }
-    }
-}
-
 // q' = H (D .* q) / sqrt(d) and p = S q' (one wave per query). Queries are
 // few, so this runs in double and stores fp32 results rounded once, which
 // keeps the rotation and projection error far below the score tolerance.
@@ -943,17 +701,8 @@ void quantize_d_b(const tq_quantizer* q, const void* x, int dtype, int64_t n, co
         }
     } else {
         static_assert(D == 256, "d = 256 kernel");
-        if constexpr (!QJL) {
-            launch_quantize_values_d256(q, x, dtype, n, o, s);
-        } else if (dtype == TQ_F16) {
-            auto kern = k_quantize_d256<B, QJL, true>;
-            hipLaunchKernelGGL(kern, dim3(resident_grid(kern, kD256Pass, n, 64 * kD256Waves)), dim3(64 * kD256Waves), 0, s, x, n, q->centroids,
-                               q->boundaries, q->diag_signs, q->S, o->codes, o->signs, o->norm, o->rnorm);
-        } else {
-            auto kern = k_quantize_d256<B, QJL, false>;
-            hipLaunchKernelGGL(kern, dim3(resident_grid(kern, kD256Pass, n, 64 * kD256Waves)), dim3(64 * kD256Waves), 0, s, x, n, q->centroids,
-                               q->boundaries, q->diag_signs, q->S, o->codes, o->signs, o->norm, o->rnorm);
-        }
+        if constexpr (QJL) launch_quantize_keys_d256(q, x, dtype, n, o, s);
+        else launch_quantize_values_d256(q, x, dtype, n, o, s);
     }
 }
 

@@ -962,6 +962,232 @@ __global__ __launch_bounds__(256) void k_quantize_values_d256(const void* __rest
     }
 }
 
+// S row feeding row c of m-tile nu in the d = 256 keys kernel (m = 256). The
+// projection lands in lane (v, c / 4), register c % 4; that lane owns sign
+// words 2 (c / 4) and 2 (c / 4) + 1 of vector v, i.e. stream bits
+// J = 64 (c / 4) + 4 nu + c % 4, and stream bit J holds the sign of row
+// J / 8 + 32 (J % 8) (groups of stride 32).
+__host__ __device__ constexpr int d256_proj_row(int nu, int c)
+{
+    return (64 * (c / 4) + 4 * nu + c % 4) / 8 + 32 * ((64 * (c / 4) + 4 * nu + c % 4) % 8);
+}
+
+// Keys (codes + QJL sketch, m = 256) for d = 256, fp16 or fp32 input. The
+// rotation and coding are the values kernel's above (k_quantize_values_d256);
+// the negated scaled residual replaces each coordinate as the codes are
+// taken, and its fp16 hi and lo parts are the projection's B operand: k-step
+// ks = 4 tau + r, element a is coordinate 32 a + 16 tau + 4 q + r, which lane
+// (v, q) holds. The A operand is S with rows and columns permuted to match
+// (fragments in LDS, 128 KiB, one block per compute unit); four m-tiles run
+// side by side so each accumulator's next MFMA is four instructions away.
+template <int B, bool F16>
+__global__ __launch_bounds__(512) void k_quantize_keys_d256(const void* __restrict__ x, int64_t n,
+                                                            const float* __restrict__ cent,
+                                                            const float* __restrict__ bnd,
+                                                            const uint32_t* __restrict__ diag,
+                                                            const uint16_t* __restrict__ S,
+                                                            uint32_t* __restrict__ codes,
+                                                            uint32_t* __restrict__ signs,
+                                                            uint16_t* __restrict__ norm,
+                                                            uint16_t* __restrict__ rnorm)
+{
+    constexpr int D = 256, NA = 8, CW = B * D / 32, NT = 16, KS = 8;
+    extern __shared__ __align__(16) half8_t dyn[];
+    half8_t* const sfrag = dyn;  // [KS][NT][64]: 128 KiB
+    __shared__ uint2 lut[lut_entries<B>()];
+    __shared__ float ctab[1 << B];
+    __shared__ float tbl[1];
+    __shared__ int lut_bad;
+    __shared__ __align__(16) half8_t slab[2][NA][64];
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int v = lane & 15, q = lane >> 4;
+    CodeConsts<B> cc;
+    build_tables<B>(cc, cent, bnd, kResUnit, ctab, lut, &lut_bad, tbl);
+    for (int i = threadIdx.x; i < 2 * NA * 64; i += blockDim.x) {
+        const int tau = i / (NA * 64), ap = (i / 64) % NA, ln = i & 63;
+        const int rho = ln & 15, kb = ln >> 4;
+        const uint32_t dw = diag[ap];
+        half8_t h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = 8 * kb + e;
+            const bool neg = ((__builtin_popcount((16 * tau + rho) & c) & 1) != 0) != (((dw >> c) & 1u) != 0);
+            h[e] = neg ? (_Float16)1.0f : (_Float16)-1.0f;
+        }
+        slab[tau][ap][ln] = h;
+    }
+    // A fragments: lane (row c, k-block kb) of fragment (ks = 4 tau + r, nu),
+    // element e holds S[d256_proj_row(nu, c)][32 e + 16 tau + 4 kb + r]
+    for (int i = threadIdx.x; i < KS * NT * 64; i += blockDim.x) {
+        const int ks = i / (NT * 64), nu = (i / 64) % NT, ln = i & 63;
+        const int c = ln & 15, kb = ln >> 4, tau = ks >> 2, r = ks & 3;
+        const uint16_t* row = S + (int64_t)d256_proj_row(nu, c) * D;
+        half8_t f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = __builtin_bit_cast(_Float16, row[32 * e + 16 * tau + 4 * kb + r]);
+        sfrag[i] = f;
+    }
+    __syncthreads();
+
+    constexpr float sqrt_d = 16.0f;
+    const int64_t step = (int64_t)gridDim.x * 128;  // vectors between a wave's batches
+    int64_t base = ((int64_t)blockIdx.x * 8 + wid) * 16;
+    if (base >= n) return;
+    typedef float f8_t __attribute__((ext_vector_type(8)));
+    uint4 in16[F16 ? NA : 1];
+    f8_t in32[F16 ? 1 : NA];
+    auto load = [&](int64_t b0) {
+        const int64_t vec = b0 + v < n ? b0 + v : n - 1;
+#pragma unroll
+        for (int ap = 0; ap < NA; ++ap) {
+            if constexpr (F16) in16[ap] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + vec * D + 32 * ap + 8 * q);
+            else in32[ap] = *reinterpret_cast<const f8_t*>(static_cast<const float*>(x) + vec * D + 32 * ap + 8 * q);
+        }
+    };
+    load(base);
+    for (; base < n; base += step) {
+        float ss = 0.f;
+#pragma unroll
+        for (int ap = 0; ap < NA; ++ap) {
+            if constexpr (F16) {
+                const uint32_t w4[4] = {in16[ap].x, in16[ap].y, in16[ap].z, in16[ap].w};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const auto h2 = __builtin_bit_cast(__attribute__((ext_vector_type(2))) _Float16, w4[w]);
+                    ss = __builtin_amdgcn_fdot2(h2, h2, ss, false);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss = fmaf(in32[ap][e], in32[ap][e], ss);
+            }
+        }
+        ss = rows_sum(ss);
+        const float nrm = __builtin_amdgcn_sqrtf(ss);
+        int ex = 0;
+        if constexpr (!F16) (void)frexpf(nrm, &ex);
+        const float scl = F16 ? 1.0f : ldexpf(1.0f, -ex);
+        float4_t acc[2][NA];
+#pragma unroll
+        for (int ap = 0; ap < NA; ++ap) {
+            half8_t bh, bl;
+            if constexpr (F16) {
+                bh = __builtin_bit_cast(half8_t, in16[ap]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float xs = in32[ap][e] * scl;
+                    const _Float16 h = (_Float16)xs;
+                    bh[e] = h;
+                    bl[e] = (_Float16)(xs - (float)h);
+                }
+            }
+#pragma unroll
+            for (int tau = 0; tau < 2; ++tau) {
+                const half8_t a = slab[tau][ap][lane];
+                acc[tau][ap] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh, float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                if constexpr (!F16) acc[tau][ap] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, acc[tau][ap], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int h = 1; h < NA; h <<= 1)
+#pragma unroll
+            for (int ap = 0; ap < NA; ++ap)
+                if (!(ap & h))
+#pragma unroll
+                    for (int tau = 0; tau < 2; ++tau) {
+                        const float4_t u = acc[tau][ap], w = acc[tau][ap + h];
+                        acc[tau][ap] = u + w;
+                        acc[tau][ap + h] = u - w;
+                    }
+        const float sr = nrm * scl * sqrt_d;
+        const float s_ = sr > 0.f ? sr : 1.0f;
+        const float sc = kResUnit * __builtin_amdgcn_rcpf(s_);
+        float Ms[CodeConsts<B>::K > 0 ? CodeConsts<B>::K : 1];
+#pragma unroll
+        for (int j = 0; j < CodeConsts<B>::K; ++j) Ms[j] = cc.Mth[j] * s_;
+        const int64_t vec = base + v;
+        float g2 = 0.f;
+        half8_t hi[KS], lo[KS];
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+            float y[8][4];
+#pragma unroll
+            for (int a = 0; a < NA; ++a)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) y[a][r] = acc[tau][a][r];
+            uint32_t W[B];
+            auto none = [](int) {};
+            if (cc.use_lut) codes_lut<B, true>(y, cc.lut, cc.ctab, s_, (float)kLutCells / s_, sc, W, g2, none, none);
+            else codes_compare<B, true>(y, Ms, cc.Cq, cc.ctab, sc, W, g2, none, none);
+            if (vec < n) {
+                uint32_t* dst = codes + vec * CW + B * (4 * tau + q);
+                typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+                typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+                if constexpr (B == 2) {
+                    __builtin_nontemporal_store(u2v{W[0], W[1]}, reinterpret_cast<u2v*>(dst));
+                } else if constexpr (B == 4) {
+                    __builtin_nontemporal_store(u4v{W[0], W[1], W[2], W[3]}, reinterpret_cast<u4v*>(dst));
+                } else {
+#pragma unroll
+                    for (int w = 0; w < B; ++w) __builtin_nontemporal_store(W[w], dst + w);
+                }
+            }
+            // the residual's fp16 parts: k-step 4 tau + r, element a; hi rounds toward
+            // zero, lo is the remainder rounded once (as in the d = 128 keys kernel)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                uint32_t hw[4], lw[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float r0 = y[2 * j][r], r1 = y[2 * j + 1][r];
+                    hw[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+                    uint32_t l;  // the mixhi below writes the high half
+                    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(l) : "v"(hw[j]), "v"(r0));
+                    asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+                        : "+v"(l) : "v"(hw[j]), "v"(r1));
+                    lw[j] = l;
+                }
+                hi[4 * tau + r] = __builtin_bit_cast(half8_t, hw);
+                lo[4 * tau + r] = __builtin_bit_cast(half8_t, lw);
+            }
+        }
+        g2 = rows_sum(g2);
+        const float gam = __builtin_amdgcn_sqrtf(g2) * (1.0f / kResUnit);
+        if (vec < n && q == 0) {
+            __builtin_nontemporal_store(f2h(nrm), norm + vec);
+            __builtin_nontemporal_store(f2h(gam), rnorm + vec);
+        }
+        load(base + step);  // the next batch, in flight during the projection
+        // projection: m-tiles from the top (sign bits enter each word from bit 31
+        // down), four at a time
+        uint32_t sw[2] = {0u, 0u};
+#pragma unroll
+        for (int g4 = NT / 4 - 1; g4 >= 0; --g4) {
+            float4_t p[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p[j] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                half8_t f[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) f[j] = sfrag[(ks * NT + 4 * g4 + j) * 64 + lane];
+#pragma unroll
+                for (int j = 3; j >= 0; --j) p[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f[j], hi[ks], p[j], 0, 0, 0);
+#pragma unroll
+                for (int j = 3; j >= 0; --j) p[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f[j], lo[ks], p[j], 0, 0, 0);
+            }
+            uint32_t& w = sw[g4 >> 1];
+#pragma unroll
+            for (int j = 3; j >= 0; --j) w = shift_signs(w, p[j]);
+        }
+        if (vec < n) {
+            typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+            __builtin_nontemporal_store(u2v{sw[0], sw[1]}, reinterpret_cast<u2v*>(signs + vec * 8 + 2 * q));
+        }
+    }
+}
+
 template <int B>
 void launch_b(const tq_quantizer* q, const uint16_t* x, int64_t n, const tq_packed* o, hipStream_t s)
 {
@@ -983,6 +1209,21 @@ void launch_b(const tq_quantizer* q, const uint16_t* x, int64_t n, const tq_pack
     }
 }
 
+template <int B, bool F16>
+void launch_keys_d256(const tq_quantizer* q, const void* x, int64_t n, const tq_packed* out, hipStream_t s)
+{
+    constexpr size_t kFrag = 8 * 16 * 64 * sizeof(half8_t);  // the S fragments, 128 KiB of dynamic LDS
+    auto kern = k_quantize_keys_d256<B, F16>;
+    // once per instance (thread-safe static initialisation): allow the dynamic
+    // LDS above the default limit
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFrag);
+    (void)attr;
+    const int grid = resident_grid(kern, 128, n, 512);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(512), kFrag, s, x, n, q->centroids, q->boundaries, q->diag_signs, q->S,
+                       out->codes, out->signs, out->norm, out->rnorm);
+}
+
 }  // namespace
 
 void launch_quantize_values_d256(const tq_quantizer* q, const void* x, int dtype, int64_t n, const tq_packed* out,
@@ -999,6 +1240,18 @@ void launch_quantize_values_d256(const tq_quantizer* q, const void* x, int dtype
         case 2: f16 ? go(k_quantize_values_d256<2, true>) : go(k_quantize_values_d256<2, false>); break;
         case 3: f16 ? go(k_quantize_values_d256<3, true>) : go(k_quantize_values_d256<3, false>); break;
         default: f16 ? go(k_quantize_values_d256<4, true>) : go(k_quantize_values_d256<4, false>); break;
+    }
+}
+
+void launch_quantize_keys_d256(const tq_quantizer* q, const void* x, int dtype, int64_t n, const tq_packed* out,
+                               hipStream_t s)
+{
+    const bool f16 = dtype == TQ_F16;
+    switch (q->mse_bits) {
+        case 1: f16 ? launch_keys_d256<1, true>(q, x, n, out, s) : launch_keys_d256<1, false>(q, x, n, out, s); break;
+        case 2: f16 ? launch_keys_d256<2, true>(q, x, n, out, s) : launch_keys_d256<2, false>(q, x, n, out, s); break;
+        case 3: f16 ? launch_keys_d256<3, true>(q, x, n, out, s) : launch_keys_d256<3, false>(q, x, n, out, s); break;
+        default: f16 ? launch_keys_d256<4, true>(q, x, n, out, s) : launch_keys_d256<4, false>(q, x, n, out, s); break;
     }
 }
 

@@ -104,13 +104,15 @@ def test_quantize_zero_and_one_hot_vectors():
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("dtype", [np.float32, np.float16])
-def test_quantize_d256_values_norm_range(bits, dtype):
-    """d = 256 values (MSE codes): vectors whose norms span 1e-3 .. 1e4 (fp32;
-    1e-1 .. 1e3 for fp16), a zero vector and one-hot vectors, in several rounds
-    of 16-vector batches with a ragged tail. The fp32 path scales each vector
-    by a power of two before splitting it into fp16 operands."""
+@pytest.mark.parametrize("m", [0, 256])
+def test_quantize_d256_norm_range(bits, dtype, m):
+    """d = 256 values (MSE codes) and keys (codes + sketch): vectors whose norms
+    span 1e-3 .. 1e4 (fp32; 1e-1 .. 1e3 for fp16), a zero vector and one-hot
+    vectors, in several rounds of 16-vector batches with a ragged tail. The
+    fp32 path scales each vector by a power of two before splitting it into
+    fp16 operands."""
     d = 256
-    qg, qo = quantizers(d, bits, 0)
+    qg, qo = quantizers(d, bits, m)
     n = 4 * 64 * 3 + 29
     x = synth.normals(41, synth.ROLE_DATA_K, np.arange(n * d)).reshape(n, d)
     lo, hi = (-3.0, 4.0) if dtype == np.float32 else (-1.0, 3.0)
