@@ -457,8 +457,10 @@ def small_keyset(tq, qk, dev, reps=50):
 def decode_step(tq, qk, qv, units, T, G, d, attn_us, tok_bytes, dev, passes=3):
     """The fused append + attend step (tq_decode_step) on the same caches: each
     stream's last token is re-quantized from its fp16 K and V into slot T - 1
-    (the append), then the attention runs over all T tokens. Reported per
-    call (one call per batch, as decode_attn), beside decode_attn alone."""
+    (the append), then the attention runs over all T tokens. Timed as
+    decode_attn is (one call per batch, every batch's calls back to back between
+    two events), in passes alternating with passes of decode_attn alone, so the
+    difference is the append's cost."""
     import torch
     apps = []
     for u in units:
@@ -468,27 +470,36 @@ def decode_step(tq, qk, qv, units, T, G, d, attn_us, tok_bytes, dev, passes=3):
     ws = tq.workspace(tq.tq_workspace_size(tq.TQ_OP_DECODE_ATTN, qk, max_ns, T, G), dev)
     stream = torch.cuda.current_stream()
 
-    def one_pass(ev):
+    def step_pass():
         for u, (kn, vn) in zip(units, apps):
-            a = b = None
-            if ev is not None:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
             tq.tq_decode_step(qk, qv, u["PK"], u["PV"], u["ns"], T - 1, T, G, kn, vn, u["Q"], u["out"], ws=ws)
-            if ev is not None:
-                b.record(stream)
-                ev.append((a, b))
-    one_pass(None)
-    ev = []
+
+    def attn_pass():
+        for u in units:
+            tq.tq_decode_attn(qk, qv, u["PK"], u["PV"], u["ns"], T, G, u["Q"], u["out"], ws=ws)
+
+    def timed(fn, ev):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        ev.append((a, b))
+
+    step_pass()
+    attn_pass()
+    ev_s, ev_a = [], []
     for _ in range(passes):
-        one_pass(ev)
+        timed(step_pass, ev_s)
+        timed(attn_pass, ev_a)
     torch.cuda.synchronize()
-    us = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e3
+    us = sum(a.elapsed_time(b) for a, b in ev_s) / (len(ev_s) * len(units)) * 1e3
+    us_a = sum(a.elapsed_time(b) for a, b in ev_a) / (len(ev_a) * len(units)) * 1e3
     ns = units[0]["ns"]
     alg = ns * T * tok_bytes + ns * G * d * 6 + ns * 2 * d * 2
-    return {"us_per_launch": round(us, 2), "decode_attn_us_per_launch": attn_us,
-            "append_overhead_us": round(us - attn_us, 2), "GB_per_s": round(alg / (us * 1e-6) / 1e9, 1),
-            "note": "append of one new token per stream (its own launch), then the decode launches"}
+    return {"us_per_launch": round(us, 2), "decode_attn_us_per_launch": round(us_a, 2),
+            "append_overhead_us": round(us - us_a, 2), "GB_per_s": round(alg / (us * 1e-6) / 1e9, 1),
+            "note": "append of one new token per stream inside the decode launch (the new token's partial "
+                    "joins the stream's combine); decode_attn timed alongside in alternating passes"}
 
 
 def wide_widths(tq, qv, u, T, G, d, diag_k, S, diag_v, dev, passes=3):

@@ -159,7 +159,8 @@ int tq_decode_step(const tq_quantizer* qk, const tq_quantizer* qv,
     if ((rc = check_dense(v_new, new_dtype, "tq_decode_step", "v_new")) != TQ_OK) return rc;
     if ((rc = check_dense(q, q_dtype, "tq_decode_step", "q")) != TQ_OK) return rc;
     if ((rc = check_dense(out, TQ_F32, "tq_decode_step", "out")) != TQ_OK) return rc;
-    const DecodePlan plan = decode_plan(qk, n_streams, T + 1, G, !mfma_decode_widths(qk->mse_bits, qv->mse_bits));
+    const DecodePlan plan =
+        decode_plan(qk, n_streams, T + 1, G, !mfma_decode_widths(qk->mse_bits, qv->mse_bits), true);
     if (!ws || ws_bytes < plan.total)
         return fail(TQ_ERR_WORKSPACE, "tq_decode_step: workspace %zu bytes < %zu", ws_bytes, plan.total);
     if ((uintptr_t)ws % 256) return fail(TQ_ERR_INVALID, "tq_decode_step: workspace must be 256-byte aligned");

@@ -156,8 +156,9 @@ int launch_decode(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packe
     float* p = (float*)((char*)ws + plan.off_p);
     float* parts = (float*)((char*)ws + plan.off_parts);
     const float zscale = scale * 1.4426950408889634f;  // scores in log2 units
-    // the decode step's append first (one block per stream and tensor)
-    if (app) {
+    // the decode step's append: inside the MFMA decode kernel, else first, as its
+    // own launch (one block per stream and tensor)
+    if (app && !plan.fused_append) {
         const dim3 ag((unsigned)n_streams, 2u);
         switch (qk->d) {
             case 64: hipLaunchKernelGGL((k_append<64>), ag, dim3(256), 0, s, *qk, *qv, *k, *v, app->k_new, app->v_new, app->dtype, stride, app->pos); break;
@@ -166,9 +167,17 @@ int launch_decode(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packe
         }
     }
     if (plan.mfma) {
-        // the MFMA kernel prepares its stream's queries itself
-        int rc = launch_decode_mfma(qk, qv, k, v, n_streams, T, stride, G, q, q_dtype, zscale, parts, plan.n_chunks,
-                                    (int)plan.tc, s);
+        // the MFMA kernel prepares its stream's queries itself; with the fused
+        // append it scans the app->pos cached tokens and adds the new one
+        AppendIn ap{};
+        int64_t Ts = T;
+        if (plan.fused_append) {
+            ap = AppendIn{app->k_new, app->v_new, app->dtype == TQ_F16 ? 1 : 0, app->pos, qv->diag_signs,
+                          qk->boundaries, qv->boundaries, k->codes, k->signs, k->norm, k->rnorm, v->codes, v->norm};
+            Ts = app->pos;
+        }
+        int rc = launch_decode_mfma(qk, qv, k, v, n_streams, Ts, stride, G, q, q_dtype, zscale, parts, plan.n_chunks,
+                                    plan.pchunks, (int)plan.tc, ap, s);
         if (rc != TQ_OK) return rc;
     } else {
         // every other shape and width pair: prepared queries and the scalar
@@ -180,9 +189,9 @@ int launch_decode(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packe
     }
     const dim3 cg((unsigned)(n_streams * G));
     switch (qk->d) {
-        case 64: hipLaunchKernelGGL((k_combine<64>), cg, dim3(256), 0, s, parts, plan.n_chunks, G, qv->diag_signs, out); break;
-        case 128: hipLaunchKernelGGL((k_combine<128>), cg, dim3(256), 0, s, parts, plan.n_chunks, G, qv->diag_signs, out); break;
-        default: hipLaunchKernelGGL((k_combine<256>), cg, dim3(256), 0, s, parts, plan.n_chunks, G, qv->diag_signs, out); break;
+        case 64: hipLaunchKernelGGL((k_combine<64>), cg, dim3(256), 0, s, parts, plan.pchunks, G, qv->diag_signs, out); break;
+        case 128: hipLaunchKernelGGL((k_combine<128>), cg, dim3(256), 0, s, parts, plan.pchunks, G, qv->diag_signs, out); break;
+        default: hipLaunchKernelGGL((k_combine<256>), cg, dim3(256), 0, s, parts, plan.pchunks, G, qv->diag_signs, out); break;
     }
     return device_status(app ? "tq_decode_step" : "tq_decode_attn");
 }

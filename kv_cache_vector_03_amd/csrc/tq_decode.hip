@@ -385,6 +385,49 @@ __device__ __forceinline__ void load_full(Step<BK, BV>& st, int64_t t0, const La
     }
 }
 
+// The decode step's new token, coded inside the decode kernel: the code of a
+// rotated unit coordinate y is the number of codebook boundaries strictly
+// below it (the 2^B - 1 sorted boundaries, the same for every lane: up to 4
+// bits a count over registers loaded once, above that a branch-free binary
+// search over the boundaries in memory).
+template <int B>
+__device__ __forceinline__ int append_code(float y, const float (&br)[B <= 4 ? (1 << B) - 1 : 1],
+                                           const float* __restrict__ bnd)
+{
+    constexpr int L = 1 << B;
+    int idx = 0;
+    if constexpr (B <= 4) {
+#pragma unroll
+        for (int j = 0; j < L - 1; ++j) idx += br[j] < y ? 1 : 0;
+    } else {
+#pragma unroll
+        for (int step = L / 2; step >= 1; step >>= 1) idx += bnd[idx + step - 1] < y ? step : 0;
+    }
+    return idx;
+}
+
+// Store one vector's codes, held by a wave as lane l: coordinates l (code c0)
+// and l + 64 (code c1), in the group-major stream: group c (coordinates
+// c + 16 t) is an 8B-bit field with code t at bit B t, stream bytes
+// B c .. B c + B - 1. Lanes c, c + 16, c + 32, c + 48 hold group c's codes;
+// their shifted codes are OR-ed together and lane c stores the field.
+template <int B>
+__device__ __forceinline__ void append_store_codes(int c0, int c1, int lane, unsigned char* __restrict__ dst)
+{
+    const int q = lane >> 4;
+    const uint64_t f = ((uint64_t)c0 << (B * q)) | ((uint64_t)c1 << (B * (4 + q)));
+    uint32_t lo = (uint32_t)f, hi = (uint32_t)(f >> 32);
+    lo |= (uint32_t)__shfl_xor((int)lo, 16);
+    hi |= (uint32_t)__shfl_xor((int)hi, 16);
+    lo |= (uint32_t)__shfl_xor((int)lo, 32);
+    hi |= (uint32_t)__shfl_xor((int)hi, 32);
+    if (lane < 16) {
+        const uint64_t g = ((uint64_t)hi << 32) | lo;
+#pragma unroll
+        for (int b = 0; b < B; ++b) dst[B * lane + b] = (unsigned char)(g >> (8 * b));
+    }
+}
+
 template <int D, int BK, bool QJL, int BV>
 __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restrict__ kcodes,
                                                      const uint32_t* __restrict__ ksigns,
@@ -397,7 +440,8 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                                                      const uint16_t* __restrict__ S,
                                                      const float* __restrict__ kcent,
                                                      const float* __restrict__ vcent, float zscale,
-                                                     float* __restrict__ parts, int n_chunks, int tc)
+                                                     float* __restrict__ parts, int n_chunks, int pchunks,
+                                                     int tc, const AppendIn ap)
 {
     static_assert(D == 128, "MFMA decode is laid out for d = 128");
     constexpr int KS = D / 32;                 // 4 code groups per lane per token
@@ -448,11 +492,37 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
 
     // the two codebooks (one global load per thread) are the first loads in
     // flight, so they can be waited for while the first item's loads are not
-    __shared__ uint16_t cb16[2][256];
+    __shared__ __align__(16) uint16_t cb16[2][256];
     const float kc_v = kcent[min(tid, (1 << BK) - 1)];  // clamped: no branch around the loads
     const float vc_v = vcent[min(tid, (1 << BV) - 1)];
 
     const int64_t item = blockIdx.x;  // one work item (stream, chunk) per block
+
+    // Decode step (ap.k_new set): the first block of each stream also quantizes
+    // the stream's new key and value into slot ap.pos (wave 0 the key, wave 1
+    // the value, as tq_quantize would) and writes the new token's partial,
+    // index n_chunks of the stream; the blocks scan the ap.pos cached tokens.
+    // Its inputs are the first loads in flight.
+    const bool appb = ap.k_new != nullptr && (uint32_t)item % (uint32_t)n_chunks == 0u;
+    const int64_t as = (int64_t)((uint32_t)item / (uint32_t)n_chunks);  // the stream (used by the append only)
+    uint32_t axw[2] = {0u, 0u};  // new row words (fp32 bits, or the word holding the fp16 value)
+    uint32_t dmv[2] = {0u, 0u};  // value rotation's sign flips
+    float kbr[BK <= 4 ? (1 << BK) - 1 : 1], vbr[BV <= 4 ? (1 << BV) - 1 : 1];
+    if (appb) {
+        if (wid < 2) {
+            const uint32_t* src = static_cast<const uint32_t*>(wid == 0 ? ap.k_new : ap.v_new);
+            const int64_t row = as * D + lane;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) axw[r] = src[ap.f16 ? (row + 64 * r) >> 1 : row + 64 * r];
+        }
+        if constexpr (BK <= 4)
+#pragma unroll
+            for (int j = 0; j < (1 << BK) - 1; ++j) kbr[j] = ap.kbound[j];
+        if constexpr (BV <= 4)
+#pragma unroll
+            for (int j = 0; j < (1 << BV) - 1; ++j) vbr[j] = ap.vbound[j];
+        load_diag<2>(ap.vdiag, lane, dmv);
+    }
 
     // the current item's geometry and first loads: the first 512 value norms of
     // each wave's range (indices clamped into it), then the first two full steps
@@ -486,7 +556,8 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
         // no branches around these loads, so that waiting for the codebooks does not
         // wait for them: indices are clamped to the range's last token, or to the
         // chunk's last one for a wave past its end
-        const int64_t lim = w1 > w0 ? w1 : c1;
+        // (a decode step on empty caches scans nothing: slot 0 is then read, and unused)
+        const int64_t lim = w1 > w0 ? w1 : (c1 > 0 ? c1 : 1);
         // the query (clamped head index, zeroed past G) and S first: they are needed first
         // (32-bit word loads for both dtypes, no branch: the fp16 pair's word)
 #pragma unroll
@@ -560,6 +631,17 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
             qs[wid + 4][64 * r + lane] = yb[r] * inv_sqrt_d;
         }
     }
+    // the new key (wave 0) or value (wave 1): n = ||x||, H D x (unnormalised)
+    float ay[2] = {0.f, 0.f}, anrm = 0.f;
+    if (appb && wid < 2) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const float v = ap.f16 ? h2f((uint16_t)(axw[r] >> (16 * (lane & 1)))) : __uint_as_float(axw[r]);
+            ay[r] = flip(v, wid == 0 ? dm[r] : dmv[r]);
+        }
+        anrm = sqrtf(wave_sum_dpp(ay[0] * ay[0] + ay[1] * ay[1]));
+        fwht_wave_dpp<2>(ay, lane);
+    }
     lds_barrier();
 
     // (2) the tables from the codebooks, and p = S q' to LDS
@@ -625,6 +707,35 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
                 if (col < 8) ps[head][16 * (2 * wid + u) + 4 * g + r] = pv;
             }
     }
+    // the new token's codes against the codebook boundaries, its fp16 centroids
+    // (ac) and, for the key, the residual r = y - c (ar) and its norm; norms and
+    // codes go to the caches
+    float ac[2] = {0.f, 0.f}, ar[2] = {0.f, 0.f}, arn = 0.f;
+    if (appb && wid < 2) {
+        const float inv = anrm > 0.f ? 1.0f / (11.313708498984761f * anrm) : 0.f;  // 1 / (sqrt(d) n)
+        const int64_t slot = as * stride + ap.pos;
+        int code[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const float yy = ay[r] * inv;
+            code[r] = wid == 0 ? append_code<BK>(yy, kbr, ap.kbound) : append_code<BV>(yy, vbr, ap.vbound);
+            ac[r] = h2f(cb16[wid][code[r]]);
+            ar[r] = yy - ac[r];
+        }
+        if (wid == 0) {
+            if constexpr (QJL) arn = sqrtf(wave_sum_dpp(ar[0] * ar[0] + ar[1] * ar[1]));
+            append_store_codes<BK>(code[0], code[1], lane,
+                                   reinterpret_cast<unsigned char*>(ap.kcodes + slot * (BK * D / 32)));
+            if (lane == 0) {
+                ap.knorm[slot] = f2h(anrm);
+                if constexpr (QJL) ap.krnorm[slot] = f2h(arn);
+            }
+        } else {
+            append_store_codes<BV>(code[0], code[1], lane,
+                                   reinterpret_cast<unsigned char*>(ap.vcodes + slot * (BV * D / 32)));
+            if (lane == 0) ap.vnorm[slot] = f2h(anrm);
+        }
+    }
     lds_barrier();
 
     // (3) the score B fragments: element e of k-steps t = 0..3 is one float4 of
@@ -645,6 +756,89 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
         }
 #pragma unroll
         for (int t = 0; t < KS; ++t) bq[KS * part + t] = __builtin_bit_cast(half8_t, w[t]);
+    }
+
+    if (appb) {
+        // The new token's sketch and partial. The codebook area is free now; it
+        // takes r (keys with the sketch: scaled by 2^10 so its fp16 lo part stays
+        // normal, the signs unchanged), the 16 sign bytes, the key's stored norms
+        // and its fp16 centroids in the order of the score A operand (coordinate
+        // 4 g + t + 16 e at [4 g + t][e]).
+        float* rr = reinterpret_cast<float*>(&cb16[0][0]);
+        uint32_t* sgw = reinterpret_cast<uint32_t*>(&cb16[0][0]) + D;
+        float* nkg = reinterpret_cast<float*>(&cb16[0][0]) + D + 4;
+        uint16_t* ckg = &cb16[0][0] + 2 * (D + 8);  // 16-byte aligned
+        if (wid == 0) {
+            if constexpr (QJL) {
+                rr[lane] = ar[0] * 1024.0f;
+                rr[lane + 64] = ar[1] * 1024.0f;
+                if (lane < 4) sgw[lane] = 0u;
+            }
+            if (lane == 0) {
+                nkg[0] = h2f(f2h(anrm));
+                nkg[1] = QJL ? h2f(f2h(arn)) : 0.f;
+            }
+            ckg[(lane & 15) * 8 + (lane >> 4)] = f2h(ac[0]);
+            ckg[(lane & 15) * 8 + 4 + (lane >> 4)] = f2h(ac[1]);
+        }
+        lds_barrier();
+        if constexpr (QJL) {
+            // S r against the rows of S this wave holds; row 16 (2 wid + u) + 4 g + r
+            // is bit 2 wid + u of sign byte 4 g + r (word g, byte r)
+            float4_t pr[2] = {float4_t{0.f, 0.f, 0.f, 0.f}, float4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float4 x0 = *reinterpret_cast<const float4*>(&rr[32 * k + 8 * g]);
+                const float4 x1 = *reinterpret_cast<const float4*>(&rr[32 * k + 8 * g + 4]);
+                const uint32_t bw[4] = {split2(x0.x, x0.y), split2(x0.z, x0.w), split2(x1.x, x1.y), split2(x1.z, x1.w)};
+                const half8_t b = __builtin_bit_cast(half8_t, bw);
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    pr[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, sA[u][k]), b, pr[u], 0, 0, 0);
+            }
+            uint32_t bits = 0u;
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float v = pr[u][r] + xor8(pr[u][r]);
+                    bits |= (v >= 0.f ? 1u : 0u) << (8 * r + 2 * wid + u);
+                }
+            if (col == 0) atomicOr(&sgw[g], bits);
+            lds_barrier();
+            if (wid == 0 && lane == 0)
+                *reinterpret_cast<uint4*>(ap.ksigns + (as * stride + ap.pos) * (D / 32)) =
+                    make_uint4(sgw[0], sgw[1], sgw[2], sgw[3]);
+        }
+        // partial of the new token (index n_chunks of the stream): its score for
+        // every head from the same score MFMAs as a cached token (row 0 of the A
+        // operands, the query fragments bq of this wave), weight sum 1 and
+        // accumulator n_v c(v) in the rotated value domain
+        float* pn = parts + ((as * pchunks + n_chunks) * G) * part_stride(D);
+        if (wid == 3) {
+            float4_t sa4 = float4_t{0.f, 0.f, 0.f, 0.f}, sq4 = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < KS; ++t) {
+                const uint4 av = col == 0 ? *reinterpret_cast<const uint4*>(&ckg[(4 * g + t) * 8]) : make_uint4(0u, 0u, 0u, 0u);
+                sa4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), bq[t], sa4, 0, 0, 0);
+                if constexpr (QJL) {
+                    const uint4 sv = col == 0 ? slut[(sgw[g] >> (8 * t)) & 0xFFu] : make_uint4(0u, 0u, 0u, 0u);
+                    sq4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, sv), bq[KS + t], sq4, 0, 0, 0);
+                }
+            }
+            // lanes 0..15 hold row 0: head col & 7's hi (col < 8) and lo parts
+            const float a = sa4[0] + xor8(sa4[0]);
+            const float fk = nkg[0] * zscale;
+            float z = fk * a;
+            if constexpr (QJL) z = fmaf(fk * (nkg[1] * kappa), sq4[0] + xor8(sq4[0]), z);
+            if (lane < G) *reinterpret_cast<float2*>(pn + lane * part_stride(D)) = make_float2(z, 1.0f);
+        } else if (wid == 1) {
+            const float nv = h2f(f2h(anrm));
+            for (int h = 0; h < G; ++h) {
+                pn[h * part_stride(D) + kPartAcc + lane] = nv * ac[0];
+                pn[h * part_stride(D) + kPartAcc + lane + 64] = nv * ac[1];
+            }
+        }
     }
 
     {
@@ -936,7 +1130,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
             mrg_m[wid][lane] = M;
             mrg_l[wid][lane] = lsum;
         }
-        float* part0 = parts + ((s * n_chunks + chunk) * G) * part_stride(D);
+        float* part0 = parts + ((s * pchunks + chunk) * G) * part_stride(D);
         lds_barrier();
 
         // ---- merge the four waves into one partial per head: the 32 factors
@@ -983,27 +1177,27 @@ struct QueryIn {
 template <int D, int BK, bool QJL, int BV>
 void launch_mfma(const tq_packed* k, const tq_packed* v, int64_t n_streams, int64_t T, int64_t stride, int G,
                  QueryIn fr, const tq_quantizer* qk, const tq_quantizer* qv, float zscale,
-                 float* parts, int n_chunks, int tc, hipStream_t s)
+                 float* parts, int n_chunks, int pchunks, int tc, const AppendIn& ap, hipStream_t s)
 {
     const int64_t n_items = n_streams * n_chunks;
     hipLaunchKernelGGL((k_decode_mfma<D, BK, QJL, BV>), dim3((unsigned)n_items), dim3(256), 0, s, k->codes, k->signs, k->norm,
                        k->rnorm, v->codes, v->norm, T, stride, G, fr.q, fr.f16, qk->diag_signs, qk->S,
-                       qk->centroids, qv->centroids, zscale, parts, n_chunks, tc);
+                       qk->centroids, qv->centroids, zscale, parts, n_chunks, pchunks, tc, ap);
 }
 
 template <int D, int BK, bool QJL>
 void launch_bv(int bv, const tq_packed* k, const tq_packed* v, int64_t ns, int64_t T, int64_t stride, int G,
                QueryIn fr,
-               const tq_quantizer* qk, const tq_quantizer* qv, float zs, float* parts, int nc, int tc,
-               hipStream_t s)
+               const tq_quantizer* qk, const tq_quantizer* qv, float zs, float* parts, int nc, int pc, int tc,
+               const AppendIn& ap, hipStream_t s)
 {
     // value widths 1..4 with keys of 1..4 bits, 3, 4 and 8 with any key width
     switch (bv) {
-        case 1: if constexpr (BK <= 4) launch_mfma<D, BK, QJL, 1>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
-        case 2: if constexpr (BK <= 4) launch_mfma<D, BK, QJL, 2>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
-        case 3: launch_mfma<D, BK, QJL, 3>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
-        case 4: launch_mfma<D, BK, QJL, 4>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
-        default: launch_mfma<D, BK, QJL, 8>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, tc, s); break;
+        case 1: if constexpr (BK <= 4) launch_mfma<D, BK, QJL, 1>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, pc, tc, ap, s); break;
+        case 2: if constexpr (BK <= 4) launch_mfma<D, BK, QJL, 2>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, pc, tc, ap, s); break;
+        case 3: launch_mfma<D, BK, QJL, 3>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, pc, tc, ap, s); break;
+        case 4: launch_mfma<D, BK, QJL, 4>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, pc, tc, ap, s); break;
+        default: launch_mfma<D, BK, QJL, 8>(k, v, ns, T, stride, G, fr, qk, qv, zs, parts, nc, pc, tc, ap, s); break;
     }
 }
 
@@ -1163,7 +1357,8 @@ void launch_scores_k(const tq_packed* k, int64_t n_keys, const half8_t* fr, int6
 
 int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
                        const tq_packed* v, int64_t n_streams, int64_t T, int64_t stride, int G, const void* q,
-                       int q_dtype, float zscale, float* parts, int n_chunks, int tc, hipStream_t s)
+                       int q_dtype, float zscale, float* parts, int n_chunks, int pchunks, int tc,
+                       const AppendIn& ap, hipStream_t s)
 {
     constexpr int D = 128;
     const bool qjl = qk->qjl_m != 0;
@@ -1172,22 +1367,22 @@ int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_
                     (long long)n_streams, n_chunks);
     const QueryIn fr{q, q_dtype == TQ_F16 ? 1 : 0};
     switch (qk->mse_bits) {
-        case 1: qjl ? launch_bv<D, 1, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
-                    : launch_bv<D, 1, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
-        case 2: qjl ? launch_bv<D, 2, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
-                    : launch_bv<D, 2, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
-        case 3: qjl ? launch_bv<D, 3, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
-                    : launch_bv<D, 3, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
-        case 4: qjl ? launch_bv<D, 4, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
-                    : launch_bv<D, 4, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
-        case 5: qjl ? launch_bv<D, 5, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
-                    : launch_bv<D, 5, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
-        case 6: qjl ? launch_bv<D, 6, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
-                    : launch_bv<D, 6, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
-        case 7: qjl ? launch_bv<D, 7, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
-                    : launch_bv<D, 7, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
-        default: qjl ? launch_bv<D, 8, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s)
-                     : launch_bv<D, 8, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, tc, s); break;
+        case 1: qjl ? launch_bv<D, 1, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, pchunks, tc, ap, s)
+                    : launch_bv<D, 1, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, pchunks, tc, ap, s); break;
+        case 2: qjl ? launch_bv<D, 2, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, pchunks, tc, ap, s)
+                    : launch_bv<D, 2, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, pchunks, tc, ap, s); break;
+        case 3: qjl ? launch_bv<D, 3, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, pchunks, tc, ap, s)
+                    : launch_bv<D, 3, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, pchunks, tc, ap, s); break;
+        case 4: qjl ? launch_bv<D, 4, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, pchunks, tc, ap, s)
+                    : launch_bv<D, 4, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, pchunks, tc, ap, s); break;
+        case 5: qjl ? launch_bv<D, 5, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, pchunks, tc, ap, s)
+                    : launch_bv<D, 5, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, pchunks, tc, ap, s); break;
+        case 6: qjl ? launch_bv<D, 6, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, pchunks, tc, ap, s)
+                    : launch_bv<D, 6, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, pchunks, tc, ap, s); break;
+        case 7: qjl ? launch_bv<D, 7, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, pchunks, tc, ap, s)
+                    : launch_bv<D, 7, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, pchunks, tc, ap, s); break;
+        default: qjl ? launch_bv<D, 8, true>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, pchunks, tc, ap, s)
+                     : launch_bv<D, 8, false>(qv->mse_bits, k, v, n_streams, T, stride, G, fr, qk, qv, zscale, parts, n_chunks, pchunks, tc, ap, s); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TQ_ERR_DEVICE, "tq_decode_attn: %s", hipGetErrorString(e));

@@ -352,10 +352,14 @@ size_t scores_ws(const tq_quantizer* q, int64_t n_q)
     return up256((size_t)n_q * q->d * 4) + up256((size_t)n_q * (q->qjl_m ? q->qjl_m : 1) * 4);
 }
 
-DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G, bool wide)
+DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G, bool wide, bool append)
 {
     DecodePlan p{};
     p.mfma = qk->d == 128 && G <= 8 && !wide;
+    p.fused_append = p.mfma && append;
+    // with the fused append the blocks scan the T - 1 cached tokens (at least
+    // one block per stream, which also quantizes the new token)
+    const int64_t Ts = p.fused_append ? (T - 1 > 1 ? T - 1 : 1) : T;
     if (p.mfma) {
         // spread the n_streams * T tokens over at most kDecodeSlots equal chunks
         // (multiples of 128 tokens: four waves of 32-token steps). With more
@@ -374,19 +378,20 @@ DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int
                 }
             }
         }
-        int64_t tc = (T + per - 1) / per;
+        int64_t tc = (Ts + per - 1) / per;
         tc = (tc + 127) / 128 * 128;
         p.tc = tc;
     } else {
         p.tc = 256;  // the scalar kernel handles one token per thread
     }
-    p.n_chunks = (int)((T + p.tc - 1) / p.tc);
+    p.n_chunks = (int)((Ts + p.tc - 1) / p.tc);
+    p.pchunks = p.n_chunks + (p.fused_append ? 1 : 0);
     const size_t nq = (size_t)n_streams * G;
     // prepared queries (scalar kernels; the MFMA kernel prepares its own), then partials
     p.off_qr = 0;
     p.off_p = p.mfma ? 0 : up256(nq * qk->d * 4);
     p.off_parts = p.off_p + (p.mfma ? 0 : up256(nq * (qk->qjl_m ? qk->qjl_m : 1) * 4));
-    p.total = p.off_parts + up256((size_t)n_streams * p.n_chunks * G * part_stride(qk->d) * 4);
+    p.total = p.off_parts + up256((size_t)n_streams * p.pchunks * G * part_stride(qk->d) * 4);
     return p;
 }
 
@@ -409,9 +414,12 @@ size_t tq_workspace_size(int op, const tq_quantizer* qk, int64_t n_a, int64_t n_
     if (op == TQ_OP_DECODE_ATTN) {
         if (G < 1 || G > 16 || n_b < 1) return 0;
         // the value width is not an argument: enough for either kernel family
+        // also the decode step's plan (n_b tokens with the new one)
         const size_t a = tq::decode_plan(qk, n_a, n_b, G, false).total;
         const size_t b = tq::decode_plan(qk, n_a, n_b, G, true).total;
-        return a > b ? a : b;
+        const size_t c = tq::decode_plan(qk, n_a, n_b, G, false, true).total;
+        const size_t ab = a > b ? a : b;
+        return ab > c ? ab : c;
     }
     return 0;
 }

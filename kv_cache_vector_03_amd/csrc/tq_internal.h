@@ -35,16 +35,22 @@ constexpr int kDecodeSlots = 512;
 
 struct DecodePlan {
     bool mfma;          // MFMA kernel (d = 128, G <= 8, mfma_decode_widths); else a scalar kernel
+    bool fused_append;  // decode step on the MFMA kernel: the new token is quantized inside it
     int64_t tc;         // tokens per block
     int n_chunks;       // blocks per stream
+    int pchunks;        // partials per stream: n_chunks, plus the new token's with fused_append
     size_t off_qr, off_p, off_parts, total;
 };
 // Key and value code widths the MFMA decode kernel takes (d = 128, G <= 8):
 // values of 1..4 bits with keys of 1..4 bits, values of 3, 4 or 8 bits with
 // any key width. Other pairs run on the scalar kernels.
 inline bool mfma_decode_widths(int bk, int bv) { return bv == 3 || bv == 4 || bv == 8 || (bk <= 4 && bv <= 4); }
-// wide: a width pair the MFMA kernel does not take (mfma_decode_widths false)
-DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G, bool wide);
+// wide: a width pair the MFMA kernel does not take (mfma_decode_widths false).
+// append: a decode step over T tokens whose last one is being appended; on the
+// MFMA kernel the blocks then scan the T - 1 cached tokens and the new token
+// becomes one more partial per stream.
+DecodePlan decode_plan(const tq_quantizer* qk, int64_t n_streams, int64_t T, int G, bool wide,
+                       bool append = false);
 
 // Fixed scratch of tq_decode_attn_noalloc: a static device array of this many
 // bytes per device, in place of a caller workspace.
@@ -89,9 +95,29 @@ int launch_decode(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packe
 // d = 128: query fragments into `frags` (scores_frag_bytes(q, n_q)), then the MFMA score kernel
 int launch_scores_mfma(const tq_quantizer* q, const tq_packed* k, int64_t n_keys, const void* queries,
                        int q_dtype, int64_t n_q, float* scores, void* frags, hipStream_t s);
+// The MFMA decode kernel's in-kernel append (the decode step): the first
+// block of each stream quantizes the stream's new key and value into slot
+// `pos` and writes the new token's partial (index n_chunks of the stream).
+struct AppendIn {
+    const void* k_new;  // [n_streams][128] rows, or null: no append
+    const void* v_new;
+    int f16;            // rows are fp16 (else fp32)
+    int64_t pos;
+    const uint32_t* vdiag;
+    const float* kbound;
+    const float* vbound;
+    uint32_t* kcodes;
+    uint32_t* ksigns;
+    uint16_t* knorm;
+    uint16_t* krnorm;
+    uint32_t* vcodes;
+    uint16_t* vnorm;
+};
+// pchunks: partials per stream in `parts` (n_chunks, plus one with an append)
 int launch_decode_mfma(const tq_quantizer* qk, const tq_quantizer* qv, const tq_packed* k,
                        const tq_packed* v, int64_t n_streams, int64_t T, int64_t stride, int G, const void* q,
-                       int q_dtype, float zscale, float* parts, int n_chunks, int tc, hipStream_t s);
+                       int q_dtype, float zscale, float* parts, int n_chunks, int pchunks, int tc,
+                       const AppendIn& ap, hipStream_t s);
 
 // scalar kernels with run-time code widths 1..8 (tq_wide.hip): quantize and
 // dequantize for widths 5..8 (and shapes the tuned kernels do not take), scores

@@ -130,10 +130,13 @@ def test_decode_zero_and_large_norm_tokens():
 
 STEP = [
     # d, kb, vb, ns, T, cap, G, k_qjl, new-token dtype
-    (128, 2, 4, 3, 300, 320, 8, True, np.float16),   # MFMA path: append blocks in the query prep
+    (128, 2, 4, 3, 300, 320, 8, True, np.float16),   # MFMA path: the append inside the decode kernel
     (128, 2, 3, 2, 0, 4, 8, True, np.float32),       # empty caches: attend over the new token only
     (128, 3, 3, 2, 1000, 1001, 4, False, np.float16),  # last slot; codes-only keys
     (128, 2, 4, 2, 2047, 4096, 8, True, np.float16),  # T + 1 = 2048: full steps only
+    (128, 6, 8, 2, 500, 640, 8, True, np.float32),   # 6-bit keys, 8-bit values: codes by binary search
+    (128, 2, 4, 8, 20000, 20480, 8, True, np.float16),  # 8 streams, many blocks per stream
+    (128, 1, 2, 5, 129, 200, 3, True, np.float16),   # 1-bit keys, 2-bit values, G = 3
     (64, 2, 3, 2, 200, 260, 8, True, np.float32),    # d = 64: separate append kernel
     (128, 2, 4, 2, 130, 200, 16, True, np.float16),  # G = 16: separate append kernel
 ]
