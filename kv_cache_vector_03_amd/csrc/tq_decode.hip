@@ -191,13 +191,18 @@ __device__ void fill_key_luts(uint2* klut4, uint32_t* klut2, uint4* slut, const 
         }
 }
 
-// fill_key_luts from fp16 centroids already in LDS (kc16[code]).
+// fill_key_luts from fp16 centroids already in LDS (kc16[code]), by the 256
+// threads of a block (fixed trip counts, so the reads of an entry issue ahead
+// of the writes).
 template <int BK, bool QJL>
 __device__ void fill_key_luts_lds(uint2* klut4, uint32_t* klut2, uint4* slut, const uint16_t* kc16, bool codes)
 {
     constexpr bool K4 = BK <= 2;
     constexpr int KLUT = key_lut_entries(BK);
-    for (int i = threadIdx.x; codes && i < KLUT; i += blockDim.x) {
+#pragma unroll
+    for (int k = 0; k < (KLUT + 255) / 256; ++k) {
+        const int i = (int)threadIdx.x + 256 * k;
+        if (!codes || i >= KLUT) continue;
         if constexpr (K4) {
             uint32_t h[4];
 #pragma unroll
@@ -209,14 +214,14 @@ __device__ void fill_key_luts_lds(uint2* klut4, uint32_t* klut2, uint4* slut, co
             klut2[i] = (uint32_t)kc16[i] * 0x10001u;
         }
     }
-    if constexpr (QJL)
-        for (int i = threadIdx.x; i < 256; i += blockDim.x) {
-            uint32_t w[4];
+    if constexpr (QJL) {
+        const int i = (int)threadIdx.x;  // sign byte i
+        uint32_t w[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                w[j] = (((i >> (2 * j)) & 1) ? 0x3C00u : 0xBC00u) | ((((i >> (2 * j + 1)) & 1) ? 0x3C00u : 0xBC00u) << 16);
-            slut[i] = make_uint4(w[0], w[1], w[2], w[3]);
-        }
+        for (int j = 0; j < 4; ++j)
+            w[j] = (((i >> (2 * j)) & 1) ? 0x3C00u : 0xBC00u) | ((((i >> (2 * j + 1)) & 1) ? 0x3C00u : 0xBC00u) << 16);
+        slut[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
 }
 
 // A operand of code group t of a key (8 codes, 8 BK bits at bit 8 BK t of
@@ -650,21 +655,30 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
         if constexpr (BV <= 4) return (uint32_t)cb16[1][e & ((1 << BV) - 1)] | ((uint32_t)cb16[1][e >> BV] << 16);
         else return (uint32_t)cb16[1][e] * 0x10001u;
     };
+    // Fixed trip counts throughout, so that the codebook reads of all of a
+    // thread's entries issue ahead of its table writes.
     if constexpr (ROWS) {
-        // the row tables: 16 uint4 per row, 8 of value copies and 8 of key copies
-        for (int i = tid; i < 256 * 16; i += 256) {
-            const int e = i >> 4, qq = i & 15;
-            if (qq < 8) {
-                if (e < VLUT) {
-                    const uint32_t v = ventry(e);
-                    reinterpret_cast<uint4*>(&rows[e][0])[qq] = make_uint4(v, v, v, v);
-                }
-            } else if constexpr (PK) {
+        // the row tables: 16 uint4 per row, 8 of value copies and 8 of key copies;
+        // thread t writes uint4 t % 8 of both halves of rows t / 8 + 32 k, a wave
+        // eight half-rows per instruction
+        const int qq = tid & 7;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int e = (tid >> 3) + 32 * k;
+            if (e < VLUT) {
+                const uint32_t v = ventry(e);
+                reinterpret_cast<uint4*>(&rows[e][0])[qq] = make_uint4(v, v, v, v);
+            }
+        }
+        if constexpr (PK) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int e = (tid >> 3) + 32 * k;
                 uint32_t h[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) h[j] = cb16[0][(e >> (2 * j)) & 3];
                 const uint32_t x = h[0] | (h[1] << 16), y = h[2] | (h[3] << 16);
-                reinterpret_cast<uint4*>(&rows[e][0])[qq] = make_uint4(x, y, x, y);
+                reinterpret_cast<uint4*>(&rows[e][0])[8 + qq] = make_uint4(x, y, x, y);
             }
         }
         fill_key_luts_lds<BK, QJL>(klut4, klut2, slut, cb16[0], !PK);
@@ -672,17 +686,22 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
         fill_key_luts_lds<BK, QJL>(klut4, klut2, slut, cb16[0], true);
         if constexpr (V12) {
             // entry aa | bb << 6: (codes aa & 7, bb & 7) for the even tile, (aa >> 3, bb >> 3) for the odd one
-            for (int i = tid; i < 4096; i += 256) {
-                const int aa = i & 63, bb = i >> 6;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int i = tid + 256 * k, aa = i & 63, bb = i >> 6;
                 vlut12[i] = (uint32_t)cb16[1][aa & 7] | ((uint32_t)cb16[1][bb & 7] << 16);
                 vlut12[kV12Odd + i] = (uint32_t)cb16[1][aa >> 3] | ((uint32_t)cb16[1][bb >> 3] << 16);
             }
         } else {
             // value table: entry e in all 32 copies; a wave writes 8 entries' 128-byte
             // rows per instruction
-            for (int i = tid; i < VLUT * 8; i += 256) {
-                const uint32_t v = ventry(i >> 3);
-                reinterpret_cast<uint4*>(&vlut[i >> 3][0])[i & 7] = make_uint4(v, v, v, v);
+#pragma unroll
+            for (int k = 0; k < (VLUT * 8 + 255) / 256; ++k) {
+                const int i = tid + 256 * k;
+                if (i < VLUT * 8) {
+                    const uint32_t v = ventry(i >> 3);
+                    reinterpret_cast<uint4*>(&vlut[i >> 3][0])[i & 7] = make_uint4(v, v, v, v);
+                }
             }
         }
     }
