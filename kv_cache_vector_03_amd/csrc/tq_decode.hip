@@ -541,8 +541,10 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
     // query preparation inputs of the item's stream: heads wid and wid + 4 (two
     // coordinates per lane each; heads past G read as zero) and this wave's two
     // 16-row tiles of S for the projection (MFMA A operands, 8 per lane)
-    __shared__ __align__(16) float qs[8][D];      // q' = H D q / sqrt(d), per head
-    __shared__ __align__(16) float ps[QJL ? 8 : 1][D];  // p = S q', per head
+    // rows padded by 4 floats: the fragment reads take the same offset of eight
+    // heads' rows at once, which then fall in eight different bank groups
+    __shared__ __align__(16) float qs[8][D + 4];             // q' = H D q / sqrt(d), per head
+    __shared__ __align__(16) float ps[QJL ? 8 : 1][D + 4];  // p = S q', per head
     uint32_t qw[2][2];  // raw query words (fp32 bits, or the 32-bit word holding the fp16 value)
     uint4 sA[QJL ? 2 : 1][4];
     uint32_t dm[2];
