@@ -433,6 +433,21 @@ __device__ __forceinline__ void append_store_codes(int c0, int c1, int lane, uns
     }
 }
 
+// Issue priority of a scanning wave from its progress (steps done of its
+// range): 3 in the first quarter down to 0 in the last. Two blocks share a
+// compute unit and the arbiter favours the older waves on ties; with these
+// levels a wave that has fallen behind wins the ties instead (measured: the
+// block dispatched second trailed the first by 5.3 us at the 128K shape
+// without them, 2.4 us with them, and the call ended about 1 us earlier).
+__device__ __forceinline__ void progress_prio(int64_t done, int64_t total)
+{
+    const int q = total > 0 ? (int)((4 * done) / total) : 4;
+    if (q <= 0) __builtin_amdgcn_s_setprio(3);
+    else if (q == 1) __builtin_amdgcn_s_setprio(2);
+    else if (q == 2) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
 template <int D, int BK, bool QJL, int BV>
 __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restrict__ kcodes,
                                                      const uint32_t* __restrict__ ksigns,
@@ -1085,6 +1100,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
             // steady state: steps i (sa, za) and i + 1 (sb); steps i + 2 and i + 3 exist
             for (; i + 3 < nfull; i += 2) {
                 const int64_t tb = w0 + 32 * i;
+                progress_prio(i, nfull);
                 issue_scores(sb, rw);
                 softmax_check(za);
                 accumulate(sa, za);
@@ -1126,6 +1142,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_mfma(const uint32_t* __restri
             accumulate(sa, za);
         }
 
+        __builtin_amdgcn_s_setprio(0);
         // ---- per-wave results: sum over the tile pair and the row groups, hi rows +
         // lo rows (permlane swaps)
         lsum += xor8(lsum);
