@@ -1292,25 +1292,46 @@ __global__ __launch_bounds__(256, 2) void k_scores_mfma(const uint32_t* __restri
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15, g = lane >> 4;
     const int64_t n_qt = (n_q + 7) / 8, n_qg = (n_qt + kScoreQT - 1) / kScoreQT, n_kt = (N + 15) / 16;
-    // packed inputs of one key tile for this lane: A row ka = k0 + col (clamped),
-    // norms of rows k0 + 4 g + r (clamped)
+    // packed inputs of one key tile for this lane: A row k0 + col, norms of rows
+    // k0 + 4 g + r. A tile inside the key range is read from a wave-uniform tile
+    // base plus fixed 32-bit lane offsets; only the last, partial tile clamps.
     struct KT {
         uint32_t kf[BK];
         uint32_t sf;
         uint16_t nk[4], ng[4];
     };
+    const int ko = col * KW + BK * g, so = col * SWN + g, no = 4 * g;
     auto load_kt = [&](KT& t, int64_t k0) {
-        const int64_t ka = min(k0 + col, N - 1);
+        if (k0 + 16 <= N) {
+            const uint32_t* kc = kcodes + k0 * KW;
 #pragma unroll
-        for (int w = 0; w < BK; ++w) t.kf[w] = kcodes[ka * KW + BK * g + w];
-        t.sf = QJL ? ksigns[ka * SWN + g] : 0u;
+            for (int w = 0; w < BK; ++w) t.kf[w] = kc[ko + w];
+            t.sf = QJL ? ksigns[k0 * SWN + so] : 0u;
+            const uint16_t* kn = knorm + k0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t kr = min(k0 + 4 * g + r, N - 1);
-            t.nk[r] = knorm[kr];
-            t.ng[r] = QJL ? krnorm[kr] : (uint16_t)0;
+            for (int r = 0; r < 4; ++r) {
+                t.nk[r] = kn[no + r];
+                t.ng[r] = QJL ? krnorm[k0 + no + r] : (uint16_t)0;
+            }
+        } else {
+            const int64_t ka = min(k0 + col, N - 1);
+#pragma unroll
+            for (int w = 0; w < BK; ++w) t.kf[w] = kcodes[ka * KW + BK * g + w];
+            t.sf = QJL ? ksigns[ka * SWN + g] : 0u;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t kr = min(k0 + 4 * g + r, N - 1);
+                t.nk[r] = knorm[kr];
+                t.ng[r] = QJL ? krnorm[kr] : (uint16_t)0;
+            }
         }
     };
+    // the wave takes key tiles in adjacent pairs (2 pr, 2 pr + 1), so the two
+    // 64-byte halves of each 128-byte line of a score row are written back to back
+    const int64_t pstep = (int64_t)gridDim.x * 4;
+    auto next_kt = [&](int64_t kt) { return (kt & 1) ? kt - 1 + 2 * pstep : kt + 1; };
+    const bool vec4 = (N & 3) == 0;
+    const int64_t lrow = (int64_t)(col & 7) * N + 4 * g;  // this lane's offset in a query tile's rows
     for (int64_t qg = blockIdx.y; qg < n_qg; qg += gridDim.y) {
         half8_t bq[kScoreQT][KSTEPS];
 #pragma unroll
@@ -1319,17 +1340,8 @@ __global__ __launch_bounds__(256, 2) void k_scores_mfma(const uint32_t* __restri
 #pragma unroll
             for (int k = 0; k < KSTEPS; ++k) bq[j][k] = frags[(qt * KSTEPS + k) * 64 + lane];
         }
-        // the wave takes key tiles in adjacent pairs (2 pr, 2 pr + 1), so the two
-        // 64-byte halves of each 128-byte line of a score row are written back to back
-        const int64_t pstep = (int64_t)gridDim.x * 4;
-        auto next_kt = [&](int64_t kt) { return (kt & 1) ? kt - 1 + 2 * pstep : kt + 1; };
-        int64_t kt = 2 * ((int64_t)blockIdx.x * 4 + wid);
-        KT cur;
-        if (kt < n_kt) load_kt(cur, kt * 16);
-        for (; kt < n_kt; kt = next_kt(kt)) {
-            const int64_t k0 = kt * 16;
-            KT nxt;
-            if (next_kt(kt) < n_kt) load_kt(nxt, next_kt(kt) * 16);
+        // the scores of one key tile against every query tile of the group
+        auto tile = [&](const KT& cur, int64_t k0) {
             half8_t ac[KS], as[QJL ? KS : 1];
 #pragma unroll
             for (int t = 0; t < KS; ++t) {
@@ -1342,6 +1354,7 @@ __global__ __launch_bounds__(256, 2) void k_scores_mfma(const uint32_t* __restri
                 fk[r] = h2f(cur.nk[r]);
                 fq[r] = QJL ? fk[r] * h2f(cur.ng[r]) * kappa : 0.f;
             }
+            const bool full = vec4 && k0 + 16 <= N;  // wave-uniform
 #pragma unroll
             for (int j = 0; j < kScoreQT; ++j) {
                 float4_t am = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
@@ -1357,10 +1370,12 @@ __global__ __launch_bounds__(256, 2) void k_scores_mfma(const uint32_t* __restri
                     z[r] = fk[r] * (am[r] + xor8(am[r]));
                     if constexpr (QJL) z[r] = fmaf(fq[r], aq[r] + xor8(aq[r]), z[r]);
                 }
-                const int64_t qrow = (qg * kScoreQT + j) * 8 + (col & 7);
-                if (col < 8 && qrow < n_q) {
-                    float* dst = scores + qrow * N + k0 + 4 * g;
-                    if ((N & 3) == 0 && k0 + 4 * g + 3 < N) {
+                // query row (qg kScoreQT + j) 8 + col (lanes col < 8): a wave-uniform
+                // tile base plus this lane's fixed offset
+                const int64_t q0 = (qg * kScoreQT + j) * 8;
+                if (col < 8 && q0 + col < n_q) {
+                    float* dst = scores + q0 * N + lrow + k0;
+                    if (full) {
                         // write-once output: streamed past the caches
                         __builtin_nontemporal_store(float4_t{z[0], z[1], z[2], z[3]}, reinterpret_cast<float4_t*>(dst));
                     } else {
@@ -1370,6 +1385,15 @@ __global__ __launch_bounds__(256, 2) void k_scores_mfma(const uint32_t* __restri
                     }
                 }
             }
+        };
+        // the next tile's loads go out before this one's work
+        int64_t kt = 2 * ((int64_t)blockIdx.x * 4 + wid);
+        KT cur;
+        if (kt < n_kt) load_kt(cur, kt * 16);
+        for (; kt < n_kt; kt = next_kt(kt)) {
+            KT nxt;
+            if (next_kt(kt) < n_kt) load_kt(nxt, next_kt(kt) * 16);
+            tile(cur, kt * 16);
             cur = nxt;
         }
     }
