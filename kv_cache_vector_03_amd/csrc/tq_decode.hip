@@ -38,6 +38,13 @@ __device__ __forceinline__ float xor8(float x)
 
 // Lanes of the upper half of each 16-lane row (bank_mask 0xC) or of the lower
 // half (0x3) take the value of lane i ^ 8; the others keep their own.
+// The same exchange with no old value: a row rotation reads a lane of every
+// row, so no lane keeps its old value and none needs one.
+__device__ __forceinline__ float ror8(float x)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
 template <int BANKS>
 __device__ __forceinline__ float take_xor8(float x)
 {
@@ -1367,8 +1374,8 @@ __global__ __launch_bounds__(256, 2) void k_scores_mfma(const uint32_t* __restri
                 float z[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    z[r] = fk[r] * (am[r] + xor8(am[r]));
-                    if constexpr (QJL) z[r] = fmaf(fq[r], aq[r] + xor8(aq[r]), z[r]);
+                    z[r] = fk[r] * (am[r] + ror8(am[r]));
+                    if constexpr (QJL) z[r] = fmaf(fq[r], aq[r] + ror8(aq[r]), z[r]);
                 }
                 // query row (qg kScoreQT + j) 8 + col (lanes col < 8): a wave-uniform
                 // tile base plus this lane's fixed offset
