@@ -111,7 +111,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = W.CONFIG5 if args.workload == "128k" else W.CONFIG3
+    cfg = W.KV_128K if args.workload == "128k" else W.KV_8K
     d, T, G, H = cfg.d, cfg.tokens, cfg.G, cfg.kv_heads
     layers = args.layers or cfg.layers
     diag_k, S, diag_v = W.quantizer_inputs(d)
@@ -353,7 +353,7 @@ def workload_8k(tq, dev, steps=10, warmup=2, replicas=5):
     import synth
     from synth import gpu as sgpu
     from synth import workloads as W
-    cfg = W.CONFIG3
+    cfg = W.KV_8K
     d, T, G, H, L = cfg.d, cfg.tokens, cfg.G, cfg.kv_heads, cfg.layers
     diag_k, S, diag_v = W.quantizer_inputs(d)
     qk = tq.Quantizer(d, cfg.k_mse_bits, d, diag_k, S, dev)
@@ -431,7 +431,7 @@ def small_keyset(tq, qk, dev, reps=50):
     beside the page's PyTorch timings (31.04 ms and 11.16 ms on a GB10)."""
     import torch
     from synth import workloads as W
-    keys, qs = W.config2_host()
+    keys, qs = W.outlier_keys_host()
     x = torch.from_numpy(keys).to(dev)
     q = torch.from_numpy(qs).to(dev)
     pk = tq.Packed.empty(qk, x.shape[0], dev)
@@ -726,7 +726,7 @@ def scores_only():
     from synth import workloads as W
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = W.CONFIG5
+    cfg = W.KV_128K
     d, T = cfg.d, cfg.tokens
     diag_k, S, _ = W.quantizer_inputs(d)
     qk = tq.Quantizer(d, cfg.k_mse_bits, d, diag_k, S, dev)

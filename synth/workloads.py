@@ -4,14 +4,14 @@ These stand in for the pages' workloads; no real model weights or datasets are
 used anywhere. Every tensor can be drawn on the host for any subset of vectors
 (``*_host``) or in full on the GPU (``*_device``), bit-identically.
 
-1 tiny       d=128, 1024 fp32 N(0,1) keys, 8 fp32 queries; keys 2-bit codes + 1-bit QJL.
-2 bench      d=128, 8192 fp16 N(0,1) keys with 4 seeded channels x20, 64 fp16 queries;
+tiny       d=128, 1024 fp32 N(0,1) keys, 8 fp32 queries; keys 2-bit codes + 1-bit QJL.
+outlier    d=128, 8192 fp16 N(0,1) keys with 4 seeded channels x20, 64 fp16 queries;
              keys 2-bit codes + QJL (the GB10 synthetic shape of the benchmark page).
-3 8K         36 layers x 2 KV heads x 8192 tokens x 128, fp16 K and V = N(0,1) times a
+8K model   36 layers x 2 KV heads x 8192 tokens x 128, fp16 K and V = N(0,1) times a
              per-(layer, head, channel) lognormal(0,1) scale; K 2-bit + QJL, V 3-bit;
              16 query heads per layer (G = 8), fp16 N(0,1).
-4 sweep      d in {64,128,256}, 2^20 normalised N(0,I) fp32 vectors.
-5 128K       one layer's share: 8 KV heads x 131072 tokens x 128, fp16 K/V with
+sweep      d in {64,128,256}, 2^20 normalised N(0,I) fp32 vectors.
+128K layer one layer's share: 8 KV heads x 131072 tokens x 128, fp16 K/V with
              per-channel lognormal scales, 80 layer instances (layer l draws from
              seed + l); K 2-bit + QJL, V 4-bit; 64 query heads per layer (G = 8).
 """
@@ -53,8 +53,8 @@ class KVConfig:
         return self.seed + layer if self.per_layer_seed else self.seed
 
 
-CONFIG3 = KVConfig("qwen2.5-3b-shaped 8K", 128, 36, 2, 8192, 8, 2, 3, 3003, False)
-CONFIG5 = KVConfig("llama-3.3-70b-shaped 128K, one layer's share", 128, 80, 8, 131072, 8, 2, 4,
+KV_8K = KVConfig("qwen2.5-3b-shaped 8K", 128, 36, 2, 8192, 8, 2, 3, 3003, False)
+KV_128K = KVConfig("llama-3.3-70b-shaped 128K, one layer's share", 128, 80, 8, 131072, 8, 2, 4,
                    5005, True)
 
 
@@ -64,16 +64,16 @@ def quantizer_inputs(d: int, seed: int = QUANT_SEED):
             diag_signs(seed, ROLE_DIAG_V, d))
 
 
-# ------------------------------------------------------------------ configs 1 and 2
+# ------------------------------------------------------------------ the two small key sets
 
-def config1_host():
+def tiny_keys_host():
     d = 128
     keys = to_f32(normals(1001, ROLE_DATA_K, np.arange(1024 * d)).reshape(1024, d))
     q = to_f32(normals(1001, ROLE_QUERY, np.arange(8 * d)).reshape(8, d))
     return keys, q
 
 
-def config2_host():
+def outlier_keys_host():
     d = 128
     sc = outlier_scales(2002, d)
     keys = to_f16(normals(2002, ROLE_DATA_K, np.arange(8192 * d)).reshape(8192, d) * sc[None, :])
@@ -81,7 +81,7 @@ def config2_host():
     return keys, q
 
 
-# ------------------------------------------------------------------ KV configs (3, 5)
+# ------------------------------------------------------------------ the KV-cache workloads
 
 def kv_scales(cfg: KVConfig, layer: int, role: int) -> np.ndarray:
     """lognormal scales [kv_heads, d] of one layer (float64)."""

@@ -1,8 +1,8 @@
 """GPU parity of the fused decode attention against the oracle (through the C ABI).
 
 Small cases cover ragged token counts around the chunk size, every supported
-head-group size range, all d and bit widths. The 8K (config 3) and 128K
-(config 5) workloads run at full size in the same launch configuration the
+head-group size range, all d and bit widths. The 8K-model and 128K-layer
+workloads run at full size in the same launch configuration the
 benchmark times; the oracle recomputes sampled streams one by one, both on
 the GPU's packed cache and on an oracle-packed copy of the stream.
 """
@@ -297,16 +297,16 @@ def _kv_case(cfg, layers, sample):
     return qkg, qvg, qko, qvo, Q
 
 
-def test_config3_full_one_call():
+def test_kv_8k_full_one_call():
     """All 36 layers in one call; one stream of every layer checked."""
-    cfg = W.CONFIG3
+    cfg = W.KV_8K
     _kv_case(cfg, list(range(cfg.layers)), [(l, l % cfg.kv_heads) for l in range(cfg.layers)])
 
 
-def test_config3_stream_oracle_packed():
+def test_kv_8k_stream_oracle_packed():
     """One whole 8K stream quantized by the oracle, decoded by the GPU kernel."""
     tq = tqmod()
-    cfg = W.CONFIG3
+    cfg = W.KV_8K
     d, T = cfg.d, cfg.tokens
     diag_k, S, diag_v = W.quantizer_inputs(d)
     qkg = tq.Quantizer(d, cfg.k_mse_bits, d, diag_k, S, DEV)
@@ -325,13 +325,13 @@ def test_config3_stream_oracle_packed():
                 what="8K stream, oracle-packed")
 
 
-def test_config5_layers_first_and_last():
+def test_kv_128k_layers_first_and_last():
     """Layers 0 and 79 in one call; all 16 streams checked."""
-    cfg = W.CONFIG5
+    cfg = W.KV_128K
     _kv_case(cfg, [0, 79], [(l, h) for l in (0, 79) for h in range(cfg.kv_heads)])
 
 
-def test_decode_step_config5_layer():
+def test_decode_step_kv_128k_layer():
     """The decode step at the 128K layer shape, in the launch configuration the
     benchmark times: 8 streams, tokens 0..131070 cached and token 131071 appended
     (inside the decode kernel, by the first of each stream's 64 blocks). The
@@ -339,7 +339,7 @@ def test_decode_step_config5_layer():
     unchanged, and the attention of the first and last stream over all 131072
     tokens matches the oracle on the cache as the GPU left it."""
     tq = tqmod()
-    cfg = W.CONFIG5
+    cfg = W.KV_128K
     d, T, G, H = cfg.d, cfg.tokens, cfg.G, cfg.kv_heads
     diag_k, S, diag_v = W.quantizer_inputs(d)
     qkg = tq.Quantizer(d, cfg.k_mse_bits, d, diag_k, S, DEV)

@@ -1,6 +1,6 @@
 """GPU parity of quantize, scores and dequantize against the oracle (through the C ABI).
 
-Sizes span several waves and blocks with ragged tails; configs 1 and 2 run in
+Sizes span several waves and blocks with ragged tails; the tiny 1024-key set and the 8192 outlier keys run in
 full. Scores are compared on identical packed inputs both ways: oracle-packed
 keys into both paths, and GPU-packed keys into both paths.
 """
@@ -139,8 +139,8 @@ def test_quantize_output_untouched_beyond_n():
     assert torch.all(p.norm[40:] == -1) and torch.all(p.rnorm[40:] == -1)
 
 
-def test_config1_full():
-    keys, q = W.config1_host()
+def test_tiny_1024_keys_full():
+    keys, q = W.tiny_keys_host()
     d = 128
     diag_k, S, _ = W.quantizer_inputs(d)
     tq = tqmod()
@@ -162,8 +162,8 @@ def test_config1_full():
                 what="scores on oracle-packed keys")
 
 
-def test_config2_full_and_determinism():
-    keys, q = W.config2_host()
+def test_outlier_8192_keys_full_and_determinism():
+    keys, q = W.outlier_keys_host()
     d = 128
     diag_k, S, _ = W.quantizer_inputs(d)
     tq = tqmod()
@@ -179,7 +179,7 @@ def test_config2_full_and_determinism():
     tq.tq_scores(qg, p, 8192, qd, sc)
     torch.cuda.synchronize()
     ref = oracle.scores(qo, to_oracle_packed(qo, host), q.astype(np.float64))
-    check_close(sc.cpu().numpy(), ref, what="config 2 scores")
+    check_close(sc.cpu().numpy(), ref, what="8192 outlier keys, scores")
     sc2 = torch.empty_like(sc)
     tq.tq_scores(qg, p, 8192, qd, sc2)
     torch.cuda.synchronize()
@@ -280,7 +280,7 @@ def test_synth_gpu_twin_matches_host():
     gpu.fill_f32(out, 77, synth.ROLE_DATA_K, first=12345)
     ref = synth.to_f32(synth.normals(77, synth.ROLE_DATA_K, np.arange(12345, 12345 + 100003)))
     assert np.array_equal(out.cpu().numpy(), ref)
-    cfg = W.CONFIG3
+    cfg = W.KV_8K
     layer = 17
     sc = gpu.scales_to_device(W.kv_seed_scales(cfg, layer, synth.ROLE_DATA_V), DEV)
     kv = torch.empty((cfg.kv_heads * cfg.tokens, cfg.d), dtype=torch.float16, device=DEV)
