@@ -1,7 +1,7 @@
 """GPU parity of quantize, scores and dequantize against the oracle (through the C ABI).
 
-Sizes span several waves and blocks with ragged tails; the tiny 1024-key set and the 8192 outlier keys run in
-full. Scores are compared on identical packed inputs both ways: oracle-packed
+Sizes span several waves and blocks with ragged tails; the tiny 1024-key set
+and the 8192 outlier keys run in full. Scores are compared on identical packed inputs both ways: oracle-packed
 keys into both paths, and GPU-packed keys into both paths.
 """
 import numpy as np
