@@ -14,6 +14,7 @@ import oracle
 import synth
 from synth import workloads as W
 
+from full_set import check_full_set
 from parity import check_close, check_quantize
 
 pytestmark = pytest.mark.gpu
@@ -239,7 +240,9 @@ def _runs(heads):
 
 
 def _kv_case(cfg, layers, sample):
-    """Generate, quantize and decode ``layers`` of cfg on the GPU; check sampled streams.
+    """Generate, quantize and decode ``layers`` of cfg on the GPU; every quantized
+    vector is checked against the definitions (check_full_set), and sampled
+    streams against the oracle.
 
     sample: list of (layer, head) streams recomputed by the oracle."""
     tq = tqmod()
@@ -264,6 +267,8 @@ def _kv_case(cfg, layers, sample):
                             pkd.norm[li * per_layer:(li + 1) * per_layer],
                             pkd.rnorm[li * per_layer:(li + 1) * per_layer] if pkd.rnorm is not None else None)
             tq.tq_quantize(qg, kbuf, sub)
+            # every vector of the layer's K (or V) against the definitions
+            check_full_set(qko if role == synth.ROLE_DATA_K else qvo, kbuf, sub)
         q_all.append(W.kv_queries_host(cfg, layer))
     Q = np.stack(q_all).reshape(nl * cfg.kv_heads, cfg.G, d)
     ns = nl * cfg.kv_heads

@@ -13,6 +13,7 @@ import synth
 from oracle import stats
 from synth import workloads as W
 
+from full_set import check_full_set
 from parity import TOL, check_close, check_quantize
 
 pytestmark = pytest.mark.gpu
@@ -337,13 +338,15 @@ def test_quantize_crowded_codebook(d, bits, dtype, m):
 SWEEP_PAGE_DIST = {(128, 3): 0.000270, (256, 3): 0.000135}   # the pages' Lloyd-Max table
 
 
+
 @pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("qjl", [False, True])
 def test_sweep_full_size(d, bits, qjl):
     """2^20 random unit vectors (normalised N(0, I), fp32) quantized in one call
     at total width `bits` (with QJL: bits - 1 code bits + the sketch). Checks:
-    2000 sampled vectors against the oracle (codes, signs, scalars); the
+    2000 sampled vectors against the oracle (codes, signs, scalars); every
+    vector against the definitions in fp64 on the device (check_full_set); the
     whole set's distortion per coordinate (from the codes-only reconstruction)
     against the distortion the oracle measures on the sample and, where the
     pages print it, against their value; and 1024 x 1024 scores on both
@@ -366,6 +369,9 @@ def test_sweep_full_size(d, bits, qjl):
     sub = tuple(None if a is None else a[rt].cpu().numpy().view(np.uint32 if a.dtype == torch.int32 else np.uint16)
                 for a in (p.codes, p.signs, p.norm, p.rnorm))
     _, _, ref = check_quantize(qo, xs, sub)
+    # and every one of the 2^20 vectors against the definitions
+    nbad = check_full_set(qo, x, p)
+    print(f"sweep d={d} bits={bits} qjl={qjl}: {nbad} code mismatches in the boundary window over {n * d} coordinates")
     # distortion per coordinate over all 2^20 vectors: ||x - x_hat||^2 / d with
     # the codes-only reconstruction (unit norms, orthogonal rotation)
     xh = torch.empty_like(x)
