@@ -303,9 +303,9 @@ def _kv_case(cfg, layers, sample):
 
 
 def test_kv_8k_full_one_call():
-    """All 36 layers in one call; one stream of every layer checked."""
+    """All 36 layers in one call; every one of the 72 streams checked."""
     cfg = W.KV_8K
-    _kv_case(cfg, list(range(cfg.layers)), [(l, l % cfg.kv_heads) for l in range(cfg.layers)])
+    _kv_case(cfg, list(range(cfg.layers)), [(l, h) for l in range(cfg.layers) for h in range(cfg.kv_heads)])
 
 
 def test_kv_8k_stream_oracle_packed():
