@@ -84,3 +84,38 @@ def check_full_set(qo, x, p, chunk=1 << 18):
     allowed = max(1, math.ceil(parity.WINDOW * n * d))
     assert bad_total <= allowed, f"{bad_total} code mismatches > {allowed}"
     return bad_total
+
+
+def scores_reference(qo, p, q, rows=None):
+    """The estimator s = n (<q', c[code]> + gamma sqrt(pi/2)/m <S q', 2 sign - 1>)
+    with q' = H (D q) / sqrt(d), in fp64 on the device, for packed keys p and
+    queries q [n_q, d] (all rows, or the slice `rows`)."""
+    d, B, m = qo.d, qo.bits, qo.m
+    dev = q.device
+    H = _hadamard(d, dev) / math.sqrt(d)
+    lane = torch.arange(d, device=dev)
+    dw = torch.from_numpy(qo.diag.astype(np.int64)).to(dev)
+    dsign = 1.0 - 2.0 * ((dw[lane >> 5] >> (lane & 31)) & 1).to(torch.float64)
+    cent = torch.from_numpy(qo.cent.astype(np.float64)).to(dev)
+    n = p.norm.view(torch.float16).to(torch.float64)
+    kv = n[:, None] * cent[_unpack_fields(p.codes, d // 8, B)]      # n c, rotated domain
+    qs = q if rows is None else q[rows]
+    qr = (qs.to(torch.float64) * dsign) @ H.T
+    out = qr @ kv.T
+    if m:
+        S = torch.from_numpy(qo.S.view(np.float16).astype(np.float64).reshape(m, d)).to(dev)
+        sg = 2.0 * _unpack_fields(p.signs, m // 8, 1).to(torch.float64) - 1.0
+        g = n * p.rnorm.view(torch.float16).to(torch.float64) * (math.sqrt(math.pi / 2.0) / m)
+        out += (qr @ S.T) @ (sg * g[:, None]).T
+    return out
+
+
+def check_scores_full(qo, p, q, sc, tol=parity.TOL, chunk=256):
+    """Every score of sc [n_q, n_keys] against scores_reference, within tol."""
+    worst = 0.0
+    for a in range(0, q.shape[0], chunk):
+        rows = torch.arange(a, min(a + chunk, q.shape[0]), device=q.device)
+        err = float((sc[rows].to(torch.float64) - scores_reference(qo, p, q, rows)).abs().max())
+        assert err <= tol, f"scores rows {a}..: max abs error {err:.3e} > {tol:.1e}"
+        worst = max(worst, err)
+    return worst

@@ -13,7 +13,7 @@ import synth
 from oracle import stats
 from synth import workloads as W
 
-from full_set import check_full_set
+from full_set import check_full_set, check_scores_full
 from parity import TOL, check_close, check_quantize
 
 pytestmark = pytest.mark.gpu
@@ -221,7 +221,8 @@ def test_scores_many_query_tiles_full(bits, m):
 def test_scores_prefill_scale_sampled():
     """The prefill-scale shape the benchmark times: 2048 queries against a
     131072-key compressed prefix (1 GiB of scores). Checked on whole sampled
-    query rows and on sampled key columns over all queries."""
+    query rows and on sampled key columns over all queries against the oracle,
+    and every score against the estimator restated in fp64 on the device."""
     tq = tqmod()
     d, n_q, n_keys = 128, 2048, 131072
     qg, qo = quantizers(d, 2, 128)
@@ -239,6 +240,9 @@ def test_scores_prefill_scale_sampled():
     cols = np.unique(np.linspace(0, n_keys - 1, 48).astype(np.int64))
     ref_cols = oracle.scores(qo, host.take(cols), q.astype(np.float64))
     check_close(sc[:, torch.from_numpy(cols).to(DEV)].cpu().numpy(), ref_cols, what="sampled key columns")
+    # and all 2^28 scores against the estimator restated in fp64 on the device
+    worst = check_scores_full(qo, p, torch.from_numpy(q).to(DEV), sc)
+    print(f"prefill-scale scores: all {n_q * n_keys} checked, max |score - reference| {worst:.2e}")
     del sc
 
 
