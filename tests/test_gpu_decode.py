@@ -336,16 +336,21 @@ def test_kv_128k_layers_first_and_last():
     _kv_case(cfg, [0, 79], [(l, h) for l in (0, 79) for h in range(cfg.kv_heads)])
 
 
-def test_decode_step_kv_128k_layer():
-    """The decode step at the 128K layer shape, in the launch configuration the
-    benchmark times: 8 streams, tokens 0..131070 cached and token 131071 appended
-    (inside the decode kernel, by the first of each stream's 64 blocks). The
-    appended slots match the oracle's quantizer, the rest of the caches is
-    unchanged, and the attention of the first and last stream over all 131072
-    tokens matches the oracle on the cache as the GPU left it."""
+@pytest.mark.parametrize("which", ["128k_layer", "8k_model"])
+def test_decode_step_full_size(which):
+    """The decode step at full size, in the launch configurations the benchmark
+    times: the 128K layer (8 streams, tokens 0..131070 cached and token 131071
+    appended; 4-bit values) and the 8K model in one call (all 36 layers, 72
+    streams of 8191 cached tokens plus the appended one; 3-bit values). The
+    append runs inside the decode kernel, in the first block of each stream.
+    The appended slots match the oracle's quantizer, the rest of the caches is
+    unchanged, and the attention of the first and last stream over all tokens
+    matches the oracle on the cache as the GPU left it."""
     tq = tqmod()
-    cfg = W.KV_128K
-    d, T, G, H = cfg.d, cfg.tokens, cfg.G, cfg.kv_heads
+    cfg = W.KV_128K if which == "128k_layer" else W.KV_8K
+    layers = [0] if which == "128k_layer" else list(range(cfg.layers))
+    d, T, G = cfg.d, cfg.tokens, cfg.G
+    H = cfg.kv_heads * len(layers)  # streams of the call
     diag_k, S, diag_v = W.quantizer_inputs(d)
     qkg = tq.Quantizer(d, cfg.k_mse_bits, d, diag_k, S, DEV)
     qvg = tq.Quantizer(d, cfg.v_bits, 0, diag_v, None, DEV)
@@ -353,11 +358,14 @@ def test_decode_step_kv_128k_layer():
     qvo = oracle.Quantizer(d, cfg.v_bits, 0, diag_v, None)
     from synth import gpu
     per = H * T
+    pl = cfg.kv_heads * T  # vectors per layer
     pk, pv = tq.Packed.empty(qkg, per, DEV), tq.Packed.empty(qvg, per, DEV)
     news = []
     for role, qg, pkd in ((synth.ROLE_DATA_K, qkg, pk), (synth.ROLE_DATA_V, qvg, pv)):
         X = torch.empty((per, d), dtype=torch.float16, device=DEV)
-        W.kv_layer_device(cfg, 0, role, X, gpu.scales_to_device(W.kv_seed_scales(cfg, 0, role), DEV))
+        for li, layer in enumerate(layers):
+            W.kv_layer_device(cfg, layer, role, X[li * pl:(li + 1) * pl],
+                              gpu.scales_to_device(W.kv_seed_scales(cfg, layer, role), DEV))
         tq.tq_quantize(qg, X, pkd)
         news.append(X.view(H, T, d)[:, T - 1].contiguous())
         del X
@@ -368,7 +376,7 @@ def test_decode_step_kv_128k_layer():
         a[sl_t] = -1
     torch.cuda.synchronize()
     before_k, before_v = pk.to_host(), pv.to_host()
-    Q = W.kv_queries_host(cfg, 0).reshape(H, G, d)
+    Q = np.stack([W.kv_queries_host(cfg, layer) for layer in layers]).reshape(H, G, d)
     out = torch.empty((H, G, d), dtype=torch.float32, device=DEV)
     tq.tq_decode_step(qkg, qvg, pk, pv, H, T - 1, T, G, news[0], news[1], torch.from_numpy(Q).to(DEV), out)
     torch.cuda.synchronize()
@@ -379,8 +387,9 @@ def test_decode_step_kv_128k_layer():
         if a is not None and a.size:
             assert np.array_equal(b[keep], a[keep]), "cache changed outside the appended slots"
     last = np.array([T - 1])
-    kx = np.concatenate([W.kv_vectors_host(cfg, 0, synth.ROLE_DATA_K, h, last) for h in range(H)]).astype(np.float64)
-    vx = np.concatenate([W.kv_vectors_host(cfg, 0, synth.ROLE_DATA_V, h, last) for h in range(H)]).astype(np.float64)
+    sh = [(layer, h) for layer in layers for h in range(cfg.kv_heads)]  # stream -> (layer, head)
+    kx = np.concatenate([W.kv_vectors_host(cfg, l, synth.ROLE_DATA_K, h, last) for l, h in sh]).astype(np.float64)
+    vx = np.concatenate([W.kv_vectors_host(cfg, l, synth.ROLE_DATA_V, h, last) for l, h in sh]).astype(np.float64)
     check_quantize(qko, kx, tuple(a[slots] for a in after_k))
     check_quantize(qvo, vx, tuple(a[slots] for a in after_v))
     o = out.cpu().numpy()
@@ -390,5 +399,5 @@ def test_decode_step_kv_128k_layer():
         gk = oracle.Packed(*(a[sl] for a in after_k))
         gv = oracle.Packed(after_v[0][sl], np.zeros((T, 0), np.uint32), after_v[2][sl], np.zeros(T, np.uint16))
         ref = oracle.decode_attn(qko, qvo, gk, gv, 1, T, G, Q[st:st + 1].astype(np.float64))
-        worst = max(worst, check_close(o[st:st + 1], ref, what=f"decode step, 128K stream {st}"))
-    print(f"128K decode step: appended slots checked, max |out - oracle| {worst:.2e}")
+        worst = max(worst, check_close(o[st:st + 1], ref, what=f"decode step, {which} stream {st}"))
+    print(f"{which} decode step: appended slots checked, max |out - oracle| {worst:.2e}")
