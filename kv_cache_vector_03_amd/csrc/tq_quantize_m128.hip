@@ -510,16 +510,18 @@ __global__ __launch_bounds__(256) void k_quantize_values_m128(const uint16_t* __
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int v = lane & 15, q = lane >> 4;
+    const int64_t step = (int64_t)gridDim.x * 64;  // vectors between a wave's batches
+    int64_t base = ((int64_t)blockIdx.x * 4 + wid) * 16;
+    // the first batch's loads go out before the tables are built (rows clamped
+    // to n - 1, so a wave past the end also reads in bounds)
+    uint4 cur[4];
+    load_clamped(cur, x, base + v, n, q);
     RotConsts rc;
     rot_consts(rc, diag, v, q);
     CodeConsts<B> cc;
     build_tables<B>(cc, cent, bnd, 1.0f, ctab, lut, &lut_bad, tbl);
 
-    const int64_t step = (int64_t)gridDim.x * 64;  // vectors between a wave's batches
-    int64_t base = ((int64_t)blockIdx.x * 4 + wid) * 16;
     if (base >= n) return;
-    uint4 cur[4];
-    load_clamped(cur, x, base + v, n, q);
     half8_t nh[4], nl[4];  // unused for values
     for (; base < n; base += step) {
         uint4 nxt[4];
@@ -582,27 +584,47 @@ __global__ __launch_bounds__(512) void k_quantize_keys_m128(const uint16_t* __re
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const bool late = wid >= 4;
     const int v = lane & 15, q = lane >> 4;
-    CodeConsts<B> cc;
-    build_tables<B>(cc, cent, bnd, kResUnit, ctab, lut, &lut_bad, tbl);
-    // A fragments: lane (row c, k-block kb) of fragment (ks, nu), element e
-    // holds S[proj_row(nu, c)][4 kb + ks + 16 e]
-    for (int e = threadIdx.x; e < KS * NT * 64; e += blockDim.x) {
+    const int64_t G = gridDim.x;
+    const int64_t first = (int64_t)blockIdx.x * 256;
+    auto pair_base = [&](int64_t k) { return ((k * G + blockIdx.x) * 8 + wid) * 32; };
+
+    // Set-up loads first, all in flight together: the wave's first pair of input
+    // batches (rows clamped to n - 1, so a block past the end also reads in
+    // bounds), its share of the S fragments, and the diagonal's signs; the tables
+    // are built while they arrive. A fragments: lane (row c, k-block kb) of
+    // fragment (ks, nu), element e holds S[proj_row(nu, c)][4 kb + ks + 16 e].
+    constexpr int kThreads = 512, kFragPer = KS * NT * 64 / kThreads;
+    static_assert(KS * NT * 64 % kThreads == 0, "fragment entries per thread");
+    uint4 inA[4], inB[4];
+    load_clamped(inA, x, pair_base(0) + v, n, q);
+    load_clamped(inB, x, pair_base(0) + 16 + v, n, q);
+    half8_t sf[kFragPer];
+#pragma unroll
+    for (int it = 0; it < kFragPer; ++it) {
+        const int e = (int)threadIdx.x + it * kThreads;
         const int ks = e / (NT * 64), nu = (e / 64) % NT, ln = e & 63;
         const int kb = ln >> 4, c = ln & 15;
         const uint16_t* row = S + (int64_t)m128_proj_row(nu, c) * kD;
-        half8_t f;
 #pragma unroll
-        for (int ee = 0; ee < 8; ++ee) f[ee] = __builtin_bit_cast(_Float16, row[4 * kb + ks + 16 * ee]);
-        sfrag[(ks * NT + nu) * 64 + ln] = f;
+        for (int ee = 0; ee < 8; ++ee) sf[it][ee] = __builtin_bit_cast(_Float16, row[4 * kb + ks + 16 * ee]);
+    }
+    RotConsts rc0;
+    if (wid == 0) rot_consts(rc0, diag, v, q);
+    CodeConsts<B> cc;
+    build_tables<B>(cc, cent, bnd, kResUnit, ctab, lut, &lut_bad, tbl);
+#pragma unroll
+    for (int it = 0; it < kFragPer; ++it) {
+        const int e = (int)threadIdx.x + it * kThreads;
+        const int ks = e / (NT * 64), nu = (e / 64) % NT, ln = e & 63;
+        sfrag[(ks * NT + nu) * 64 + ln] = sf[it];
     }
     if (wid == 0) {
-        RotConsts rc;
-        rot_consts(rc, diag, v, q);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) rot_a[t][lane] = rc.hA[t >> 1][t & 1];
+        for (int t = 0; t < 4; ++t) rot_a[t][lane] = rc0.hA[t >> 1][t & 1];
         if (v == 0)
 #pragma unroll
-            for (int a = 0; a < 4; ++a) rot_m[q][a] = make_uint4(rc.dm[a][0], rc.dm[a][1], rc.dm[a][2], rc.dm[a][3]);
+            for (int a = 0; a < 4; ++a)
+                rot_m[q][a] = make_uint4(rc0.dm[a][0], rc0.dm[a][1], rc0.dm[a][2], rc0.dm[a][3]);
     }
     __syncthreads();
     auto rotate_pair = [&](const uint4(&ia)[4], const uint4(&ib)[4], float4_t(&aa)[2][4], float4_t(&ab)[2][4],
@@ -622,17 +644,11 @@ __global__ __launch_bounds__(512) void k_quantize_keys_m128(const uint16_t* __re
         rotate_batch(ib, rc, ab, sb);
     };
 
-    const int64_t G = gridDim.x;
-    const int64_t first = (int64_t)blockIdx.x * 256;
     if (first >= n) return;  // the whole block: no barrier is left waiting
     const int64_t rounds = (n - first + G * 256 - 1) / (G * 256);
-    auto pair_base = [&](int64_t k) { return ((k * G + blockIdx.x) * 8 + wid) * 32; };
 
-    uint4 inA[4], inB[4];
     float4_t accA[2][4], accB[2][4];
     float ssA, ssB;
-    load_clamped(inA, x, pair_base(0) + v, n, q);
-    load_clamped(inB, x, pair_base(0) + 16 + v, n, q);
     rotate_pair(inA, inB, accA, accB, ssA, ssB);
     if (rounds > 1) {
         load_clamped(inA, x, pair_base(1) + v, n, q);
@@ -730,25 +746,41 @@ __global__ __launch_bounds__(256) void k_quantize_keys_m128_short(const uint16_t
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int v = lane & 15, q = lane >> 4;
-    CodeConsts<B> cc;
-    build_tables<B>(cc, cent, bnd, kResUnit, ctab, lut, &lut_bad, tbl);
-    // A fragments: lane (row c, k-block kb) of fragment (ks, nu), element e
-    // holds S[proj_row(nu, c)][4 kb + ks + 16 e]
-    for (int e = threadIdx.x; e < KS * NT * 64; e += 256) {
+    const int64_t step = (int64_t)gridDim.x * 64;  // vectors between a wave's batches
+    int64_t base = ((int64_t)blockIdx.x * 4 + wid) * 16;
+
+    // Set-up loads first, all in flight together: the wave's first two input
+    // batches (rows clamped to n - 1, so a wave past the end also reads in
+    // bounds) and the thread's share of the S fragments; the tables are built
+    // while they arrive. A fragments: lane (row c, k-block kb) of fragment
+    // (ks, nu), element e holds S[proj_row(nu, c)][4 kb + ks + 16 e].
+    constexpr int kThreads = 256, kFragPer = KS * NT * 64 / kThreads;
+    static_assert(KS * NT * 64 % kThreads == 0, "fragment entries per thread");
+    uint4 inA[4], inB[4];
+    load_clamped(inA, x, base + v, n, q);
+    load_clamped(inB, x, base + step + v, n, q);
+    half8_t sf[kFragPer];
+#pragma unroll
+    for (int it = 0; it < kFragPer; ++it) {
+        const int e = (int)threadIdx.x + it * kThreads;
         const int ks = e / (NT * 64), nu = (e / 64) % NT, ln = e & 63;
         const int kb = ln >> 4, c = ln & 15;
         const uint16_t* row = S + (int64_t)m128_proj_row(nu, c) * kD;
-        half8_t f;
 #pragma unroll
-        for (int ee = 0; ee < 8; ++ee) f[ee] = __builtin_bit_cast(_Float16, row[4 * kb + ks + 16 * ee]);
-        sfrag[(ks * NT + nu) * 64 + ln] = f;
+        for (int ee = 0; ee < 8; ++ee) sf[it][ee] = __builtin_bit_cast(_Float16, row[4 * kb + ks + 16 * ee]);
     }
-    __syncthreads();
     RotConsts rc;
     rot_consts(rc, diag, v, q);
+    CodeConsts<B> cc;
+    build_tables<B>(cc, cent, bnd, kResUnit, ctab, lut, &lut_bad, tbl);
+#pragma unroll
+    for (int it = 0; it < kFragPer; ++it) {
+        const int e = (int)threadIdx.x + it * kThreads;
+        const int ks = e / (NT * 64), nu = (e / 64) % NT, ln = e & 63;
+        sfrag[(ks * NT + nu) * 64 + ln] = sf[it];
+    }
+    __syncthreads();
 
-    const int64_t step = (int64_t)gridDim.x * 64;  // vectors between a wave's batches
-    int64_t base = ((int64_t)blockIdx.x * 4 + wid) * 16;
     if (base >= n) return;
     // one batch: rotation, codes and norms (stored), residual operands
     auto batch = [&](const uint4(&in)[4], int64_t b0, half8_t(&hi)[KS], half8_t(&lo)[KS]) {
@@ -759,9 +791,6 @@ __global__ __launch_bounds__(256) void k_quantize_keys_m128_short(const uint16_t
         code_batch<B, true>(acc, ss, cc, W, nrm, gam, hi, lo);
         store_coded<B, true>(W, nrm, gam, b0 + v, n, q, codes, norm, rnorm);
     };
-    uint4 inA[4], inB[4];
-    load_clamped(inA, x, base + v, n, q);
-    load_clamped(inB, x, base + step + v, n, q);
     for (; base < n; base += 2 * step) {
         const int64_t baseB = base + step;
         half8_t hiA[KS], loA[KS], hiB[KS], loB[KS];
