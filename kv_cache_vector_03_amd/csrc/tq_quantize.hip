@@ -101,6 +101,43 @@ __global__ __launch_bounds__(256) void k_quantize_quad(const void* __restrict__ 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int v = lane & 15, q = lane >> 4;
 
+    const unsigned char* xb = static_cast<const unsigned char*>(x);
+    unsigned char* st = stage[wid];
+
+    // coalesced loads of a pass's NV vectors per wave (16 bytes per lane per
+    // chunk); the next pass's chunks are in flight while a pass is processed.
+    // The first pass's loads and (for keys) the S gathers go out before the
+    // tables are built, so their latencies overlap.
+    const int64_t pstep = (int64_t)gridDim.x * (kWavesPerBlock * NV);
+    uint4 pre[CH];
+    auto fetch = [&](int64_t b0) {
+        const int64_t vb0 = b0 + (int64_t)wid * NV;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int off = (c * 64 + lane) * 16;
+            const int vec = off / (D * ES);
+            pre[c] = vb0 + vec < n ? *reinterpret_cast<const uint4*>(xb + (vb0 * D) * ES + off)
+                                   : make_uint4(0, 0, 0, 0);
+        }
+    };
+    fetch((int64_t)blockIdx.x * (kWavesPerBlock * NV));
+    // B fragments: lane (qq, nn) of fragment (t, nu) holds S[proj_row(nu, nn)][coord(qq, 8t + e)];
+    // a fixed trip count, so all of a thread's gathers are in flight together
+    constexpr int kFragPer = QJL ? KS * NT * 64 / 256 : 1;
+    static_assert(!QJL || KS * NT * 64 % 256 == 0, "fragment entries per thread");
+    half8_t sf[kFragPer];
+    if constexpr (QJL) {
+#pragma unroll
+        for (int it = 0; it < kFragPer; ++it) {
+            const int e = (int)threadIdx.x + it * 256;
+            const int t = e / (NT * 64), nu = (e / 64) % NT, ln = e & 63;
+            const int qq = ln >> 4, nn = ln & 15;
+            const uint16_t* row = S + (int64_t)Sh::proj_row(nu, nn) * D;
+#pragma unroll
+            for (int ee = 0; ee < 8; ++ee) sf[it][ee] = __builtin_bit_cast(_Float16, row[Sh::coord(qq, 8 * t + ee)]);
+        }
+    }
+
     float Mth[K > 0 ? K : 1], Cm[K + 1];
 #pragma unroll
     for (int j = 1; j <= K; ++j) Mth[j - 1] = bnd[L / 2 - 1 + j];
@@ -163,39 +200,14 @@ __global__ __launch_bounds__(256) void k_quantize_quad(const void* __restrict__ 
     }
 
     if constexpr (QJL) {
-        // B fragments: lane (qq, nn) of fragment (t, nu) holds S[proj_row(nu, nn)][coord(qq, 8t + e)]
-        for (int e = threadIdx.x; e < KS * NT * 64; e += 256) {
-            const int t = e / (NT * 64), nu = (e / 64) % NT, ln = e & 63;
-            const int qq = ln >> 4, nn = ln & 15;
-            const uint16_t* row = S + (int64_t)Sh::proj_row(nu, nn) * D;
-            half8_t f;
 #pragma unroll
-            for (int ee = 0; ee < 8; ++ee) {
-                const uint16_t h = row[Sh::coord(qq, 8 * t + ee)];
-                f[ee] = __builtin_bit_cast(_Float16, h);
-            }
-            bfrag[(t * NT + nu) * 64 + ln] = f;
+        for (int it = 0; it < kFragPer; ++it) {
+            const int e = (int)threadIdx.x + it * 256;
+            const int t = e / (NT * 64), nu = (e / 64) % NT, ln = e & 63;
+            bfrag[(t * NT + nu) * 64 + ln] = sf[it];
         }
     }
 
-    const unsigned char* xb = static_cast<const unsigned char*>(x);
-    unsigned char* st = stage[wid];
-
-    // coalesced loads of a pass's NV vectors per wave (16 bytes per lane per
-    // chunk); the next pass's chunks are in flight while a pass is processed
-    const int64_t pstep = (int64_t)gridDim.x * (kWavesPerBlock * NV);
-    uint4 pre[CH];
-    auto fetch = [&](int64_t b0) {
-        const int64_t vb0 = b0 + (int64_t)wid * NV;
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int off = (c * 64 + lane) * 16;
-            const int vec = off / (D * ES);
-            pre[c] = vb0 + vec < n ? *reinterpret_cast<const uint4*>(xb + (vb0 * D) * ES + off)
-                                   : make_uint4(0, 0, 0, 0);
-        }
-    };
-    fetch((int64_t)blockIdx.x * (kWavesPerBlock * NV));
     for (int64_t base = (int64_t)blockIdx.x * (kWavesPerBlock * NV); base < n; base += pstep) {
         const int64_t vb = base + (int64_t)wid * NV;
         // this pass's chunks into the wave's staging rows
