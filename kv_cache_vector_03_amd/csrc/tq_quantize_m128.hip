@@ -858,6 +858,25 @@ __global__ __launch_bounds__(256) void k_quantize_values_d256(const void* __rest
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int v = lane & 15, q = lane >> 4;
+    constexpr float sqrt_d = 16.0f;
+    const int64_t step = (int64_t)gridDim.x * 64;  // vectors between a wave's batches
+    int64_t base = ((int64_t)blockIdx.x * 4 + wid) * 16;
+    // one batch's input for lane (v, q): chunk a' holds coordinates 32 a' + 8 q .. + 7;
+    // rows past the end repeat the last row (not stored)
+    typedef float f8_t __attribute__((ext_vector_type(8)));
+    uint4 in16[F16 ? NA : 1];
+    f8_t in32[F16 ? 1 : NA];
+    auto load = [&](int64_t b0) {
+        const int64_t vec = b0 + v < n ? b0 + v : n - 1;
+#pragma unroll
+        for (int ap = 0; ap < NA; ++ap) {
+            if constexpr (F16) in16[ap] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + vec * D + 32 * ap + 8 * q);
+            else in32[ap] = *reinterpret_cast<const f8_t*>(static_cast<const float*>(x) + vec * D + 32 * ap + 8 * q);
+        }
+    };
+    // fp16 rows are issued before the tables are built (rows clamped, so in
+    // bounds); fp32 rows (twice the registers) after them, to keep two waves per SIMD
+    if constexpr (F16) load(base);
     CodeConsts<B> cc;
     build_tables<B>(cc, cent, bnd, 1.0f, ctab, lut, &lut_bad, tbl);
     // lane (row rho, k-block kb) of slab (tau, a'), element e: column c = 8 kb + e,
@@ -877,24 +896,8 @@ __global__ __launch_bounds__(256) void k_quantize_values_d256(const void* __rest
     }
     __syncthreads();
 
-    constexpr float sqrt_d = 16.0f;
-    const int64_t step = (int64_t)gridDim.x * 64;  // vectors between a wave's batches
-    int64_t base = ((int64_t)blockIdx.x * 4 + wid) * 16;
     if (base >= n) return;
-    // one batch's input for lane (v, q): chunk a' holds coordinates 32 a' + 8 q .. + 7;
-    // rows past the end repeat the last row (not stored)
-    typedef float f8_t __attribute__((ext_vector_type(8)));
-    uint4 in16[F16 ? NA : 1];
-    f8_t in32[F16 ? 1 : NA];
-    auto load = [&](int64_t b0) {
-        const int64_t vec = b0 + v < n ? b0 + v : n - 1;
-#pragma unroll
-        for (int ap = 0; ap < NA; ++ap) {
-            if constexpr (F16) in16[ap] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + vec * D + 32 * ap + 8 * q);
-            else in32[ap] = *reinterpret_cast<const f8_t*>(static_cast<const float*>(x) + vec * D + 32 * ap + 8 * q);
-        }
-    };
-    load(base);
+    if constexpr (!F16) load(base);
     for (; base < n; base += step) {
         // norm (the lane's 64 coordinates, then the four lanes of the vector)
         float ss = 0.f;
@@ -1031,6 +1034,38 @@ __global__ __launch_bounds__(512) void k_quantize_keys_d256(const void* __restri
     const int lane = threadIdx.x & 63;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int v = lane & 15, q = lane >> 4;
+    constexpr float sqrt_d = 16.0f;
+    const int64_t step = (int64_t)gridDim.x * 128;  // vectors between a wave's batches
+    int64_t base = ((int64_t)blockIdx.x * 8 + wid) * 16;
+    typedef float f8_t __attribute__((ext_vector_type(8)));
+    uint4 in16[F16 ? NA : 1];
+    f8_t in32[F16 ? 1 : NA];
+    auto load = [&](int64_t b0) {
+        const int64_t vec = b0 + v < n ? b0 + v : n - 1;
+#pragma unroll
+        for (int ap = 0; ap < NA; ++ap) {
+            if constexpr (F16) in16[ap] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + vec * D + 32 * ap + 8 * q);
+            else in32[ap] = *reinterpret_cast<const f8_t*>(static_cast<const float*>(x) + vec * D + 32 * ap + 8 * q);
+        }
+    };
+    // Set-up loads first, all in flight together: the wave's first batch (rows
+    // clamped to n - 1, so a wave past the end also reads in bounds) and the
+    // thread's share of the S fragments (a fixed trip count); the tables are
+    // built while they arrive. A fragments: lane (row c, k-block kb) of fragment
+    // (ks = 4 tau + r, nu), element e holds S[d256_proj_row(nu, c)][32 e + 16 tau + 4 kb + r].
+    constexpr int kThreads = 512, kFragPer = KS * NT * 64 / kThreads;
+    static_assert(KS * NT * 64 % kThreads == 0, "fragment entries per thread");
+    load(base);
+    half8_t sf[kFragPer];
+#pragma unroll
+    for (int it = 0; it < kFragPer; ++it) {
+        const int i = (int)threadIdx.x + it * kThreads;
+        const int ks = i / (NT * 64), nu = (i / 64) % NT, ln = i & 63;
+        const int c = ln & 15, kb = ln >> 4, tau = ks >> 2, r = ks & 3;
+        const uint16_t* row = S + (int64_t)d256_proj_row(nu, c) * D;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sf[it][e] = __builtin_bit_cast(_Float16, row[32 * e + 16 * tau + 4 * kb + r]);
+    }
     CodeConsts<B> cc;
     build_tables<B>(cc, cent, bnd, kResUnit, ctab, lut, &lut_bad, tbl);
     for (int i = threadIdx.x; i < 2 * NA * 64; i += blockDim.x) {
@@ -1046,35 +1081,11 @@ __global__ __launch_bounds__(512) void k_quantize_keys_d256(const void* __restri
         }
         slab[tau][ap][ln] = h;
     }
-    // A fragments: lane (row c, k-block kb) of fragment (ks = 4 tau + r, nu),
-    // element e holds S[d256_proj_row(nu, c)][32 e + 16 tau + 4 kb + r]
-    for (int i = threadIdx.x; i < KS * NT * 64; i += blockDim.x) {
-        const int ks = i / (NT * 64), nu = (i / 64) % NT, ln = i & 63;
-        const int c = ln & 15, kb = ln >> 4, tau = ks >> 2, r = ks & 3;
-        const uint16_t* row = S + (int64_t)d256_proj_row(nu, c) * D;
-        half8_t f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = __builtin_bit_cast(_Float16, row[32 * e + 16 * tau + 4 * kb + r]);
-        sfrag[i] = f;
-    }
+    for (int it = 0; it < kFragPer; ++it) sfrag[(int)threadIdx.x + it * kThreads] = sf[it];
     __syncthreads();
 
-    constexpr float sqrt_d = 16.0f;
-    const int64_t step = (int64_t)gridDim.x * 128;  // vectors between a wave's batches
-    int64_t base = ((int64_t)blockIdx.x * 8 + wid) * 16;
     if (base >= n) return;
-    typedef float f8_t __attribute__((ext_vector_type(8)));
-    uint4 in16[F16 ? NA : 1];
-    f8_t in32[F16 ? 1 : NA];
-    auto load = [&](int64_t b0) {
-        const int64_t vec = b0 + v < n ? b0 + v : n - 1;
-#pragma unroll
-        for (int ap = 0; ap < NA; ++ap) {
-            if constexpr (F16) in16[ap] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + vec * D + 32 * ap + 8 * q);
-            else in32[ap] = *reinterpret_cast<const f8_t*>(static_cast<const float*>(x) + vec * D + 32 * ap + 8 * q);
-        }
-    };
-    load(base);
     for (; base < n; base += step) {
         float ss = 0.f;
 #pragma unroll
